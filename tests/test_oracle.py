@@ -1,0 +1,366 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+None of these re-types the oracle's own formula: each checks it against an
+independent route (a library routine, a closed form, exhaustive enumeration,
+a rank-counting characterisation, Monte Carlo of the stated model) or against
+a value derived by hand (tests/golden).
+"""
+
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import topk as otopk
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _bf16_bits(t):
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def rank_count_topk(v, k):
+    """Element i is in the top-k iff (#greater) + (#equal with lower index) < k;
+    that count is also its output position.  An O(n^2) characterisation that
+    shares nothing with a sort."""
+    v = np.asarray(v, dtype=np.float64) + 0.0
+    n = v.shape[0]
+    pos = np.empty(n, dtype=np.int64)
+    for i in range(n):
+        pos[i] = int((v > v[i]).sum() + (v[:i] == v[i]).sum())
+    out = np.full(k, -1, dtype=np.int64)
+    for i in range(n):
+        if pos[i] < k:
+            out[pos[i]] = i
+    return out
+
+
+# ----------------------------------------------------------------- exact ----
+
+def test_exact_matches_rank_count_with_ties():
+    rng = np.random.default_rng(1)
+    alphabet = np.array([-1.0, -0.0, 0.0, 2.0], dtype=np.float32)
+    for n in range(1, 11):
+        for _ in range(20):
+            x = alphabet[rng.integers(0, 4, size=(1, n))]
+            for k in range(1, n + 1):
+                idx, vals = oracle.exact_topk(x, k, "f32")
+                np.testing.assert_array_equal(idx[0], rank_count_topk(x[0], k))
+                # values are the elements' own bit patterns (-0.0 stays -0.0)
+                np.testing.assert_array_equal(vals.view(np.uint32), x[0, idx[0]].view(np.uint32)[None])
+
+
+def test_exact_top1_is_first_argmax():
+    rng = np.random.default_rng(2)
+    x = rng.integers(0, 5, size=(50, 40)).astype(np.float32)
+    idx, _ = oracle.exact_topk(x, 1, "f32")
+    np.testing.assert_array_equal(idx[:, 0], np.argmax(x, axis=1))
+
+
+def test_exact_matches_torch_topk_on_distinct_values():
+    g = torch.Generator().manual_seed(3)
+    x = torch.randperm(5000, generator=g).reshape(5, 1000).to(torch.float32) - 2500.0
+    for k in (1, 7, 64, 1000):
+        idx, vals = oracle.exact_topk(x.numpy(), k, "f32")
+        tv, ti = torch.topk(x, k, dim=1, sorted=True)
+        np.testing.assert_array_equal(idx, ti.numpy())
+        np.testing.assert_array_equal(vals, tv.numpy())
+
+
+def test_exact_bf16_widening_and_order():
+    # bf16 bit patterns: the order must follow the real values, including
+    # negative numbers (whose raw bit patterns sort the other way) and infinities.
+    vals = torch.tensor([[1.5, -3.0, float("inf"), -0.0, 0.0, -float("inf"), 2.0, -0.5]])
+    bits = _bf16_bits(vals)
+    idx, out = oracle.exact_topk(bits, 8, "bf16")
+    np.testing.assert_array_equal(idx[0], [2, 6, 0, 3, 4, 7, 1, 5])
+    np.testing.assert_array_equal(out[0], bits[0, [2, 6, 0, 3, 4, 7, 1, 5]])
+
+
+def test_exact_rejects_nan():
+    x = np.array([[1.0, np.nan, 0.0]], dtype=np.float32)
+    with pytest.raises(AssertionError):
+        oracle.exact_topk(x, 1, "f32")
+
+
+def test_planted_tie_mistake_is_caught():
+    """A plausible mistake (ties to the HIGHER index) fails the rank pin."""
+    x = np.array([[1.0, 3.0, 3.0, 0.0, 3.0]], dtype=np.float32)
+    saved = otopk._rank_order
+    try:
+        otopk._rank_order = lambda vals, idx: np.lexsort((-idx, -vals))
+        idx, _ = oracle.exact_topk(x, 2, "f32")
+        assert not np.array_equal(idx[0], rank_count_topk(x[0], 2))
+    finally:
+        otopk._rank_order = saved
+    idx, _ = oracle.exact_topk(x, 2, "f32")
+    np.testing.assert_array_equal(idx[0], rank_count_topk(x[0], 2))
+
+
+# -------------------------------------------------------------- bucketed ----
+
+def test_fig2_toy_golden():
+    with open(os.path.join(HERE, "golden", "fig2_toy.json")) as f:
+        gd = json.load(f)
+    x = np.array([gd["x"]], dtype=np.float32)
+    n, k, b, kb = gd["n"], gd["k"], gd["b"], gd["kb"]
+    for r in range(b):
+        np.testing.assert_array_equal(oracle.bucket_members(n, b, r), gd["bucket_members"][r])
+    s1, _ = oracle.bucketed_topk(x, k, b, kb, False, "f32")
+    np.testing.assert_array_equal(s1[0], gd["stage1_idx"])
+    fin, _ = oracle.bucketed_topk(x, k, b, kb, True, "f32")
+    np.testing.assert_array_equal(fin[0], gd["final_idx"])
+    ex, _ = oracle.exact_topk(x, k, "f32")
+    np.testing.assert_array_equal(ex[0], gd["exact_idx"])
+    assert oracle.recall(fin, ex)[0] == gd["recall"]
+    assert Fraction(oracle.eq1(k, b, kb)).limit_denominator(1000) == Fraction(gd["eq1_numerator"], gd["eq1_denominator"])
+
+
+def test_bucketed_reduces_to_exact():
+    rng = np.random.default_rng(4)
+    x = rng.integers(0, 6, size=(6, 48)).astype(np.float32)  # many ties
+    n = 48
+    for k in (1, 5, 12):
+        ex, _ = oracle.exact_topk(x, k, "f32")
+        # one bucket holding everything
+        got, _ = oracle.bucketed_topk(x, k, 1, k, True, "f32")
+        np.testing.assert_array_equal(got, ex)
+        # every element is its own bucket
+        got, _ = oracle.bucketed_topk(x, k, n, 1, True, "f32")
+        np.testing.assert_array_equal(got, ex)
+        # k_b equal to the bucket size keeps every element as a candidate
+        for b in (2, 3, 8):
+            got, _ = oracle.bucketed_topk(x, k, b, n // b, True, "f32")
+            np.testing.assert_array_equal(got, ex)
+
+
+def test_bucketed_stage1_by_columns_and_rank_count():
+    """With b | n, bucket r is column r of x.reshape(n/b, b); its top-k_b by
+    the rank-count rule (ties to the lower row = lower index)."""
+    rng = np.random.default_rng(5)
+    n, b, kb = 60, 6, 3
+    x = rng.integers(0, 4, size=(4, n)).astype(np.float32)
+    got, _ = oracle.bucketed_topk(x, kb * b, b, kb, False, "f32")
+    for row in range(x.shape[0]):
+        cols = x[row].reshape(n // b, b)
+        for r in range(b):
+            local = rank_count_topk(cols[:, r], kb)
+            np.testing.assert_array_equal(got[row, r * kb:(r + 1) * kb], r + b * local)
+
+
+def test_bucketed_ragged_buckets():
+    rng = np.random.default_rng(6)
+    n, b, kb = 37, 5, 2  # b does not divide n: sizes 8, 8, 7, 7, 7
+    x = rng.standard_normal((3, n)).astype(np.float32)
+    got, _ = oracle.bucketed_topk(x, 8, b, kb, False, "f32")
+    for row in range(3):
+        for r in range(b):
+            members = np.arange(r, n, b)
+            local = rank_count_topk(x[row, members], kb)
+            np.testing.assert_array_equal(got[row, r * kb:(r + 1) * kb], members[local])
+
+
+def test_bucketed_invariants():
+    rng = np.random.default_rng(7)
+    m, n, b, k = 40, 256, 16, 32
+    x = rng.standard_normal((m, n)).astype(np.float32)
+    ex, _ = oracle.exact_topk(x, k, "f32")
+    prev = None
+    for kb in (2, 3, 4, 6):
+        cand, _ = oracle.bucketed_topk(x, k, b, kb, False, "f32")
+        fin, _ = oracle.bucketed_topk(x, k, b, kb, True, "f32")
+        for row in range(m):
+            s = set(cand[row].tolist())
+            if prev is not None:
+                assert prev[row] <= s  # candidates grow with k_b
+            # the k_b largest values of the row always survive
+            assert set(ex[row, :kb].tolist()) <= s
+        # the per-row identity R = sum_r min(k_b, t_r) / k
+        np.testing.assert_array_equal(oracle.recall(fin, ex), oracle.recall_by_bucket_counts(ex, n, b, kb))
+        prev = [set(c.tolist()) for c in cand]
+
+
+def test_bucketed_invariant_enforced():
+    x = np.zeros((1, 16), dtype=np.float32)
+    with pytest.raises(AssertionError):
+        oracle.bucketed_topk(x, 9, 4, 2, True, "f32")  # b * k_b = 8 < k
+    with pytest.raises(AssertionError):
+        oracle.bucketed_topk(x, 4, 4, 5, True, "f32")  # k_b > n / b
+
+
+# ------------------------------------------------------- recall models ----
+
+def test_eq1_closed_forms():
+    for k in (1, 4, 64, 512):
+        for b in (1, 2, 3, 64, 256):
+            # k_b = 1: (b/k) (1 - (1 - 1/b)^k)
+            assert oracle.eq1(k, b, 1) == pytest.approx(b / k * (1 - (1 - 1 / b) ** k), rel=1e-12, abs=1e-15)
+        for kb in range(1, min(k, 8) + 1):
+            assert oracle.eq1(k, 1, kb) == pytest.approx(kb / k, rel=1e-12)  # one bucket
+
+
+def _exact_model_expectation(k, b, kb):
+    """E[sum_r min(k_b, t_r)] / k over all b^k equally likely bucket labels."""
+    total = Fraction(0)
+    for labels in itertools.product(range(b), repeat=k):
+        t = np.bincount(labels, minlength=b)
+        total += int(np.minimum(t, kb).sum())
+    return total / (k * b ** k)
+
+
+@pytest.mark.parametrize("k,b,kb", [(4, 3, 2), (5, 2, 2), (6, 3, 1), (6, 2, 3), (7, 3, 2)])
+def test_eq1_exhaustive_model(k, b, kb):
+    exact = _exact_model_expectation(k, b, kb)
+    assert oracle.eq1(k, b, kb) == pytest.approx(float(exact), rel=1e-12)
+
+
+def test_eq1_monte_carlo_large():
+    rng = np.random.default_rng(8)
+    for k, b, kb in [(64, 64, 1), (64, 32, 2), (512, 512, 4)]:
+        reps = 4000
+        labels = rng.integers(0, b, size=(reps, k))
+        vals = np.array([np.minimum(np.bincount(l, minlength=b), kb).sum() / k for l in labels])
+        se = vals.std() / math.sqrt(reps)
+        assert abs(vals.mean() - oracle.eq1(k, b, kb)) < 5 * se + 1e-12
+
+
+def _exhaustive_finite(n, k, b, kb):
+    """Exact E[R] over all C(n, k) equally likely position sets of the top k."""
+    tot = Fraction(0)
+    cnt = 0
+    for pos in itertools.combinations(range(n), k):
+        t = np.bincount(np.array(pos) % b, minlength=b)
+        tot += int(np.minimum(t, kb).sum())
+        cnt += 1
+    return tot / (cnt * k)
+
+
+@pytest.mark.parametrize("n,k,b,kb", [(8, 3, 2, 1), (8, 4, 4, 1), (9, 4, 3, 2), (12, 5, 4, 2), (12, 6, 3, 3)])
+def test_eq1_finite_exhaustive(n, k, b, kb):
+    assert oracle.eq1_finite(n, k, b, kb) == pytest.approx(float(_exhaustive_finite(n, k, b, kb)), rel=1e-10)
+
+
+def test_eq1_finite_closed_form_kb1():
+    for n, k, b in [(4096, 64, 64), (131072, 64, 64), (1024, 100, 8)]:
+        s = n // b
+        ratio = 1.0  # C(n - s, k) / C(n, k) as a running product
+        for i in range(k):
+            ratio *= (n - s - i) / (n - i)
+        closed = b / k * (1 - ratio)
+        assert oracle.eq1_finite(n, k, b, 1) == pytest.approx(closed, rel=1e-9)
+
+
+def test_eq1_is_below_finite_expectation():
+    """Eq. (1) upper-bounds the expected recall error ("Core claim"); at the
+    configurations used here the finite-n expectation is at least Eq. (1)."""
+    for n, k, b, kb in [(4096, 64, 64, 1), (4096, 64, 32, 2), (131072, 64, 64, 1), (131072, 64, 128, 2),
+                        (32768, 512, 256, 2), (131072, 512, 512, 4), (1 << 20, 8192, 512, 16)]:
+        assert oracle.eq1_finite(n, k, b, kb) >= oracle.eq1(k, b, kb) - 1e-12
+
+
+def test_oracle_recall_monte_carlo_vs_finite():
+    """Run the bucketed oracle on iid rows: mean recall within sampling error
+    of the finite-n expectation."""
+    g = torch.Generator().manual_seed(9)
+    n, k, b, kb, reps = 512, 32, 16, 2, 300
+    x = torch.rand((reps, n), generator=g).numpy()
+    ex, _ = oracle.exact_topk(x, k, "f32")
+    fin, _ = oracle.bucketed_topk(x, k, b, kb, True, "f32")
+    r = oracle.recall(fin, ex)
+    se = r.std() / math.sqrt(reps)
+    assert abs(r.mean() - oracle.eq1_finite(n, k, b, kb)) < 5 * se
+
+
+@pytest.mark.parametrize("n,k,b,kb", [(8, 3, 2, 1), (8, 4, 2, 2), (9, 5, 3, 2), (12, 6, 4, 1), (12, 7, 3, 2)])
+def test_eq2_is_the_minimum_over_placements(n, k, b, kb):
+    worst = min(
+        np.minimum(np.bincount(np.array(pos) % b, minlength=b), kb).sum() / k
+        for pos in itertools.combinations(range(n), k)
+    )
+    assert oracle.eq2(n, k, b, kb) == pytest.approx(worst, abs=1e-15)
+
+
+def test_eq2_reached_on_planted_rows():
+    from top_sparse_attention_exact_amd import workloads
+
+    n, b, k, kb = 256, 16, 48, 4  # s = 16, top 48 fill residues {0, 1, 2}
+    x = workloads.rows_planted_residues(4, n, b, k, seed=0).numpy()
+    ex, _ = oracle.exact_topk(x, k, "f32")
+    assert set((ex[1] % b).tolist()) == {0, 1, 2}
+    fin, _ = oracle.bucketed_topk(x, k, b, kb, True, "f32")
+    r = oracle.recall(fin, ex)
+    assert r[1] == oracle.eq2(n, k, b, kb) == r[3]
+    assert r[1] == 3 * kb / k
+
+
+# ------------------------------------------------------------- decode ----
+
+def _decode_inputs(bsz, hq, hkv, length, d, seed):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn((bsz, hq, d), generator=g).to(torch.bfloat16)
+    kk = torch.randn((bsz, hkv, length, d), generator=g).to(torch.bfloat16)
+    vv = torch.randn((bsz, hkv, length, d), generator=g).to(torch.bfloat16)
+    return q, kk, vv
+
+
+def _bits(t):
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def test_decode_full_selection_is_dense_attention():
+    bsz, hq, hkv, length, d = 2, 4, 2, 64, 16
+    q, kk, vv = _decode_inputs(bsz, hq, hkv, length, d, 10)
+    scale = 1 / math.sqrt(d)
+    out, sel, _ = oracle.attn_decode(_bits(q), _bits(kk), _bits(vv), scale, length, 1, length)
+    g = hq // hkv
+    qf = q.to(torch.float64)[:, :, None, :]
+    kf = kk.to(torch.float64).repeat_interleave(g, dim=1)
+    vf = vv.to(torch.float64).repeat_interleave(g, dim=1)
+    ref = torch.nn.functional.scaled_dot_product_attention(qf, kf, vf, scale=scale)[:, :, 0, :]
+    np.testing.assert_allclose(out, ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_decode_single_key_is_argmax_row():
+    q, kk, vv = _decode_inputs(1, 2, 1, 50, 8, 11)
+    out, sel, s = oracle.attn_decode(_bits(q), _bits(kk), _bits(vv), 0.3, 1, 1, 1)
+    for h in range(2):
+        j = int(np.argmax(s[0, h]))
+        assert sel[0, h, 0] == j
+        np.testing.assert_array_equal(out[0, h], vv[0, 0, j].to(torch.float64).numpy())
+
+
+def test_decode_equal_scores_average_lowest_indices():
+    bsz, h, length, d = 1, 1, 40, 8
+    q = torch.zeros((bsz, h, d), dtype=torch.bfloat16)
+    _, kk, vv = _decode_inputs(bsz, h, h, length, d, 12)
+    out, sel, _ = oracle.attn_decode(_bits(q), _bits(kk), _bits(vv), 1.0, 10, 1, 10)
+    np.testing.assert_array_equal(sel[0, 0], np.arange(10))
+    np.testing.assert_allclose(out[0, 0], vv[0, 0, :10].to(torch.float64).mean(0).numpy(), rtol=1e-14)
+
+
+def test_decode_scores_against_fsum():
+    q, kk, _ = _decode_inputs(1, 2, 1, 5, 6, 13)
+    s = oracle.decode_scores(_bits(q), _bits(kk), 0.5)
+    qf, kf = q.to(torch.float64).numpy(), kk.to(torch.float64).numpy()
+    for h in range(2):
+        for j in range(5):
+            assert s[0, h, j] == 0.5 * math.fsum(qf[0, h] * kf[0, 0, j])
+
+
+def test_decode_bucketed_selection_contains_planted_keys():
+    from top_sparse_attention_exact_amd import workloads
+
+    q, kk, vv, planted = workloads.decode_mha(1, 2, 2048, 128, 16, 0.8, seed=1)
+    scale = 1 / math.sqrt(128)
+    out, sel, s = oracle.attn_decode(_bits(q), _bits(kk), _bits(vv), scale, 64, 16, 4)
+    for h in range(2):
+        assert set(planted[0, h].tolist()) <= set(sel[0, h].tolist())
+        # planted scores sit near 0.8 * sqrt(128)
+        assert np.all(s[0, h, planted[0, h].numpy()] > 7.0)
