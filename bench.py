@@ -1,0 +1,289 @@
+#!/usr/bin/env python3
+"""Benchmark of the top-k selection hot path on one MI355X.
+
+Workload (one "step"): the 256 x 131072 bf16 vocabulary-sampling batch
+(N(0, 2^2) logits, k = 64) through every selection mode of the path:
+exact top-64, bucketed (b, k_b) = (64, 1) without the final stage, and
+bucketed (128, 2) with the final exact top-64.  Inputs are resident in HBM
+before timing starts; each library call is bracketed by HIP events on the
+stream it runs on, after a 1 GiB write that evicts the L2 and Infinity Cache
+(timing protocol after the benchmark protocol printed with "Approximate
+Top-k for Increased Parallelism": warm-up, then events around each top-k
+launch queued behind a short spin kernel).
+
+The same run also times the sparse-attention decode steps (scoring, Top-K
+selection, softmax-V) of the two decode workloads, and times the CPU oracle
+on a bounded sample of the selection batch.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only MODE]
+"""
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "top-k score elements/s + HBM GB/s vs peak; recall vs Eq.(1); decode µs/step"
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", default="all", help="all | exact | b64k1 | b128k2 | mha | gqa")
+    ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between calls (warm numbers)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "top_sparse_attention_exact_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(name):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    the named kernel, if the kernel sources still hash the same."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.md" % name)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.strip().startswith("- "):
+            key, val = line.strip()[2:].split(":", 1)
+            fields[key.strip()] = val.strip().strip("`")
+    if fields.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    try:
+        return int(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class EventTimer:
+    """Times callables with HIP events on the current stream, behind a cache
+    flush and a short spin so that the events are queued before the work."""
+
+    def __init__(self, flush):
+        import torch
+
+        self.torch = torch
+        self.flush_buf = None if not flush else torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+    def run(self, calls, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            for _, fn in calls:
+                fn()
+        torch.cuda.synchronize()
+        pairs = {name: [] for name, _ in calls}
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            for name, fn in calls:
+                if self.flush_buf is not None:
+                    self.flush_buf.fill_(1)
+                torch.cuda._sleep(20000)
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                pairs[name].append((e0, e1))
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = {name: [a.elapsed_time(b) for a, b in v] for name, v in pairs.items()}
+        return ms, wall
+
+
+def selection_step(args, timer):
+    import numpy as np
+    import torch
+
+    import top_sparse_attention_exact_amd as atk
+    from top_sparse_attention_exact_amd import workloads
+
+    cfg = workloads.SELECTION["vocab-128k"]
+    m, n, k = cfg["m"], cfg["n"], cfg["k"]
+    x = workloads.rows_normal_bf16(m, n, 2.0, seed=0, device="cuda")
+    torch.cuda.synchronize()
+    outs = {}
+
+    def mk(name, f):
+        def call():
+            outs[name] = f()
+        return name, call
+
+    calls = []
+    if args.only in ("all", "exact"):
+        calls.append(mk("exact", lambda: atk.exact(x, k)))
+    if args.only in ("all", "b64k1"):
+        calls.append(mk("b64k1", lambda: atk.bucketed(x, k, 64, 1, False)))
+    if args.only in ("all", "b128k2"):
+        calls.append(mk("b128k2", lambda: atk.bucketed(x, k, 128, 2, True)))
+    if not calls:
+        return None
+    ms, wall = timer.run(calls, args.steps, args.warmup)
+    width = {"exact": k, "b64k1": 64, "b128k2": k}
+    modes = {}
+    for name, _ in calls:
+        t = float(np.mean(ms[name])) * 1e-3
+        alg = m * n * 2 + m * width[name] * (2 + 4)
+        modes[name] = {
+            "us": round(t * 1e6, 2),
+            "us_p10": round(float(np.percentile(ms[name], 10)) * 1e3, 2),
+            "us_p90": round(float(np.percentile(ms[name], 90)) * 1e3, 2),
+            "elements_per_s": m * n / t,
+            "alg_bytes": alg,
+            "gbps": alg / t / 1e9,
+            "frac_hbm_peak": alg / t / 1e9 / HBM_PEAK_GBPS,
+        }
+    recall = {}
+    if "exact" in outs:
+        ex = outs["exact"][1].cpu().numpy()
+        for name in ("b64k1", "b128k2"):
+            if name in outs:
+                got = outs[name][1].cpu().numpy()
+                r = [len(np.intersect1d(a, e)) / k for a, e in zip(got, ex)]
+                recall[name] = float(np.mean(r))
+    step_s = sum(modes[nm]["us"] for nm in modes) * 1e-6
+    return dict(m=m, n=n, k=k, modes=modes, step_s=step_s, wall_s=wall, recall=recall, x=x)
+
+
+def decode_steps(args, timer):
+    import numpy as np
+    import torch
+
+    import top_sparse_attention_exact_amd as atk
+    from top_sparse_attention_exact_amd import workloads
+
+    res = {}
+    todo = [w for w in ("mha", "gqa") if args.only in ("all", w)]
+    for w in todo:
+        if w == "mha":
+            c = workloads.DECODE["mha-32k"]
+            q, K, V, _ = workloads.decode_mha(c["bsz"], c["hq"], c["ctx"], c["d"], 64, 0.8, seed=0, device="cuda")
+        else:
+            c = workloads.DECODE["gqa-128k"]
+            q, K, V, _ = workloads.decode_gqa(c["bsz"], c["hq"], c["hkv"], c["ctx"], c["d"], 0.01, 3.0, seed=0,
+                                              device="cuda")
+        torch.cuda.synchronize()
+        modes = [("bucketed", c["b"], c["kb"]), ("exact", 1, c["k_sel"])]
+        calls = [(name, (lambda b=b, kb=kb: atk.sparse_attn_decode(q, K, V, c["k_sel"], b, kb)))
+                 for name, b, kb in modes]
+        ms, _ = timer.run(calls, max(3, min(args.steps, 10)), 2)
+        kbytes = K.numel() * 2
+        alg = kbytes + q.numel() * 2 + c["bsz"] * c["hq"] * c["k_sel"] * c["d"] * 2 + q.numel() * 2
+        out = {"workload": "%s-%dk" % (w, c["ctx"] // 1024), "B": c["bsz"], "Hq": c["hq"], "Hkv": c["hkv"],
+               "L": c["ctx"], "K_sel": c["k_sel"], "b": c["b"], "kb": c["kb"], "alg_bytes": alg}
+        for name, _, _ in modes:
+            t = float(np.mean(ms[name])) * 1e-3
+            out[name] = {"us_per_step": round(t * 1e6, 1), "gbps": alg / t / 1e9,
+                         "frac_hbm_peak": alg / t / 1e9 / HBM_PEAK_GBPS,
+                         "scores_per_s": c["bsz"] * c["hq"] * c["ctx"] / t}
+        res[out["workload"]] = out
+        del q, K, V
+        torch.cuda.empty_cache()
+    return res
+
+
+def cpu_leg(sel, seconds):
+    """The CPU oracle (as it stands) on a bounded sample of the same batch."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    x = sel["x"]
+    m, n, k = sel["m"], sel["n"], sel["k"]
+    hx = x.cpu().view(torch.int16).numpy().view(np.uint16)
+    rows = 0
+    t0 = time.perf_counter()
+    while rows < m and (rows < 8 or time.perf_counter() - t0 < seconds):
+        r = hx[rows:rows + 1]
+        oracle.exact_topk(r, k, "bf16")
+        oracle.bucketed_topk(r, k, 64, 1, False, "bf16")
+        oracle.bucketed_topk(r, k, 128, 2, True, "bf16")
+        rows += 1
+    dt = time.perf_counter() - t0
+    ref = {
+        "b64k1": {"eq1": oracle.eq1(k, 64, 1), "eq1_finite_n": oracle.eq1_finite(n, k, 64, 1)},
+        "b128k2": {"eq1": oracle.eq1(k, 128, 2), "eq1_finite_n": oracle.eq1_finite(n, k, 128, 2)},
+    }
+    return {
+        "value": rows * n * 3 / dt,
+        "unit": "elements/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": "%d of %d rows of the step's batch, all three modes (numpy, one thread, %s)" % (
+            rows, m, platform.processor() or platform.machine()),
+    }, ref
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (rows and heads shard with no "
+              "communication; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    torch.cuda.set_device(0)
+    timer = EventTimer(flush=not args.no_flush)
+    sel = selection_step(args, timer) if args.only in ("all", "exact", "b64k1", "b128k2") else None
+    dec = decode_steps(args, timer) if (not args.no_decode and args.only in ("all", "mha", "gqa")) else {}
+
+    line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
+    if sel is not None:
+        modes = sel["modes"]
+        passes = len(modes)
+        value = passes * sel["m"] * sel["n"] / sel["step_s"]
+        dom = max(modes, key=lambda nm: modes[nm]["us"])
+        kern = {"exact": "exact_filter", "b64k1": "bucket_stage1", "b128k2": "bucket_stage1"}[dom]
+        line.update({
+            "value": value,
+            "unit": "elements/s",
+            "ms_per_step": sel["step_s"] * 1e3,
+            "config": {"workload": "vocab-128k: 256 x 131072 bf16 ~ N(0, 2^2), k = 64; one step = " +
+                                   " + ".join(modes) + " (value counts m*n elements per mode)",
+                       "m": sel["m"], "n": sel["n"], "k": sel["k"], "modes": list(modes),
+                       "cache": "flushed before every call" if not args.no_flush else "warm"},
+            "roofline": {"bound": "hbm", "kernel": kern + " (" + dom + ")", "achieved": modes[dom]["gbps"],
+                         "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": modes[dom]["gbps"] / HBM_PEAK_GBPS,
+                         "traffic": recorded_traffic(dom)},
+            "modes": modes,
+            "recall": sel["recall"],
+            "wall_ms_per_step": sel["wall_s"] / args.steps * 1e3,
+        })
+    else:
+        first = next(iter(dec.values()))
+        line.update({"value": first["bucketed"]["scores_per_s"], "unit": "scores/s",
+                     "ms_per_step": first["bucketed"]["us_per_step"] / 1e3, "config": {"workload": first["workload"]}})
+    if dec:
+        line["decode"] = dec
+    if sel is not None and not args.no_cpu_baseline:
+        cpu, ref = cpu_leg(sel, args.cpu_seconds)
+        line["cpu_baseline"] = cpu
+        for nm, r in ref.items():
+            if nm in line["recall"]:
+                line["recall"][nm] = {"measured": line["recall"][nm], **r}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,130 @@
+/*
+ * atopk.h -- C ABI of libatopk.so: exact and bucketed top-k selection and
+ * top-K sparse-attention decode on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (pages cited by title and section):
+ *  - "Approximate Top-k for Increased Parallelism" (Pith review page),
+ *    "The reading": exact top-k finds the k largest entries of a vector.
+ *    "What carries the argument": the two-stage bucketed top-k splits the n
+ *    inputs into b interleaved buckets, takes an exact top-k_b inside every
+ *    bucket, and, when the b*k_b candidates exceed k, an exact top-k of them.
+ *    Benchmark protocol (reference list): x has shape (m, n).
+ *  - "Recall Before You Rank: Similarity-Guided Top-K Reuse ..." (fugumt
+ *    page), Abstract: Top-K sparse attention scores the current query against
+ *    the full KV cache, selects a global Top-K, and runs softmax and value
+ *    aggregation over that subset only.
+ *  - STARC (Pith review page), Figure 3 caption: q in R^{1 x d_h} and
+ *    K, V in R^{L x d_h} per attention head.
+ *
+ * Conventions shared by every entry point
+ *  - Order: value descending, ties to the LOWER index.  -0.0 equals +0.0.
+ *    NaN inputs are a precondition violation (result unspecified, no fault).
+ *  - Bucket of element i is i mod b (interleaved).  Bucket r holds
+ *    ceil((n - r) / b) elements; every bucket must hold at least k_b of them.
+ *  - Returned values are bit copies of the selected input elements.
+ *  - Indices are int32 positions inside the row (0 <= idx < n).
+ *  - All pointers except `stream` are DEVICE pointers owned by the caller.
+ *    The library never allocates, frees or synchronises: it enqueues kernels
+ *    on `stream` (a hipStream_t; NULL = the default stream) and returns.  A
+ *    caller-provided workspace (`ws`, at least the size the matching
+ *    *_workspace query returns, 256-byte aligned) holds intermediate results.
+ *    The workspace and outputs must not be in use by other work on other
+ *    streams until the enqueued work completes.
+ *  - Every call validates all arguments on the host before any launch and
+ *    returns a status; on error nothing is written.  No C++ exception leaves
+ *    the library.  Device faults surface at the caller's next synchronisation.
+ *  - The library runs only on gfx950; any other device gives
+ *    ATOPK_ERR_UNSUPPORTED.  It is thread safe (the only state is a one-time
+ *    per-device property cache).
+ */
+#ifndef ATOPK_H
+#define ATOPK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types of x / out_vals */
+typedef enum atopk_dtype { ATOPK_F32 = 0, ATOPK_BF16 = 1 } atopk_dtype;
+
+/* status codes */
+enum {
+  ATOPK_OK = 0,
+  ATOPK_ERR_NULL = 1,        /* a required pointer is NULL                        */
+  ATOPK_ERR_SHAPE = 2,       /* m < 0, n < 1, ldx < n, k < 1, k > n, ctx < 1, ...  */
+  ATOPK_ERR_PARAM = 3,       /* b < 1, kb < 1, b*kb < k, kb > floor(n / b), ...    */
+  ATOPK_ERR_UNSUPPORTED = 4, /* dtype, d != 128, kb > 16, k > 8192, n >= 2^31, arch */
+  ATOPK_ERR_WORKSPACE = 5,   /* ws NULL or smaller than the query says, misaligned */
+  ATOPK_ERR_HIP = 6          /* the HIP runtime refused a launch or a query        */
+};
+
+#define ATOPK_MAX_K 8192
+#define ATOPK_MAX_KB 16
+
+/* Static, human-readable text for a status code. */
+const char* atopk_status_str(int status);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int atopk_version(void);
+
+/*
+ * Exact top-k of every row of x.
+ *   x         [m, ldx] row-major, dtype `dtype`; row r is x[r*ldx .. r*ldx+n).
+ *   out_vals  [m, k] same dtype as x; out_idx [m, k] int32.  Row r lists the
+ *             k largest entries of row r, value descending then index ascending.
+ * Limits: 1 <= k <= min(n, 8192), n < 2^31.  m == 0 is a no-op.
+ */
+int atopk_exact_workspace(int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k, size_t* ws_bytes);
+int atopk_exact(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k,
+                void* out_vals, int32_t* out_idx, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Two-stage bucketed top-k (stage 1: exact top-kb of each of b interleaved
+ * buckets; stage 2 when final_exact != 0: exact top-k of the b*kb candidates).
+ *   final_exact != 0: out_* are [m, k], sorted like atopk_exact.
+ *   final_exact == 0: out_* are [m, b*kb], bucket-major: slot r*kb + j is the
+ *                     j-th best element of bucket r.
+ * Requires 1 <= b <= n, 1 <= kb <= floor(n / b), k <= b*kb (the invariant
+ * b*k_b >= k), kb <= 16, k <= 8192, b*kb <= 2^20.  (b, kb) = (1, k) runs the
+ * exact path (same result).
+ */
+int atopk_bucketed_workspace(int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k, int64_t b,
+                             int64_t kb, int final_exact, size_t* ws_bytes);
+int atopk_bucketed(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k, int64_t b,
+                   int64_t kb, int final_exact, void* out_vals, int32_t* out_idx, void* ws,
+                   size_t ws_bytes, void* stream);
+
+/*
+ * Top-K sparse-attention decode for one layer, one new token per sequence.
+ *   q      [batch, hq, d] bf16 (contiguous)
+ *   K, V   [batch, hkv, ctx_stride, d] bf16; key j of (batch i, KV head h) is
+ *          K[((i*hkv + h)*ctx_stride + j)*d ...]; the first ctx rows are used.
+ *   scale  score multiplier (usually 1/sqrt(d)); s_j = scale * <q, K_j>,
+ *          accumulated in fp32 and scaled in fp32.
+ *   Selection per QUERY head h (KV head h / (hq/hkv)): (b, kb) = (1, k_sel)
+ *   is the exact Top-K; otherwise bucketed with b interleaved buckets of the
+ *   ctx keys, k_b per bucket, and an exact final Top-K when b*kb > k_sel.
+ *   out      [batch, hq, d] bf16 = softmax over the selected scores (maximum
+ *            subtracted, fp32) times the selected V rows, rounded to nearest.
+ *   sel_idx  [batch, hq, k_sel] int32, nullable: selected keys, score desc.
+ *   scores   [batch, hq, ctx] fp32, nullable: every score (debug dump, costs
+ *            bandwidth).
+ * Requires d == 128, hq % hkv == 0, hq/hkv <= 8, ctx_stride >= ctx >= 1,
+ * 1 <= k_sel <= min(ctx, 8192), b*kb >= k_sel, kb <= floor(ctx / b).
+ */
+int atopk_sparse_attn_decode_workspace(int64_t batch, int64_t hq, int64_t hkv, int64_t ctx,
+                                       int64_t d, int64_t k_sel, int64_t b, int64_t kb,
+                                       size_t* ws_bytes);
+int atopk_sparse_attn_decode(const void* q, const void* K, const void* V, int64_t batch, int64_t hq,
+                             int64_t hkv, int64_t ctx, int64_t ctx_stride, int64_t d, float scale,
+                             int64_t k_sel, int64_t b, int64_t kb, void* out, int32_t* sel_idx,
+                             float* scores, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATOPK_H */

@@ -1,0 +1,133 @@
+"""The C ABI boundary on the CPU: the library loads, exports every entry
+point include/atopk.h declares, and every argument error is reported before
+any HIP call (so these run without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "atopk.h")
+
+lib_mod = pytest.importorskip("top_sparse_attention_exact_amd._lib")
+
+if not os.path.exists(lib_mod.LIB_PATH):
+    pytest.skip("libatopk.so not built", allow_module_level=True)
+
+OK, ENULL, ESHAPE, EPARAM, EUNSUP, EWS, EHIP = range(7)
+F32, BF16 = 0, 1
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(atopk_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return lib_mod.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) == 8
+    handle = ctypes.CDLL(lib_mod.LIB_PATH)
+    for name in names:
+        assert hasattr(handle, name), name
+    assert set(names) == set(lib_mod.EXPORTED)
+
+
+def test_status_strings(L):
+    for s in range(7):
+        assert L.atopk_status_str(s)
+    assert L.atopk_status_str(99) == b"unknown status"
+    assert L.atopk_version() >= 100
+
+
+def _ws_exact(L, dt, m, n, ldx, k):
+    sz = ctypes.c_size_t(0)
+    return L.atopk_exact_workspace(dt, m, n, ldx, k, ctypes.byref(sz)), sz.value
+
+
+def _ws_bucketed(L, dt, m, n, ldx, k, b, kb, fin):
+    sz = ctypes.c_size_t(0)
+    return L.atopk_bucketed_workspace(dt, m, n, ldx, k, b, kb, fin, ctypes.byref(sz)), sz.value
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case below fails validation first
+
+
+def test_exact_validation(L):
+    assert _ws_exact(L, F32, 4, 100, 100, 10)[0] == OK
+    assert _ws_exact(L, F32, -1, 100, 100, 10)[0] == ESHAPE
+    assert _ws_exact(L, F32, 4, 0, 100, 1)[0] == ESHAPE
+    assert _ws_exact(L, F32, 4, 100, 99, 10)[0] == ESHAPE  # ldx < n
+    assert _ws_exact(L, F32, 4, 100, 100, 0)[0] == ESHAPE
+    assert _ws_exact(L, F32, 4, 100, 100, 101)[0] == ESHAPE  # k > n
+    assert _ws_exact(L, 7, 4, 100, 100, 10)[0] == EUNSUP
+    assert _ws_exact(L, F32, 4, 20000, 20000, 8193)[0] == EUNSUP  # k > 8192
+    assert _ws_exact(L, F32, 1, 1 << 31, 1 << 31, 10)[0] == EUNSUP
+    assert L.atopk_exact_workspace(F32, 4, 100, 100, 10, None) == ENULL
+    # null pointers
+    assert L.atopk_exact(None, F32, 4, 100, 100, 10, FAKE, FAKE, None, 0, None) == ENULL
+    assert L.atopk_exact(FAKE, F32, 4, 100, 100, 10, None, FAKE, None, 0, None) == ENULL
+    assert L.atopk_exact(FAKE, F32, 4, 100, 100, 10, FAKE, None, None, 0, None) == ENULL
+    # m == 0 is a no-op, even with null pointers
+    assert L.atopk_exact(None, F32, 0, 100, 100, 10, None, None, None, 0, None) == OK
+
+
+def test_exact_workspace_checks(L):
+    st, need = _ws_exact(L, F32, 64, 1 << 20, 1 << 20, 8192)  # split rows need a workspace
+    assert st == OK and need > 0
+    assert L.atopk_exact(FAKE, F32, 64, 1 << 20, 1 << 20, 8192, FAKE, FAKE, None, 0, None) == EWS
+    assert L.atopk_exact(FAKE, F32, 64, 1 << 20, 1 << 20, 8192, FAKE, FAKE, FAKE, need - 1, None) == EWS
+    assert L.atopk_exact(FAKE, F32, 64, 1 << 20, 1 << 20, 8192, FAKE, FAKE, ctypes.c_void_p(0x1008), need, None) == EWS
+
+
+def test_bucketed_validation(L):
+    assert _ws_bucketed(L, BF16, 256, 131072, 131072, 64, 128, 2, 1)[0] == OK
+    assert _ws_bucketed(L, BF16, 256, 131072, 131072, 64, 0, 2, 1)[0] == EPARAM
+    assert _ws_bucketed(L, BF16, 256, 131072, 131072, 64, 64, 0, 1)[0] == EPARAM
+    assert _ws_bucketed(L, BF16, 256, 131072, 131072, 64, 31, 2, 1)[0] == EPARAM  # b*kb < k
+    assert _ws_bucketed(L, BF16, 256, 131072, 131072, 64, 31, 2, 0)[0] == EPARAM
+    assert _ws_bucketed(L, F32, 1, 100, 100, 4, 30, 4, 1)[0] == EPARAM  # kb > floor(n/b)
+    assert _ws_bucketed(L, F32, 1, 100, 100, 4, 101, 1, 1)[0] == EPARAM  # b > n
+    assert _ws_bucketed(L, F32, 1, 10000, 10000, 64, 8, 17, 1)[0] == EUNSUP  # kb > 16
+    assert _ws_bucketed(L, F32, 1, 10000, 10000, 64, 1, 64, 1)[0] == OK  # exact route
+    assert _ws_bucketed(L, F32, 1, 10000, 10000, 10, 1, 20, 1)[0] == EUNSUP  # b = 1 but kb != k, kb > 16
+    assert _ws_bucketed(L, F32, 1, 20000, 20000, 8193, 1024, 16, 1)[0] == EUNSUP
+    assert _ws_bucketed(L, F32, 1, 100, 99, 4, 4, 1, 1)[0] == ESHAPE
+    assert L.atopk_bucketed(None, F32, 2, 100, 100, 4, 4, 1, 1, FAKE, FAKE, None, 0, None) == ENULL
+    assert L.atopk_bucketed(None, F32, 0, 100, 100, 4, 4, 1, 1, None, None, None, 0, None) == OK
+    st, need = _ws_bucketed(L, BF16, 256, 131072, 131072, 64, 128, 2, 1)
+    assert st == OK and need > 0
+    assert L.atopk_bucketed(FAKE, BF16, 256, 131072, 131072, 64, 128, 2, 1, FAKE, FAKE, None, 0, None) == EWS
+
+
+def _ws_decode(L, bsz, hq, hkv, ctx, d, ks, b, kb):
+    sz = ctypes.c_size_t(0)
+    return L.atopk_sparse_attn_decode_workspace(bsz, hq, hkv, ctx, d, ks, b, kb, ctypes.byref(sz)), sz.value
+
+
+def test_decode_validation(L):
+    assert _ws_decode(L, 16, 32, 32, 32768, 128, 512, 256, 2)[0] == OK
+    assert _ws_decode(L, 4, 32, 8, 131072, 128, 512, 512, 4)[0] == OK
+    assert _ws_decode(L, 4, 32, 8, 131072, 128, 512, 1, 512)[0] == OK  # exact Top-K
+    assert _ws_decode(L, 4, 30, 8, 1024, 128, 16, 16, 1)[0] == ESHAPE  # hq % hkv
+    assert _ws_decode(L, 4, 32, 8, 1024, 128, 2000, 1, 2000)[0] == ESHAPE  # k_sel > ctx
+    assert _ws_decode(L, 4, 32, 8, 1024, 64, 16, 16, 1)[0] == EUNSUP  # d != 128
+    assert _ws_decode(L, 4, 32, 2, 1024, 128, 16, 16, 1)[0] == EUNSUP  # group of 16 heads
+    assert _ws_decode(L, 4, 32, 8, 1024, 128, 16, 8, 1)[0] == EPARAM  # b*kb < k_sel
+    assert _ws_decode(L, 4, 32, 8, 1024, 128, 16, 512, 4)[0] == EPARAM  # kb > ctx/b
+    f = ctypes.c_float(0.1)
+    assert L.atopk_sparse_attn_decode(None, FAKE, FAKE, 1, 8, 8, 256, 256, 128, f, 16, 16, 1, FAKE, None, None, None,
+                                      0, None) == ENULL
+    assert L.atopk_sparse_attn_decode(FAKE, FAKE, FAKE, 1, 8, 8, 256, 255, 128, f, 16, 16, 1, FAKE, None, None, None,
+                                      0, None) == ESHAPE  # ctx_stride < ctx
+    assert L.atopk_sparse_attn_decode(ctypes.c_void_p(0x1004), FAKE, FAKE, 1, 8, 8, 256, 256, 128, f, 16, 16, 1, FAKE,
+                                      None, None, None, 0, None) == EUNSUP  # misaligned q
+    assert L.atopk_sparse_attn_decode(FAKE, FAKE, FAKE, 1, 8, 8, 256, 256, 128, f, 16, 16, 1, FAKE, None, None, None,
+                                      0, None) == EWS

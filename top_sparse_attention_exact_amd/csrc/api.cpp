@@ -1,0 +1,315 @@
+// Host side of the C ABI declared in include/atopk.h: argument validation,
+// workspace layout and kernel dispatch.  Nothing here allocates, frees or
+// synchronises; every argument is checked before the first HIP call, so the
+// error paths run (and are tested) without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstring>
+#include <new>
+
+#include "atopk.h"
+#include "launch.h"
+
+using namespace atopk;
+
+namespace {
+
+constexpr int64_t kMaxN = (int64_t)1 << 31;  // indices are int32
+constexpr int64_t kMaxCand = (int64_t)1 << 20;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Workspace carving: successive 256-byte aligned regions.
+struct Carve {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  }
+};
+
+int64_t pow2_ceil(int64_t v) {
+  int64_t p = 1;
+  while (p < v) p <<= 1;
+  return p;
+}
+
+// ---- device check (cached per device) ---------------------------------------
+
+std::atomic<int> g_arch_ok[64];  // 0 unknown, 1 gfx950, 2 other
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return ATOPK_ERR_HIP;
+  if (dev >= 0 && dev < 64) {
+    int c = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (c == 1) return ATOPK_OK;
+    if (c == 2) return ATOPK_ERR_UNSUPPORTED;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ATOPK_ERR_HIP;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev >= 0 && dev < 64) g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? ATOPK_OK : ATOPK_ERR_UNSUPPORTED;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? ATOPK_OK : ATOPK_ERR_HIP; }
+
+// ---- exact -----------------------------------------------------------------------
+
+int validate_exact(int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k) {
+  if (m < 0 || n < 1 || ldx < n || k < 1 || k > n) return ATOPK_ERR_SHAPE;
+  if (dtype != ATOPK_F32 && dtype != ATOPK_BF16) return ATOPK_ERR_UNSUPPORTED;
+  if (n >= kMaxN || k > ATOPK_MAX_K) return ATOPK_ERR_UNSUPPORTED;
+  return ATOPK_OK;
+}
+
+size_t exact_ws_bytes(int dtype, int64_t m, int64_t n, int64_t k) {
+  const ExactPlan p = plan_exact(dtype, m, n, k);
+  if (p.splits <= 1) return 0;
+  Carve c;
+  c.take((size_t)m * p.splits * k * 8);
+  return c.off;
+}
+
+int run_exact(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k, void* out_vals,
+              int32_t* out_idx, void* ws, hipStream_t s) {
+  const ExactPlan p = plan_exact(dtype, m, n, k);
+  if (p.splits <= 1) return hip_status(launch_exact(p, x, dtype, m, n, ldx, k, nullptr, x, dtype, ldx, out_vals, out_idx, s));
+  uint64_t* part = static_cast<uint64_t*>(ws);
+  hipError_t e = launch_exact(p, x, dtype, m, n, ldx, k, part, x, dtype, ldx, nullptr, nullptr, s);
+  if (e != hipSuccess) return ATOPK_ERR_HIP;
+  const int64_t n2 = (int64_t)p.splits * k;
+  const ExactPlan p2 = plan_exact(IN_KEY64, m, n2, k);
+  return hip_status(launch_exact(p2, part, IN_KEY64, m, n2, n2, k, nullptr, x, dtype, ldx, out_vals, out_idx, s));
+}
+
+// ---- bucketed --------------------------------------------------------------------
+
+bool exact_route(int64_t k, int64_t b, int64_t kb) { return b == 1 && kb == k; }
+
+int validate_bucketed(int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k, int64_t b, int64_t kb) {
+  if (m < 0 || n < 1 || ldx < n || k < 1 || k > n) return ATOPK_ERR_SHAPE;
+  if (b < 1 || b > n || kb < 1 || kb > n / b || b * kb < k) return ATOPK_ERR_PARAM;
+  if (dtype != ATOPK_F32 && dtype != ATOPK_BF16) return ATOPK_ERR_UNSUPPORTED;
+  if (n >= kMaxN || k > ATOPK_MAX_K) return ATOPK_ERR_UNSUPPORTED;
+  if (exact_route(k, b, kb)) return ATOPK_OK;
+  if (kb > ATOPK_MAX_KB || b * kb > kMaxCand) return ATOPK_ERR_UNSUPPORTED;
+  return ATOPK_OK;
+}
+
+struct BucketLayout {
+  BucketPlan plan;
+  size_t lists_off, lists_bytes;
+  size_t cand_off, cand_bytes;  // merged candidates when the final stage runs on the exact path
+  size_t total;
+};
+
+int64_t kb_slots_host(int64_t kb) { return pow2_ceil(kb); }
+
+BucketLayout bucket_layout(int dtype, int64_t m, int64_t n, int64_t b, int64_t kb, int final_exact, bool aligned) {
+  BucketLayout L{};
+  L.plan = plan_bucketed(dtype, m, n, b, kb, aligned);
+  Carve c;
+  L.lists_bytes = (size_t)m * L.plan.lists_per_row * b * kb_slots_host(kb) * 8;
+  L.lists_off = c.take(L.lists_bytes);
+  L.cand_bytes = (final_exact && b * kb > kFinishMaxCand) ? (size_t)m * b * kb * 8 : 0;
+  L.cand_off = c.take(L.cand_bytes);
+  L.total = c.off;
+  return L;
+}
+
+size_t bucketed_ws_bytes(int dtype, int64_t m, int64_t n, int64_t k, int64_t b, int64_t kb, int final_exact) {
+  if (exact_route(k, b, kb)) return exact_ws_bytes(dtype, m, n, k);
+  // The plan depends on the data pointer's alignment; report the larger need.
+  return std::max(bucket_layout(dtype, m, n, b, kb, final_exact, true).total,
+                  bucket_layout(dtype, m, n, b, kb, final_exact, false).total);
+}
+
+int run_bucketed(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k, int64_t b, int64_t kb,
+                 int final_exact, void* out_vals, int32_t* out_idx, void* ws, hipStream_t s) {
+  if (exact_route(k, b, kb)) return run_exact(x, dtype, m, n, ldx, k, out_vals, out_idx, ws, s);
+  const int64_t es = dtype == ATOPK_F32 ? 4 : 2;
+  const bool aligned = ((reinterpret_cast<uintptr_t>(x) | (uintptr_t)(ldx * es)) & 15) == 0;
+  const BucketLayout L = bucket_layout(dtype, m, n, b, kb, final_exact, aligned);
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  uint64_t* lists = reinterpret_cast<uint64_t*>(w + L.lists_off);
+  uint64_t* cand = L.cand_bytes ? reinterpret_cast<uint64_t*>(w + L.cand_off) : nullptr;
+  if (launch_bucket_stage1(L.plan, x, dtype, m, n, ldx, b, kb, lists, s) != hipSuccess) return ATOPK_ERR_HIP;
+  if (launch_bucket_finish(lists, L.plan.lists_per_row, m, b, kb, k, final_exact, x, dtype, ldx, out_vals, out_idx,
+                           cand, s) != hipSuccess)
+    return ATOPK_ERR_HIP;
+  if (cand) {
+    const int64_t nc = b * kb;
+    const ExactPlan p2 = plan_exact(IN_KEY64, m, nc, k);
+    return hip_status(launch_exact(p2, cand, IN_KEY64, m, nc, nc, k, nullptr, x, dtype, ldx, out_vals, out_idx, s));
+  }
+  return ATOPK_OK;
+}
+
+// ---- decode --------------------------------------------------------------------------
+
+int validate_decode(int64_t batch, int64_t hq, int64_t hkv, int64_t ctx, int64_t ctx_stride, int64_t d, int64_t k_sel,
+                    int64_t b, int64_t kb) {
+  if (batch < 0 || hq < 1 || hkv < 1 || hq % hkv != 0 || ctx < 1 || ctx_stride < ctx || d < 1 || k_sel < 1 ||
+      k_sel > ctx)
+    return ATOPK_ERR_SHAPE;
+  if (b < 1 || b > ctx || kb < 1 || kb > ctx / b || b * kb < k_sel) return ATOPK_ERR_PARAM;
+  if (d != 128 || hq / hkv > 8 || ctx >= kMaxN || k_sel > ATOPK_MAX_K) return ATOPK_ERR_UNSUPPORTED;
+  if (!exact_route(k_sel, b, kb) && (kb > ATOPK_MAX_KB || b * kb > kMaxCand)) return ATOPK_ERR_UNSUPPORTED;
+  return ATOPK_OK;
+}
+
+struct DecodeLayout {
+  size_t scores_off, vals_off, idx_off, sel_ws_off, total;
+  size_t sel_ws_bytes;
+};
+
+DecodeLayout decode_layout(int64_t batch, int64_t hq, int64_t ctx, int64_t k_sel, int64_t b, int64_t kb) {
+  DecodeLayout L{};
+  const int64_t rows = batch * hq;
+  Carve c;
+  L.scores_off = c.take((size_t)rows * ctx * 4);
+  L.vals_off = c.take((size_t)rows * k_sel * 4);
+  L.idx_off = c.take((size_t)rows * k_sel * 4);
+  L.sel_ws_bytes = bucketed_ws_bytes(ATOPK_F32, rows, ctx, k_sel, b, kb, 1);
+  L.sel_ws_off = c.take(L.sel_ws_bytes);
+  L.total = c.off;
+  return L;
+}
+
+int check_ws(const void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return ATOPK_OK;
+  if (ws == nullptr || ws_bytes < need) return ATOPK_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign != 0) return ATOPK_ERR_WORKSPACE;
+  return ATOPK_OK;
+}
+
+template <typename F>
+int guarded(F&& f) {
+  try {
+    return f();
+  } catch (...) {
+    return ATOPK_ERR_HIP;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* atopk_status_str(int status) {
+  switch (status) {
+    case ATOPK_OK: return "ok";
+    case ATOPK_ERR_NULL: return "a required pointer is NULL";
+    case ATOPK_ERR_SHAPE: return "invalid shape (sizes, leading dimension, k)";
+    case ATOPK_ERR_PARAM: return "invalid bucket parameters (b, k_b, b*k_b >= k)";
+    case ATOPK_ERR_UNSUPPORTED: return "unsupported dtype, size, alignment or device (gfx950 only)";
+    case ATOPK_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
+    case ATOPK_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int atopk_version(void) { return 10000 * 0 + 100 * 1 + 0; }
+
+int atopk_exact_workspace(int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k, size_t* ws_bytes) {
+  return guarded([&] {
+    if (ws_bytes == nullptr) return (int)ATOPK_ERR_NULL;
+    int st = validate_exact(dtype, m, n, ldx, k);
+    if (st) return st;
+    *ws_bytes = m == 0 ? 0 : exact_ws_bytes(dtype, m, n, k);
+    return (int)ATOPK_OK;
+  });
+}
+
+int atopk_exact(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k, void* out_vals,
+                int32_t* out_idx, void* ws, size_t ws_bytes, void* stream) {
+  return guarded([&] {
+    int st = validate_exact(dtype, m, n, ldx, k);
+    if (st) return st;
+    if (m == 0) return (int)ATOPK_OK;
+    if (!x || !out_vals || !out_idx) return (int)ATOPK_ERR_NULL;
+    st = check_ws(ws, ws_bytes, exact_ws_bytes(dtype, m, n, k));
+    if (st) return st;
+    st = check_device();
+    if (st) return st;
+    return run_exact(x, dtype, m, n, ldx, k, out_vals, out_idx, ws, static_cast<hipStream_t>(stream));
+  });
+}
+
+int atopk_bucketed_workspace(int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k, int64_t b, int64_t kb,
+                             int final_exact, size_t* ws_bytes) {
+  return guarded([&] {
+    if (ws_bytes == nullptr) return (int)ATOPK_ERR_NULL;
+    int st = validate_bucketed(dtype, m, n, ldx, k, b, kb);
+    if (st) return st;
+    *ws_bytes = m == 0 ? 0 : bucketed_ws_bytes(dtype, m, n, k, b, kb, final_exact);
+    return (int)ATOPK_OK;
+  });
+}
+
+int atopk_bucketed(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k, int64_t b, int64_t kb,
+                   int final_exact, void* out_vals, int32_t* out_idx, void* ws, size_t ws_bytes, void* stream) {
+  return guarded([&] {
+    int st = validate_bucketed(dtype, m, n, ldx, k, b, kb);
+    if (st) return st;
+    if (m == 0) return (int)ATOPK_OK;
+    if (!x || !out_vals || !out_idx) return (int)ATOPK_ERR_NULL;
+    st = check_ws(ws, ws_bytes, bucketed_ws_bytes(dtype, m, n, k, b, kb, final_exact));
+    if (st) return st;
+    st = check_device();
+    if (st) return st;
+    return run_bucketed(x, dtype, m, n, ldx, k, b, kb, final_exact, out_vals, out_idx, ws,
+                        static_cast<hipStream_t>(stream));
+  });
+}
+
+int atopk_sparse_attn_decode_workspace(int64_t batch, int64_t hq, int64_t hkv, int64_t ctx, int64_t d, int64_t k_sel,
+                                       int64_t b, int64_t kb, size_t* ws_bytes) {
+  return guarded([&] {
+    if (ws_bytes == nullptr) return (int)ATOPK_ERR_NULL;
+    int st = validate_decode(batch, hq, hkv, ctx, ctx, d, k_sel, b, kb);
+    if (st) return st;
+    *ws_bytes = batch == 0 ? 0 : decode_layout(batch, hq, ctx, k_sel, b, kb).total;
+    return (int)ATOPK_OK;
+  });
+}
+
+int atopk_sparse_attn_decode(const void* q, const void* K, const void* V, int64_t batch, int64_t hq, int64_t hkv,
+                             int64_t ctx, int64_t ctx_stride, int64_t d, float scale, int64_t k_sel, int64_t b,
+                             int64_t kb, void* out, int32_t* sel_idx, float* scores, void* ws, size_t ws_bytes,
+                             void* stream) {
+  return guarded([&] {
+    int st = validate_decode(batch, hq, hkv, ctx, ctx_stride, d, k_sel, b, kb);
+    if (st) return st;
+    if (batch == 0) return (int)ATOPK_OK;
+    if (!q || !K || !V || !out) return (int)ATOPK_ERR_NULL;
+    if (((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(K) | reinterpret_cast<uintptr_t>(V)) & 15) != 0)
+      return (int)ATOPK_ERR_UNSUPPORTED;
+    const DecodeLayout L = decode_layout(batch, hq, ctx, k_sel, b, kb);
+    st = check_ws(ws, ws_bytes, L.total);
+    if (st) return st;
+    st = check_device();
+    if (st) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* w = static_cast<uint8_t*>(ws);
+    float* sc = scores ? scores : reinterpret_cast<float*>(w + L.scores_off);
+    float* vals = reinterpret_cast<float*>(w + L.vals_off);
+    int32_t* idx = sel_idx ? sel_idx : reinterpret_cast<int32_t*>(w + L.idx_off);
+    const int64_t rows = batch * hq;
+    if (launch_decode_scores(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(K), batch, hq, hkv, ctx,
+                             ctx_stride, scale, sc, s) != hipSuccess)
+      return (int)ATOPK_ERR_HIP;
+    st = run_bucketed(sc, ATOPK_F32, rows, ctx, ctx, k_sel, b, kb, 1, vals, idx, w + L.sel_ws_off, s);
+    if (st) return st;
+    return hip_status(launch_sparse_softmax_v(vals, idx, static_cast<const uint16_t*>(V), batch, hq, hkv, ctx_stride,
+                                              k_sel, static_cast<uint16_t*>(out), s));
+  });
+}
+
+}  // extern "C"

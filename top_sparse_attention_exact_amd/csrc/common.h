@@ -1,0 +1,240 @@
+// Device-side building blocks shared by the selection and decode kernels
+// (gfx950, wave64).
+//
+// Ordering.  Every stage compares elements by (value descending, index
+// ascending), the tie rule that makes each top-k result unique.  A value is
+// mapped to a 32-bit unsigned "order key" whose unsigned order is the
+// numeric order, with -0.0 and +0.0 mapped to the same key; a 64-bit key
+// packs (order key << 32) | ~index, so one unsigned comparison decides value
+// and tie at once.  Key 0 never comes from a real element and marks an empty
+// slot.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace atopk {
+
+constexpr int kWave = 64;
+
+// ----------------------------------------------------------------- keys ---
+
+// fp32 bits -> order key.  Positive values get the sign bit set; negative
+// values become 0x80000000 - |bits|, so -0.0 lands on the same key as +0.0.
+__device__ __forceinline__ uint32_t ord_f32(uint32_t bits) {
+  return (bits & 0x80000000u) ? (0x80000000u - (bits & 0x7fffffffu)) : (bits | 0x80000000u);
+}
+
+// Inverse of ord_f32 (a key from -0.0 comes back as +0.0).
+__device__ __forceinline__ uint32_t bits_from_ord(uint32_t o) {
+  return (o & 0x80000000u) ? (o & 0x7fffffffu) : (0x80000000u | (0x80000000u - o));
+}
+
+__device__ __forceinline__ uint64_t make_key(uint32_t ord, uint32_t idx) {
+  return ((uint64_t)ord << 32) | (uint64_t)(~idx);
+}
+__device__ __forceinline__ uint32_t key_idx(uint64_t key) { return ~(uint32_t)key; }
+__device__ __forceinline__ uint32_t key_ord(uint64_t key) { return (uint32_t)(key >> 32); }
+__device__ __forceinline__ float key_value_f32(uint64_t key) { return __uint_as_float(bits_from_ord(key_ord(key))); }
+
+template <typename K>
+__device__ __forceinline__ K kmax(K a, K b) { return a > b ? a : b; }
+template <typename K>
+__device__ __forceinline__ K kmin(K a, K b) { return a < b ? a : b; }
+
+// --------------------------------------------------- register queues ------
+//
+// A queue is KB keys held in registers, sorted descending.  Inserting x keeps
+// the KB largest of queue + {x}: slot j becomes the median of (old q[j-1],
+// old q[j], x), i.e. x clamped to [q[j], q[j-1]]; one max/min pair per slot
+// and no data-dependent branch.
+
+template <int KB, typename K>
+__device__ __forceinline__ void queue_insert(K (&q)[KB], K x) {
+#pragma unroll
+  for (int j = KB - 1; j >= 1; --j) q[j] = kmax(q[j], kmin(q[j - 1], x));
+  q[0] = kmax(q[0], x);
+}
+
+// a := top-KB of (a union c), both sorted descending.  max(a_i, c_{KB-1-i})
+// holds the KB largest of the union as a bitonic sequence, which a bitonic
+// half-cleaner cascade then sorts.  KB must be a power of two.
+template <int KB, typename K>
+__device__ __forceinline__ void queue_merge(K (&a)[KB], const K (&c)[KB]) {
+  K d[KB];
+#pragma unroll
+  for (int i = 0; i < KB; ++i) d[i] = kmax(a[i], c[KB - 1 - i]);
+#pragma unroll
+  for (int stride = KB / 2; stride > 0; stride /= 2) {
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      if ((i & stride) == 0) {
+        K hi = kmax(d[i], d[i + stride]);
+        K lo = kmin(d[i], d[i + stride]);
+        d[i] = hi;
+        d[i + stride] = lo;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < KB; ++i) a[i] = d[i];
+}
+
+// ------------------------------------------------------- wave helpers -----
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Number of set bits of `mask` below this lane.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  lo = (uint32_t)__shfl_xor((int)lo, m, kWave);
+  hi = (uint32_t)__shfl_xor((int)hi, m, kWave);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Inclusive prefix sum over the wave.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int t = __shfl_up(v, o, kWave);
+    if (l >= o) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// ------------------------------------------------------ block helpers -----
+//
+// All block helpers must be called by every thread of the block.
+
+// The threshold key t such that exactly k of the n unique keys in `keys`
+// (LDS) are >= t (radix select, 8-bit digits from the top).  `hist` is a
+// 256-entry LDS array, `ctl` 4 LDS words.
+template <int T>
+__device__ uint64_t block_kth_key(const uint64_t* keys, int n, int k, uint32_t* hist, uint32_t* ctl) {
+  const int tid = threadIdx.x;
+  uint64_t prefix = 0;
+  int rem = k;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 256; i += T) hist[i] = 0;
+    __syncthreads();
+    const uint64_t hi_prefix = (shift == 56) ? 0 : (prefix >> (shift + 8));
+    for (int i = tid; i < n; i += T) {
+      uint64_t key = keys[i];
+      bool match = (shift == 56) || ((key >> (shift + 8)) == hi_prefix);
+      if (match) atomicAdd(&hist[(uint32_t)(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid < kWave) {
+      // lane l owns digits 255-4l .. 252-4l (high to low)
+      uint32_t h[4];
+      int s = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        h[j] = hist[255 - 4 * tid - j];
+        s += (int)h[j];
+      }
+      int incl = wave_incl_scan(s);  // keys in digits above this lane's low end
+      int excl = incl - s;
+      if (excl < rem && rem <= incl) {
+        int acc = excl;
+        int d = 0;
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (d == 0 && acc + (int)h[j] >= rem) {
+            d = 255 - 4 * tid - j + 1;  // stored +1 so 0 means "not found yet"
+            cnt = h[j];
+          } else if (d == 0) {
+            acc += (int)h[j];
+          }
+        }
+        ctl[0] = (uint32_t)(d - 1);
+        ctl[1] = (uint32_t)(rem - acc);
+        ctl[2] = cnt;
+      }
+    }
+    __syncthreads();
+    const uint32_t digit = ctl[0];
+    const int new_rem = (int)ctl[1];
+    const uint32_t cnt = ctl[2];
+    __syncthreads();
+    prefix |= (uint64_t)digit << shift;
+    rem = new_rem;
+    if ((int)cnt == rem) break;  // every key with this prefix is in
+  }
+  return prefix;
+}
+
+// Sort keys[0..n_pow2) descending in LDS (bitonic network).
+template <int T>
+__device__ void block_sort_desc(uint64_t* keys, int n_pow2) {
+  const int tid = threadIdx.x;
+  for (int size = 2; size <= n_pow2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      __syncthreads();
+      for (int i = tid; i < (n_pow2 >> 1); i += T) {
+        int lo = 2 * stride * (i / stride) + (i % stride);
+        int hi = lo + stride;
+        bool desc = (lo & size) == 0;
+        uint64_t a = keys[lo], c = keys[hi];
+        bool swap = desc ? (a < c) : (a > c);
+        if (swap) {
+          keys[lo] = c;
+          keys[hi] = a;
+        }
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Keep the keys >= thr of keys[0..n) at the front (order not kept) and
+// return their count to every thread.  n <= T * MAXPER: every thread first
+// reads its MAXPER slots into registers, so the in-place writes cannot
+// overwrite unread keys.  `ctl` is one LDS word.
+template <int T, int MAXPER>
+__device__ int block_compact_ge(uint64_t* keys, int n, uint64_t thr, uint32_t* ctl) {
+  const int tid = threadIdx.x;
+  uint64_t v[MAXPER];
+#pragma unroll
+  for (int j = 0; j < MAXPER; ++j) {
+    int i = j * T + tid;
+    v[j] = (i < n) ? keys[i] : 0;
+  }
+  if (tid == 0) ctl[0] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < MAXPER; ++j) {
+    bool keep = v[j] != 0 && v[j] >= thr;
+    uint64_t mask = __ballot(keep);
+    if (mask) {
+      uint32_t pos = 0;
+      if (lane_id() == 0) pos = atomicAdd(&ctl[0], (uint32_t)__popcll(mask));
+      pos = __shfl(pos, 0, kWave);
+      if (keep) keys[pos + lanes_below(mask)] = v[j];
+    }
+  }
+  __syncthreads();
+  const int cnt = (int)ctl[0];
+  __syncthreads();
+  return cnt;
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+}  // namespace atopk

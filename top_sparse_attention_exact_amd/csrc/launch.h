@@ -1,0 +1,68 @@
+// Internal launchers: the host API (api.cpp) validates arguments and sizes
+// the workspace, then calls these to enqueue kernels on a stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace atopk {
+
+// Element types (match atopk_dtype) plus pre-built 64-bit keys.
+enum InKind { IN_F32 = 0, IN_BF16 = 1, IN_KEY64 = 2 };
+
+// ---- bucketed stage 1 ------------------------------------------------------
+
+// Fast stage 1: register queues over 16-byte loads.  Grid rows x splits.
+// Writes `lists_per_row` sorted k_b-lists per bucket to `lists`
+// ([m][lists_per_row][b][kb] keys).
+struct BucketPlan {
+  int threads;        // workgroup size
+  int splits;         // workgroups per row
+  int64_t chunk;      // elements per workgroup (multiple of threads * vec)
+  int lists_per_row;  // k_b-lists per bucket and row written by stage 1
+  bool fast;          // register-queue kernel (else one thread per bucket)
+};
+BucketPlan plan_bucketed(int dtype, int64_t m, int64_t n, int64_t b, int64_t kb, bool aligned);
+
+hipError_t launch_bucket_stage1(const BucketPlan& p, const void* x, int dtype, int64_t m, int64_t n,
+                                int64_t ldx, int64_t b, int64_t kb, uint64_t* lists, hipStream_t s);
+
+// Merge the lists of every bucket; then either write the bucket-major
+// candidates (final_exact == 0), or select and sort the final top-k
+// (b * kb <= kFinishMaxCand), or write merged candidates to `cand_out`
+// ([m][b*kb] keys) for the exact path to finish.
+constexpr int kFinishMaxCand = 8192;
+hipError_t launch_bucket_finish(const uint64_t* lists, int lists_per_row, int64_t m, int64_t b, int64_t kb,
+                                int64_t k, int final_exact, const void* x, int dtype, int64_t ldx,
+                                void* out_vals, int32_t* out_idx, uint64_t* cand_out, hipStream_t s);
+
+// ---- exact top-k ------------------------------------------------------------
+
+struct ExactPlan {
+  int splits;       // workgroups per row in the first pass
+  int64_t chunk;    // elements per workgroup
+  int cap;          // LDS candidate capacity (keys)
+};
+ExactPlan plan_exact(int in_kind, int64_t m, int64_t n, int64_t k);
+
+// Exact top-k over rows of `x` (values or 64-bit keys).  With splits > 1
+// every workgroup writes its chunk's top-k keys to `part` ([m][splits][k]);
+// otherwise sorted results go to out_vals / out_idx, the values being
+// gathered from `src` (dtype src_dtype, row stride src_ld elements).
+hipError_t launch_exact(const ExactPlan& p, const void* x, int in_kind, int64_t m, int64_t n, int64_t ld,
+                        int64_t k, uint64_t* part, const void* src, int src_dtype, int64_t src_ld,
+                        void* out_vals, int32_t* out_idx, hipStream_t s);
+
+// ---- decode -------------------------------------------------------------------
+
+// scores[(i*hq + h)*ctx + j] = scale * <q[i, h], K[i, h / g, j]> (fp32).
+hipError_t launch_decode_scores(const uint16_t* q, const uint16_t* K, int64_t batch, int64_t hq, int64_t hkv,
+                                int64_t ctx, int64_t ctx_stride, float scale, float* scores, hipStream_t s);
+
+// out[r] = softmax(sel_vals[r]) @ V[sel_idx[r]] for r = i*hq + h.
+hipError_t launch_sparse_softmax_v(const float* sel_vals, const int32_t* sel_idx, const uint16_t* V,
+                                   int64_t batch, int64_t hq, int64_t hkv, int64_t ctx_stride, int64_t k_sel,
+                                   uint16_t* out, hipStream_t s);
+
+}  // namespace atopk

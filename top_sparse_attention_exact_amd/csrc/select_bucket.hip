@@ -1,0 +1,368 @@
+// Bucketed top-k, stage 1 (exact top-k_b inside each of b interleaved
+// buckets) and the merge / final stage.
+//
+// "Approximate Top-k for Increased Parallelism" (Pith review page), "What
+// carries the argument": split the n inputs into b interleaved buckets,
+// take an exact top-k_b in each bucket independently, and, if the b*k_b
+// candidates exceed k, take an exact top-k of them.  The pages' kernel keeps
+// one small priority queue per thread in registers (k_b <= 4); here every
+// lane keeps one sorted k_b-queue per element slot of its 16-byte loads, so
+// a sweep of the workgroup over T*V consecutive elements (a multiple of b)
+// always feeds the same buckets into the same registers.  Queues of lanes
+// that share a bucket are merged with cross-lane shuffles, then across the
+// waves of the workgroup in LDS, then across workgroups of a row by the
+// finish kernel.
+#include "common.h"
+#include "launch.h"
+
+namespace atopk {
+
+namespace {
+
+constexpr int kStage1Threads = 256;
+constexpr int kStage1LdsBytes = 32768;
+constexpr int kTargetBlocks = 1024;
+
+// The kernels keep KB = next power of two >= k_b entries per queue; the
+// top-k_b of a bucket is the first k_b of its sorted top-KB, so the finish
+// kernel reads only those.
+int kb_slots(int64_t kb) {
+  int v = 1;
+  while (v < kb) v <<= 1;
+  return v;
+}
+
+
+template <int DT>
+struct VecOf {
+  static constexpr int V = (DT == IN_F32) ? 4 : 8;   // elements per 16-byte load
+  static constexpr int ES = (DT == IN_F32) ? 4 : 2;  // element bytes
+};
+
+// fp32 bit pattern of element e of a 16-byte vector.
+template <int DT>
+__device__ __forceinline__ uint32_t elem_bits(const uint4& w, int e) {
+  const uint32_t word[4] = {w.x, w.y, w.z, w.w};
+  if constexpr (DT == IN_F32) {
+    return word[e];
+  } else {
+    const uint32_t v = word[e >> 1];
+    return (e & 1) ? (v & 0xffff0000u) : (v << 16);
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t load_elem_bits(const uint8_t* row, int64_t i) {
+  if constexpr (DT == IN_F32) {
+    return *reinterpret_cast<const uint32_t*>(row + i * 4);
+  } else {
+    return (uint32_t)(*reinterpret_cast<const uint16_t*>(row + i * 2)) << 16;
+  }
+}
+
+template <int DT, int KB>
+__device__ __forceinline__ void consume_vec(uint64_t (&q)[VecOf<DT>::V][KB], const uint4& w, uint32_t idx0) {
+#pragma unroll
+  for (int e = 0; e < VecOf<DT>::V; ++e) queue_insert<KB>(q[e], make_key(ord_f32(elem_bits<DT>(w, e)), idx0 + e));
+}
+
+template <int DT, int KB>
+__global__ __launch_bounds__(kStage1Threads) void bucket_stage1_kernel(const uint8_t* __restrict__ x, int64_t ld_bytes,
+                                                                      int n, int b, int64_t chunk, int lds_merge,
+                                                                      int lists_per_row,
+                                                                      uint64_t* __restrict__ lists) {
+  constexpr int T = kStage1Threads;
+  constexpr int V = VecOf<DT>::V;
+  constexpr int ES = VecOf<DT>::ES;
+  constexpr int W = T * V;
+  constexpr int U = (V * KB >= 32) ? 1 : 4;  // loads in flight, bounded by queue registers
+  constexpr int NW = T / kWave;
+  __shared__ uint64_t lds[kStage1LdsBytes / 8];
+
+  const int t = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = t / kWave;
+  const int row = blockIdx.y;
+  const int split = blockIdx.x;
+  const int64_t c0 = (int64_t)split * chunk;
+  const int64_t c1 = min((int64_t)n, c0 + chunk);
+  const uint8_t* xr = x + (int64_t)row * ld_bytes;
+
+  uint64_t q[V][KB];
+#pragma unroll
+  for (int e = 0; e < V; ++e)
+#pragma unroll
+    for (int j = 0; j < KB; ++j) q[e][j] = 0;
+
+  int64_t base = c0;
+  for (; base + U * W <= c1; base += U * W) {
+    uint4 w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      w[u] = *reinterpret_cast<const uint4*>(xr + (base + (int64_t)u * W + (int64_t)t * V) * ES);
+#pragma unroll
+    for (int u = 0; u < U; ++u) consume_vec<DT, KB>(q, w[u], (uint32_t)(base + (int64_t)u * W + t * V));
+  }
+  for (; base + W <= c1; base += W) {
+    uint4 w = *reinterpret_cast<const uint4*>(xr + (base + (int64_t)t * V) * ES);
+    consume_vec<DT, KB>(q, w, (uint32_t)(base + t * V));
+  }
+  if (base < c1) {  // ragged tail: element-wise, bounds-checked
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const int64_t i = base + (int64_t)t * V + e;
+      if (i < c1) queue_insert<KB>(q[e], make_key(ord_f32(load_elem_bits<DT>(xr, i)), (uint32_t)i));
+    }
+  }
+
+  // Slots e and e + half of one lane share a bucket when b <= half.
+#pragma unroll
+  for (int half = V / 2; half >= 1; half /= 2) {
+    if (b <= half) {
+#pragma unroll
+      for (int e = 0; e < half; ++e) queue_merge<KB>(q[e], q[e + half]);
+    }
+  }
+  // Lanes l and l ^ m share all their buckets when m * V is a multiple of b.
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) {
+    if (m * V >= b) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        uint64_t o[KB];
+#pragma unroll
+        for (int j = 0; j < KB; ++j) o[j] = shfl_xor_u64(q[e][j], m);
+        queue_merge<KB>(q[e], o);
+      }
+    }
+  }
+
+  // Representatives: one queue per (bucket, copy) left in the workgroup.
+  const bool wave_has_all = kWave * V >= b;
+  const int ncopies = wave_has_all ? NW : W / b;
+  if (lds_merge) {
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const int p = wave * kWave * V + lane * V + e;
+      const bool rep = wave_has_all ? (lane * V + e < b) : true;
+      const int c = wave_has_all ? wave : p / b;
+      const int r = p % b;
+      if (rep) {
+#pragma unroll
+        for (int j = 0; j < KB; ++j) lds[((int64_t)c * b + r) * KB + j] = q[e][j];
+      }
+    }
+    __syncthreads();
+    for (int r = t; r < b; r += T) {
+      uint64_t a[KB];
+#pragma unroll
+      for (int j = 0; j < KB; ++j) a[j] = lds[(int64_t)r * KB + j];
+      for (int c = 1; c < ncopies; ++c) {
+        uint64_t o[KB];
+#pragma unroll
+        for (int j = 0; j < KB; ++j) o[j] = lds[((int64_t)c * b + r) * KB + j];
+        queue_merge<KB>(a, o);
+      }
+      uint64_t* dst = lists + (((int64_t)row * lists_per_row + split) * b + r) * KB;
+#pragma unroll
+      for (int j = 0; j < KB; ++j) dst[j] = a[j];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const int p = wave * kWave * V + lane * V + e;
+      const bool rep = wave_has_all ? (lane * V + e < b) : true;
+      const int c = wave_has_all ? wave : p / b;
+      const int r = p % b;
+      if (rep) {
+        uint64_t* dst = lists + (((int64_t)row * lists_per_row + (int64_t)split * ncopies + c) * b + r) * KB;
+#pragma unroll
+        for (int j = 0; j < KB; ++j) dst[j] = q[e][j];
+      }
+    }
+  }
+}
+
+// Any b: one thread walks one bucket r, r + b, r + 2b, ... of one row.
+template <int DT, int KB>
+__global__ __launch_bounds__(256) void bucket_generic_kernel(const uint8_t* __restrict__ x, int64_t ld_bytes, int n,
+                                                            int b, uint64_t* __restrict__ lists) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  const int row = blockIdx.y;
+  if (r >= b) return;
+  const uint8_t* xr = x + (int64_t)row * ld_bytes;
+  uint64_t q[KB];
+#pragma unroll
+  for (int j = 0; j < KB; ++j) q[j] = 0;
+  for (int64_t i = r; i < n; i += b) queue_insert<KB>(q, make_key(ord_f32(load_elem_bits<DT>(xr, i)), (uint32_t)i));
+  uint64_t* dst = lists + ((int64_t)row * b + r) * KB;
+#pragma unroll
+  for (int j = 0; j < KB; ++j) dst[j] = q[j];
+}
+
+__device__ __forceinline__ void write_result(uint8_t* out_vals, int32_t* out_idx, int64_t o, const uint8_t* xr,
+                                             int dt, uint64_t key) {
+  const uint32_t idx = key_idx(key);
+  out_idx[o] = (int32_t)idx;
+  if (dt == IN_F32) {
+    reinterpret_cast<uint32_t*>(out_vals)[o] = reinterpret_cast<const uint32_t*>(xr)[idx];
+  } else {
+    reinterpret_cast<uint16_t*>(out_vals)[o] = reinterpret_cast<const uint16_t*>(xr)[idx];
+  }
+}
+
+constexpr int kFinishThreads = 256;
+
+// mode 0: write the stage-1 candidates bucket-major; mode 1: final exact
+// top-k in LDS; mode 2: write merged candidate keys to cand_out.
+template <int KB>
+__global__ __launch_bounds__(kFinishThreads) void bucket_finish_kernel(const uint64_t* __restrict__ lists, int nl,
+                                                                      int b, int k, int mode,
+                                                                      int kb, const uint8_t* __restrict__ x, int dt,
+                                                                      int64_t ld_bytes, uint8_t* out_vals,
+                                                                      int32_t* out_idx, uint64_t* cand_out) {
+  constexpr int T = kFinishThreads;
+  __shared__ uint64_t cand[kFinishMaxCand];
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t ctl[8];
+  const int t = threadIdx.x;
+  const int row = blockIdx.x;
+  const uint8_t* xr = x + (int64_t)row * ld_bytes;
+  const int64_t nc = (int64_t)b * kb;
+
+  for (int r = t; r < b; r += T) {
+    uint64_t a[KB];
+    const uint64_t* src = lists + ((int64_t)row * nl * b + r) * KB;
+#pragma unroll
+    for (int j = 0; j < KB; ++j) a[j] = src[j];
+    for (int l = 1; l < nl; ++l) {
+      uint64_t o[KB];
+      const uint64_t* s2 = src + (int64_t)l * b * KB;
+#pragma unroll
+      for (int j = 0; j < KB; ++j) o[j] = s2[j];
+      queue_merge<KB>(a, o);
+    }
+    if (mode == 0) {
+#pragma unroll
+      for (int j = 0; j < KB; ++j)
+        if (j < kb) write_result(out_vals, out_idx, (int64_t)row * nc + (int64_t)r * kb + j, xr, dt, a[j]);
+    } else if (mode == 1) {
+#pragma unroll
+      for (int j = 0; j < KB; ++j)
+        if (j < kb) cand[r * kb + j] = a[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < KB; ++j)
+        if (j < kb) cand_out[(int64_t)row * nc + (int64_t)r * kb + j] = a[j];
+    }
+  }
+  if (mode != 1) return;
+  __syncthreads();
+  int cnt = (int)nc;
+  if (cnt > k) {
+    const uint64_t thr = block_kth_key<T>(cand, cnt, k, hist, ctl);
+    cnt = block_compact_ge<T, kFinishMaxCand / T>(cand, cnt, thr, ctl);
+  }
+  int npow = 1;
+  while (npow < k) npow <<= 1;
+  for (int i = cnt + t; i < npow; i += T) cand[i] = 0;
+  block_sort_desc<T>(cand, npow);
+  for (int j = t; j < k; j += T) write_result(out_vals, out_idx, (int64_t)row * k + j, xr, dt, cand[j]);
+}
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+template <int DT>
+hipError_t launch_stage1_dt(const BucketPlan& p, const void* x, int64_t m, int64_t n, int64_t ldx, int64_t b,
+                            int64_t kb, uint64_t* lists, hipStream_t s) {
+  const int64_t ld_bytes = ldx * VecOf<DT>::ES;
+  const uint8_t* xb = static_cast<const uint8_t*>(x);
+  if (p.fast) {
+    const int V = VecOf<DT>::V;
+    const int W = kStage1Threads * V;
+    const bool wave_has_all = kWave * V >= b;
+    const int ncopies = wave_has_all ? kStage1Threads / kWave : (int)(W / b);
+    const int lds_merge = (int64_t)ncopies * b * kb_slots(kb) * 8 <= kStage1LdsBytes;
+    dim3 grid((unsigned)p.splits, (unsigned)m);
+#define ATOPK_S1(KBV)                                                                                          \
+  case KBV:                                                                                                    \
+    hipLaunchKernelGGL((bucket_stage1_kernel<DT, KBV>), grid, dim3(kStage1Threads), 0, s, xb, ld_bytes, (int)n, \
+                       (int)b, p.chunk, lds_merge, p.lists_per_row, lists);                                   \
+    break;
+    switch (kb_slots(kb)) {
+      ATOPK_S1(1) ATOPK_S1(2) ATOPK_S1(4) ATOPK_S1(8) ATOPK_S1(16)
+      default: return hipErrorInvalidValue;
+    }
+#undef ATOPK_S1
+  } else {
+    dim3 grid((unsigned)((b + 255) / 256), (unsigned)m);
+#define ATOPK_G(KBV)                                                                                                   \
+  case KBV:                                                                                                            \
+    hipLaunchKernelGGL((bucket_generic_kernel<DT, KBV>), grid, dim3(256), 0, s, xb, ld_bytes, (int)n, (int)b, lists); \
+    break;
+    switch (kb_slots(kb)) {
+      ATOPK_G(1) ATOPK_G(2) ATOPK_G(4) ATOPK_G(8) ATOPK_G(16)
+      default: return hipErrorInvalidValue;
+    }
+#undef ATOPK_G
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+BucketPlan plan_bucketed(int dtype, int64_t m, int64_t n, int64_t b, int64_t kb, bool aligned) {
+  BucketPlan p{};
+  const int V = dtype == IN_F32 ? 4 : 8;
+  const int W = kStage1Threads * V;
+  p.threads = kStage1Threads;
+  p.fast = aligned && is_pow2(b) && b <= W && (int64_t)V * kb_slots(kb) <= 64;
+  if (!p.fast) {
+    p.splits = 1;
+    p.chunk = n;
+    p.lists_per_row = 1;
+    return p;
+  }
+  // Long chunks amortise the per-workgroup merge; enough of them fill the chip.
+  const int64_t sweeps = (n + W - 1) / W;
+  int64_t splits = (kTargetBlocks + m - 1) / (m > 0 ? m : 1);
+  splits = std::min<int64_t>(splits, std::max<int64_t>(1, sweeps / 8));
+  splits = std::max<int64_t>(splits, 1);
+  const int64_t chunk_sweeps = (sweeps + splits - 1) / splits;
+  p.chunk = chunk_sweeps * W;
+  p.splits = (int)((n + p.chunk - 1) / p.chunk);
+  const bool wave_has_all = (int64_t)kWave * V >= b;
+  const int ncopies = wave_has_all ? kStage1Threads / kWave : (int)(W / b);
+  const bool lds_merge = (int64_t)ncopies * b * kb_slots(kb) * 8 <= kStage1LdsBytes;
+  p.lists_per_row = p.splits * (lds_merge ? 1 : ncopies);
+  return p;
+}
+
+hipError_t launch_bucket_stage1(const BucketPlan& p, const void* x, int dtype, int64_t m, int64_t n, int64_t ldx,
+                                int64_t b, int64_t kb, uint64_t* lists, hipStream_t s) {
+  if (dtype == IN_F32) return launch_stage1_dt<IN_F32>(p, x, m, n, ldx, b, kb, lists, s);
+  return launch_stage1_dt<IN_BF16>(p, x, m, n, ldx, b, kb, lists, s);
+}
+
+hipError_t launch_bucket_finish(const uint64_t* lists, int lists_per_row, int64_t m, int64_t b, int64_t kb, int64_t k,
+                                int final_exact, const void* x, int dtype, int64_t ldx, void* out_vals,
+                                int32_t* out_idx, uint64_t* cand_out, hipStream_t s) {
+  const int64_t es = dtype == IN_F32 ? 4 : 2;
+  int mode = 0;
+  if (final_exact) mode = (b * kb <= kFinishMaxCand) ? 1 : 2;
+  dim3 grid((unsigned)m);
+#define ATOPK_F(KBV)                                                                                               \
+  case KBV:                                                                                                        \
+    hipLaunchKernelGGL((bucket_finish_kernel<KBV>), grid, dim3(kFinishThreads), 0, s, lists, lists_per_row, (int)b, \
+                       (int)k, mode, (int)kb, static_cast<const uint8_t*>(x), dtype, ldx * es,                     \
+                       static_cast<uint8_t*>(out_vals), out_idx, cand_out);                                        \
+    break;
+  switch (kb_slots(kb)) {
+    ATOPK_F(1) ATOPK_F(2) ATOPK_F(4) ATOPK_F(8) ATOPK_F(16)
+    default: return hipErrorInvalidValue;
+  }
+#undef ATOPK_F
+  return hipGetLastError();
+}
+
+}  // namespace atopk
