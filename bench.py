@@ -6,7 +6,7 @@ Workload (one "step"): the 256 x 131072 bf16 vocabulary-sampling batch
 exact top-64, bucketed (b, k_b) = (64, 1) without the final stage, and
 bucketed (128, 2) with the final exact top-64.  Inputs are resident in HBM
 before timing starts; each library call is bracketed by HIP events on the
-stream it runs on, after a 1 GiB write that evicts the L2 and Infinity Cache
+stream it runs on, after a 1 GiB read that evicts the L2 and Infinity Cache
 (timing protocol after the benchmark protocol printed with "Approximate
 Top-k for Increased Parallelism": warm-up, then events around each top-k
 launch queued behind a short spin kernel).
@@ -77,13 +77,17 @@ def recorded_traffic(name):
 
 class EventTimer:
     """Times callables with HIP events on the current stream, behind a cache
-    flush and a short spin so that the events are queued before the work."""
+    flush and a short spin so that the events are queued before the work.
+
+    The flush READS 1 GiB (more than the 4 MB-per-XCD L2 plus the 256 MB
+    Infinity Cache), leaving only clean lines behind: a write-based flush
+    leaves dirty lines whose write-back would compete with the timed reads."""
 
     def __init__(self, flush):
         import torch
 
         self.torch = torch
-        self.flush_buf = None if not flush else torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        self.flush_buf = None if not flush else torch.ones(1 << 28, dtype=torch.float32, device="cuda")
 
     def run(self, calls, steps, warmup):
         torch = self.torch
@@ -96,7 +100,7 @@ class EventTimer:
         for _ in range(steps):
             for name, fn in calls:
                 if self.flush_buf is not None:
-                    self.flush_buf.fill_(1)
+                    self.flush_sink = self.flush_buf.sum()
                 torch.cuda._sleep(20000)
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)

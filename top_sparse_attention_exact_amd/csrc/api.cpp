@@ -76,8 +76,15 @@ size_t exact_ws_bytes(int dtype, int64_t m, int64_t n, int64_t k) {
   return c.off;
 }
 
+bool rows_aligned(const void* x, int64_t ldx, int64_t es) {
+  return ((reinterpret_cast<uintptr_t>(x) | (uintptr_t)(ldx * es)) & 15) == 0;
+}
+
 int run_exact(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k, void* out_vals,
               int32_t* out_idx, void* ws, hipStream_t s) {
+  const int64_t es = dtype == ATOPK_F32 ? 4 : 2;
+  if (row_exact_ok(dtype, m, n, k, rows_aligned(x, ldx, es)))
+    return hip_status(launch_row_exact(x, dtype, m, n, ldx, k, out_vals, out_idx, s));
   const ExactPlan p = plan_exact(dtype, m, n, k);
   if (p.splits <= 1) return hip_status(launch_exact(p, x, dtype, m, n, ldx, k, nullptr, x, dtype, ldx, out_vals, out_idx, s));
   uint64_t* part = static_cast<uint64_t*>(ws);
@@ -134,7 +141,9 @@ int run_bucketed(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, in
                  int final_exact, void* out_vals, int32_t* out_idx, void* ws, hipStream_t s) {
   if (exact_route(k, b, kb)) return run_exact(x, dtype, m, n, ldx, k, out_vals, out_idx, ws, s);
   const int64_t es = dtype == ATOPK_F32 ? 4 : 2;
-  const bool aligned = ((reinterpret_cast<uintptr_t>(x) | (uintptr_t)(ldx * es)) & 15) == 0;
+  const bool aligned = rows_aligned(x, ldx, es);
+  if (row_bucket_ok(dtype, m, n, b, kb, aligned))
+    return hip_status(launch_row_bucket(x, dtype, m, n, ldx, k, b, kb, final_exact, out_vals, out_idx, s));
   const BucketLayout L = bucket_layout(dtype, m, n, b, kb, final_exact, aligned);
   uint8_t* w = static_cast<uint8_t*>(ws);
   uint64_t* lists = reinterpret_cast<uint64_t*>(w + L.lists_off);

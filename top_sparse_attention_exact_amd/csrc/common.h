@@ -96,6 +96,13 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  lo = (uint32_t)__shfl((int)lo, src, kWave);
+  hi = (uint32_t)__shfl((int)hi, src, kWave);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 // Inclusive prefix sum over the wave.
 __device__ __forceinline__ int wave_incl_scan(int v) {
   const int l = lane_id();
@@ -116,6 +123,135 @@ __device__ __forceinline__ int wave_sum(int v) {
 // ------------------------------------------------------ block helpers -----
 //
 // All block helpers must be called by every thread of the block.
+
+// Workgroup barrier that orders LDS only.  __syncthreads() also fences
+// global memory, which makes every wave wait for its outstanding global
+// loads at the barrier; this one leaves prefetched loads in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Sort one key per lane descending across the wave (bitonic, lane = rank).
+__device__ __forceinline__ uint64_t wave_sort64_desc(uint64_t key) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int size = 2; size <= kWave; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const uint64_t o = shfl_xor_u64(key, stride);
+      const bool desc = (lane & size) == 0;
+      const bool lower = (lane & stride) == 0;
+      key = (lower == desc) ? kmax(key, o) : kmin(key, o);
+    }
+  }
+  return key;
+}
+
+// Sort 64*P keys held P per lane (key index lane*P + p) descending, bitonic.
+template <int P>
+__device__ __forceinline__ void wave_sort_desc(uint64_t (&key)[P]) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int size = 2; size <= kWave * P; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      if (stride < P) {
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          if ((p & stride) == 0) {
+            const bool desc = ((lane * P + p) & size) == 0;
+            const uint64_t a = key[p], c = key[p + stride];
+            key[p] = desc ? kmax(a, c) : kmin(a, c);
+            key[p + stride] = desc ? kmin(a, c) : kmax(a, c);
+          }
+        }
+      } else {
+        const int ls = stride / P;
+        const bool lower = (lane & ls) == 0;
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          const bool desc = ((lane * P + p) & size) == 0;
+          const uint64_t o = shfl_xor_u64(key[p], ls);
+          key[p] = (lower == desc) ? kmax(key[p], o) : kmin(key[p], o);
+        }
+      }
+    }
+  }
+}
+
+// Number of keys greater than x in a descending run of 64 keys (0..64).
+__device__ __forceinline__ int run_count_greater(const uint64_t* run, uint64_t x) {
+  if (run[kWave - 1] > x) return kWave;
+  int lo = 0;  // invariant: run[lo - 1] > x (or lo == 0), answer < 64
+#pragma unroll
+  for (int step = 32; step > 0; step >>= 1)
+    if (run[lo + step - 1] > x) lo += step;
+  return lo;
+}
+
+// a := the 64 largest of two descending 64-runs, a in registers (one key
+// per lane) and b in LDS: lane p takes max(a_p, b_{63-p}), a bitonic
+// sequence holding the 64 largest, which six half-cleaner steps sort.
+__device__ __forceinline__ uint64_t wave_merge_top64(uint64_t a, const uint64_t* b) {
+  const int lane = lane_id();
+  uint64_t m = kmax(a, b[kWave - 1 - lane]);
+#pragma unroll
+  for (int stride = kWave / 2; stride > 0; stride >>= 1) {
+    const uint64_t o = shfl_xor_u64(m, stride);
+    m = (lane & stride) == 0 ? kmax(m, o) : kmin(m, o);
+  }
+  return m;
+}
+
+// Rank of `key` among the 64-key descending runs runs[0..nr) (LDS): its
+// place `own_rank` in its own run `own` plus, per other run, the number of
+// larger keys -- one binary search per run, all runs advanced in lockstep so
+// their LDS reads overlap.
+template <int MAXR>
+__device__ __forceinline__ int rank_in_runs(const uint64_t* runs, int nr, int own, int own_rank, uint64_t key) {
+  int lo[MAXR];
+#pragma unroll
+  for (int r = 0; r < MAXR; ++r) lo[r] = (r < nr && r != own && runs[r * kWave + kWave - 1] > key) ? kWave : 0;
+#pragma unroll
+  for (int step = 32; step > 0; step >>= 1) {
+#pragma unroll
+    for (int r = 0; r < MAXR; ++r) {
+      if (r < nr && r != own && lo[r] < kWave) {
+        if (runs[r * kWave + lo[r] + step - 1] > key) lo[r] += step;
+      }
+    }
+  }
+  int rank = own_rank;
+#pragma unroll
+  for (int r = 0; r < MAXR; ++r) rank += (r < nr && r != own) ? lo[r] : 0;
+  return rank;
+}
+
+// Exact top-k of n <= T unique nonzero keys in cand[] (LDS), written in
+// descending order through write(rank, key): every wave sorts a run of 64,
+// then each key's rank is its place in its run plus, per other run, the
+// count of larger keys found by binary search.  `runs` holds 64*ceil(n/64)
+// keys and may alias cand.
+template <int T, typename Writer>
+__device__ void block_sortmerge_final(const uint64_t* cand, uint64_t* runs, int n, int k, Writer&& write) {
+  const int t = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = t / kWave;
+  const int nr = (n + kWave - 1) / kWave;
+  uint64_t key = t < n ? cand[t] : 0;
+  __syncthreads();
+  if (wave < nr) {
+    key = wave_sort64_desc(key);
+    runs[wave * kWave + lane] = key;
+  }
+  __syncthreads();
+  if (wave < nr && key != 0) {
+    const int rank = rank_in_runs<T / kWave>(runs, nr, wave, lane, key);
+    if (rank < k) write(rank, key);
+  }
+}
 
 // The threshold key t such that exactly k of the n unique keys in `keys`
 // (LDS) are >= t (radix select, 8-bit digits from the top).  `hist` is a

@@ -54,6 +54,15 @@ hipError_t launch_exact(const ExactPlan& p, const void* x, int in_kind, int64_t 
                         int64_t k, uint64_t* part, const void* src, int src_dtype, int64_t src_ld,
                         void* out_vals, int32_t* out_idx, hipStream_t s);
 
+// ---- one workgroup per row (single launch, no workspace) -------------------
+
+bool row_bucket_ok(int dtype, int64_t m, int64_t n, int64_t b, int64_t kb, bool aligned);
+bool row_exact_ok(int dtype, int64_t m, int64_t n, int64_t k, bool aligned);
+hipError_t launch_row_bucket(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k, int64_t b,
+                             int64_t kb, int final_exact, void* out_vals, int32_t* out_idx, hipStream_t s);
+hipError_t launch_row_exact(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k, void* out_vals,
+                            int32_t* out_idx, hipStream_t s);
+
 // ---- decode -------------------------------------------------------------------
 
 // scores[(i*hq + h)*ctx + j] = scale * <q[i, h], K[i, h / g, j]> (fp32).

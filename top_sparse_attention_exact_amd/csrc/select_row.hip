@@ -1,0 +1,586 @@
+// One workgroup per row: single-launch exact and bucketed top-k for batches
+// with enough rows to occupy the chip (one 1024-thread workgroup per CU).
+//
+// Bucketed ("Approximate Top-k for Increased Parallelism", Pith review page,
+// "What carries the argument"): every lane keeps a sorted k_b-queue per
+// element slot of its 16-byte loads.  For bf16 the key is packed into 32 bits
+// -- the 16-bit order key of the value above a 16-bit complemented ordinal
+// of the element inside its bucket (i = r + b*j) -- so a queue insert is one
+// v_max_u32 plus one v_med3_u32 per further slot, and the value/tie order is
+// decided by one unsigned compare.  Queues of lanes that share a bucket are
+// merged by cross-lane shuffles, then by a tree across the 16 waves through
+// LDS, and the final exact top-k of the b*k_b candidates is taken in LDS.
+//
+// Exact (same page, "The reading"; Figures 11-14 on radix select and its
+// tie "collect" step): the row is streamed once through a threshold filter.
+// The first tile seeds the threshold with a provable lower bound of the k-th
+// largest value -- in each of the 16 waves the ceil(k/16)-th largest of its
+// 64 lane maxima; 16*ceil(k/16) >= k distinct elements reach the smallest of
+// those -- so from the start only a small fraction of elements is appended
+// to the LDS candidate buffer, which is compacted by radix select when full.
+#include <type_traits>
+
+#include "common.h"
+#include "launch.h"
+
+namespace atopk {
+
+namespace {
+
+constexpr int kRowT = 1024;
+constexpr int kRowWaves = kRowT / kWave;
+constexpr int kRowLds = 65536;  // bytes: tree-merge exchange, then final candidates
+
+typedef int16_t i16x2 __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+// Order keys of the two bf16 halves of w, packed the same way: per 16-bit
+// half, a positive h maps to h ^ 0x8000 and a negative h to -h mod 2^16, so
+// -0.0 and +0.0 both map to 0x8000 (packed 16-bit integer ops, 4 per word).
+__device__ __forceinline__ uint32_t ord_bf16x2(uint32_t w) {
+  const i16x2 s = __builtin_bit_cast(i16x2, w);
+  const u16x2 m = __builtin_bit_cast(u16x2, (i16x2)(s >> (i16x2)(15)));
+  const u16x2 u = __builtin_bit_cast(u16x2, w) ^ (m | (u16x2)(0x8000));
+  return __builtin_bit_cast(uint32_t, (u16x2)(u - m));
+}
+
+// bf16 bits of a 16-bit order key (0x8000 -> +0.0).
+__device__ __forceinline__ uint16_t bf16_from_ord16(uint32_t o) {
+  return (uint16_t)((o & 0x8000u) ? (o & 0x7fffu) : ((0x10000u - o) & 0xffffu));
+}
+
+// Final exact top-k of n <= kRowT unique keys in LDS, written sorted with no
+// sort: the rank of a key (how many keys beat it) is its output position.
+// `per` threads share one key, each counting over a strided part of the set.
+template <typename Writer>
+__device__ __forceinline__ void block_rank_final(const uint64_t* cand, int n, int k, Writer&& write) {
+  const int t = threadIdx.x;
+  int per = 1;
+  while (per < kWave && n * per * 2 <= kRowT) per *= 2;
+  const int c = t / per;
+  const int part = t % per;
+  if (c < n) {
+    const uint64_t key = cand[c];
+    // parts interleave (j = part + per*m) so a wave reads `per` adjacent
+    // keys per step: distinct banks, each broadcast to its group
+    int cnt0 = 0, cnt1 = 0, cnt2 = 0, cnt3 = 0;
+    int j = part;
+    for (; j + 3 * per < n; j += 4 * per) {
+      cnt0 += cand[j] > key ? 1 : 0;
+      cnt1 += cand[j + per] > key ? 1 : 0;
+      cnt2 += cand[j + 2 * per] > key ? 1 : 0;
+      cnt3 += cand[j + 3 * per] > key ? 1 : 0;
+    }
+    for (; j < n; j += per) cnt0 += cand[j] > key ? 1 : 0;
+    int cnt = cnt0 + cnt1 + cnt2 + cnt3;
+    for (int o = per / 2; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, kWave);
+    if (part == 0 && cnt < k) write(cnt, key);
+  }
+}
+
+// Exact top-k of n unique keys in LDS, sorted, written through `write`
+// (every thread calls; n <= kRowLds / 8).
+template <typename Writer>
+__device__ void block_final(uint64_t* cand, int n, int k, uint32_t* hist, uint32_t* ctl, Writer&& write) {
+  const int t = threadIdx.x;
+  if (n <= 256) {
+    block_rank_final(cand, n, k, write);
+    return;
+  }
+  if (n <= kRowT) {
+    block_sortmerge_final<kRowT>(cand, cand, n, k, write);
+    return;
+  }
+  int cnt = n;
+  if (cnt > k) {
+    const uint64_t thr = block_kth_key<kRowT>(cand, cnt, k, hist, ctl);
+    cnt = block_compact_ge<kRowT, (kRowLds / 8) / kRowT>(cand, cnt, thr, ctl);
+  }
+  if (cnt <= kRowT) {
+    block_sortmerge_final<kRowT>(cand, cand, cnt, k, write);
+    return;
+  }
+  int npow = 1;
+  while (npow < k) npow <<= 1;
+  for (int i = cnt + t; i < npow; i += kRowT) cand[i] = 0;
+  block_sort_desc<kRowT>(cand, npow);
+  for (int j = t; j < k; j += kRowT) write(j, cand[j]);
+}
+
+// Maximum over the wave: DPP inside each row of 16 lanes, then the 4 rows.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xb1, 0xf, 0xf, true));   // quad_perm 1,0,3,2
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4e, 0xf, 0xf, true));   // quad_perm 2,3,0,1
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xf, 0xf, true));  // row_half_mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xf, 0xf, true));  // row_mirror
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(a, b), max(c, d));
+}
+
+// c-th largest (1-based, duplicates counted) of one value per lane: c rounds
+// of "take the maximum, retire one lane holding it".
+__device__ __forceinline__ uint32_t wave_cth_largest(uint32_t v, int c) {
+  uint32_t m = 0;
+  for (int r = 0; r < c; ++r) {
+    m = wave_max_u32(v);
+    const uint64_t hit = __ballot(v == m);
+    const int first = __builtin_ctzll(hit);
+    if (lane_id() == first) v = 0;
+  }
+  return m;
+}
+
+// ------------------------------------------------------------- bucketed ----
+
+template <int KB, bool FINAL>
+__global__ __launch_bounds__(kRowT) void row_bucket_bf16_kernel(const uint8_t* __restrict__ x, int64_t ld_bytes,
+                                                               int n, int b, int kb, int k,
+                                                               uint16_t* __restrict__ out_vals,
+                                                               int32_t* __restrict__ out_idx) {
+  constexpr int T = kRowT;
+  constexpr int V = 8;        // bf16 per 16-byte load
+  constexpr int U = 4;        // loads in flight per lane
+  constexpr int SW = T * V;   // elements per sweep
+  __shared__ __align__(16) uint8_t smem[kRowLds];
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t ctl[8];
+  uint32_t* xch = reinterpret_cast<uint32_t*>(smem);
+  uint64_t* cand = reinterpret_cast<uint64_t*>(smem);
+
+  const int t = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = t / kWave;
+  const int row = blockIdx.x;
+  const uint16_t* xr = reinterpret_cast<const uint16_t*>(x + (int64_t)row * ld_bytes);
+
+  uint32_t q[V][KB];
+#pragma unroll
+  for (int e = 0; e < V; ++e)
+#pragma unroll
+    for (int j = 0; j < KB; ++j) q[e][j] = 0;
+
+  // Element (t, e) of sweep s has index s*SW + t*V + e, bucket (t*V + e) mod b
+  // and ordinal j = s*(SW/b) + (t*V)/b inside its bucket (b >= 8, b | SW).
+  const uint32_t step = (uint32_t)(SW / b);
+  const uint32_t pos0 = 0xffffu - (uint32_t)((t * V) / b);
+  const int full_sweeps = n / SW;
+
+  auto consume = [&](const uint4& w, uint32_t pos) {
+    const uint32_t word[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const uint32_t o = ord_bf16x2(word[h]);
+      queue_insert<KB>(q[2 * h], (o << 16) | pos);
+      queue_insert<KB>(q[2 * h + 1], (o & 0xffff0000u) | pos);
+    }
+  };
+
+  int s = 0;
+  for (; s + U <= full_sweeps; s += U) {
+    uint4 w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) w[u] = *reinterpret_cast<const uint4*>(xr + (int64_t)(s + u) * SW + t * V);
+#pragma unroll
+    for (int u = 0; u < U; ++u) consume(w[u], pos0 - (uint32_t)(s + u) * step);
+  }
+  for (; s < full_sweeps; ++s) consume(*reinterpret_cast<const uint4*>(xr + (int64_t)s * SW + t * V), pos0 - (uint32_t)s * step);
+  if ((int64_t)s * SW < n) {  // ragged last sweep, element by element
+    const uint32_t pos = pos0 - (uint32_t)s * step;
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const int64_t i = (int64_t)s * SW + t * V + e;
+      if (i < n) {
+        const uint32_t o = ord_bf16x2((uint32_t)xr[i]) << 16;
+        queue_insert<KB>(q[e], o | pos);
+      }
+    }
+  }
+
+  // Lanes l and l ^ m hold the same buckets when 8*m is a multiple of b.
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) {
+    if (m * V >= b) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        uint32_t o[KB];
+#pragma unroll
+        for (int j = 0; j < KB; ++j) o[j] = (uint32_t)__shfl_xor((int)q[e][j], m, kWave);
+        queue_merge<KB>(q[e], o);
+      }
+    }
+  }
+  const int64_t nc = (int64_t)b * kb;
+  // Bucket r's final top-k_b -> bucket-major output, or a final-stage key.
+  auto emit = [&](int r, const uint32_t (&a)[KB]) {
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      if (j < kb) {
+        const uint32_t key = a[j];
+        const uint32_t idx = (uint32_t)r + (uint32_t)b * (0xffffu - (key & 0xffffu));
+        if constexpr (FINAL) {
+          cand[r * kb + j] = make_key(key & 0xffff0000u, idx);
+        } else {
+          const uint32_t o16 = key >> 16;
+          const int64_t at = (int64_t)row * nc + (int64_t)r * kb + j;
+          out_idx[at] = (int32_t)idx;
+          out_vals[at] = o16 == 0x8000u ? xr[idx] : bf16_from_ord16(o16);
+        }
+      }
+    }
+  };
+
+  if (b <= kWave * V && kRowWaves * b * KB * 4 <= kRowLds) {
+    // Every wave holds all b buckets (lanes with lane*8 + e < b): one LDS
+    // exchange, then thread r merges the 16 copies of bucket r.
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const int r = lane * V + e;
+      if (r < b) {
+#pragma unroll
+        for (int j = 0; j < KB; ++j) xch[(wave * b + r) * KB + j] = q[e][j];
+      }
+    }
+    __syncthreads();
+    uint32_t a[KB];
+    if (t < b) {
+#pragma unroll
+      for (int j = 0; j < KB; ++j) a[j] = xch[t * KB + j];
+      uint32_t o[kRowWaves - 1][KB];
+#pragma unroll
+      for (int w2 = 1; w2 < kRowWaves; ++w2)
+#pragma unroll
+        for (int j = 0; j < KB; ++j) o[w2 - 1][j] = xch[(w2 * b + t) * KB + j];
+#pragma unroll
+      for (int w2 = 1; w2 < kRowWaves; ++w2) queue_merge<KB>(a, o[w2 - 1]);
+    }
+    __syncthreads();
+    if (t < b) emit(t, a);
+  } else {
+    // Tree across waves: waves w and w + st hold the same buckets when
+    // 512 * st is a multiple of b.
+    const int smin = b > kWave * V ? b / (kWave * V) : 1;
+    for (int st = kRowWaves / 2; st >= smin; st >>= 1) {
+      if (wave >= st && wave < 2 * st) {
+#pragma unroll
+        for (int e = 0; e < V; ++e)
+#pragma unroll
+          for (int j = 0; j < KB; ++j) xch[(((wave - st) * kWave + lane) * V + e) * KB + j] = q[e][j];
+      }
+      __syncthreads();
+      if (wave < st) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          uint32_t o[KB];
+#pragma unroll
+          for (int j = 0; j < KB; ++j) o[j] = xch[((wave * kWave + lane) * V + e) * KB + j];
+          queue_merge<KB>(q[e], o);
+        }
+      }
+      __syncthreads();
+    }
+    // Waves < smin now hold every bucket once: slot p = wave*512 + lane*8 + e
+    // is bucket p when b >= 512; for b < 512 the lanes with lane*8 + e < b.
+    if (wave < smin) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const int r = wave * kWave * V + lane * V + e;
+        if (r < b) emit(r, q[e]);
+      }
+    }
+  }
+  if constexpr (FINAL) {
+    __syncthreads();
+    block_final(cand, (int)nc, k, hist, ctl, [&](int i, uint64_t key) {
+      const uint32_t idx = key_idx(key);
+      const uint32_t o16 = key_ord(key) >> 16;
+      out_idx[(int64_t)row * k + i] = (int32_t)idx;
+      out_vals[(int64_t)row * k + i] = o16 == 0x8000u ? xr[idx] : bf16_from_ord16(o16);
+    });
+  }
+}
+
+// ---------------------------------------------------------------- exact ----
+
+template <int DT>
+struct RowIn {
+  static constexpr int V = DT == IN_F32 ? 4 : 8;  // elements per 16-byte load
+  static constexpr int U = 4;                      // loads per lane per tile
+  static constexpr int ES = DT == IN_F32 ? 4 : 2;
+};
+
+// Order key (ord32) of element e of a 16-byte vector.
+template <int DT>
+__device__ __forceinline__ uint32_t ord_elem(const uint4& w, int e) {
+  const uint32_t word[4] = {w.x, w.y, w.z, w.w};
+  if constexpr (DT == IN_F32) {
+    return ord_f32(word[e]);
+  } else {
+    const uint32_t p = ord_bf16x2(word[e >> 1]);
+    return (e & 1) ? (p & 0xffff0000u) : (p << 16);
+  }
+}
+
+// Load vector u of a tile: whole 16-byte loads when the tile is inside the
+// row, element by element (zero-filled) in the row's last tile.
+template <int DT, int T>
+__device__ __forceinline__ void load_tile(const uint8_t* xr, int64_t base, int n, int t, uint4 (&w)[RowIn<DT>::U]) {
+  constexpr int V = RowIn<DT>::V, U = RowIn<DT>::U, ES = RowIn<DT>::ES;
+  const int64_t tile = (int64_t)T * V * U;
+  if (base + tile <= n) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) w[u] = *reinterpret_cast<const uint4*>(xr + (base + (int64_t)u * T * V + t * V) * ES);
+  } else {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      uint32_t word[4] = {0, 0, 0, 0};
+      const int64_t i0 = base + (int64_t)u * T * V + t * V;
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        if (i0 + e < n) {
+          if constexpr (DT == IN_F32) {
+            word[e] = reinterpret_cast<const uint32_t*>(xr)[i0 + e];
+          } else {
+            word[e >> 1] |= (uint32_t)reinterpret_cast<const uint16_t*>(xr)[i0 + e] << ((e & 1) * 16);
+          }
+        }
+      }
+      w[u] = make_uint4(word[0], word[1], word[2], word[3]);
+    }
+  }
+}
+
+// Every wave keeps its own candidate region in LDS and its own threshold, so
+// the streaming loop has no workgroup barrier: the wave's top-k of the
+// elements it reads contains the row's top-k restricted to those elements.
+// Lower bounds of the row's k-th largest value are shared through LDS
+// without synchronisation (each published value is valid whenever read).
+constexpr int kRowExactMaxK = 64;
+constexpr int kWaveRegion = kRowLds / 8 / kRowWaves;  // keys per wave (256)
+
+// Keep the wave's top-k of its region (cnt keys) at the front; return the
+// order key of the k-th (the wave's new lower bound) -- wave-synchronous.
+__device__ __noinline__ uint32_t wave_compact_region(uint64_t* mine, int cnt, int k) {
+  constexpr int P = kWaveRegion / kWave;
+  const int lane = lane_id();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
+  uint64_t key[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int i = lane * P + p;
+    key[p] = i < cnt ? mine[i] : 0;
+  }
+  wave_sort_desc<P>(key);
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int i = lane * P + p;
+    if (i < k) mine[i] = key[p];
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
+  uint64_t kth = 0;
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+    if (lane * P + p == k - 1) kth = key[p];
+  return (uint32_t)(shfl_u64(kth, (k - 1) / P) >> 32);
+}
+
+// Largest order key among the elements of a 16-byte vector.
+template <int DT>
+__device__ __forceinline__ uint32_t vec_max_ord(const uint4& w) {
+  const uint32_t word[4] = {w.x, w.y, w.z, w.w};
+  if constexpr (DT == IN_F32) {
+    return max(max(ord_f32(word[0]), ord_f32(word[1])), max(ord_f32(word[2]), ord_f32(word[3])));
+  } else {
+    u16x2 m = __builtin_bit_cast(u16x2, ord_bf16x2(word[0]));
+#pragma unroll
+    for (int h = 1; h < 4; ++h) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, ord_bf16x2(word[h])));
+    return (uint32_t)max(m.x, m.y) << 16;
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kRowT) void row_exact_kernel(const uint8_t* __restrict__ x, int64_t ld_bytes, int n, int k,
+                                                         uint8_t* __restrict__ out_vals,
+                                                         int32_t* __restrict__ out_idx) {
+  constexpr int T = kRowT;
+  constexpr int V = RowIn<DT>::V;
+  constexpr int U = RowIn<DT>::U;
+  constexpr int ES = RowIn<DT>::ES;
+  constexpr int TILE = T * U * V;
+  __shared__ uint64_t buf[kRowLds / 8];
+  __shared__ uint32_t wthr[kRowWaves];
+  volatile uint32_t* pub = wthr;  // read fresh every tile, written without barriers
+
+  const int t = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = t / kWave;
+  const int row = blockIdx.x;
+  const uint8_t* xr = x + (int64_t)row * ld_bytes;
+  uint64_t* mine = buf + wave * kWaveRegion;
+  const int cpw = (k + kRowWaves - 1) / kRowWaves;  // lane maxima each wave vouches for
+
+  uint32_t lmax = 0;  // largest order key this lane has seen
+  uint32_t thr = 1;   // filter: order key >= thr (real keys are >= 0x00800000)
+  int cnt = 0;        // keys in this wave's region (wave-uniform)
+  bool first = true;
+
+  // One tile: lane t holds elements base + u*T*V + t*V + e.  `full` tiles are
+  // whole 16-byte vectors; the last, partial tile is zero-filled and checked.
+  auto tile = [&](const uint4 (&w)[U], int64_t base, auto full_c) {
+    constexpr bool full = decltype(full_c)::value;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (full) {
+        lmax = max(lmax, vec_max_ord<DT>(w[u]));
+      } else {
+#pragma unroll
+        for (int e = 0; e < V; ++e)
+          if (base + (int64_t)u * T * V + t * V + e < n) lmax = max(lmax, ord_elem<DT>(w[u], e));
+      }
+    }
+    // The c-th largest lane maximum of each wave, c = ceil(k / 16): 16 * c
+    // >= k distinct elements reach the smallest of the 16 published values.
+    const uint32_t tc = wave_cth_largest(lmax, cpw);
+    if (lane == 0) pub[wave] = tc;
+    if (first) {
+      lds_barrier();  // every wave has published once
+      first = false;
+    }
+    uint32_t th = 0xffffffffu;
+#pragma unroll
+    for (int w2 = 0; w2 < kRowWaves; ++w2) th = min(th, pub[w2]);
+    thr = max(thr, th);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const uint32_t idx0 = (uint32_t)(base + u * T * V + t * V + e);
+        const uint32_t oe = ord_elem<DT>(w[u], e);
+        bool pass = oe >= thr && (full || (int64_t)idx0 < n);
+        uint64_t mask = __ballot(pass);
+        if (mask) {
+          if (cnt + kWave > kWaveRegion) {  // region full: keep the wave's top-k
+            thr = max(thr, wave_compact_region(mine, cnt, k));
+            cnt = k;
+            pass = pass && oe >= thr;
+            mask = __ballot(pass);
+          }
+          const uint32_t idx = (uint32_t)(base + u * T * V + t * V + e);
+          if (pass) mine[cnt + lanes_below(mask)] = make_key(oe, idx);
+          cnt += __popcll(mask);
+        }
+      }
+    }
+  };
+
+  const int nfull = n / TILE;
+  uint4 w[U];
+  if (nfull > 0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) w[u] = *reinterpret_cast<const uint4*>(xr + ((int64_t)u * T * V + t * V) * ES);
+  }
+  for (int it = 0; it < nfull; ++it) {
+    const int64_t base = (int64_t)it * TILE;
+    uint4 wn[U];
+    if (it + 1 < nfull) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        wn[u] = *reinterpret_cast<const uint4*>(xr + (base + TILE + (int64_t)u * T * V + t * V) * ES);
+    }
+    tile(w, base, std::true_type{});
+#pragma unroll
+    for (int u = 0; u < U; ++u) w[u] = wn[u];
+  }
+  if ((int64_t)nfull * TILE < n) {
+    load_tile<DT, T>(xr, (int64_t)nfull * TILE, n, t, w);
+    tile(w, (int64_t)nfull * TILE, std::false_type{});
+  }
+
+  // Each wave reduces its region to its top-min(k, cnt), sorted: a run of 64;
+  // a tree of pairwise top-64 merges across the waves leaves the row's top-k
+  // (k <= 64) in wave 0, lane = rank.
+  if (cnt > kWave) {
+    wave_compact_region(mine, cnt, k);
+    cnt = k;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
+  uint64_t key = lane < cnt ? mine[lane] : 0;
+  key = wave_sort64_desc(key);
+  uint64_t* runs = buf;  // run w at buf[64 w]
+  __syncthreads();
+  for (int st = kRowWaves / 2; st >= 1; st >>= 1) {
+    if (wave >= st && wave < 2 * st) runs[(wave - st) * kWave + lane] = key;
+    __syncthreads();
+    if (wave < st) key = wave_merge_top64(key, runs + wave * kWave);
+    __syncthreads();
+  }
+  if (wave == 0 && lane < k && key != 0) {
+    const uint32_t idx = key_idx(key);
+    const int64_t at = (int64_t)row * k + lane;
+    out_idx[at] = (int32_t)idx;
+    if constexpr (DT == IN_F32) {
+      reinterpret_cast<uint32_t*>(out_vals)[at] = reinterpret_cast<const uint32_t*>(xr)[idx];
+    } else {
+      reinterpret_cast<uint16_t*>(out_vals)[at] = reinterpret_cast<const uint16_t*>(xr)[idx];
+    }
+  }
+}
+
+}  // namespace
+
+bool row_bucket_ok(int dtype, int64_t m, int64_t n, int64_t b, int64_t kb, bool aligned) {
+  if (dtype != IN_BF16 || !aligned) return false;
+  if (b < 8 || b > 8192 || (b & (b - 1)) != 0) return false;
+  if (n / b > 65535 + 1) return false;  // ordinal fits 16 bits
+  if ((n + b - 1) / b > 65536) return false;
+  if (kb > 4) return false;
+  if (b * kb > kRowLds / 8) return false;
+  if ((int64_t)(kRowWaves / 2) * kWave * 8 * (kb <= 1 ? 1 : kb <= 2 ? 2 : 4) * 4 > kRowLds) return false;
+  return m >= 128 || n <= 65536;
+}
+
+bool row_exact_ok(int dtype, int64_t m, int64_t n, int64_t k, bool aligned) {
+  if (!aligned || k > kRowExactMaxK) return false;
+  return m >= 128 || n <= 65536;
+}
+
+hipError_t launch_row_bucket(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k, int64_t b,
+                             int64_t kb, int final_exact, void* out_vals, int32_t* out_idx, hipStream_t s) {
+  (void)dtype;
+  const int64_t ld_bytes = ldx * 2;
+  const uint8_t* xb = static_cast<const uint8_t*>(x);
+  uint16_t* ov = static_cast<uint16_t*>(out_vals);
+  dim3 grid((unsigned)m);
+  const int kbs = kb <= 1 ? 1 : kb <= 2 ? 2 : 4;
+#define ATOPK_RB(KBV, FIN)                                                                                  \
+  hipLaunchKernelGGL((row_bucket_bf16_kernel<KBV, FIN>), grid, dim3(kRowT), 0, s, xb, ld_bytes, (int)n, \
+                     (int)b, (int)kb, (int)k, ov, out_idx)
+  if (final_exact) {
+    if (kbs == 1) ATOPK_RB(1, true);
+    else if (kbs == 2) ATOPK_RB(2, true);
+    else ATOPK_RB(4, true);
+  } else {
+    if (kbs == 1) ATOPK_RB(1, false);
+    else if (kbs == 2) ATOPK_RB(2, false);
+    else ATOPK_RB(4, false);
+  }
+#undef ATOPK_RB
+  return hipGetLastError();
+}
+
+hipError_t launch_row_exact(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k, void* out_vals,
+                            int32_t* out_idx, hipStream_t s) {
+  dim3 grid((unsigned)m);
+  const uint8_t* xb = static_cast<const uint8_t*>(x);
+  uint8_t* ov = static_cast<uint8_t*>(out_vals);
+  if (dtype == IN_F32) {
+    hipLaunchKernelGGL((row_exact_kernel<IN_F32>), grid, dim3(kRowT), 0, s, xb, ldx * 4, (int)n, (int)k, ov, out_idx);
+  } else {
+    hipLaunchKernelGGL((row_exact_kernel<IN_BF16>), grid, dim3(kRowT), 0, s, xb, ldx * 2, (int)n, (int)k, ov, out_idx);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace atopk
