@@ -270,7 +270,9 @@ def test_decode_ctx_stride(gpu):
     V = torch.randn((1, 4, 4000, 128), generator=g).to(torch.bfloat16).to(gpu)
     out, sel, sc = atk.sparse_attn_decode(q, K, V, 32, 32, 1, ctx=2500, return_sel=True, return_scores=True)
     assert int(sel.max()) < 2500
-    ref = atk.sparse_attn_decode(q, K[:, :, :2500].contiguous(), V[:, :, :2500].contiguous(), 32, 32, 1)
+    ref, rsel = atk.sparse_attn_decode(q, K[:, :, :2500].contiguous(), V[:, :, :2500].contiguous(), 32, 32, 1,
+                                       return_sel=True)
+    assert torch.equal(sel, rsel)
     assert torch.equal(out, ref)
 
 

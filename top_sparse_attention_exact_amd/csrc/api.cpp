@@ -174,19 +174,27 @@ int validate_decode(int64_t batch, int64_t hq, int64_t hkv, int64_t ctx, int64_t
 }
 
 struct DecodeLayout {
-  size_t scores_off, vals_off, idx_off, sel_ws_off, total;
+  DecodePlan plan;
+  size_t partial_off;                                      // fused path
+  size_t scores_off, vals_off, idx_off, sel_ws_off;        // separate passes
   size_t sel_ws_bytes;
+  size_t total;
 };
 
-DecodeLayout decode_layout(int64_t batch, int64_t hq, int64_t ctx, int64_t k_sel, int64_t b, int64_t kb) {
+DecodeLayout decode_layout(int64_t batch, int64_t hq, int64_t hkv, int64_t ctx, int64_t k_sel, int64_t b, int64_t kb) {
   DecodeLayout L{};
-  const int64_t rows = batch * hq;
+  L.plan = plan_decode(batch, hq, hkv, ctx, k_sel, b, kb);
   Carve c;
-  L.scores_off = c.take((size_t)rows * ctx * 4);
-  L.vals_off = c.take((size_t)rows * k_sel * 4);
-  L.idx_off = c.take((size_t)rows * k_sel * 4);
-  L.sel_ws_bytes = bucketed_ws_bytes(ATOPK_F32, rows, ctx, k_sel, b, kb, 1);
-  L.sel_ws_off = c.take(L.sel_ws_bytes);
+  if (L.plan.fused) {
+    L.partial_off = c.take(L.plan.partial_bytes);
+  } else {
+    const int64_t rows = batch * hq;
+    L.scores_off = c.take((size_t)rows * ctx * 4);
+    L.vals_off = c.take((size_t)rows * k_sel * 4);
+    L.idx_off = c.take((size_t)rows * k_sel * 4);
+    L.sel_ws_bytes = bucketed_ws_bytes(ATOPK_F32, rows, ctx, k_sel, b, kb, 1);
+    L.sel_ws_off = c.take(L.sel_ws_bytes);
+  }
   L.total = c.off;
   return L;
 }
@@ -284,7 +292,7 @@ int atopk_sparse_attn_decode_workspace(int64_t batch, int64_t hq, int64_t hkv, i
     if (ws_bytes == nullptr) return (int)ATOPK_ERR_NULL;
     int st = validate_decode(batch, hq, hkv, ctx, ctx, d, k_sel, b, kb);
     if (st) return st;
-    *ws_bytes = batch == 0 ? 0 : decode_layout(batch, hq, ctx, k_sel, b, kb).total;
+    *ws_bytes = batch == 0 ? 0 : decode_layout(batch, hq, hkv, ctx, k_sel, b, kb).total;
     return (int)ATOPK_OK;
   });
 }
@@ -300,24 +308,31 @@ int atopk_sparse_attn_decode(const void* q, const void* K, const void* V, int64_
     if (!q || !K || !V || !out) return (int)ATOPK_ERR_NULL;
     if (((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(K) | reinterpret_cast<uintptr_t>(V)) & 15) != 0)
       return (int)ATOPK_ERR_UNSUPPORTED;
-    const DecodeLayout L = decode_layout(batch, hq, ctx, k_sel, b, kb);
+    const DecodeLayout L = decode_layout(batch, hq, hkv, ctx, k_sel, b, kb);
     st = check_ws(ws, ws_bytes, L.total);
     if (st) return st;
     st = check_device();
     if (st) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint8_t* w = static_cast<uint8_t*>(ws);
+    const uint16_t* q16 = static_cast<const uint16_t*>(q);
+    const uint16_t* k16 = static_cast<const uint16_t*>(K);
+    const uint16_t* v16 = static_cast<const uint16_t*>(V);
+    if (L.plan.fused) {
+      return hip_status(launch_decode_fused(L.plan, q16, k16, v16, batch, hq, hkv, ctx, ctx_stride, scale, k_sel, b,
+                                            kb, reinterpret_cast<uint64_t*>(w + L.partial_off),
+                                            static_cast<uint16_t*>(out), sel_idx, scores, s));
+    }
     float* sc = scores ? scores : reinterpret_cast<float*>(w + L.scores_off);
     float* vals = reinterpret_cast<float*>(w + L.vals_off);
     int32_t* idx = sel_idx ? sel_idx : reinterpret_cast<int32_t*>(w + L.idx_off);
     const int64_t rows = batch * hq;
-    if (launch_decode_scores(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(K), batch, hq, hkv, ctx,
-                             ctx_stride, scale, sc, s) != hipSuccess)
+    if (launch_decode_scores(q16, k16, batch, hq, hkv, ctx, ctx_stride, scale, sc, s) != hipSuccess)
       return (int)ATOPK_ERR_HIP;
     st = run_bucketed(sc, ATOPK_F32, rows, ctx, ctx, k_sel, b, kb, 1, vals, idx, w + L.sel_ws_off, s);
     if (st) return st;
-    return hip_status(launch_sparse_softmax_v(vals, idx, static_cast<const uint16_t*>(V), batch, hq, hkv, ctx_stride,
-                                              k_sel, static_cast<uint16_t*>(out), s));
+    return hip_status(launch_sparse_softmax_v(vals, idx, v16, batch, hq, hkv, ctx_stride, k_sel,
+                                              static_cast<uint16_t*>(out), s));
   });
 }
 

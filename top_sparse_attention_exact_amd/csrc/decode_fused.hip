@@ -1,0 +1,336 @@
+// Fused top-K sparse-attention decode: scoring + bucketed stage 1 in one
+// pass over K, then per query head the merge, the final exact Top-K and the
+// softmax / value aggregation over the selected keys.
+//
+// "Recall Before You Rank ..." (fugumt page), Abstract: score the current
+// query against the full KV cache, select a global Top-K, run softmax and
+// value aggregation over that subset only.  "Approximate Top-k for Increased
+// Parallelism" (Pith review page), "What carries the argument": the bucketed
+// two-stage selection that replaces the single global Top-K.
+//
+// Kernel 1 (grid: context chunks x (batch, KV head)): 16 lanes read one
+// 256-byte key row with 16-byte loads and form its dot products with the g
+// query heads that share the KV head (packed bf16 dot products, fp32
+// accumulation, DPP row sums).  Scores of 512 keys at a time are staged in
+// LDS (double buffered, one LDS-only barrier per step, so K loads stay in
+// flight); then every thread folds the staged scores of the (head, bucket)
+// pairs it owns into sorted k_b-queues of 64-bit keys (order key of the
+// score, then ~key index).  Scores never go to HBM unless a debug dump is
+// asked for.  Each workgroup writes its per-pair lists to the workspace.
+//
+// Kernel 2 (grid: batch x query heads): merge the chunk lists of every
+// bucket, take the exact Top-K of the b*k_b candidates in LDS (radix select),
+// optionally sort them for the index output, then softmax over the selected
+// scores (maximum subtracted, fp32) and the weighted sum of the gathered V
+// rows, rounded to bf16.
+#include "common.h"
+#include "launch.h"
+
+namespace atopk {
+
+namespace {
+
+constexpr int kD = 128;
+constexpr int kT1 = 256;
+constexpr int kSub = 512;          // keys staged per step
+constexpr int kSubPad = kSub + 1;  // LDS row pitch (heads on different banks)
+constexpr int kMaxG = 8;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot8_bf16(const uint4& a, const uint4& b) {
+  float acc = 0.0f;
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.x), __builtin_bit_cast(bf16x2_t, b.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.y), __builtin_bit_cast(bf16x2_t, b.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.z), __builtin_bit_cast(bf16x2_t, b.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.w), __builtin_bit_cast(bf16x2_t, b.w), acc, false);
+  return acc;
+}
+
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xb1, 0xf, 0xf, true));   // quad_perm 1,0,3,2
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4e, 0xf, 0xf, true));   // quad_perm 2,3,0,1
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xf, 0xf, true));  // row_half_mirror
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xf, 0xf, true));  // row_mirror
+  return v;
+}
+
+// PPT (head, bucket) pairs per thread, KB queue slots per pair.
+template <int PPT, int KB>
+__global__ __launch_bounds__(kT1) void decode_select_kernel(const uint16_t* __restrict__ q,
+                                                           const uint16_t* __restrict__ K, int hq, int hkv,
+                                                           int ctx, int64_t ctx_stride, float scale, int b,
+                                                           int64_t chunk, int nchunks,
+                                                           uint64_t* __restrict__ partial,
+                                                           float* __restrict__ scores) {
+  constexpr int U = 8;                 // keys in flight per 16-lane group
+  constexpr int PASSES = kSub / (16 * U);
+  __shared__ float sc[2][kMaxG][kSubPad];
+
+  const int t = threadIdx.x;
+  const int sub = t & 15;   // 16-byte slice of a key row
+  const int slot = t >> 4;  // key slot (16 per workgroup step)
+  const int bh = blockIdx.y;
+  const int bi = bh / hkv;
+  const int h = bh - bi * hkv;
+  const int G = hq / hkv;
+  const int c = blockIdx.x;
+  const int j0 = (int)(c * chunk);
+  const int j1 = (int)min((int64_t)ctx, (int64_t)j0 + chunk);
+
+  uint4 qv[kMaxG];
+#pragma unroll
+  for (int g = 0; g < kMaxG; ++g)
+    qv[g] = g < G ? *reinterpret_cast<const uint4*>(q + ((int64_t)(bi * hq + h * G + g) * kD + sub * 8))
+                  : make_uint4(0, 0, 0, 0);
+  const uint16_t* kh = K + (int64_t)bh * ctx_stride * kD + sub * 8;
+
+  uint64_t qq[PPT][KB];
+#pragma unroll
+  for (int i = 0; i < PPT; ++i)
+#pragma unroll
+    for (int j = 0; j < KB; ++j) qq[i][j] = 0;
+  const int npairs = G * b;
+
+  int buf = 0;
+  for (int s0 = j0; s0 < j1; s0 += kSub) {
+    const int s1 = min(j1, s0 + kSub);
+    // score keys s0 + slot + 16 * (u + U * p)
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      uint4 kv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int jj = s0 + slot + 16 * (u + U * p);
+        kv[u] = jj < s1 ? *reinterpret_cast<const uint4*>(kh + (int64_t)jj * kD) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int li = slot + 16 * (u + U * p);
+#pragma unroll
+        for (int g = 0; g < kMaxG; ++g) {
+          if (g < G) {
+            const float s = row16_sum(dot8_bf16(kv[u], qv[g])) * scale;
+            if (sub == g) sc[buf][g][li] = s;
+          }
+        }
+      }
+    }
+    lds_barrier();
+    const int nk = s1 - s0;
+    if (scores != nullptr) {  // debug dump, coalesced
+      for (int i = t; i < G * nk; i += kT1) {
+        const int g = i / nk, li = i - g * nk;
+        scores[(int64_t)(bi * hq + h * G + g) * ctx + s0 + li] = sc[buf][g][li];
+      }
+    }
+    // fold the staged scores of the owned (head, bucket) pairs: bucket r
+    // holds keys j with j mod b == r
+    const int rs = s0 % b;
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int pr = t + kT1 * i;
+      if (pr < npairs) {
+        const int g = pr / b;
+        const int r = pr - g * b;
+        for (int li = r - rs + (r < rs ? b : 0); li < nk; li += b) {
+          const uint32_t bits = __float_as_uint(sc[buf][g][li]);
+          queue_insert<KB>(qq[i], make_key(ord_f32(bits), (uint32_t)(s0 + li)));
+        }
+      }
+    }
+    buf ^= 1;
+  }
+#pragma unroll
+  for (int i = 0; i < PPT; ++i) {
+    const int pr = t + kT1 * i;
+    if (pr < npairs) {
+      const int g = pr / b;
+      const int r = pr - g * b;
+      uint64_t* dst = partial + ((((int64_t)bh * nchunks + c) * G + g) * b + r) * KB;
+#pragma unroll
+      for (int j = 0; j < KB; ++j) dst[j] = qq[i][j];
+    }
+  }
+}
+
+constexpr int kT2 = 256;
+constexpr int kMaxCand = 8192;
+
+template <int KB>
+__global__ __launch_bounds__(kT2) void decode_finish_kernel(const uint64_t* __restrict__ partial, int nchunks, int hq,
+                                                           int hkv, int b, int kb, int k_sel,
+                                                           const uint16_t* __restrict__ V, int64_t ctx_stride,
+                                                           uint16_t* __restrict__ out, int32_t* __restrict__ sel_idx) {
+  constexpr int T = kT2;
+  __shared__ uint64_t cand[kMaxCand];
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t ctl[8];
+  __shared__ float acc_lds[16][kD];
+  __shared__ float w_lds[16];
+  __shared__ float red[T / kWave];
+
+  const int t = threadIdx.x;
+  const int r_out = blockIdx.x;  // = bi * hq + hh
+  const int bi = r_out / hq;
+  const int hh = r_out - bi * hq;
+  const int G = hq / hkv;
+  const int kvh = hh / G;
+  const int g = hh - kvh * G;
+  const int bh = bi * hkv + kvh;
+
+  // merge the chunk lists of every bucket
+  for (int r = t; r < b; r += T) {
+    uint64_t a[KB];
+    const uint64_t* src = partial + ((((int64_t)bh * nchunks) * G + g) * b + r) * KB;
+    const int64_t cstride = (int64_t)G * b * KB;
+#pragma unroll
+    for (int j = 0; j < KB; ++j) a[j] = src[j];
+    for (int c = 1; c < nchunks; ++c) {
+      uint64_t o[KB];
+#pragma unroll
+      for (int j = 0; j < KB; ++j) o[j] = src[c * cstride + j];
+      queue_merge<KB>(a, o);
+    }
+#pragma unroll
+    for (int j = 0; j < KB; ++j)
+      if (j < kb) cand[r * kb + j] = a[j];
+  }
+  __syncthreads();
+  int n = b * kb;
+  if (n > k_sel) {
+    const uint64_t thr = block_kth_key<T>(cand, n, k_sel, hist, ctl);
+    n = block_compact_ge<T, kMaxCand / T>(cand, n, thr, ctl);
+  }
+  if (sel_idx != nullptr) {
+    int npow = 1;
+    while (npow < n) npow <<= 1;
+    for (int i = n + t; i < npow; i += T) cand[i] = 0;
+    block_sort_desc<T>(cand, npow);
+    for (int i = t; i < n; i += T) sel_idx[(int64_t)r_out * k_sel + i] = (int32_t)key_idx(cand[i]);
+  }
+  __syncthreads();
+
+  // softmax over the selected scores, weighted sum of their V rows
+  float mx = -INFINITY;
+  for (int i = t; i < n; i += T) mx = fmaxf(mx, key_value_f32(cand[i]));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+  if (lane_id() == 0) red[t / kWave] = mx;
+  __syncthreads();
+  mx = red[0];
+#pragma unroll
+  for (int w = 1; w < T / kWave; ++w) mx = fmaxf(mx, red[w]);
+
+  constexpr int U = 4;
+  const int group = t >> 4;
+  const int sub = t & 15;
+  const uint16_t* vh = V + (int64_t)bh * ctx_stride * kD + sub * 8;
+  float acc[8];
+#pragma unroll
+  for (int d = 0; d < 8; ++d) acc[d] = 0.0f;
+  float wsum = 0.0f;
+  for (int i = group; i < n; i += 16 * U) {
+    uint4 v[U];
+    float w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int ii = i + 16 * u;
+      if (ii < n) {
+        const uint64_t key = cand[ii];
+        v[u] = *reinterpret_cast<const uint4*>(vh + (int64_t)key_idx(key) * kD);
+        w[u] = expf(key_value_f32(key) - mx);
+      } else {
+        v[u] = make_uint4(0, 0, 0, 0);
+        w[u] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t word[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        acc[2 * d] += w[u] * __uint_as_float(word[d] << 16);
+        acc[2 * d + 1] += w[u] * __uint_as_float(word[d] & 0xffff0000u);
+      }
+      wsum += w[u];
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < 8; ++d) acc_lds[group][sub * 8 + d] = acc[d];
+  if (sub == 0) w_lds[group] = wsum;
+  __syncthreads();
+  if (t < kD) {
+    float s = 0.0f, wt = 0.0f;
+#pragma unroll
+    for (int gg = 0; gg < 16; ++gg) {
+      s += acc_lds[gg][t];
+      wt += w_lds[gg];
+    }
+    out[(int64_t)r_out * kD + t] = f32_to_bf16_rne(s / wt);
+  }
+}
+
+int kb_pow2(int64_t kb) {
+  int v = 1;
+  while (v < kb) v <<= 1;
+  return v;
+}
+
+}  // namespace
+
+DecodePlan plan_decode(int64_t batch, int64_t hq, int64_t hkv, int64_t ctx, int64_t k_sel, int64_t b, int64_t kb) {
+  DecodePlan p{};
+  const int64_t g = hq / hkv;
+  const int kbs = kb_pow2(kb);
+  int ppt = 1;
+  while ((int64_t)ppt * kT1 < g * b) ppt *= 2;
+  p.ppt = ppt;
+  p.fused = !(b == 1 && kb == k_sel) && ppt <= 8 && (int64_t)ppt * kbs <= 64 && b * kb <= kMaxCand && kbs <= 16;
+  // chunks: enough workgroups to fill the chip, long enough that the lists
+  // written per chunk stay small next to the K bytes read
+  const int64_t heads = batch * hkv;
+  int64_t nchunks = std::max<int64_t>(1, (512 + heads - 1) / std::max<int64_t>(heads, 1));
+  nchunks = std::min<int64_t>(nchunks, std::max<int64_t>(1, ctx / 4096));
+  int64_t chunk = (ctx + nchunks - 1) / nchunks;
+  chunk = (chunk + kSub - 1) / kSub * kSub;
+  p.chunk = chunk;
+  p.nchunks = (int)((ctx + chunk - 1) / chunk);
+  p.partial_bytes = (size_t)heads * p.nchunks * g * b * kbs * 8;
+  return p;
+}
+
+hipError_t launch_decode_fused(const DecodePlan& p, const uint16_t* q, const uint16_t* K, const uint16_t* V,
+                               int64_t batch, int64_t hq, int64_t hkv, int64_t ctx, int64_t ctx_stride, float scale,
+                               int64_t k_sel, int64_t b, int64_t kb, uint64_t* partial, uint16_t* out,
+                               int32_t* sel_idx, float* scores, hipStream_t s) {
+  const int kbs = kb_pow2(kb);
+  dim3 g1((unsigned)p.nchunks, (unsigned)(batch * hkv));
+#define ATOPK_D1(P, KBV)                                                                                           \
+  if (p.ppt == P && kbs == KBV) {                                                                                  \
+    hipLaunchKernelGGL((decode_select_kernel<P, KBV>), g1, dim3(kT1), 0, s, q, K, (int)hq, (int)hkv, (int)ctx,      \
+                       ctx_stride, scale, (int)b, p.chunk, p.nchunks, partial, scores);                             \
+  } else
+  ATOPK_D1(1, 1) ATOPK_D1(1, 2) ATOPK_D1(1, 4) ATOPK_D1(1, 8) ATOPK_D1(1, 16)
+  ATOPK_D1(2, 1) ATOPK_D1(2, 2) ATOPK_D1(2, 4) ATOPK_D1(2, 8) ATOPK_D1(2, 16)
+  ATOPK_D1(4, 1) ATOPK_D1(4, 2) ATOPK_D1(4, 4) ATOPK_D1(4, 8) ATOPK_D1(4, 16)
+  ATOPK_D1(8, 1) ATOPK_D1(8, 2) ATOPK_D1(8, 4) ATOPK_D1(8, 8)
+  { return hipErrorInvalidValue; }
+#undef ATOPK_D1
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 g2((unsigned)(batch * hq));
+#define ATOPK_D2(KBV)                                                                                              \
+  case KBV:                                                                                                        \
+    hipLaunchKernelGGL((decode_finish_kernel<KBV>), g2, dim3(kT2), 0, s, partial, p.nchunks, (int)hq, (int)hkv,     \
+                       (int)b, (int)kb, (int)k_sel, V, ctx_stride, out, sel_idx);                                  \
+    break;
+  switch (kbs) {
+    ATOPK_D2(1) ATOPK_D2(2) ATOPK_D2(4) ATOPK_D2(8) ATOPK_D2(16)
+    default: return hipErrorInvalidValue;
+  }
+#undef ATOPK_D2
+  return hipGetLastError();
+}
+
+}  // namespace atopk

@@ -69,6 +69,21 @@ hipError_t launch_row_exact(const void* x, int dtype, int64_t m, int64_t n, int6
 hipError_t launch_decode_scores(const uint16_t* q, const uint16_t* K, int64_t batch, int64_t hq, int64_t hkv,
                                 int64_t ctx, int64_t ctx_stride, float scale, float* scores, hipStream_t s);
 
+// Fused decode: scoring + bucketed stage 1 per (batch, KV head, chunk), then
+// merge + final Top-K + softmax-V per query head.
+struct DecodePlan {
+  bool fused;            // false: scores, selection and softmax-V as separate passes
+  int ppt;               // (head, bucket) pairs per thread in the scoring kernel
+  int64_t chunk;         // keys per scoring workgroup
+  int nchunks;
+  size_t partial_bytes;  // per-chunk k_b-lists
+};
+DecodePlan plan_decode(int64_t batch, int64_t hq, int64_t hkv, int64_t ctx, int64_t k_sel, int64_t b, int64_t kb);
+hipError_t launch_decode_fused(const DecodePlan& p, const uint16_t* q, const uint16_t* K, const uint16_t* V,
+                               int64_t batch, int64_t hq, int64_t hkv, int64_t ctx, int64_t ctx_stride, float scale,
+                               int64_t k_sel, int64_t b, int64_t kb, uint64_t* partial, uint16_t* out,
+                               int32_t* sel_idx, float* scores, hipStream_t s);
+
 // out[r] = softmax(sel_vals[r]) @ V[sel_idx[r]] for r = i*hq + h.
 hipError_t launch_sparse_softmax_v(const float* sel_vals, const int32_t* sel_idx, const uint16_t* V,
                                    int64_t batch, int64_t hq, int64_t hkv, int64_t ctx_stride, int64_t k_sel,
