@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="all", help="all | exact | b64k1 | b128k2 | mha | gqa")
+    ap.add_argument("--only", default="all", help="all | exact | b64k1 | b128k2 | mha | gqa | sel4k | wide")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between calls (warm numbers)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
@@ -205,6 +205,42 @@ def decode_steps(args, timer):
     return res
 
 
+def other_selection(args, timer):
+    """The 1 x 4096 fp32 and 64 x 2^20 fp32 selection workloads (secondary)."""
+    import numpy as np
+    import torch
+
+    import top_sparse_attention_exact_amd as atk
+    from top_sparse_attention_exact_amd import workloads
+
+    res = {}
+    todo = [w for w in ("sel4k", "wide") if args.only in ("all", w)]
+    for w in todo:
+        if w == "sel4k":
+            c = workloads.SELECTION["sel-4k"]
+            x = workloads.rows_uniform(c["m"], c["n"], seed=0, device="cuda")
+        else:
+            c = workloads.SELECTION["wide-1m"]
+            x = workloads.rows_planted_residues(c["m"], c["n"], 512, c["k"], seed=0, device="cuda")
+        m, n, k = c["m"], c["n"], c["k"]
+        calls = [("exact", lambda: atk.exact(x, k))]
+        for b, kb, fin in c["modes"]:
+            calls.append(("b%dk%d%s" % (b, kb, "_final" if fin else ""),
+                          (lambda b=b, kb=kb, fin=fin: atk.bucketed(x, k, b, kb, fin))))
+        torch.cuda.synchronize()
+        ms, _ = timer.run(calls, max(3, min(args.steps, 10)), 2)
+        out = {"m": m, "n": n, "k": k, "dtype": "f32"}
+        for name, _ in calls:
+            t = float(np.mean(ms[name])) * 1e-3
+            alg = m * n * 4 + m * k * 8
+            out[name] = {"us": round(t * 1e6, 2), "elements_per_s": m * n / t, "gbps": alg / t / 1e9,
+                         "frac_hbm_peak": alg / t / 1e9 / HBM_PEAK_GBPS}
+        res["sel-4k" if w == "sel4k" else "wide-1m"] = out
+        del x
+        torch.cuda.empty_cache()
+    return res
+
+
 def cpu_leg(sel, seconds):
     """The CPU oracle (as it stands) on a bounded sample of the same batch."""
     import numpy as np
@@ -250,6 +286,7 @@ def main():
     timer = EventTimer(flush=not args.no_flush)
     sel = selection_step(args, timer) if args.only in ("all", "exact", "b64k1", "b128k2") else None
     dec = decode_steps(args, timer) if (not args.no_decode and args.only in ("all", "mha", "gqa")) else {}
+    other = other_selection(args, timer) if args.only in ("all", "sel4k", "wide") else {}
 
     line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
@@ -274,12 +311,18 @@ def main():
             "recall": sel["recall"],
             "wall_ms_per_step": sel["wall_s"] / args.steps * 1e3,
         })
-    else:
+    elif dec:
         first = next(iter(dec.values()))
         line.update({"value": first["bucketed"]["scores_per_s"], "unit": "scores/s",
                      "ms_per_step": first["bucketed"]["us_per_step"] / 1e3, "config": {"workload": first["workload"]}})
+    else:
+        name, first = next(iter(other.items()))
+        line.update({"value": first["exact"]["elements_per_s"], "unit": "elements/s",
+                     "ms_per_step": first["exact"]["us"] / 1e3, "config": {"workload": name}})
     if dec:
         line["decode"] = dec
+    if other:
+        line["other_selection"] = other
     if sel is not None and not args.no_cpu_baseline:
         cpu, ref = cpu_leg(sel, args.cpu_seconds)
         line["cpu_baseline"] = cpu
