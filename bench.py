@@ -5,21 +5,27 @@ Workload (one "step"): the 256 x 131072 bf16 vocabulary-sampling batch
 (N(0, 2^2) logits, k = 64) through every selection mode of the path:
 exact top-64, bucketed (b, k_b) = (64, 1) without the final stage, and
 bucketed (128, 2) with the final exact top-64.  Inputs are resident in HBM
-before timing starts; each library call is bracketed by HIP events on the
-stream it runs on, after a 1 GiB read that evicts the L2 and Infinity Cache
+before timing starts.
+
+Throughput ("value", "us" per mode): K launches per mode back to back on one
+stream, queued behind a spin kernel so that the GPU never waits for the
+host, bracketed by HIP events on that stream; the launches rotate over
+enough copies of the batch (640 MB) that no launch finds its input in the
+256 MB Infinity Cache.  Latency ("us_cold"): single calls with HIP events
+around each, after a 1 GiB read that evicts the L2 and the Infinity Cache
 (timing protocol after the benchmark protocol printed with "Approximate
 Top-k for Increased Parallelism": warm-up, then events around each top-k
 launch queued behind a short spin kernel).
 
 The same run also times the sparse-attention decode steps (scoring, Top-K
-selection, softmax-V) of the two decode workloads, and times the CPU oracle
-on a bounded sample of the selection batch.
+selection, softmax-V) of the two decode workloads, the small-row and
+wide-row selection workloads, and the CPU oracle on a bounded sample of the
+selection batch.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--only MODE]
 """
 
 import argparse
-import glob
 import hashlib
 import json
 import math
@@ -40,18 +46,22 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="all", help="all | exact | b64k1 | b128k2 | mha | gqa | sel4k | wide")
-    ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between calls (warm numbers)")
+    ap.add_argument("--only", default="all", help="all | sel | exact | b64k1 | b128k2 | decode | mha | gqa | sel4k | wide | copy")
+    ap.add_argument("--no-flush", action="store_true", help="no cache flush before the single-call latency runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     return ap.parse_args()
 
 
+# Sources the selection kernels of the step are compiled from.
+KERNEL_SOURCES = ("common.h", "select_row.hip")
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "top_sparse_attention_exact_amd", "csrc", "*"))):
-        with open(p, "rb") as f:
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "top_sparse_attention_exact_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -76,28 +86,70 @@ def recorded_traffic(name):
 
 
 class EventTimer:
-    """Times callables with HIP events on the current stream, behind a cache
-    flush and a short spin so that the events are queued before the work.
+    """Times library calls with HIP events on torch's current stream (the
+    stream the library launches on).
 
-    The flush READS 1 GiB (more than the 4 MB-per-XCD L2 plus the 256 MB
-    Infinity Cache), leaving only clean lines behind: a write-based flush
-    leaves dirty lines whose write-back would compete with the timed reads."""
+    stream(): K launches per call back to back, queued behind a spin kernel
+    long enough that the whole batch is queued before the GPU reaches it
+    (checked: the first event must still be pending when queueing ends; the
+    spin grows and the batch is re-run otherwise).  Gives the average launch
+    duration with no host gaps.
+
+    cold(): one call at a time after a cache flush.  The flush READS 1 GiB
+    (more than the 4 MB-per-XCD L2 plus the 256 MB Infinity Cache), leaving
+    only clean lines: a write-based flush leaves dirty lines whose
+    write-back would compete with the timed reads."""
 
     def __init__(self, flush):
         import torch
 
         self.torch = torch
-        self.flush_buf = None if not flush else torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        self.flush = flush
+        self.flush_buf = None
+        self.spin = 1 << 21
 
-    def run(self, calls, steps, warmup):
+    def stream(self, calls, steps, warmup):
         torch = self.torch
-        for _ in range(warmup):
+        for w in range(warmup):
             for _, fn in calls:
-                fn()
+                fn(w)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            torch.cuda._sleep(self.spin)
+            first = torch.cuda.Event(enable_timing=True)
+            first.record()
+            ev = {}
+            for name, fn in calls:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for s in range(steps):
+                    fn(s)
+                e1.record()
+                ev[name] = (e0, e1)
+            ahead = not first.query()
+            last = ev[calls[-1][0]][1]
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+            if ahead:
+                break
+            self.spin *= 4
+        us = {name: e0.elapsed_time(e1) * 1e3 / steps for name, (e0, e1) in ev.items()}
+        gpu_s = first.elapsed_time(last) * 1e-3
+        return us, {"gpu_s": gpu_s, "wall_s": wall, "queued_ahead": ahead}
+
+    def cold(self, calls, steps, warmup):
+        torch = self.torch
+        if self.flush and self.flush_buf is None:
+            self.flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        for w in range(warmup):
+            for _, fn in calls:
+                fn(w)
         torch.cuda.synchronize()
         pairs = {name: [] for name, _ in calls}
-        t0 = time.perf_counter()
-        for _ in range(steps):
+        for s in range(steps):
             for name, fn in calls:
                 if self.flush_buf is not None:
                     self.flush_sink = self.flush_buf.sum()
@@ -105,13 +157,21 @@ class EventTimer:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record()
-                fn()
+                fn(s)
                 e1.record()
                 pairs[name].append((e0, e1))
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        ms = {name: [a.elapsed_time(b) for a, b in v] for name, v in pairs.items()}
-        return ms, wall
+        return {name: [a.elapsed_time(b) * 1e3 for a, b in v] for name, v in pairs.items()}
+
+
+def copies(x, min_bytes):
+    """x plus clones of it, together at least min_bytes."""
+    nb = x.numel() * x.element_size()
+    r = max(1, -(-min_bytes // nb))
+    return [x] + [x.clone() for _ in range(r - 1)]
+
+
+ROTATE_BYTES = 640 << 20
 
 
 def selection_step(args, timer):
@@ -124,33 +184,36 @@ def selection_step(args, timer):
     cfg = workloads.SELECTION["vocab-128k"]
     m, n, k = cfg["m"], cfg["n"], cfg["k"]
     x = workloads.rows_normal_bf16(m, n, 2.0, seed=0, device="cuda")
+    xs = copies(x, ROTATE_BYTES)
     torch.cuda.synchronize()
     outs = {}
 
     def mk(name, f):
-        def call():
-            outs[name] = f()
+        def call(i):
+            outs[name] = f(xs[i % len(xs)])
         return name, call
 
     calls = []
-    if args.only in ("all", "exact"):
-        calls.append(mk("exact", lambda: atk.exact(x, k)))
-    if args.only in ("all", "b64k1"):
-        calls.append(mk("b64k1", lambda: atk.bucketed(x, k, 64, 1, False)))
-    if args.only in ("all", "b128k2"):
-        calls.append(mk("b128k2", lambda: atk.bucketed(x, k, 128, 2, True)))
+    if args.only in ("all", "sel", "exact"):
+        calls.append(mk("exact", lambda t: atk.exact(t, k)))
+    if args.only in ("all", "sel", "b64k1"):
+        calls.append(mk("b64k1", lambda t: atk.bucketed(t, k, 64, 1, False)))
+    if args.only in ("all", "sel", "b128k2"):
+        calls.append(mk("b128k2", lambda t: atk.bucketed(t, k, 128, 2, True)))
     if not calls:
         return None
-    ms, wall = timer.run(calls, args.steps, args.warmup)
+    us, info = timer.stream(calls, args.steps, args.warmup)
+    cold = timer.cold(calls, max(3, min(args.steps, 10)), 1)
     width = {"exact": k, "b64k1": 64, "b128k2": k}
     modes = {}
     for name, _ in calls:
-        t = float(np.mean(ms[name])) * 1e-3
+        t = us[name] * 1e-6
         alg = m * n * 2 + m * width[name] * (2 + 4)
         modes[name] = {
-            "us": round(t * 1e6, 2),
-            "us_p10": round(float(np.percentile(ms[name], 10)) * 1e3, 2),
-            "us_p90": round(float(np.percentile(ms[name], 90)) * 1e3, 2),
+            "us": round(us[name], 2),
+            "us_cold": round(float(np.mean(cold[name])), 2),
+            "us_cold_p10": round(float(np.percentile(cold[name], 10)), 2),
+            "us_cold_p90": round(float(np.percentile(cold[name], 90)), 2),
             "elements_per_s": m * n / t,
             "alg_bytes": alg,
             "gbps": alg / t / 1e9,
@@ -165,18 +228,17 @@ def selection_step(args, timer):
                 r = [len(np.intersect1d(a, e)) / k for a, e in zip(got, ex)]
                 recall[name] = float(np.mean(r))
     step_s = sum(modes[nm]["us"] for nm in modes) * 1e-6
-    return dict(m=m, n=n, k=k, modes=modes, step_s=step_s, wall_s=wall, recall=recall, x=x)
+    return dict(m=m, n=n, k=k, modes=modes, step_s=step_s, info=info, recall=recall, x=x, copies=len(xs))
 
 
 def decode_steps(args, timer):
-    import numpy as np
     import torch
 
     import top_sparse_attention_exact_amd as atk
     from top_sparse_attention_exact_amd import workloads
 
     res = {}
-    todo = [w for w in ("mha", "gqa") if args.only in ("all", w)]
+    todo = [w for w in ("mha", "gqa") if args.only in ("all", "decode", w)]
     for w in todo:
         if w == "mha":
             c = workloads.DECODE["mha-32k"]
@@ -187,16 +249,17 @@ def decode_steps(args, timer):
                                               device="cuda")
         torch.cuda.synchronize()
         modes = [("bucketed", c["b"], c["kb"]), ("exact", 1, c["k_sel"])]
-        calls = [(name, (lambda b=b, kb=kb: atk.sparse_attn_decode(q, K, V, c["k_sel"], b, kb)))
+        calls = [(name, (lambda i, b=b, kb=kb: atk.sparse_attn_decode(q, K, V, c["k_sel"], b, kb)))
                  for name, b, kb in modes]
-        ms, _ = timer.run(calls, max(3, min(args.steps, 10)), 2)
+        us, info = timer.stream(calls, max(3, min(args.steps, 10)), 2)
         kbytes = K.numel() * 2
         alg = kbytes + q.numel() * 2 + c["bsz"] * c["hq"] * c["k_sel"] * c["d"] * 2 + q.numel() * 2
         out = {"workload": "%s-%dk" % (w, c["ctx"] // 1024), "B": c["bsz"], "Hq": c["hq"], "Hkv": c["hkv"],
-               "L": c["ctx"], "K_sel": c["k_sel"], "b": c["b"], "kb": c["kb"], "alg_bytes": alg}
+               "L": c["ctx"], "K_sel": c["k_sel"], "b": c["b"], "kb": c["kb"], "alg_bytes": alg,
+               "queued_ahead": info["queued_ahead"]}
         for name, _, _ in modes:
-            t = float(np.mean(ms[name])) * 1e-3
-            out[name] = {"us_per_step": round(t * 1e6, 1), "gbps": alg / t / 1e9,
+            t = us[name] * 1e-6
+            out[name] = {"us_per_step": round(us[name], 1), "gbps": alg / t / 1e9,
                          "frac_hbm_peak": alg / t / 1e9 / HBM_PEAK_GBPS,
                          "scores_per_s": c["bsz"] * c["hq"] * c["ctx"] / t}
         res[out["workload"]] = out
@@ -207,7 +270,6 @@ def decode_steps(args, timer):
 
 def other_selection(args, timer):
     """The 1 x 4096 fp32 and 64 x 2^20 fp32 selection workloads (secondary)."""
-    import numpy as np
     import torch
 
     import top_sparse_attention_exact_amd as atk
@@ -222,23 +284,37 @@ def other_selection(args, timer):
         else:
             c = workloads.SELECTION["wide-1m"]
             x = workloads.rows_planted_residues(c["m"], c["n"], 512, c["k"], seed=0, device="cuda")
+        xs = copies(x, ROTATE_BYTES)
         m, n, k = c["m"], c["n"], c["k"]
-        calls = [("exact", lambda: atk.exact(x, k))]
+        calls = [("exact", lambda i: atk.exact(xs[i % len(xs)], k))]
         for b, kb, fin in c["modes"]:
             calls.append(("b%dk%d%s" % (b, kb, "_final" if fin else ""),
-                          (lambda b=b, kb=kb, fin=fin: atk.bucketed(x, k, b, kb, fin))))
+                          (lambda i, b=b, kb=kb, fin=fin: atk.bucketed(xs[i % len(xs)], k, b, kb, fin))))
         torch.cuda.synchronize()
-        ms, _ = timer.run(calls, max(3, min(args.steps, 10)), 2)
-        out = {"m": m, "n": n, "k": k, "dtype": "f32"}
+        us, info = timer.stream(calls, max(3, min(args.steps, 10)), 2)
+        out = {"m": m, "n": n, "k": k, "dtype": "f32", "queued_ahead": info["queued_ahead"]}
         for name, _ in calls:
-            t = float(np.mean(ms[name])) * 1e-3
+            t = us[name] * 1e-6
             alg = m * n * 4 + m * k * 8
-            out[name] = {"us": round(t * 1e6, 2), "elements_per_s": m * n / t, "gbps": alg / t / 1e9,
+            out[name] = {"us": round(us[name], 2), "elements_per_s": m * n / t, "gbps": alg / t / 1e9,
                          "frac_hbm_peak": alg / t / 1e9 / HBM_PEAK_GBPS}
         res["sel-4k" if w == "sel4k" else "wide-1m"] = out
-        del x
+        del x, xs
         torch.cuda.empty_cache()
     return res
+
+
+def copy_calibration(args, timer):
+    """A plain elementwise copy (negation) of 256 MiB, the yardstick that
+    scales the rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+
+    nbytes = 256 << 20
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    us, _ = timer.stream([("copy", lambda i: torch.neg(src, out=dst))], max(3, min(args.steps, 10)), 1)
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "us": round(us["copy"], 2),
+            "gbps": 2 * nbytes / us["copy"] / 1e3}
 
 
 def cpu_leg(sel, seconds):
@@ -274,18 +350,26 @@ def cpu_leg(sel, seconds):
     }, ref
 
 
+# The kernel each selection mode of the step launches (one launch per call).
+MODE_KERNEL = {"exact": "row_exact_kernel", "b64k1": "row_bucket_bf16_kernel<1, false>",
+               "b128k2": "row_bucket_bf16_kernel<2, true>"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (rows and heads shard with no "
-              "communication; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+              "communication across GPUs). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
 
     torch.cuda.set_device(0)
     timer = EventTimer(flush=not args.no_flush)
-    sel = selection_step(args, timer) if args.only in ("all", "exact", "b64k1", "b128k2") else None
-    dec = decode_steps(args, timer) if (not args.no_decode and args.only in ("all", "mha", "gqa")) else {}
+    if args.only == "copy":
+        print(json.dumps({"copy_calibration": copy_calibration(args, timer)}), flush=True)
+        return
+    sel = selection_step(args, timer) if args.only in ("all", "sel", "exact", "b64k1", "b128k2") else None
+    dec = decode_steps(args, timer) if (not args.no_decode and args.only in ("all", "decode", "mha", "gqa")) else {}
     other = other_selection(args, timer) if args.only in ("all", "sel4k", "wide") else {}
 
     line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
@@ -295,7 +379,6 @@ def main():
         passes = len(modes)
         value = passes * sel["m"] * sel["n"] / sel["step_s"]
         dom = max(modes, key=lambda nm: modes[nm]["us"])
-        kern = {"exact": "exact_filter", "b64k1": "bucket_stage1", "b128k2": "bucket_stage1"}[dom]
         line.update({
             "value": value,
             "unit": "elements/s",
@@ -303,13 +386,16 @@ def main():
             "config": {"workload": "vocab-128k: 256 x 131072 bf16 ~ N(0, 2^2), k = 64; one step = " +
                                    " + ".join(modes) + " (value counts m*n elements per mode)",
                        "m": sel["m"], "n": sel["n"], "k": sel["k"], "modes": list(modes),
-                       "cache": "flushed before every call" if not args.no_flush else "warm"},
-            "roofline": {"bound": "hbm", "kernel": kern + " (" + dom + ")", "achieved": modes[dom]["gbps"],
-                         "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": modes[dom]["gbps"] / HBM_PEAK_GBPS,
-                         "traffic": recorded_traffic(dom)},
+                       "input_copies": sel["copies"]},
+            "roofline": {"bound": "hbm", "kernel": MODE_KERNEL[dom] + " (" + dom + ")",
+                         "achieved": modes[dom]["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": modes[dom]["gbps"] / HBM_PEAK_GBPS, "traffic": recorded_traffic(dom),
+                         "alg_bytes_per_launch": modes[dom]["alg_bytes"], "launch_us": modes[dom]["us"]},
             "modes": modes,
             "recall": sel["recall"],
-            "wall_ms_per_step": sel["wall_s"] / args.steps * 1e3,
+            "timing": {"gpu_ms_per_step": sel["info"]["gpu_s"] / args.steps * 1e3,
+                       "wall_ms_per_step_incl_spin": sel["info"]["wall_s"] / args.steps * 1e3,
+                       "queued_ahead": sel["info"]["queued_ahead"]},
         })
     elif dec:
         first = next(iter(dec.values()))
