@@ -205,6 +205,68 @@ def test_wide1m_sampled_and_worst_case(gpu):
     assert abs(r[0::2].mean() - oracle.eq1_finite(n, k, b, kb)) < 0.01
 
 
+# -------------------------------------- wide fp32 rows (two-pass route) ----
+
+def quantized_rows(m, n, levels, seed, gpu):
+    """fp32 rows holding only `levels` distinct values (heavy ties)."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    return (torch.floor(torch.rand((m, n), generator=g) * levels) / levels).to(gpu)
+
+
+@pytest.mark.parametrize("m,n", [(1, 16384), (3, 65536 + 77), (5, 100000)])
+def test_wide_exact(gpu, m, n):
+    x = rand_rows(m, n, torch.float32, m * n, gpu)
+    for k in (65, 1000, 8192):
+        check_exact(x, k)
+
+
+def test_wide_exact_ties(gpu):
+    # three levels: the collection holds every tie at the threshold
+    check_exact(quantized_rows(2, 65536, 3, 1, gpu), 5000)
+    # two levels: more elements reach the threshold than the collection
+    # holds, so each row runs the full radix select with index-ordered ties
+    check_exact(quantized_rows(2, 131072, 2, 2, gpu), 8192)
+    x = torch.full((1, 40000), -0.0, device=gpu)
+    x[0, ::7] = 0.0
+    check_exact(x, 3000)  # -0.0 and +0.0 are one value: lowest indices win
+
+
+def test_wide_exact_special_values(gpu):
+    x = workloads.rows_ties_bf16(3, 70000, 8, seed=3, device="cpu").float().to(gpu)
+    for k in (100, 4000):
+        check_exact(x, k)
+
+
+@pytest.mark.parametrize("b,kb", [(512, 16), (256, 8), (64, 5), (1024, 12), (4096, 16), (192, 7)])
+def test_wide_bucketed(gpu, b, kb):
+    n = 70001
+    x = rand_rows(3, n, torch.float32, b * 100 + kb, gpu)
+    check_bucketed(x, min(64, b * kb), b, kb, False)
+    if b * kb <= 8192:
+        check_bucketed(x, b * kb, b, kb, True)
+        check_bucketed(x, b * kb // 3, b, kb, True)
+
+
+@pytest.mark.parametrize("levels", [2, 64, 1024])
+def test_wide_bucketed_ties(gpu, levels):
+    # 2 levels: hundreds of ties per bucket (index-ordered walk); 64 and 1024
+    # levels: a few ties at T_r (the recorded tie list)
+    x = quantized_rows(2, 65536 + 33, levels, levels, gpu)
+    for b, kb in [(256, 8), (512, 16)]:
+        check_bucketed(x, 64, b, kb, False)
+        check_bucketed(x, b * kb, b, kb, True)
+        check_bucketed(x, 1000, b, kb, True)
+
+
+def test_wide_strided_and_misaligned(gpu):
+    n = 50000
+    big = rand_rows(3, n + 9, torch.float32, 77, gpu)
+    x = big[:, 1:n + 1]  # row stride n + 9, start one element in
+    check_exact(x, 1000)
+    check_bucketed(x, 64, 512, 16, False)
+    check_bucketed(x, 4096, 512, 8, True)
+
+
 # --------------------------------------------------------------- decode ----
 
 def _decode_check(q, K, V, k_sel, b, kb, rows=None):

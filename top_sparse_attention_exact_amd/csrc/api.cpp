@@ -68,7 +68,59 @@ int validate_exact(int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k) {
   return ATOPK_OK;
 }
 
+// ---- wide fp32 rows ------------------------------------------------------------------
+
+struct WideLayout {
+  WidePlan plan;
+  size_t vals, thr, need, cand, rowthr, row_cnt, row_keys;
+  size_t total;
+};
+
+WideLayout wide_layout(int dtype, int64_t m, int64_t n, int64_t k, int64_t b, int64_t kb, bool exact,
+                       bool final_exact) {
+  WideLayout L{};
+  L.plan = plan_wide(dtype, m, n, k, b, kb, exact, final_exact);
+  if (!L.plan.ok) return L;
+  const WidePlan& p = L.plan;
+  Carve c;
+  L.vals = c.take(p.vals_bytes);
+  L.thr = c.take(exact ? 0 : p.bucket_bytes);
+  L.need = c.take(exact ? 0 : p.bucket_bytes);
+  L.cand = c.take(p.cand_bytes);
+  L.rowthr = c.take(exact ? p.bucket_bytes : 0);
+  L.row_cnt = c.take(exact ? p.bucket_bytes : 0);
+  L.row_keys = c.take(p.row_bytes);
+  L.total = c.off;
+  return L;
+}
+
+// Large k on fp32 rows goes to the two-pass path (k <= 64 has the row kernel).
+bool wide_exact(int dtype, int64_t m, int64_t n, int64_t k) {
+  return k > 64 && plan_wide(dtype, m, n, k, 0, 0, true, true).ok;
+}
+
+// fp32 rows with k_b > 4 go to the two-pass path.
+bool wide_bucketed(int dtype, int64_t m, int64_t n, int64_t k, int64_t b, int64_t kb, int final_exact) {
+  return kb > 4 && plan_wide(dtype, m, n, k, b, kb, false, final_exact != 0).ok;
+}
+
+int run_wide(const WideLayout& L, const void* x, int64_t m, int64_t n, int64_t ldx, int64_t k, bool exact,
+             bool final_exact, void* out_vals, int32_t* out_idx, void* ws, hipStream_t s) {
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  WideBuffers B{};
+  B.vals = reinterpret_cast<float*>(w + L.vals);
+  B.thr = reinterpret_cast<float*>(w + L.thr);
+  B.need = reinterpret_cast<int*>(w + L.need);
+  B.cand = reinterpret_cast<uint64_t*>(w + L.cand);
+  B.rowthr = reinterpret_cast<float*>(w + L.rowthr);
+  B.row_cnt = reinterpret_cast<int*>(w + L.row_cnt);
+  B.row_keys = reinterpret_cast<uint64_t*>(w + L.row_keys);
+  return hip_status(launch_wide(L.plan, static_cast<const float*>(x), m, n, ldx, k, exact, final_exact, B, out_vals,
+                                out_idx, s));
+}
+
 size_t exact_ws_bytes(int dtype, int64_t m, int64_t n, int64_t k) {
+  if (wide_exact(dtype, m, n, k)) return wide_layout(dtype, m, n, k, 0, 0, true, true).total;
   const ExactPlan p = plan_exact(dtype, m, n, k);
   if (p.splits <= 1) return 0;
   Carve c;
@@ -85,6 +137,9 @@ int run_exact(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, int64
   const int64_t es = dtype == ATOPK_F32 ? 4 : 2;
   if (row_exact_ok(dtype, m, n, k, rows_aligned(x, ldx, es)))
     return hip_status(launch_row_exact(x, dtype, m, n, ldx, k, out_vals, out_idx, s));
+  if (wide_exact(dtype, m, n, k))
+    return run_wide(wide_layout(dtype, m, n, k, 0, 0, true, true), x, m, n, ldx, k, true, true, out_vals, out_idx, ws,
+                    s);
   const ExactPlan p = plan_exact(dtype, m, n, k);
   if (p.splits <= 1) return hip_status(launch_exact(p, x, dtype, m, n, ldx, k, nullptr, x, dtype, ldx, out_vals, out_idx, s));
   uint64_t* part = static_cast<uint64_t*>(ws);
@@ -132,6 +187,8 @@ BucketLayout bucket_layout(int dtype, int64_t m, int64_t n, int64_t b, int64_t k
 
 size_t bucketed_ws_bytes(int dtype, int64_t m, int64_t n, int64_t k, int64_t b, int64_t kb, int final_exact) {
   if (exact_route(k, b, kb)) return exact_ws_bytes(dtype, m, n, k);
+  if (wide_bucketed(dtype, m, n, k, b, kb, final_exact))
+    return wide_layout(dtype, m, n, k, b, kb, false, final_exact != 0).total;
   // The plan depends on the data pointer's alignment; report the larger need.
   return std::max(bucket_layout(dtype, m, n, b, kb, final_exact, true).total,
                   bucket_layout(dtype, m, n, b, kb, final_exact, false).total);
@@ -144,6 +201,9 @@ int run_bucketed(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, in
   const bool aligned = rows_aligned(x, ldx, es);
   if (row_bucket_ok(dtype, m, n, b, kb, aligned))
     return hip_status(launch_row_bucket(x, dtype, m, n, ldx, k, b, kb, final_exact, out_vals, out_idx, s));
+  if (wide_bucketed(dtype, m, n, k, b, kb, final_exact))
+    return run_wide(wide_layout(dtype, m, n, k, b, kb, false, final_exact != 0), x, m, n, ldx, k, false,
+                    final_exact != 0, out_vals, out_idx, ws, s);
   const BucketLayout L = bucket_layout(dtype, m, n, b, kb, final_exact, aligned);
   uint8_t* w = static_cast<uint8_t*>(ws);
   uint64_t* lists = reinterpret_cast<uint64_t*>(w + L.lists_off);

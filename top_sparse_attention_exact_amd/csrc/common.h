@@ -253,6 +253,25 @@ __device__ void block_sortmerge_final(const uint64_t* cand, uint64_t* runs, int 
   }
 }
 
+// hist[bin] += 1 for every active lane with `add`.  Keys near a selection
+// threshold share their high digits, and per-lane LDS atomics on one
+// address serialise, so the first few distinct bins of the wave take one
+// atomic each (count = lanes in that bin); the rest go lane by lane.
+__device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool add) {
+  uint64_t todo = __ballot(add);
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    if (!todo) return;
+    const int leader = __builtin_ctzll(todo);
+    const uint32_t lb = __shfl(bin, leader, kWave);
+    const uint64_t same = __ballot(add && bin == lb);
+    if (lane_id() == leader) atomicAdd(&hist[lb], (uint32_t)__popcll(same));
+    add = add && bin != lb;
+    todo &= ~same;
+  }
+  if (add) atomicAdd(&hist[bin], 1u);
+}
+
 // The threshold key t such that exactly k of the n unique keys in `keys`
 // (LDS) are >= t (radix select, 8-bit digits from the top).  `hist` is a
 // 256-entry LDS array, `ctl` 4 LDS words.
@@ -265,10 +284,11 @@ __device__ uint64_t block_kth_key(const uint64_t* keys, int n, int k, uint32_t* 
     for (int i = tid; i < 256; i += T) hist[i] = 0;
     __syncthreads();
     const uint64_t hi_prefix = (shift == 56) ? 0 : (prefix >> (shift + 8));
-    for (int i = tid; i < n; i += T) {
-      uint64_t key = keys[i];
-      bool match = (shift == 56) || ((key >> (shift + 8)) == hi_prefix);
-      if (match) atomicAdd(&hist[(uint32_t)(key >> shift) & 255u], 1u);
+    for (int i0 = 0; i0 < n; i0 += T) {
+      const int i = i0 + tid;
+      const uint64_t key = i < n ? keys[i] : 0;
+      const bool match = i < n && ((shift == 56) || ((key >> (shift + 8)) == hi_prefix));
+      hist_add(hist, (uint32_t)(key >> shift) & 255u, match);
     }
     __syncthreads();
     if (tid < kWave) {

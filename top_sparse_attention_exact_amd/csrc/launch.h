@@ -63,6 +63,31 @@ hipError_t launch_row_bucket(const void* x, int dtype, int64_t m, int64_t n, int
 hipError_t launch_row_exact(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k, void* out_vals,
                             int32_t* out_idx, hipStream_t s);
 
+// ---- wide fp32 rows: two streaming passes (values, then collect) -----------
+
+struct WidePlan {
+  bool ok;               // the shape fits this path
+  int64_t b, kb;         // bucketing used (exact mode: a fixed one)
+  int kbn;               // width of the value network (8 or 16)
+  int64_t groups;        // 64-bucket groups per row
+  int nchunks;           // waves per streaming workgroup (chunks of sweeps)
+  int sweeps_per_chunk;
+  int64_t blocks;        // streaming workgroups: rows * groups
+  size_t vals_bytes, bucket_bytes, cand_bytes, row_bytes;
+};
+struct WideBuffers {
+  float* vals;         // exact: top values per bucket
+  float* thr;          // bucketed: T_r per (row, bucket)
+  int* need;           // bucketed: ties each bucket takes
+  uint64_t* cand;      // bucketed with final stage: the b * kb candidates
+  float* rowthr;       // exact: lower bound of the k-th value per row
+  int* row_cnt;        // exact: keys collected per row
+  uint64_t* row_keys;  // exact: collected keys
+};
+WidePlan plan_wide(int dtype, int64_t m, int64_t n, int64_t k, int64_t b, int64_t kb, bool exact, bool final_exact);
+hipError_t launch_wide(const WidePlan& p, const float* x, int64_t m, int64_t n, int64_t ldx, int64_t k, bool exact,
+                       bool final_exact, const WideBuffers& w, void* out_vals, int32_t* out_idx, hipStream_t s);
+
 // ---- decode -------------------------------------------------------------------
 
 // scores[(i*hq + h)*ctx + j] = scale * <q[i, h], K[i, h / g, j]> (fp32).
