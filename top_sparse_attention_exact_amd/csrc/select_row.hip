@@ -410,8 +410,14 @@ __global__ __launch_bounds__(kRowT) void row_exact_kernel(const uint8_t* __restr
   constexpr int ES = RowIn<DT>::ES;
   constexpr int TILE = T * U * V;
   __shared__ uint64_t buf[kRowLds / 8];
-  __shared__ uint32_t wthr[kRowWaves];
-  volatile uint32_t* pub = wthr;  // read fresh every tile, written without barriers
+  // Bounds published by the waves, read fresh every tile and written without
+  // barriers: relaxed workgroup-scope atomics (a volatile access would also
+  // wait for the next tile's loads in flight).
+  __shared__ uint32_t pub[kRowWaves];
+  auto pub_store = [&](int w2, uint32_t v) {
+    __hip_atomic_store(&pub[w2], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  };
+  auto pub_load = [&](int w2) { return __hip_atomic_load(&pub[w2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP); };
 
   const int t = threadIdx.x;
   const int lane = lane_id();
@@ -430,30 +436,37 @@ __global__ __launch_bounds__(kRowT) void row_exact_kernel(const uint8_t* __restr
   // whole 16-byte vectors; the last, partial tile is zero-filled and checked.
   auto tile = [&](const uint4 (&w)[U], int64_t base, auto full_c) {
     constexpr bool full = decltype(full_c)::value;
+    uint32_t vm[U];  // largest order key of each vector (in-row elements only)
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (full) {
-        lmax = max(lmax, vec_max_ord<DT>(w[u]));
+        vm[u] = vec_max_ord<DT>(w[u]);
       } else {
+        vm[u] = 0;
 #pragma unroll
         for (int e = 0; e < V; ++e)
-          if (base + (int64_t)u * T * V + t * V + e < n) lmax = max(lmax, ord_elem<DT>(w[u], e));
+          if (base + (int64_t)u * T * V + t * V + e < n) vm[u] = max(vm[u], ord_elem<DT>(w[u], e));
       }
+      lmax = max(lmax, vm[u]);
     }
     // The c-th largest lane maximum of each wave, c = ceil(k / 16): 16 * c
     // >= k distinct elements reach the smallest of the 16 published values.
+    // The first tile waits once for every wave to publish: the pooled bound
+    // is far tighter than any one wave's.
     const uint32_t tc = wave_cth_largest(lmax, cpw);
-    if (lane == 0) pub[wave] = tc;
+    if (lane == 0) pub_store(wave, tc);
     if (first) {
-      lds_barrier();  // every wave has published once
+      lds_barrier();
       first = false;
     }
-    uint32_t th = 0xffffffffu;
+    uint32_t tm = 0xffffffffu;
 #pragma unroll
-    for (int w2 = 0; w2 < kRowWaves; ++w2) th = min(th, pub[w2]);
-    thr = max(thr, th);
+    for (int w2 = 0; w2 < kRowWaves; ++w2) tm = min(tm, pub_load(w2));
+    thr = max(thr, tm);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      // after the first tile almost no vector holds an element that passes
+      if (__ballot(vm[u] >= thr) == 0) continue;
 #pragma unroll
       for (int e = 0; e < V; ++e) {
         const uint32_t idx0 = (uint32_t)(base + u * T * V + t * V + e);
@@ -517,13 +530,18 @@ __global__ __launch_bounds__(kRowT) void row_exact_kernel(const uint8_t* __restr
     __syncthreads();
   }
   if (wave == 0 && lane < k && key != 0) {
+    // the order key gives the value back, except the sign of a zero
     const uint32_t idx = key_idx(key);
+    const uint32_t o = key_ord(key);
     const int64_t at = (int64_t)row * k + lane;
     out_idx[at] = (int32_t)idx;
     if constexpr (DT == IN_F32) {
-      reinterpret_cast<uint32_t*>(out_vals)[at] = reinterpret_cast<const uint32_t*>(xr)[idx];
+      reinterpret_cast<uint32_t*>(out_vals)[at] =
+          o == 0x80000000u ? reinterpret_cast<const uint32_t*>(xr)[idx] : bits_from_ord(o);
     } else {
-      reinterpret_cast<uint16_t*>(out_vals)[at] = reinterpret_cast<const uint16_t*>(xr)[idx];
+      const uint32_t o16 = o >> 16;
+      reinterpret_cast<uint16_t*>(out_vals)[at] =
+          o16 == 0x8000u ? reinterpret_cast<const uint16_t*>(xr)[idx] : bf16_from_ord16(o16);
     }
   }
 }
