@@ -6,6 +6,7 @@ obvious reference written from the method's definition on the pages:
 * "Approximate Top-k for Increased Parallelism" (Pith review page):
   "What carries the argument" (the two-stage bucketed top-k, Eq. (1) and the
   description of Eq. (2)), "What would settle it" (one residue class modulo b),
+  Figures 6 and 8 captions (contiguous against interleaved assignment),
   Figure 2 caption (n = 11, k = 4, b = 3, k_b = 2 toy) and Figure 12 caption
   (ties at the k-th value need a "collect" step).
 * "Recall Before You Rank: Similarity-Guided Top-K Reuse ..." (fugumt page),
@@ -25,6 +26,8 @@ from .topk import (  # noqa: F401
     exact_topk,
     bucketed_topk,
     bucket_members,
+    contiguous_members,
+    bucket_of,
 )
 from .recall import (  # noqa: F401
     recall,

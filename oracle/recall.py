@@ -35,15 +35,18 @@ def recall(out_idx, exact_idx):
     return np.array([len(np.intersect1d(o, e)) / k for o, e in zip(out_idx, exact_idx)])
 
 
-def recall_by_bucket_counts(exact_idx, n, b, kb):
+def recall_by_bucket_counts(exact_idx, n, b, kb, assignment="interleaved"):
     """Recall computed without running the method: with t_r the number of
     true top-k indices in bucket r, stage 1 keeps min(k_b, t_r) of them, so
-    R = sum_r min(k_b, t_r) / k.  Used as an identity check of the oracle."""
+    R = sum_r min(k_b, t_r) / k.  Used as an identity check of the oracle.
+    Buckets: i mod b (interleaved) or floor(i * b / n) (contiguous)."""
     exact_idx = np.atleast_2d(exact_idx)
     k = exact_idx.shape[1]
     out = []
     for row in exact_idx:
-        t = np.bincount(np.asarray(row) % b, minlength=b)
+        row = np.asarray(row, dtype=np.int64)
+        bucket = row % b if assignment == "interleaved" else (row * b) // n
+        t = np.bincount(bucket, minlength=b)
         out.append(np.minimum(t, kb).sum() / k)
     return np.array(out)
 

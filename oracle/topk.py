@@ -78,11 +78,35 @@ def bucket_members(n, b, r):
     return np.arange(r, n, b, dtype=np.int64)
 
 
-def bucketed_topk(x, k, b, kb, final_exact, dtype="f32"):
+def contiguous_members(n, b, r):
+    """Indices of contiguous bucket r: the i with floor(i * b / n) == r.
+
+    The contiguous assignment the Approximate Top-k page compares against the
+    interleaved one (Figure 6: recall on correlated inputs; Figure 8:
+    runtime).  The page gives no formula; the plainest reading is b blocks of
+    consecutive positions, bucket(i) = floor(i * b / n), whose sizes differ by
+    at most one when b does not divide n.
+    """
+    i = np.arange(n, dtype=np.int64)
+    return i[(i * b) // n == r]
+
+
+def bucket_of(i, n, b, assignment="interleaved"):
+    """Bucket of position i under either assignment."""
+    i = np.asarray(i, dtype=np.int64)
+    if assignment == "interleaved":
+        return i % b
+    if assignment == "contiguous":
+        return (i * b) // n
+    raise ValueError(assignment)
+
+
+def bucketed_topk(x, k, b, kb, final_exact, dtype="f32", assignment="interleaved"):
     """Two-stage bucketed top-k (Approximate Top-k page, "What carries the
     argument"): split the n inputs into b interleaved buckets, take an exact
     top-k_b inside every bucket, and optionally take an exact top-k of the
-    b * k_b concatenated candidates.
+    b * k_b concatenated candidates.  assignment="contiguous" uses the
+    contiguous buckets of contiguous_members instead.
 
     Stage 1 output (final_exact False): [m, b * kb], bucket-major, slot
     r * kb + j holding the j-th best element of bucket r.
@@ -98,9 +122,10 @@ def bucketed_topk(x, k, b, kb, final_exact, dtype="f32"):
     assert kb <= n // b, "every bucket must hold at least k_b elements"
     assert b * kb >= k >= 1, "the invariant b * k_b >= k"
     v = to_f64(x, dtype)
+    members_of = {"interleaved": bucket_members, "contiguous": contiguous_members}[assignment]
     cand = np.empty((m, b * kb), dtype=np.int64)
     for r in range(b):
-        members = bucket_members(n, b, r)
+        members = members_of(n, b, r)
         for row in range(m):
             order = _rank_order(v[row, members], members)
             cand[row, r * kb:(r + 1) * kb] = members[order[:kb]]

@@ -300,6 +300,102 @@ def test_eq2_reached_on_planted_rows():
     assert r[1] == 3 * kb / k
 
 
+# -------------------------------------------- contiguous assignment ----
+
+@pytest.mark.parametrize("n,b", [(11, 3), (64, 8), (100, 7), (4096, 64), (5, 5)])
+def test_contiguous_buckets_partition_the_row(n, b):
+    """floor(i * b / n) buckets: disjoint runs of consecutive positions in
+    order, covering the row, sizes floor(n / b) or ceil(n / b)."""
+    seen = []
+    for r in range(b):
+        m = oracle.contiguous_members(n, b, r)
+        assert len(m) in (n // b, -(-n // b))
+        assert np.array_equal(m, np.arange(m[0], m[0] + len(m)))
+        seen.extend(m.tolist())
+    assert seen == list(range(n))
+
+
+def test_contiguous_matches_row_segments():
+    """When b divides n, contiguous bucket r is segment r of the row:
+    compare with an argsort of each reshaped segment (another formulation)."""
+    g = torch.Generator().manual_seed(21)
+    n, b, kb = 96, 8, 3
+    x = torch.randint(0, 9, (5, n), generator=g).float().numpy()  # many ties
+    got, _ = oracle.bucketed_topk(x, 8, b, kb, False, "f32", assignment="contiguous")
+    s = n // b
+    for row in range(5):
+        seg = x[row].reshape(b, s)
+        for r in range(b):
+            order = sorted(range(s), key=lambda j: (-seg[r, j], j))[:kb]
+            assert got[row, r * kb:(r + 1) * kb].tolist() == [r * s + j for j in order]
+
+
+def test_contiguous_reduces_to_exact():
+    g = torch.Generator().manual_seed(22)
+    x = torch.randn((3, 300), generator=g).numpy()
+    ex, _ = oracle.exact_topk(x, 17, "f32")
+    one, _ = oracle.bucketed_topk(x, 17, 1, 17, True, "f32", assignment="contiguous")
+    assert np.array_equal(one, ex)
+    whole, _ = oracle.bucketed_topk(x, 17, 3, 100, True, "f32", assignment="contiguous")  # k_b = bucket size
+    assert np.array_equal(whole, ex)
+
+
+def test_contiguous_recall_identity_and_iid_expectation():
+    """On iid rows the assignment does not matter in distribution, so the
+    contiguous recall has the same finite-n expectation; and per row the
+    recall equals sum_r min(k_b, t_r) / k over contiguous buckets."""
+    g = torch.Generator().manual_seed(23)
+    n, k, b, kb, reps = 512, 32, 16, 2, 300
+    x = torch.rand((reps, n), generator=g).numpy()
+    ex, _ = oracle.exact_topk(x, k, "f32")
+    fin, _ = oracle.bucketed_topk(x, k, b, kb, True, "f32", assignment="contiguous")
+    r = oracle.recall(fin, ex)
+    assert np.array_equal(r, oracle.recall_by_bucket_counts(ex, n, b, kb, "contiguous"))
+    se = r.std() / math.sqrt(reps)
+    assert abs(r.mean() - oracle.eq1_finite(n, k, b, kb)) < 5 * se
+
+
+def test_contiguous_worst_case_is_eq2():
+    """The top-k packed into consecutive positions fill the fewest contiguous
+    buckets: the recall is Eq.(2)'s worst case."""
+    n, k, b, kb = 256, 40, 16, 3  # segments of 16: the top 40 fill 2.5 segments
+    x = np.arange(n, dtype=np.float32)[None, :] * -1.0
+    ex, _ = oracle.exact_topk(x, k, "f32")
+    fin, _ = oracle.bucketed_topk(x, k, b, kb, True, "f32", assignment="contiguous")
+    assert oracle.recall(fin, ex)[0] == oracle.eq2(n, k, b, kb) == (2 * kb + min(kb, 8)) / k
+
+
+def test_ar1_rows_are_stationary_with_lag1_correlation():
+    from top_sparse_attention_exact_amd import workloads
+
+    x = workloads.rows_ar1(64, 4096, 0.9, seed=0).numpy().astype(np.float64)
+    assert abs(x.var() - 1.0) < 0.05
+    assert abs(x[:, 0].var() - 1.0) < 0.5  # the first element is already stationary
+    lag1 = np.mean(x[:, 1:] * x[:, :-1])
+    assert abs(lag1 - 0.9) < 0.02
+
+
+def test_interleaved_keeps_recall_under_correlation():
+    """Figure 6 of the Approximate Top-k page: on AR(1) Gaussian rows the
+    interleaved assignment keeps the recall of Eq.(1) at every correlation,
+    while contiguous buckets lose it as neighbouring values become alike."""
+    from top_sparse_attention_exact_amd import workloads
+
+    n, k, b, kb, reps = 4096, 64, 64, 1, 128
+    model = oracle.eq1_finite(n, k, b, kb)
+    contiguous = []
+    for rho in (0.0, 0.9, 0.99):
+        x = workloads.rows_ar1(reps, n, rho, seed=1).numpy()
+        ex, _ = oracle.exact_topk(x, k, "f32")
+        ri = oracle.recall_by_bucket_counts(ex, n, b, kb, "interleaved")
+        rc = oracle.recall_by_bucket_counts(ex, n, b, kb, "contiguous")
+        assert ri.mean() > model - 4 * ri.std() / math.sqrt(reps)
+        contiguous.append(rc.mean())
+    assert abs(contiguous[0] - model) < 0.02
+    assert contiguous[0] > contiguous[1] > contiguous[2]
+    assert contiguous[2] < 0.2
+
+
 # ------------------------------------------------------------- decode ----
 
 def _decode_inputs(bsz, hq, hkv, length, d, seed):

@@ -15,13 +15,16 @@ Workloads (the shapes of the pages' top-k and decode settings, synthetic):
   gqa-128k   decode B4 Hq32 Hkv8 D128 L131072, 1% of keys scaled 3x
   wide-1m    64 x 2^20 fp32 Uniform[0,1), k = 8192; odd rows hold their top-k
              in the fewest residue classes modulo b (worst case for buckets)
+  ar1        fp32 AR(1) Gaussian rows of a chosen correlation (interleaved
+             against contiguous bucket assignment)
 """
 
 import math
 
+import numpy as np
 import torch
 
-_WORKLOAD_IDS = {"sel-4k": 1, "vocab-128k": 2, "mha-32k": 3, "gqa-128k": 4, "wide-1m": 5, "misc": 9}
+_WORKLOAD_IDS = {"sel-4k": 1, "vocab-128k": 2, "mha-32k": 3, "gqa-128k": 4, "wide-1m": 5, "ar1": 6, "misc": 9}
 
 
 def generator(workload, seed, device="cpu"):
@@ -59,6 +62,23 @@ def rows_planted_residues(m, n, b, k, seed, device="cpu", workload="wide-1m"):
     x_odd[:, mask] = lift[odd]
     x[odd] = x_odd
     return x
+
+
+def rows_ar1(m, n, rho, seed, device="cpu", workload="ar1"):
+    """[m, n] fp32 stationary AR(1) Gaussian rows: x_0 ~ N(0, 1) and
+    x_i = rho * x_{i-1} + sqrt(1 - rho^2) * e_i with e_i ~ N(0, 1) (the
+    correlated-Gaussian inputs of the interleaved / contiguous comparison).
+    The recurrence runs on the host in float64 (an IIR filter), then the rows
+    go to `device`."""
+    from scipy.signal import lfilter
+
+    g = generator(workload, seed, "cpu")
+    e = torch.randn((m, n), generator=g, dtype=torch.float64).numpy()
+    c = math.sqrt(1.0 - rho * rho)
+    if c > 0:
+        e[:, 0] /= c  # so that x_0 = e_0 has unit variance
+    x = lfilter([c], [1.0, -rho], e, axis=1) if c > 0 else np.repeat(e[:, :1], n, axis=1)
+    return torch.from_numpy(x.astype(np.float32)).to(device)
 
 
 def rows_ties_bf16(m, n, levels, seed, device="cpu"):
