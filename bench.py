@@ -46,7 +46,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="all", help="all | sel | exact | b64k1 | b128k2 | decode | mha | gqa | sel4k | wide | copy")
+    ap.add_argument("--only", default="all",
+                    help="all | sel | exact | b64k1 | b128k2 | decode | mha | gqa | sel4k | wide | assign | copy")
     ap.add_argument("--no-flush", action="store_true", help="no cache flush before the single-call latency runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
@@ -304,6 +305,45 @@ def other_selection(args, timer):
     return res
 
 
+def assignment_compare(args, timer):
+    """Runtime of contiguous against interleaved buckets on the vocab-128k
+    batch (the comparison of Figure 8 on the Approximate Top-k page), and
+    their recall on AR(1) rows of correlation 0.99 (Figure 6)."""
+    import numpy as np
+    import torch
+
+    import top_sparse_attention_exact_amd as atk
+    from top_sparse_attention_exact_amd import workloads
+
+    cfg = workloads.SELECTION["vocab-128k"]
+    m, n, k = cfg["m"], cfg["n"], cfg["k"]
+    x = workloads.rows_normal_bf16(m, n, 2.0, seed=0, device="cuda")
+    xs = copies(x, ROTATE_BYTES)
+    calls = []
+    for b, kb, fin in cfg["modes"]:
+        for assign in ("interleaved", "contiguous"):
+            calls.append(("b%dk%d%s_%s" % (b, kb, "_final" if fin else "", assign),
+                          (lambda i, b=b, kb=kb, fin=fin, a=assign: atk.bucketed(xs[i % len(xs)], k, b, kb, fin,
+                                                                                  assignment=a))))
+    torch.cuda.synchronize()
+    us, info = timer.stream(calls, max(3, min(args.steps, 20)), 2)
+    out = {"workload": "vocab-128k", "queued_ahead": info["queued_ahead"]}
+    for name, _ in calls:
+        out[name] = {"us": round(us[name], 2), "frac_hbm_peak": (m * n * 2) / (us[name] * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+    del x, xs
+    ar = workloads.rows_ar1(64, n, 0.99, seed=0, device="cuda")
+    _, ex = atk.exact(ar, k)
+    ex = ex.cpu().numpy()
+    rec = {}
+    for assign in ("interleaved", "contiguous"):
+        _, idx = atk.bucketed(ar, k, 64, 1, False, assignment=assign)
+        got = idx.cpu().numpy()
+        rec[assign] = float(np.mean([len(np.intersect1d(a, e)) / k for a, e in zip(got, ex)]))
+    out["recall_ar1_rho0.99_b64k1"] = rec
+    torch.cuda.empty_cache()
+    return out
+
+
 def copy_calibration(args, timer):
     """A plain elementwise copy (negation) of 256 MiB, the yardstick that
     scales the rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes."""
@@ -371,6 +411,7 @@ def main():
     sel = selection_step(args, timer) if args.only in ("all", "sel", "exact", "b64k1", "b128k2") else None
     dec = decode_steps(args, timer) if (not args.no_decode and args.only in ("all", "decode", "mha", "gqa")) else {}
     other = other_selection(args, timer) if args.only in ("all", "sel4k", "wide") else {}
+    assign = assignment_compare(args, timer) if args.only in ("all", "assign") else None
 
     line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
@@ -397,6 +438,8 @@ def main():
                        "wall_ms_per_step_incl_spin": sel["info"]["wall_s"] / args.steps * 1e3,
                        "queued_ahead": sel["info"]["queued_ahead"]},
         })
+    elif assign is not None and not dec and not other:
+        line.update({"value": None, "unit": "elements/s", "ms_per_step": None, "config": {"workload": "vocab-128k"}})
     elif dec:
         first = next(iter(dec.values()))
         line.update({"value": first["bucketed"]["scores_per_s"], "unit": "scores/s",
@@ -409,6 +452,8 @@ def main():
         line["decode"] = dec
     if other:
         line["other_selection"] = other
+    if assign is not None:
+        line["assignment"] = assign
     if sel is not None and not args.no_cpu_baseline:
         cpu, ref = cpu_leg(sel, args.cpu_seconds)
         line["cpu_baseline"] = cpu

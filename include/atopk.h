@@ -97,6 +97,29 @@ int atopk_bucketed(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, 
                    int64_t kb, int final_exact, void* out_vals, int32_t* out_idx, void* ws,
                    size_t ws_bytes, void* stream);
 
+/* bucket assignments for atopk_bucketed_ex */
+typedef enum atopk_assignment {
+  ATOPK_INTERLEAVED = 0, /* bucket of i = i mod b (what atopk_bucketed uses)    */
+  ATOPK_CONTIGUOUS = 1   /* bucket of i = floor(i * b / n): runs of consecutive */
+} atopk_assignment;
+
+/*
+ * atopk_bucketed with a choice of bucket assignment.  "Approximate Top-k for
+ * Increased Parallelism" (Pith review page), Figures 6 and 8 captions,
+ * compares interleaved buckets with contiguous ones (recall on correlated
+ * inputs, runtime); the page gives no formula for the contiguous buckets, and
+ * the reading taken here is b runs of consecutive positions, bucket(i) =
+ * floor(i * b / n) (sizes differ by at most one).  Arguments, outputs and
+ * limits as atopk_bucketed; ATOPK_CONTIGUOUS with final_exact additionally
+ * needs b*kb <= 8192 and uses no workspace.  An unknown assignment gives
+ * ATOPK_ERR_PARAM.
+ */
+int atopk_bucketed_ex_workspace(int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k, int64_t b,
+                                int64_t kb, int final_exact, int assignment, size_t* ws_bytes);
+int atopk_bucketed_ex(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k, int64_t b,
+                      int64_t kb, int final_exact, int assignment, void* out_vals, int32_t* out_idx,
+                      void* ws, size_t ws_bytes, void* stream);
+
 /*
  * Top-K sparse-attention decode for one layer, one new token per sequence.
  *   q      [batch, hq, d] bf16 (contiguous)

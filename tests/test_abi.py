@@ -33,7 +33,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 8
+    assert len(names) == 10
     handle = ctypes.CDLL(lib_mod.LIB_PATH)
     for name in names:
         assert hasattr(handle, name), name
@@ -105,6 +105,30 @@ def test_bucketed_validation(L):
     st, need = _ws_bucketed(L, BF16, 256, 131072, 131072, 64, 128, 2, 1)
     assert st == OK and need > 0
     assert L.atopk_bucketed(FAKE, BF16, 256, 131072, 131072, 64, 128, 2, 1, FAKE, FAKE, None, 0, None) == EWS
+
+
+def _ws_bucketed_ex(L, dt, m, n, ldx, k, b, kb, fin, assign):
+    sz = ctypes.c_size_t(0)
+    return L.atopk_bucketed_ex_workspace(dt, m, n, ldx, k, b, kb, fin, assign, ctypes.byref(sz)), sz.value
+
+
+def test_bucketed_ex_validation(L):
+    INTER, CONTIG = 0, 1
+    # interleaved: same answers and workspace as atopk_bucketed
+    st, need = _ws_bucketed_ex(L, BF16, 256, 131072, 131072, 64, 128, 2, 1, INTER)
+    assert (st, need) == _ws_bucketed(L, BF16, 256, 131072, 131072, 64, 128, 2, 1)
+    # contiguous: no workspace
+    assert _ws_bucketed_ex(L, BF16, 256, 131072, 131072, 64, 128, 2, 1, CONTIG) == (OK, 0)
+    assert _ws_bucketed_ex(L, F32, 3, 1000, 1000, 64, 7, 16, 0, CONTIG) == (OK, 0)
+    assert _ws_bucketed_ex(L, F32, 3, 1000, 1000, 64, 8, 2, 1, 2)[0] == EPARAM  # unknown assignment
+    assert _ws_bucketed_ex(L, F32, 3, 1000, 1000, 64, 8, 2, 1, -1)[0] == EPARAM
+    assert _ws_bucketed_ex(L, F32, 3, 1000, 1000, 64, 31, 2, 1, CONTIG)[0] == EPARAM  # b*kb < k
+    assert _ws_bucketed_ex(L, F32, 1, 20000, 20000, 64, 1024, 16, 1, CONTIG)[0] == EUNSUP  # 16384 candidates
+    assert _ws_bucketed_ex(L, F32, 1, 20000, 20000, 64, 1024, 16, 0, CONTIG)[0] == OK  # no final stage
+    assert L.atopk_bucketed_ex_workspace(F32, 1, 100, 100, 4, 4, 1, 1, CONTIG, None) == ENULL
+    assert L.atopk_bucketed_ex(None, F32, 2, 100, 100, 4, 4, 1, 1, CONTIG, FAKE, FAKE, None, 0, None) == ENULL
+    assert L.atopk_bucketed_ex(None, F32, 0, 100, 100, 4, 4, 1, 1, CONTIG, None, None, None, 0, None) == OK
+    assert L.atopk_bucketed_ex(FAKE, F32, 2, 100, 100, 4, 4, 1, 1, 5, FAKE, FAKE, None, 0, None) == EPARAM
 
 
 def _ws_decode(L, bsz, hq, hkv, ctx, d, ks, b, kb):

@@ -50,10 +50,10 @@ def check_exact(x, k):
     np.testing.assert_array_equal(out_bits(vals), ref_bits(rvals, tag))
 
 
-def check_bucketed(x, k, b, kb, final):
-    vals, idx = atk.bucketed(x, k, b, kb, final)
+def check_bucketed(x, k, b, kb, final, assignment="interleaved"):
+    vals, idx = atk.bucketed(x, k, b, kb, final, assignment=assignment)
     hx, tag = host(x)
-    ridx, rvals = oracle.bucketed_topk(hx, k, b, kb, final, tag)
+    ridx, rvals = oracle.bucketed_topk(hx, k, b, kb, final, tag, assignment=assignment)
     np.testing.assert_array_equal(idx.cpu().numpy(), ridx)
     np.testing.assert_array_equal(out_bits(vals), ref_bits(rvals, tag))
 
@@ -265,6 +265,51 @@ def test_wide_strided_and_misaligned(gpu):
     check_exact(x, 1000)
     check_bucketed(x, 64, 512, 16, False)
     check_bucketed(x, 4096, 512, 8, True)
+
+
+# ----------------------------------------- contiguous bucket assignment ----
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("n,b,kb", [(4096, 64, 1), (4096, 32, 2), (131072, 64, 1), (131072, 128, 2), (5000, 7, 3),
+                                    (11, 3, 2), (1000, 1000, 1), (70001, 512, 16), (20000, 100, 8), (3000, 16, 5)])
+def test_contiguous_shapes(gpu, dtype, n, b, kb):
+    x = rand_rows(3, n, dtype, n * 7 + b + kb, gpu)
+    k = max(1, min(b * kb, 64))
+    check_bucketed(x, k, b, kb, False, "contiguous")
+    check_bucketed(x, k, b, kb, True, "contiguous")
+    if b * kb <= 8192:
+        check_bucketed(x, b * kb, b, kb, True, "contiguous")
+
+
+def test_contiguous_ties_strided_and_exact_route(gpu):
+    x = workloads.rows_ties_bf16(4, 9000, 8, seed=5, device="cpu").to(gpu)
+    for b, kb in [(64, 1), (16, 4), (9, 3)]:
+        check_bucketed(x, min(64, b * kb), b, kb, True, "contiguous")
+        check_bucketed(x, min(64, b * kb), b, kb, False, "contiguous")
+    check_bucketed(x.float(), 64, 64, 2, True, "contiguous")
+    big = rand_rows(3, 8192 + 3, torch.bfloat16, 91, gpu)
+    xs = big[:, 1:8193]  # misaligned rows: element loads
+    check_bucketed(xs, 64, 64, 1, False, "contiguous")
+    check_bucketed(xs, 64, 32, 4, True, "contiguous")
+    check_bucketed(xs, 50, 1, 50, True, "contiguous")  # (1, k): the exact route
+
+
+def test_contiguous_recall_under_correlation(gpu):
+    """The interleaved / contiguous comparison on AR(1) rows, run on the GPU:
+    recall per row equals the oracle's bucket-count identity, and contiguous
+    buckets lose recall where interleaved ones keep Eq.(1)'s."""
+    n, k, b, kb = 131072, 64, 64, 1
+    x = workloads.rows_ar1(32, n, 0.99, seed=2, device=gpu)
+    _, ex = atk.exact(x, k)
+    ex = ex.cpu().numpy()
+    rec = {}
+    for assign in ("interleaved", "contiguous"):
+        _, idx = atk.bucketed(x, k, b, kb, False, assignment=assign)
+        r = oracle.recall(idx.cpu().numpy(), ex)
+        np.testing.assert_array_equal(r, oracle.recall_by_bucket_counts(ex, n, b, kb, assign))
+        rec[assign] = r.mean()
+    assert rec["interleaved"] > oracle.eq1_finite(n, k, b, kb) - 0.03
+    assert rec["contiguous"] < 0.2
 
 
 # --------------------------------------------------------------- decode ----

@@ -7,7 +7,9 @@ There is no Python or CPU implementation behind them: without the built
 library every call raises.
 
     exact(x, k)                       -> (values, indices)   exact top-k per row
-    bucketed(x, k, b, kb, final_exact) -> (values, indices)  two-stage bucketed
+    bucketed(x, k, b, kb, final_exact, assignment=...) -> (values, indices)
+                                      two-stage bucketed (interleaved or
+                                      contiguous buckets)
     sparse_attn_decode(q, K, V, k_sel, b, kb) -> out (, sel_idx, scores)
 """
 
@@ -58,10 +60,16 @@ def exact_workspace_bytes(dtype, m, n, k, ldx=None):
     return size.value
 
 
-def bucketed_workspace_bytes(dtype, m, n, k, b, kb, final_exact, ldx=None):
+INTERLEAVED = 0
+CONTIGUOUS = 1
+_ASSIGN = {"interleaved": INTERLEAVED, "contiguous": CONTIGUOUS}
+
+
+def bucketed_workspace_bytes(dtype, m, n, k, b, kb, final_exact, ldx=None, assignment="interleaved"):
     size = ctypes.c_size_t(0)
-    check(lib().atopk_bucketed_workspace(_DTYPES[dtype], m, n, ldx if ldx is not None else n, k, b, kb,
-                                         int(bool(final_exact)), ctypes.byref(size)), "atopk_bucketed_workspace")
+    check(lib().atopk_bucketed_ex_workspace(_DTYPES[dtype], m, n, ldx if ldx is not None else n, k, b, kb,
+                                            int(bool(final_exact)), _ASSIGN[assignment], ctypes.byref(size)),
+          "atopk_bucketed_ex_workspace")
     return size.value
 
 
@@ -88,21 +96,28 @@ def exact(x, k, workspace=None):
     return vals, idx
 
 
-def bucketed(x, k, b, kb, final_exact=True, workspace=None):
-    """Bucketed top-k: exact top-kb in each of b interleaved buckets (i mod b),
-    then, if final_exact, the exact top-k of the b*kb candidates ([m, k],
-    sorted); otherwise the candidates themselves, bucket-major [m, b*kb]."""
+def bucketed(x, k, b, kb, final_exact=True, workspace=None, assignment="interleaved"):
+    """Bucketed top-k: exact top-kb in each of b buckets -- interleaved
+    (i mod b) or contiguous (floor(i*b/n)) -- then, if final_exact, the exact
+    top-k of the b*kb candidates ([m, k], sorted); otherwise the candidates
+    themselves, bucket-major [m, b*kb]."""
     _check_rows(x)
     m, n = x.shape
     ldx = x.stride(0) if m > 1 else n
     width = k if final_exact else b * kb
     vals = torch.empty((m, width), dtype=x.dtype, device=x.device)
     idx = torch.empty((m, width), dtype=torch.int32, device=x.device)
-    need = bucketed_workspace_bytes(x.dtype, m, n, k, b, kb, final_exact, ldx)
+    need = bucketed_workspace_bytes(x.dtype, m, n, k, b, kb, final_exact, ldx, assignment)
     ws, nbytes = (workspace, workspace.numel()) if workspace is not None else _workspace(need, x.device)
-    st = lib().atopk_bucketed(_ptr(x), _DTYPES[x.dtype], m, n, ldx, k, b, kb, int(bool(final_exact)), _ptr(vals),
-                              _ptr(idx), _ptr(ws), nbytes, _stream_ptr(x.device))
-    check(st, "atopk_bucketed")
+    if assignment == "interleaved":
+        st = lib().atopk_bucketed(_ptr(x), _DTYPES[x.dtype], m, n, ldx, k, b, kb, int(bool(final_exact)),
+                                  _ptr(vals), _ptr(idx), _ptr(ws), nbytes, _stream_ptr(x.device))
+        check(st, "atopk_bucketed")
+    else:
+        st = lib().atopk_bucketed_ex(_ptr(x), _DTYPES[x.dtype], m, n, ldx, k, b, kb, int(bool(final_exact)),
+                                     _ASSIGN[assignment], _ptr(vals), _ptr(idx), _ptr(ws), nbytes,
+                                     _stream_ptr(x.device))
+        check(st, "atopk_bucketed_ex")
     return vals, idx
 
 

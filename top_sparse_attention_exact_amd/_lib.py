@@ -21,6 +21,14 @@ _SIGNATURES = {
         _c_int,
         [_c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_vp, ctypes.c_size_t, _c_vp],
     ),
+    "atopk_bucketed_ex_workspace": (
+        _c_int, [_c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_int, _c_int, _c_size_p]
+    ),
+    "atopk_bucketed_ex": (
+        _c_int,
+        [_c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_int, _c_int, _c_vp, _c_vp, _c_vp,
+         ctypes.c_size_t, _c_vp],
+    ),
     "atopk_sparse_attn_decode_workspace": (
         _c_int,
         [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_size_p],

@@ -275,6 +275,14 @@ int guarded(F&& f) {
   }
 }
 
+int validate_assignment(int dtype, int64_t n, int64_t k, int64_t b, int64_t kb, int final_exact, int assignment) {
+  if (assignment != ATOPK_INTERLEAVED && assignment != ATOPK_CONTIGUOUS) return ATOPK_ERR_PARAM;
+  if (assignment == ATOPK_CONTIGUOUS && !exact_route(k, b, kb) && !row_contig_ok(n, b, kb, final_exact))
+    return ATOPK_ERR_UNSUPPORTED;
+  (void)dtype;
+  return ATOPK_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -327,6 +335,45 @@ int atopk_bucketed_workspace(int dtype, int64_t m, int64_t n, int64_t ldx, int64
     if (st) return st;
     *ws_bytes = m == 0 ? 0 : bucketed_ws_bytes(dtype, m, n, k, b, kb, final_exact);
     return (int)ATOPK_OK;
+  });
+}
+
+int atopk_bucketed_ex_workspace(int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k, int64_t b, int64_t kb,
+                                int final_exact, int assignment, size_t* ws_bytes) {
+  return guarded([&] {
+    if (ws_bytes == nullptr) return (int)ATOPK_ERR_NULL;
+    int st = validate_bucketed(dtype, m, n, ldx, k, b, kb);
+    if (st) return st;
+    st = validate_assignment(dtype, n, k, b, kb, final_exact, assignment);
+    if (st) return st;
+    const bool contig = assignment == ATOPK_CONTIGUOUS && !exact_route(k, b, kb);
+    *ws_bytes = (m == 0 || contig) ? 0 : bucketed_ws_bytes(dtype, m, n, k, b, kb, final_exact);
+    return (int)ATOPK_OK;
+  });
+}
+
+int atopk_bucketed_ex(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k, int64_t b, int64_t kb,
+                      int final_exact, int assignment, void* out_vals, int32_t* out_idx, void* ws, size_t ws_bytes,
+                      void* stream) {
+  return guarded([&] {
+    int st = validate_bucketed(dtype, m, n, ldx, k, b, kb);
+    if (st) return st;
+    st = validate_assignment(dtype, n, k, b, kb, final_exact, assignment);
+    if (st) return st;
+    if (m == 0) return (int)ATOPK_OK;
+    if (!x || !out_vals || !out_idx) return (int)ATOPK_ERR_NULL;
+    const bool contig = assignment == ATOPK_CONTIGUOUS && !exact_route(k, b, kb);
+    st = check_ws(ws, ws_bytes, contig ? 0 : bucketed_ws_bytes(dtype, m, n, k, b, kb, final_exact));
+    if (st) return st;
+    st = check_device();
+    if (st) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (contig) {
+      const int64_t es = dtype == ATOPK_F32 ? 4 : 2;
+      return hip_status(launch_row_contig(x, dtype, m, n, ldx, k, b, kb, final_exact, rows_aligned(x, ldx, es),
+                                          out_vals, out_idx, s));
+    }
+    return run_bucketed(x, dtype, m, n, ldx, k, b, kb, final_exact, out_vals, out_idx, ws, s);
   });
 }
 

@@ -63,6 +63,13 @@ hipError_t launch_row_bucket(const void* x, int dtype, int64_t m, int64_t n, int
 hipError_t launch_row_exact(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k, void* out_vals,
                             int32_t* out_idx, hipStream_t s);
 
+// Contiguous bucket assignment (bucket of i = floor(i * b / n)), one
+// workgroup per row, no workspace.
+bool row_contig_ok(int64_t n, int64_t b, int64_t kb, int final_exact);
+hipError_t launch_row_contig(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k, int64_t b,
+                             int64_t kb, int final_exact, bool aligned, void* out_vals, int32_t* out_idx,
+                             hipStream_t s);
+
 // ---- wide fp32 rows: two streaming passes (values, then collect) -----------
 
 struct WidePlan {

@@ -546,6 +546,139 @@ __global__ __launch_bounds__(kRowT) void row_exact_kernel(const uint8_t* __restr
   }
 }
 
+// ------------------------------------------------------------ contiguous ----
+
+// Contiguous assignment (same page, Figures 6 and 8 compare it with the
+// interleaved one): bucket r holds the positions i with floor(i * b / n) ==
+// r, a run of consecutive elements.  Each wave owns whole buckets (r = wave,
+// wave + 16, ...): its lanes stream the run with coalesced loads into a
+// k_b-queue of (order key, index) keys each, a butterfly of shuffles merges
+// the 64 queues into the bucket's top-k_b, and the final exact top-k of the
+// b * k_b candidates is taken in LDS.  vec: every run starts and ends on a
+// 16-byte boundary (the runs are then read as 16-byte vectors).
+template <int DT, int KB, bool FINAL, bool PACK>
+__global__ __launch_bounds__(kRowT) void row_contig_kernel(const uint8_t* __restrict__ x, int64_t ld_bytes, int n,
+                                                          int b, int kb, int k, int vec,
+                                                          uint8_t* __restrict__ out_vals,
+                                                          int32_t* __restrict__ out_idx) {
+  // PACK (bf16, runs of at most 65536): 32-bit keys, the 16-bit order key
+  // above the complemented position inside the run; otherwise 64-bit keys.
+  using Key = std::conditional_t<PACK, uint32_t, uint64_t>;
+  constexpr int V = RowIn<DT>::V;
+  constexpr int ES = RowIn<DT>::ES;
+  constexpr int U = 4;
+  __shared__ uint64_t cand[kRowLds / 8];
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t ctl[8];
+  const int t = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = t / kWave;
+  const int row = blockIdx.x;
+  const uint8_t* xr = x + (int64_t)row * ld_bytes;
+
+  auto write = [&](int64_t at, uint64_t key) {
+    // the order key gives the value back, except the sign of a zero
+    const uint32_t idx = key_idx(key);
+    const uint32_t o = key_ord(key);
+    out_idx[at] = (int32_t)idx;
+    if constexpr (DT == IN_F32) {
+      reinterpret_cast<uint32_t*>(out_vals)[at] =
+          o == 0x80000000u ? reinterpret_cast<const uint32_t*>(xr)[idx] : bits_from_ord(o);
+    } else {
+      const uint32_t o16 = o >> 16;
+      reinterpret_cast<uint16_t*>(out_vals)[at] =
+          o16 == 0x8000u ? reinterpret_cast<const uint16_t*>(xr)[idx] : bf16_from_ord16(o16);
+    }
+  };
+
+  for (int r = wave; r < b; r += kRowWaves) {
+    const int s0 = (int)(((int64_t)r * n + b - 1) / b);
+    const int s1 = (int)(((int64_t)(r + 1) * n + b - 1) / b);
+    // key of the element with order key o (ord32 layout) at position i
+    auto mk = [&](uint32_t o, int i) -> Key {
+      if constexpr (PACK)
+        return (o & 0xffff0000u) | (0xffffu - (uint32_t)(i - s0));
+      else
+        return make_key(o, (uint32_t)i);
+    };
+    Key q[KB];
+#pragma unroll
+    for (int j = 0; j < KB; ++j) q[j] = 0;
+    if (vec) {
+      const int nv = (s1 - s0) / V;
+      for (int v0 = lane; v0 < nv; v0 += kWave * U) {
+        uint4 w[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int v = v0 + u * kWave;
+          w[u] = v < nv ? *reinterpret_cast<const uint4*>(xr + ((int64_t)s0 + (int64_t)v * V) * ES)
+                        : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int v = v0 + u * kWave;
+          if (v < nv) {
+#pragma unroll
+            for (int e = 0; e < V; ++e) queue_insert<KB>(q, mk(ord_elem<DT>(w[u], e), s0 + v * V + e));
+          }
+        }
+      }
+    } else {
+      for (int i0 = s0 + lane; i0 < s1; i0 += kWave * U) {
+        uint32_t bits[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int i = i0 + u * kWave;
+          if constexpr (DT == IN_F32)
+            bits[u] = i < s1 ? reinterpret_cast<const uint32_t*>(xr)[i] : 0u;
+          else
+            bits[u] = i < s1 ? (uint32_t)reinterpret_cast<const uint16_t*>(xr)[i] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int i = i0 + u * kWave;
+          if (i < s1) {
+            const uint32_t o = DT == IN_F32 ? ord_f32(bits[u]) : (ord_bf16x2(bits[u]) << 16);
+            queue_insert<KB>(q, mk(o, i));
+          }
+        }
+      }
+    }
+    // every lane ends with the bucket's top-KB
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      Key c[KB];
+#pragma unroll
+      for (int j = 0; j < KB; ++j) {
+        if constexpr (PACK)
+          c[j] = (Key)__shfl_xor((int)q[j], o, kWave);
+        else
+          c[j] = shfl_xor_u64(q[j], o);
+      }
+      queue_merge<KB>(q, c);
+    }
+    Key mine = 0;
+#pragma unroll
+    for (int j = 0; j < KB; ++j)
+      if (j == lane) mine = q[j];
+    uint64_t key;
+    if constexpr (PACK)
+      key = make_key(mine & 0xffff0000u, (uint32_t)s0 + (0xffffu - (mine & 0xffffu)));
+    else
+      key = mine;
+    if (lane < kb) {
+      if constexpr (FINAL)
+        cand[r * kb + lane] = key;
+      else
+        write(((int64_t)row * b + r) * kb + lane, key);
+    }
+  }
+  if constexpr (FINAL) {
+    __syncthreads();
+    block_final(cand, b * kb, k, hist, ctl, [&](int i, uint64_t key) { write((int64_t)row * k + i, key); });
+  }
+}
+
 }  // namespace
 
 bool row_bucket_ok(int dtype, int64_t m, int64_t n, int64_t b, int64_t kb, bool aligned) {
@@ -585,6 +718,55 @@ hipError_t launch_row_bucket(const void* x, int dtype, int64_t m, int64_t n, int
     else ATOPK_RB(4, false);
   }
 #undef ATOPK_RB
+  return hipGetLastError();
+}
+
+bool row_contig_ok(int64_t n, int64_t b, int64_t kb, int final_exact) {
+  return kb >= 1 && kb <= 16 && n / b >= kb && n <= INT32_MAX && (!final_exact || b * kb <= kRowLds / 8);
+}
+
+template <int DT, int KB, bool FIN>
+void launch_contig_t(dim3 grid, hipStream_t s, const uint8_t* xb, int64_t ld_bytes, int64_t n, int64_t b, int64_t kb,
+                     int64_t k, int vec, bool pack, uint8_t* ov, int32_t* out_idx) {
+  if constexpr (DT == IN_BF16) {
+    if (pack) {
+      hipLaunchKernelGGL((row_contig_kernel<DT, KB, FIN, true>), grid, dim3(kRowT), 0, s, xb, ld_bytes, (int)n, (int)b,
+                         (int)kb, (int)k, vec, ov, out_idx);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((row_contig_kernel<DT, KB, FIN, false>), grid, dim3(kRowT), 0, s, xb, ld_bytes, (int)n, (int)b,
+                     (int)kb, (int)k, vec, ov, out_idx);
+}
+
+template <int DT, bool FIN>
+void launch_contig_kb(int kbs, dim3 grid, hipStream_t s, const uint8_t* xb, int64_t ld_bytes, int64_t n, int64_t b,
+                      int64_t kb, int64_t k, int vec, bool pack, uint8_t* ov, int32_t* out_idx) {
+  if (kbs == 1) launch_contig_t<DT, 1, FIN>(grid, s, xb, ld_bytes, n, b, kb, k, vec, pack, ov, out_idx);
+  else if (kbs == 2) launch_contig_t<DT, 2, FIN>(grid, s, xb, ld_bytes, n, b, kb, k, vec, pack, ov, out_idx);
+  else if (kbs == 4) launch_contig_t<DT, 4, FIN>(grid, s, xb, ld_bytes, n, b, kb, k, vec, pack, ov, out_idx);
+  else if (kbs == 8) launch_contig_t<DT, 8, FIN>(grid, s, xb, ld_bytes, n, b, kb, k, vec, pack, ov, out_idx);
+  else launch_contig_t<DT, 16, FIN>(grid, s, xb, ld_bytes, n, b, kb, k, vec, pack, ov, out_idx);
+}
+
+hipError_t launch_row_contig(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k, int64_t b,
+                             int64_t kb, int final_exact, bool aligned, void* out_vals, int32_t* out_idx,
+                             hipStream_t s) {
+  const int64_t es = dtype == IN_F32 ? 4 : 2;
+  const int64_t vlen = 16 / es;
+  const int vec = aligned && n % b == 0 && (n / b) % vlen == 0 ? 1 : 0;
+  const bool pack = (n + b - 1) / b <= 65536;  // positions inside a run fit 16 bits
+  const uint8_t* xb = static_cast<const uint8_t*>(x);
+  uint8_t* ov = static_cast<uint8_t*>(out_vals);
+  const dim3 grid((unsigned)m);
+  const int kbs = kb <= 1 ? 1 : kb <= 2 ? 2 : kb <= 4 ? 4 : kb <= 8 ? 8 : 16;
+  if (dtype == IN_F32) {
+    if (final_exact) launch_contig_kb<IN_F32, true>(kbs, grid, s, xb, ldx * es, n, b, kb, k, vec, pack, ov, out_idx);
+    else launch_contig_kb<IN_F32, false>(kbs, grid, s, xb, ldx * es, n, b, kb, k, vec, pack, ov, out_idx);
+  } else {
+    if (final_exact) launch_contig_kb<IN_BF16, true>(kbs, grid, s, xb, ldx * es, n, b, kb, k, vec, pack, ov, out_idx);
+    else launch_contig_kb<IN_BF16, false>(kbs, grid, s, xb, ldx * es, n, b, kb, k, vec, pack, ov, out_idx);
+  }
   return hipGetLastError();
 }
 
