@@ -154,8 +154,127 @@ __global__ __launch_bounds__(kT1) void decode_select_kernel(const uint16_t* __re
   }
 }
 
-constexpr int kT2 = 256;
+// Kernel 1 for query-head groups (G >= 2): the g dot products of a key are a
+// dense contraction, Q [G x 128] times K^T [128 x keys], so they go to the
+// matrix cores: v_mfma_f32_16x16x32_bf16 with the G query rows as A (rows G..15
+// zero) and 16 keys as B; lane l holds A row l % 16 / B column l % 16 over
+// k = 8 (l / 16) .. + 8 of each 32-wide k step, and gets C rows 4 (l / 16) + i,
+// column l % 16.  A key row is read as 4 x 64 contiguous bytes per k step.
+// 512 threads, so each thread owns half as many (head, bucket) queues.
+constexpr int kT1M = 512;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int PPT, int KB>
+__global__ __launch_bounds__(kT1M, 2) void decode_select_mfma_kernel(const uint16_t* __restrict__ q,
+                                                                 const uint16_t* __restrict__ K, int hq, int hkv,
+                                                                 int ctx, int64_t ctx_stride, float scale, int b,
+                                                                 int64_t chunk, int nchunks,
+                                                                 uint64_t* __restrict__ partial,
+                                                                 float* __restrict__ scores) {
+  constexpr int NW = kT1M / kWave;  // 8 waves
+  constexpr int GR = kSub / (NW * 16);  // 16-key groups per wave per step
+  constexpr int KS = kD / 32;           // k steps of one MFMA each
+  __shared__ float sc[2][kMaxG][kSubPad];
+
+  const int t = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = t / kWave;
+  const int bh = blockIdx.y;
+  const int bi = bh / hkv;
+  const int h = bh - bi * hkv;
+  const int G = hq / hkv;
+  const int c = blockIdx.x;
+  const int j0 = (int)(c * chunk);
+  const int j1 = (int)min((int64_t)ctx, (int64_t)j0 + chunk);
+
+  const int col = lane & 15;         // A row (query head) / B column (key)
+  const int kq = 8 * (lane >> 4);    // k offset inside a k step
+  bf16x8_t qa[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const uint4 v = col < G ? *reinterpret_cast<const uint4*>(q + ((int64_t)(bi * hq + h * G + col) * kD + 32 * ks + kq))
+                            : make_uint4(0, 0, 0, 0);
+    qa[ks] = __builtin_bit_cast(bf16x8_t, v);
+  }
+  const uint16_t* kh = K + (int64_t)bh * ctx_stride * kD + kq;
+
+  uint64_t qq[PPT][KB];
+#pragma unroll
+  for (int i = 0; i < PPT; ++i)
+#pragma unroll
+    for (int j = 0; j < KB; ++j) qq[i][j] = 0;
+  const int npairs = G * b;
+
+  int buf = 0;
+  for (int s0 = j0; s0 < j1; s0 += kSub) {
+    const int s1 = min(j1, s0 + kSub);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {  // two 16-key groups in flight: fewer registers
+      uint4 kv[GR / 2][KS];
+#pragma unroll
+      for (int gh = 0; gh < GR / 2; ++gh) {
+        const int jj = s0 + (wave * GR + half * (GR / 2) + gh) * 16 + col;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          kv[gh][ks] = jj < s1 ? *reinterpret_cast<const uint4*>(kh + (int64_t)jj * kD + 32 * ks) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int gh = 0; gh < GR / 2; ++gh) {
+        f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], __builtin_bit_cast(bf16x8_t, kv[gh][ks]), acc, 0, 0, 0);
+        const int li = (wave * GR + half * (GR / 2) + gh) * 16 + col;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int g = 4 * (lane >> 4) + i;
+          if (g < G) sc[buf][g][li] = acc[i] * scale;
+        }
+      }
+    }
+    lds_barrier();
+    const int nk = s1 - s0;
+    if (scores != nullptr) {  // debug dump, coalesced
+      for (int i = t; i < G * nk; i += kT1M) {
+        const int g = i / nk, li = i - g * nk;
+        scores[(int64_t)(bi * hq + h * G + g) * ctx + s0 + li] = sc[buf][g][li];
+      }
+    }
+    // fold the staged scores of the owned (head, bucket) pairs: bucket r
+    // holds keys j with j mod b == r
+    const int rs = s0 % b;
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int pr = t + kT1M * i;
+      if (pr < npairs) {
+        const int g = pr / b;
+        const int r = pr - g * b;
+        for (int li = r - rs + (r < rs ? b : 0); li < nk; li += b) {
+          const uint32_t bits = __float_as_uint(sc[buf][g][li]);
+          queue_insert<KB>(qq[i], make_key(ord_f32(bits), (uint32_t)(s0 + li)));
+        }
+      }
+    }
+    buf ^= 1;
+  }
+#pragma unroll
+  for (int i = 0; i < PPT; ++i) {
+    const int pr = t + kT1M * i;
+    if (pr < npairs) {
+      const int g = pr / b;
+      const int r = pr - g * b;
+      uint64_t* dst = partial + ((((int64_t)bh * nchunks + c) * G + g) * b + r) * KB;
+#pragma unroll
+      for (int j = 0; j < KB; ++j) dst[j] = qq[i][j];
+    }
+  }
+}
+
+constexpr int kT2 = 512;
 constexpr int kMaxCand = 8192;
+constexpr int kVGroups = kT2 / 16;  // 16-lane groups gathering V rows
 
 template <int KB>
 __global__ __launch_bounds__(kT2) void decode_finish_kernel(const uint64_t* __restrict__ partial, int nchunks, int hq,
@@ -166,8 +285,8 @@ __global__ __launch_bounds__(kT2) void decode_finish_kernel(const uint64_t* __re
   __shared__ uint64_t cand[kMaxCand];
   __shared__ uint32_t hist[256];
   __shared__ uint32_t ctl[8];
-  __shared__ float acc_lds[16][kD];
-  __shared__ float w_lds[16];
+  __shared__ float acc_lds[kVGroups][kD];
+  __shared__ float w_lds[kVGroups];
   __shared__ float red[T / kWave];
 
   const int t = threadIdx.x;
@@ -186,7 +305,17 @@ __global__ __launch_bounds__(kT2) void decode_finish_kernel(const uint64_t* __re
     const int64_t cstride = (int64_t)G * b * KB;
 #pragma unroll
     for (int j = 0; j < KB; ++j) a[j] = src[j];
-    for (int c = 1; c < nchunks; ++c) {
+    int c = 1;
+    for (; c + 4 <= nchunks; c += 4) {  // four lists in flight
+      uint64_t o[4][KB];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < KB; ++j) o[u][j] = src[(c + u) * cstride + j];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) queue_merge<KB>(a, o[u]);
+    }
+    for (; c < nchunks; ++c) {
       uint64_t o[KB];
 #pragma unroll
       for (int j = 0; j < KB; ++j) o[j] = src[c * cstride + j];
@@ -222,7 +351,7 @@ __global__ __launch_bounds__(kT2) void decode_finish_kernel(const uint64_t* __re
 #pragma unroll
   for (int w = 1; w < T / kWave; ++w) mx = fmaxf(mx, red[w]);
 
-  constexpr int U = 4;
+  constexpr int U = 8;
   const int group = t >> 4;
   const int sub = t & 15;
   const uint16_t* vh = V + (int64_t)bh * ctx_stride * kD + sub * 8;
@@ -230,12 +359,12 @@ __global__ __launch_bounds__(kT2) void decode_finish_kernel(const uint64_t* __re
 #pragma unroll
   for (int d = 0; d < 8; ++d) acc[d] = 0.0f;
   float wsum = 0.0f;
-  for (int i = group; i < n; i += 16 * U) {
+  for (int i = group; i < n; i += kVGroups * U) {
     uint4 v[U];
     float w[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int ii = i + 16 * u;
+      const int ii = i + kVGroups * u;
       if (ii < n) {
         const uint64_t key = cand[ii];
         v[u] = *reinterpret_cast<const uint4*>(vh + (int64_t)key_idx(key) * kD);
@@ -263,7 +392,7 @@ __global__ __launch_bounds__(kT2) void decode_finish_kernel(const uint64_t* __re
   if (t < kD) {
     float s = 0.0f, wt = 0.0f;
 #pragma unroll
-    for (int gg = 0; gg < 16; ++gg) {
+    for (int gg = 0; gg < kVGroups; ++gg) {
       s += acc_lds[gg][t];
       wt += w_lds[gg];
     }
@@ -283,14 +412,17 @@ DecodePlan plan_decode(int64_t batch, int64_t hq, int64_t hkv, int64_t ctx, int6
   DecodePlan p{};
   const int64_t g = hq / hkv;
   const int kbs = kb_pow2(kb);
+  p.mfma = g >= 2;  // the G dot products of a key on the matrix cores
+  const int threads = p.mfma ? kT1M : kT1;
   int ppt = 1;
-  while ((int64_t)ppt * kT1 < g * b) ppt *= 2;
+  while ((int64_t)ppt * threads < g * b) ppt *= 2;
   p.ppt = ppt;
   p.fused = !(b == 1 && kb == k_sel) && ppt <= 8 && (int64_t)ppt * kbs <= 64 && b * kb <= kMaxCand && kbs <= 16;
   // chunks: enough workgroups to fill the chip, long enough that the lists
   // written per chunk stay small next to the K bytes read
   const int64_t heads = batch * hkv;
-  int64_t nchunks = std::max<int64_t>(1, (512 + heads - 1) / std::max<int64_t>(heads, 1));
+  const int64_t target = 512;  // workgroups
+  int64_t nchunks = std::max<int64_t>(1, (target + heads - 1) / std::max<int64_t>(heads, 1));
   nchunks = std::min<int64_t>(nchunks, std::max<int64_t>(1, ctx / 4096));
   int64_t chunk = (ctx + nchunks - 1) / nchunks;
   chunk = (chunk + kSub - 1) / kSub * kSub;
@@ -306,10 +438,14 @@ hipError_t launch_decode_fused(const DecodePlan& p, const uint16_t* q, const uin
                                int32_t* sel_idx, float* scores, hipStream_t s) {
   const int kbs = kb_pow2(kb);
   dim3 g1((unsigned)p.nchunks, (unsigned)(batch * hkv));
-#define ATOPK_D1(P, KBV)                                                                                           \
-  if (p.ppt == P && kbs == KBV) {                                                                                  \
-    hipLaunchKernelGGL((decode_select_kernel<P, KBV>), g1, dim3(kT1), 0, s, q, K, (int)hq, (int)hkv, (int)ctx,      \
-                       ctx_stride, scale, (int)b, p.chunk, p.nchunks, partial, scores);                             \
+#define ATOPK_D1(P, KBV)                                                                                            \
+  if (p.ppt == P && kbs == KBV) {                                                                                   \
+    if (p.mfma)                                                                                                     \
+      hipLaunchKernelGGL((decode_select_mfma_kernel<P, KBV>), g1, dim3(kT1M), 0, s, q, K, (int)hq, (int)hkv,         \
+                         (int)ctx, ctx_stride, scale, (int)b, p.chunk, p.nchunks, partial, scores);                  \
+    else                                                                                                            \
+      hipLaunchKernelGGL((decode_select_kernel<P, KBV>), g1, dim3(kT1), 0, s, q, K, (int)hq, (int)hkv, (int)ctx,     \
+                         ctx_stride, scale, (int)b, p.chunk, p.nchunks, partial, scores);                            \
   } else
   ATOPK_D1(1, 1) ATOPK_D1(1, 2) ATOPK_D1(1, 4) ATOPK_D1(1, 8) ATOPK_D1(1, 16)
   ATOPK_D1(2, 1) ATOPK_D1(2, 2) ATOPK_D1(2, 4) ATOPK_D1(2, 8) ATOPK_D1(2, 16)

@@ -105,6 +105,7 @@ hipError_t launch_decode_scores(const uint16_t* q, const uint16_t* K, int64_t ba
 // merge + final Top-K + softmax-V per query head.
 struct DecodePlan {
   bool fused;            // false: scores, selection and softmax-V as separate passes
+  bool mfma;             // query-head groups: scores on the matrix cores
   int ppt;               // (head, bucket) pairs per thread in the scoring kernel
   int64_t chunk;         // keys per scoring workgroup
   int nchunks;
