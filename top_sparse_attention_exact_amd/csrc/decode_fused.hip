@@ -18,6 +18,9 @@
 // score, then ~key index).  Scores never go to HBM unless a debug dump is
 // asked for.  Each workgroup writes its per-pair lists to the workspace.
 //
+// With b = 0 kernel 1 only writes every score (the exact Top-K route selects
+// on the written scores).
+//
 // Kernel 2 (grid: batch x query heads): merge the chunk lists of every
 // bucket, take the exact Top-K of the b*k_b candidates in LDS (radix select),
 // optionally sort them for the index output, then softmax over the selected
@@ -126,7 +129,7 @@ __global__ __launch_bounds__(kT1) void decode_select_kernel(const uint16_t* __re
     }
     // fold the staged scores of the owned (head, bucket) pairs: bucket r
     // holds keys j with j mod b == r
-    const int rs = s0 % b;
+    const int rs = b > 0 ? s0 % b : 0;  // b == 0: scores only
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
       const int pr = t + kT1 * i;
@@ -244,7 +247,7 @@ __global__ __launch_bounds__(kT1M, 2) void decode_select_mfma_kernel(const uint1
     }
     // fold the staged scores of the owned (head, bucket) pairs: bucket r
     // holds keys j with j mod b == r
-    const int rs = s0 % b;
+    const int rs = b > 0 ? s0 % b : 0;  // b == 0: scores only
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
       const int pr = t + kT1M * i;
@@ -430,6 +433,20 @@ DecodePlan plan_decode(int64_t batch, int64_t hq, int64_t hkv, int64_t ctx, int6
   p.nchunks = (int)((ctx + chunk - 1) / chunk);
   p.partial_bytes = (size_t)heads * p.nchunks * g * b * kbs * 8;
   return p;
+}
+
+hipError_t launch_decode_scores(const uint16_t* q, const uint16_t* K, int64_t batch, int64_t hq, int64_t hkv,
+                                int64_t ctx, int64_t ctx_stride, float scale, float* scores, hipStream_t s) {
+  // the scoring kernels with no bucket (b = 0): every score to `scores`
+  const DecodePlan p = plan_decode(batch, hq, hkv, ctx, 1, 1, 1);
+  dim3 g1((unsigned)p.nchunks, (unsigned)(batch * hkv));
+  if (p.mfma)
+    hipLaunchKernelGGL((decode_select_mfma_kernel<1, 1>), g1, dim3(kT1M), 0, s, q, K, (int)hq, (int)hkv, (int)ctx,
+                       ctx_stride, scale, 0, p.chunk, p.nchunks, nullptr, scores);
+  else
+    hipLaunchKernelGGL((decode_select_kernel<1, 1>), g1, dim3(kT1), 0, s, q, K, (int)hq, (int)hkv, (int)ctx,
+                       ctx_stride, scale, 0, p.chunk, p.nchunks, nullptr, scores);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode_fused(const DecodePlan& p, const uint16_t* q, const uint16_t* K, const uint16_t* V,
