@@ -12,7 +12,8 @@ obvious reference written from the method's definition on the pages:
 * "Recall Before You Rank: Similarity-Guided Top-K Reuse ..." (fugumt page),
   Abstract: Top-K sparse attention scores the current query against the full
   KV cache, takes a global Top-K, and does softmax and value aggregation over
-  that subset only.
+  that subset only; ReTopK reranks a compact candidate set (retrieved
+  supports united with a recent window) with exact current-query scores.
 * STARC (Pith review page), Figure 3 caption: q in R^{1 x d_h}, K, V in
   R^{L x d_h} per head.
 
@@ -43,4 +44,6 @@ from .attention import (  # noqa: F401
     decode_scores,
     attn_decode,
     softmax_v_subset,
+    rerank_candidates,
+    rerank_decode,
 )

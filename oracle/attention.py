@@ -21,6 +21,12 @@ Readings (the pages leave these open):
 * Grouped-query heads: query head h reads KV head h // (H_q / H_kv), and
   every query head selects its own Top-K.
 * Selected indices are reported by score descending, then index ascending.
+* Candidate rerank ("Recall Before You Rank ...", Abstract: the supports of
+  the most similar cached queries are united with a recent window, and only
+  that compact candidate set is reranked with exact current-query scores):
+  the candidate set is the union, as a set, of the given indices that lie in
+  [0, L) and the last `window` positions; the Top-K is exact within it, and a
+  set smaller than K is attended whole.
 """
 
 import numpy as np
@@ -93,4 +99,36 @@ def attn_decode(q_bits, k_bits, v_bits, scale, k_sel, b, kb, scores=None):
         sel[bi] = select(np.asarray(scores[bi], dtype=np.float64), k_sel, b, kb)
         for h in range(hq):
             out[bi, h] = softmax_v_subset(np.asarray(scores[bi, h], dtype=np.float64), sel[bi, h], vv[bi, h // g])
+    return out, sel, scores
+
+
+def rerank_candidates(cand_row, window, length):
+    """The candidate set of one head: the given indices inside [0, L) united
+    with the last `window` positions, as a sorted array without repeats."""
+    c = set(int(j) for j in np.asarray(cand_row).ravel() if 0 <= int(j) < length)
+    c.update(range(length - window, length))
+    return np.array(sorted(c), dtype=np.int64)
+
+
+def rerank_decode(q_bits, k_bits, v_bits, scale, cand, window, k_sel, scores=None):
+    """Reference candidate-rerank decode step.  cand: [B, Hq, C] indices per
+    query head (entries outside [0, L) are ignored).  Returns (out [B, Hq, D]
+    float64, sel [B, Hq, K] int64 padded with -1 when a candidate set holds
+    fewer than K keys, scores [B, Hq, L] float64)."""
+    if scores is None:
+        scores = decode_scores(q_bits, k_bits, scale)
+    vv = bf16_bits_to_f64(v_bits)
+    bsz, hq, length = scores.shape
+    g = hq // vv.shape[1]
+    out = np.empty((bsz, hq, vv.shape[3]), dtype=np.float64)
+    sel = np.full((bsz, hq, k_sel), -1, dtype=np.int64)
+    for bi in range(bsz):
+        for h in range(hq):
+            c = rerank_candidates(cand[bi, h], window, length)
+            s_row = np.asarray(scores[bi, h], dtype=np.float64)
+            kk = min(k_sel, len(c))
+            top, _ = exact_topk(s_row[c][None, :], kk, dtype="f64")
+            chosen = c[top[0]]
+            sel[bi, h, :kk] = chosen
+            out[bi, h] = softmax_v_subset(s_row, chosen, vv[bi, h // g])
     return out, sel, scores

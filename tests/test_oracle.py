@@ -423,6 +423,60 @@ def test_decode_full_selection_is_dense_attention():
     np.testing.assert_allclose(out, ref.numpy(), rtol=1e-12, atol=1e-12)
 
 
+def test_rerank_with_the_whole_cache_is_exact_topk():
+    bsz, hq, hkv, length, d, k = 2, 4, 2, 96, 16, 12
+    q, kk, vv = _decode_inputs(bsz, hq, hkv, length, d, 14)
+    scale = 1 / math.sqrt(d)
+    cand = np.full((bsz, hq, 1), -1)
+    out, sel, _ = oracle.rerank_decode(_bits(q), _bits(kk), _bits(vv), scale, cand, length, k)
+    out2, sel2, _ = oracle.attn_decode(_bits(q), _bits(kk), _bits(vv), scale, k, 1, k)
+    assert np.array_equal(sel, sel2)
+    np.testing.assert_allclose(out, out2, rtol=0, atol=0)
+
+
+def test_rerank_small_set_is_masked_attention():
+    """A candidate set of at most K keys is attended whole: compare with
+    scaled_dot_product_attention under a boolean mask (another formulation);
+    repeats and out-of-range entries change nothing."""
+    bsz, hq, hkv, length, d, k = 1, 2, 1, 64, 8, 16
+    q, kk, vv = _decode_inputs(bsz, hq, hkv, length, d, 15)
+    scale = 1 / math.sqrt(d)
+    g = torch.Generator().manual_seed(16)
+    cand = torch.randint(0, length - 4, (bsz, hq, 8), generator=g).numpy()
+    noisy = np.concatenate([cand, cand[:, :, :3], np.full((bsz, hq, 2), length + 5), np.full((bsz, hq, 1), -3)], axis=2)
+    out, sel, _ = oracle.rerank_decode(_bits(q), _bits(kk), _bits(vv), scale, noisy, 4, k)
+    out_clean, sel_clean, _ = oracle.rerank_decode(_bits(q), _bits(kk), _bits(vv), scale, cand, 4, k)
+    assert np.array_equal(sel, sel_clean)
+    np.testing.assert_array_equal(out, out_clean)
+    for h in range(hq):
+        c = set(cand[0, h].tolist()) | set(range(length - 4, length))
+        assert set(sel[0, h][sel[0, h] >= 0].tolist()) == c
+        assert (sel[0, h] >= 0).sum() == len(c) and (sel[0, h][len(c):] == -1).all()
+        mask = torch.zeros(length, dtype=torch.bool)
+        mask[list(c)] = True
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            q.to(torch.float64)[0, h][None, None, :], kk.to(torch.float64)[0, h // (hq // hkv)][None],
+            vv.to(torch.float64)[0, h // (hq // hkv)][None], attn_mask=mask[None, None, :], scale=scale)[0, 0]
+        np.testing.assert_allclose(out[0, h], ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_rerank_is_topk_of_the_masked_row():
+    """With more than K candidates the selection is the exact Top-K of the
+    score row masked to -inf outside the candidate set."""
+    bsz, hq, hkv, length, d, k = 1, 3, 3, 200, 16, 10
+    q, kk, vv = _decode_inputs(bsz, hq, hkv, length, d, 17)
+    scale = 1 / math.sqrt(d)
+    g = torch.Generator().manual_seed(18)
+    cand = torch.randint(0, length, (bsz, hq, 40), generator=g).numpy()
+    _, sel, sc = oracle.rerank_decode(_bits(q), _bits(kk), _bits(vv), scale, cand, 8, k)
+    for h in range(hq):
+        row = np.full(length, -np.inf)
+        c = oracle.rerank_candidates(cand[0, h], 8, length)
+        row[c] = sc[0, h, c]
+        order = sorted(range(length), key=lambda j: (-row[j], j))[:k]
+        assert sel[0, h].tolist() == order
+
+
 def test_decode_single_key_is_argmax_row():
     q, kk, vv = _decode_inputs(1, 2, 1, 50, 8, 11)
     out, sel, s = oracle.attn_decode(_bits(q), _bits(kk), _bits(vv), 0.3, 1, 1, 1)
