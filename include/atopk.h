@@ -146,6 +146,32 @@ int atopk_sparse_attn_decode(const void* q, const void* K, const void* V, int64_
                              int64_t k_sel, int64_t b, int64_t kb, void* out, int32_t* sel_idx,
                              float* scores, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Candidate-set rerank decode ("Recall Before You Rank: Similarity-Guided
+ * Top-K Reuse ..." (fugumt page), Abstract: the supports of the most similar
+ * cached queries are united with a recent window and only that compact
+ * candidate set is reranked with exact current-query scores).  This is the
+ * rerank step; the cache of query / support pairs and the fallback policy
+ * are the caller's.
+ *   q, K, V, scale, ctx, ctx_stride, d, out   as atopk_sparse_attn_decode.
+ *   cand    [batch, hq, cand_stride] int32 DEVICE array, row (i, h) holding
+ *           ncand candidate key indices of query head h (entries outside
+ *           [0, ctx) are skipped; repeats count once); NULL when ncand == 0.
+ *   window  the last `window` keys [ctx - window, ctx) are candidates too.
+ *   Per query head: the exact Top-k_sel of the candidate set by score (ties
+ *   to the lower index) -- the whole set when it holds fewer keys -- then
+ *   softmax and value aggregation over it.
+ *   sel_idx [batch, hq, k_sel] int32, nullable: selected keys, score desc,
+ *           padded with -1 when the set holds fewer than k_sel keys.
+ * Requires d == 128, hq % hkv == 0, 1 <= ctx <= 262144, ctx_stride >= ctx,
+ * 1 <= window <= ctx, 0 <= ncand <= cand_stride, ncand + window <= 8192,
+ * 1 <= k_sel <= 8192, 16-byte aligned q, K, V.  No workspace.
+ */
+int atopk_sparse_attn_rerank(const void* q, const void* K, const void* V, int64_t batch, int64_t hq, int64_t hkv,
+                             int64_t ctx, int64_t ctx_stride, int64_t d, float scale, const int32_t* cand,
+                             int64_t ncand, int64_t cand_stride, int64_t window, int64_t k_sel, void* out,
+                             int32_t* sel_idx, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -33,7 +33,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 10
+    assert len(names) == 11
     handle = ctypes.CDLL(lib_mod.LIB_PATH)
     for name in names:
         assert hasattr(handle, name), name
@@ -155,3 +155,25 @@ def test_decode_validation(L):
                                       None, None, None, 0, None) == EUNSUP  # misaligned q
     assert L.atopk_sparse_attn_decode(FAKE, FAKE, FAKE, 1, 8, 8, 256, 256, 128, f, 16, 16, 1, FAKE, None, None, None,
                                       0, None) == EWS
+
+
+def test_rerank_validation(L):
+    def call(bsz=2, hq=8, hkv=2, ctx=4096, stride=4096, d=128, cand=FAKE, ncand=100, cstride=128, window=64,
+             k=64, q=FAKE, out=FAKE):
+        return L.atopk_sparse_attn_rerank(q, FAKE, FAKE, bsz, hq, hkv, ctx, stride, d, 0.1, cand, ncand, cstride,
+                                          window, k, out, None, None)
+    assert call(hq=6, hkv=4) == ESHAPE          # hq % hkv
+    assert call(stride=100) == ESHAPE           # ctx_stride < ctx
+    assert call(cstride=50) == ESHAPE           # cand_stride < ncand
+    assert call(ncand=-1) == ESHAPE
+    assert call(k=0) == ESHAPE
+    assert call(window=0) == EPARAM
+    assert call(window=5000) == EPARAM          # window > ctx
+    assert call(d=64) == EUNSUP
+    assert call(ctx=300000, stride=300000) == EUNSUP
+    assert call(ncand=8150, cstride=8192) == EUNSUP  # ncand + window > 8192
+    assert call(k=8193) == EUNSUP
+    assert call(bsz=0, q=None, out=None, cand=None) == OK
+    assert call(q=None) == ENULL
+    assert call(cand=None) == ENULL
+    assert call(q=ctypes.c_void_p(0x1008)) == EUNSUP  # misaligned

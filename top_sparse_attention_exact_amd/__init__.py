@@ -11,6 +11,8 @@ library every call raises.
                                       two-stage bucketed (interleaved or
                                       contiguous buckets)
     sparse_attn_decode(q, K, V, k_sel, b, kb) -> out (, sel_idx, scores)
+    sparse_attn_rerank(q, K, V, cand, window, k_sel) -> out (, sel_idx)
+                                      Top-K over a given candidate set
 """
 
 import ctypes
@@ -155,3 +157,33 @@ def sparse_attn_decode(q, K, V, k_sel, b=1, kb=None, scale=None, ctx=None, retur
     if return_scores:
         res.append(scores)
     return res[0] if len(res) == 1 else tuple(res)
+
+
+def sparse_attn_rerank(q, K, V, cand, window, k_sel, scale=None, ctx=None, return_sel=False):
+    """Candidate-set rerank decode.  q [B, Hq, D], K/V [B, Hkv, Lmax, D] bf16;
+    cand [B, Hq, C] int32 candidate key indices per query head (entries
+    outside [0, ctx) are skipped, repeats count once); the last `window` keys
+    are candidates too.  Returns out [B, Hq, D] bf16 (plus int32 sel_idx
+    [B, Hq, k_sel], -1 padded, when asked)."""
+    for t in (q, K, V):
+        if t.dtype != torch.bfloat16 or not t.is_cuda:
+            raise TypeError("q, K, V must be bf16 GPU tensors")
+    if not (q.is_contiguous() and K.is_contiguous() and V.is_contiguous()):
+        raise ValueError("q, K, V must be contiguous")
+    if cand.dtype != torch.int32 or not cand.is_cuda or cand.dim() != 3 or not cand.is_contiguous():
+        raise TypeError("cand must be a contiguous int32 GPU tensor [B, Hq, C]")
+    bsz, hq, d = q.shape
+    _, hkv, lmax, d2 = K.shape
+    if V.shape != K.shape or d2 != d or tuple(cand.shape[:2]) != (bsz, hq):
+        raise ValueError("shape mismatch")
+    ctx = lmax if ctx is None else ctx
+    scale = (1.0 / d ** 0.5) if scale is None else scale
+    out = torch.empty((bsz, hq, d), dtype=torch.bfloat16, device=q.device)
+    sel = torch.empty((bsz, hq, k_sel), dtype=torch.int32, device=q.device) if return_sel else None
+    ncand = cand.shape[2]
+    st = lib().atopk_sparse_attn_rerank(_ptr(q), _ptr(K), _ptr(V), bsz, hq, hkv, ctx, lmax, d, float(scale),
+                                        _ptr(cand) if ncand > 0 else ctypes.c_void_p(0), ncand,
+                                        ncand, window, k_sel, _ptr(out), _ptr(sel),
+                                        _stream_ptr(q.device))
+    check(st, "atopk_sparse_attn_rerank")
+    return (out, sel) if return_sel else out

@@ -38,6 +38,11 @@ _SIGNATURES = {
         [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, ctypes.c_float, _c_i64, _c_i64, _c_i64,
          _c_vp, _c_vp, _c_vp, _c_vp, ctypes.c_size_t, _c_vp],
     ),
+    "atopk_sparse_attn_rerank": (
+        _c_int,
+        [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, ctypes.c_float, _c_vp, _c_i64, _c_i64,
+         _c_i64, _c_i64, _c_vp, _c_vp, _c_vp],
+    ),
 }
 
 EXPORTED = tuple(_SIGNATURES)

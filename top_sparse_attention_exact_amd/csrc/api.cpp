@@ -443,4 +443,28 @@ int atopk_sparse_attn_decode(const void* q, const void* K, const void* V, int64_
   });
 }
 
+int atopk_sparse_attn_rerank(const void* q, const void* K, const void* V, int64_t batch, int64_t hq, int64_t hkv,
+                             int64_t ctx, int64_t ctx_stride, int64_t d, float scale, const int32_t* cand,
+                             int64_t ncand, int64_t cand_stride, int64_t window, int64_t k_sel, void* out,
+                             int32_t* sel_idx, void* stream) {
+  return guarded([&] {
+    if (batch < 0 || hq < 1 || hkv < 1 || hq % hkv != 0 || ctx < 1 || ctx_stride < ctx || d < 1 || k_sel < 1 ||
+        ncand < 0 || cand_stride < ncand)
+      return (int)ATOPK_ERR_SHAPE;
+    if (window < 1 || window > ctx) return (int)ATOPK_ERR_PARAM;
+    if (d != 128 || ctx > kRerankMaxCtx || ncand + window > kRerankMaxCand || k_sel > ATOPK_MAX_K)
+      return (int)ATOPK_ERR_UNSUPPORTED;
+    if (batch == 0) return (int)ATOPK_OK;
+    if (!q || !K || !V || !out || (ncand > 0 && !cand)) return (int)ATOPK_ERR_NULL;
+    if (((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(K) | reinterpret_cast<uintptr_t>(V)) & 15) != 0)
+      return (int)ATOPK_ERR_UNSUPPORTED;
+    int st = check_device();
+    if (st) return st;
+    return hip_status(launch_rerank(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(K),
+                                    static_cast<const uint16_t*>(V), batch, hq, hkv, ctx, ctx_stride, scale, cand,
+                                    ncand, cand_stride, window, k_sel, static_cast<uint16_t*>(out), sel_idx,
+                                    static_cast<hipStream_t>(stream)));
+  });
+}
+
 }  // extern "C"

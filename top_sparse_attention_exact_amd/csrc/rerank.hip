@@ -1,0 +1,203 @@
+// Candidate-set rerank decode.
+//
+// "Recall Before You Rank: Similarity-Guided Top-K Reuse ..." (fugumt page),
+// Abstract: instead of scoring the query against the whole KV cache, the
+// supports of the most similar cached queries are united with a recent
+// window, and only that compact candidate set is reranked with exact
+// current-query scores; the Top-K of it feeds softmax and value aggregation.
+// This is that inner step (the cache of query / support pairs and the
+// fallback policy stay with the caller).
+//
+// One workgroup per query head:
+//  1. candidate set: the head's given indices inside [0, ctx) and the last
+//     `window` positions, made unique with an LDS bitmap (one bit per key);
+//  2. scores: 16 lanes read one 256-byte key row with 16-byte loads and form
+//     its dot product with the query (packed bf16 dot products, fp32
+//     accumulation, DPP row sums), scaled in fp32;
+//  3. exact Top-K of the set by (score desc, index asc) -- radix select on
+//     the keys in LDS -- or the whole set when it holds fewer than K keys;
+//  4. softmax over the selected scores (maximum subtracted) and the weighted
+//     sum of their V rows, rounded to bf16.
+#include "common.h"
+#include "launch.h"
+
+namespace atopk {
+
+namespace {
+
+constexpr int kD = 128;
+constexpr int kRT = 512;
+constexpr int kGroups = kRT / 16;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot8_bf16(const uint4& a, const uint4& b) {
+  float acc = 0.0f;
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.x), __builtin_bit_cast(bf16x2_t, b.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.y), __builtin_bit_cast(bf16x2_t, b.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.z), __builtin_bit_cast(bf16x2_t, b.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.w), __builtin_bit_cast(bf16x2_t, b.w), acc, false);
+  return acc;
+}
+
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xb1, 0xf, 0xf, true));   // quad_perm 1,0,3,2
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4e, 0xf, 0xf, true));   // quad_perm 2,3,0,1
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xf, 0xf, true));  // row_half_mirror
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xf, 0xf, true));  // row_mirror
+  return v;
+}
+
+__global__ __launch_bounds__(kRT) void rerank_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ K,
+                                                    const uint16_t* __restrict__ V, int hq, int hkv, int ctx,
+                                                    int64_t ctx_stride, float scale,
+                                                    const int32_t* __restrict__ cand, int ncand, int64_t cand_stride,
+                                                    int window, int k_sel, uint16_t* __restrict__ out,
+                                                    int32_t* __restrict__ sel_idx) {
+  constexpr int T = kRT;
+  __shared__ uint64_t keys[kRerankMaxCand];
+  __shared__ uint32_t list[kRerankMaxCand];      // the candidate indices
+  __shared__ uint32_t bits[kRerankMaxCtx / 32];  // candidate bitmap, then the V partial sums
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t ctl[8];
+  __shared__ float w_lds[kGroups];
+  __shared__ float red[T / kWave];
+  float* acc_lds = reinterpret_cast<float*>(bits);  // [kGroups][kD] after the bitmap is done
+  static_assert(kRerankMaxCtx / 32 >= kGroups * kD, "the V partial sums live in the bitmap's words");
+
+  const int t = threadIdx.x;
+  const int r_out = blockIdx.x;  // = bi * hq + h
+  const int bi = r_out / hq;
+  const int h = r_out - bi * hq;
+  const int kvh = h / (hq / hkv);
+  const int64_t bh = (int64_t)bi * hkv + kvh;
+
+  // 1. candidate set
+  const int words = (ctx + 31) / 32;
+  for (int i = t; i < words; i += T) bits[i] = 0;
+  if (t == 0) ctl[7] = 0;
+  __syncthreads();
+  const int32_t* cr = cand + (int64_t)r_out * cand_stride;
+  const int total = ncand + window;
+  for (int i = t; i < total; i += T) {
+    const int j = i < ncand ? cr[i] : ctx - window + (i - ncand);
+    if (j >= 0 && j < ctx) {
+      const uint32_t bit = 1u << (j & 31);
+      if ((atomicOr(&bits[j >> 5], bit) & bit) == 0) list[atomicAdd(&ctl[7], 1u)] = (uint32_t)j;
+    }
+  }
+  __syncthreads();
+  const int nc = (int)ctl[7];  // <= ncand + window <= kRerankMaxCand
+
+  // 2. scores
+  const int group = t >> 4;
+  const int sub = t & 15;
+  const uint4 qv = *reinterpret_cast<const uint4*>(q + (int64_t)r_out * kD + sub * 8);
+  const uint16_t* kh = K + bh * ctx_stride * kD + sub * 8;
+  constexpr int U = 8;
+  for (int i0 = 0; i0 < nc; i0 += kGroups * U) {
+    uint32_t jj[U];
+    uint4 kv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + group + kGroups * u;
+      jj[u] = i < nc ? list[i] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + group + kGroups * u;
+      kv[u] = i < nc ? *reinterpret_cast<const uint4*>(kh + (int64_t)jj[u] * kD) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + group + kGroups * u;
+      const float s = row16_sum(dot8_bf16(kv[u], qv)) * scale;
+      if (i < nc && sub == 0) keys[i] = make_key(ord_f32(__float_as_uint(s)), jj[u]);
+    }
+  }
+  __syncthreads();
+
+  // 3. exact Top-K of the set (the whole set when it is smaller)
+  int n = nc;
+  if (n > k_sel) {
+    const uint64_t thr = block_kth_key<T>(keys, n, k_sel, hist, ctl);
+    n = block_compact_ge<T, kRerankMaxCand / T>(keys, n, thr, ctl);
+  }
+  if (sel_idx != nullptr) {
+    int npow = 1;
+    while (npow < n) npow <<= 1;
+    for (int i = n + t; i < npow; i += T) keys[i] = 0;
+    block_sort_desc<T>(keys, npow);
+    for (int i = t; i < k_sel; i += T) sel_idx[(int64_t)r_out * k_sel + i] = i < n ? (int32_t)key_idx(keys[i]) : -1;
+  }
+  __syncthreads();
+
+  // 4. softmax over the selected scores, weighted sum of their V rows
+  float mx = -INFINITY;
+  for (int i = t; i < n; i += T) mx = fmaxf(mx, key_value_f32(keys[i]));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+  if (lane_id() == 0) red[t / kWave] = mx;
+  __syncthreads();
+  mx = red[0];
+#pragma unroll
+  for (int w = 1; w < T / kWave; ++w) mx = fmaxf(mx, red[w]);
+
+  const uint16_t* vh = V + bh * ctx_stride * kD + sub * 8;
+  float acc[8];
+#pragma unroll
+  for (int d = 0; d < 8; ++d) acc[d] = 0.0f;
+  float wsum = 0.0f;
+  for (int i = group; i < n; i += kGroups * U) {
+    uint4 v[U];
+    float w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int ii = i + kGroups * u;
+      if (ii < n) {
+        const uint64_t key = keys[ii];
+        v[u] = *reinterpret_cast<const uint4*>(vh + (int64_t)key_idx(key) * kD);
+        w[u] = expf(key_value_f32(key) - mx);
+      } else {
+        v[u] = make_uint4(0, 0, 0, 0);
+        w[u] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t word[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        acc[2 * d] += w[u] * __uint_as_float(word[d] << 16);
+        acc[2 * d + 1] += w[u] * __uint_as_float(word[d] & 0xffff0000u);
+      }
+      wsum += w[u];
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < 8; ++d) acc_lds[group * kD + sub * 8 + d] = acc[d];
+  if (sub == 0) w_lds[group] = wsum;
+  __syncthreads();
+  if (t < kD) {
+    float s = 0.0f, wt = 0.0f;
+#pragma unroll
+    for (int gg = 0; gg < kGroups; ++gg) {
+      s += acc_lds[gg * kD + t];
+      wt += w_lds[gg];
+    }
+    out[(int64_t)r_out * kD + t] = f32_to_bf16_rne(s / wt);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rerank(const uint16_t* q, const uint16_t* K, const uint16_t* V, int64_t batch, int64_t hq,
+                         int64_t hkv, int64_t ctx, int64_t ctx_stride, float scale, const int32_t* cand, int64_t ncand,
+                         int64_t cand_stride, int64_t window, int64_t k_sel, uint16_t* out, int32_t* sel_idx,
+                         hipStream_t s) {
+  hipLaunchKernelGGL(rerank_kernel, dim3((unsigned)(batch * hq)), dim3(kRT), 0, s, q, K, V, (int)hq, (int)hkv,
+                     (int)ctx, ctx_stride, scale, cand, (int)ncand, cand_stride, (int)window, (int)k_sel, out, sel_idx);
+  return hipGetLastError();
+}
+
+}  // namespace atopk
