@@ -232,7 +232,11 @@ def selection_step(args, timer):
     return dict(m=m, n=n, k=k, modes=modes, step_s=step_s, info=info, recall=recall, x=x, copies=len(xs))
 
 
+RERANK_SUPPORTS = 4
+
+
 def decode_steps(args, timer):
+    import numpy as np
     import torch
 
     import top_sparse_attention_exact_amd as atk
@@ -252,6 +256,14 @@ def decode_steps(args, timer):
         modes = [("bucketed", c["b"], c["kb"]), ("exact", 1, c["k_sel"])]
         calls = [(name, (lambda i, b=b, kb=kb: atk.sparse_attn_decode(q, K, V, c["k_sel"], b, kb)))
                  for name, b, kb in modes]
+        if w == "gqa":
+            # Candidate rerank on the same cache: per query head, 4 retrieved
+            # supports of K_sel positions each (seeded uniform draws; repeats
+            # allowed) united with the last K_sel keys, exact Top-K_sel inside.
+            g = torch.Generator(device="cpu").manual_seed(11)
+            ncand = RERANK_SUPPORTS * c["k_sel"]
+            cand = torch.randint(0, c["ctx"], (c["bsz"], c["hq"], ncand), generator=g, dtype=torch.int32).cuda()
+            calls.append(("rerank", lambda i: atk.sparse_attn_rerank(q, K, V, cand, c["k_sel"], c["k_sel"])))
         us, info = timer.stream(calls, max(3, min(args.steps, 10)), 2)
         kbytes = K.numel() * 2
         alg = kbytes + q.numel() * 2 + c["bsz"] * c["hq"] * c["k_sel"] * c["d"] * 2 + q.numel() * 2
@@ -263,6 +275,18 @@ def decode_steps(args, timer):
             out[name] = {"us_per_step": round(us[name], 1), "gbps": alg / t / 1e9,
                          "frac_hbm_peak": alg / t / 1e9 / HBM_PEAK_GBPS,
                          "scores_per_s": c["bsz"] * c["hq"] * c["ctx"] / t}
+        if w == "gqa":
+            # Each head reads its unique candidates' K rows, its K_sel V rows
+            # and its candidate list (plus q and out).
+            heads = c["bsz"] * c["hq"]
+            nuniq = sum(len(np.union1d(row, np.arange(c["ctx"] - c["k_sel"], c["ctx"])))
+                        for row in cand.view(heads, -1).cpu().numpy())
+            ralg = nuniq * c["d"] * 2 + heads * (c["k_sel"] * c["d"] * 2 + ncand * 4 + 2 * c["d"] * 2)
+            t = us["rerank"] * 1e-6
+            out["rerank"] = {"us_per_step": round(us["rerank"], 1), "supports": RERANK_SUPPORTS,
+                             "window": c["k_sel"], "mean_candidates": nuniq / heads, "alg_bytes": ralg,
+                             "gbps": ralg / t / 1e9, "frac_hbm_peak": ralg / t / 1e9 / HBM_PEAK_GBPS,
+                             "speedup_vs_exact": us["exact"] / us["rerank"]}
         res[out["workload"]] = out
         del q, K, V
         torch.cuda.empty_cache()
