@@ -19,7 +19,11 @@ Readings (the pages leave these open):
   binomial by a hypergeometric: the i-th largest value survives stage 1 iff
   fewer than k_b of the i larger values share its bucket, and those i values
   are a uniform i-subset of the other n - 1 positions, s - 1 of which are in
-  its bucket.
+  its bucket.  When b does not divide n, buckets i mod b hold ceil(n/b)
+  (the first n mod b of them) or floor(n/b) elements; the i-th largest value
+  sits at a uniform position, so its bucket has each size with probability
+  proportional to the elements of that size, and the hypergeometric term is
+  averaged over the two sizes.
 """
 
 import math
@@ -91,11 +95,12 @@ def _hypergeom_cdf(x, pop, succ, draws):
 
 
 def eq1_finite(n, k, b, kb):
-    """Exact expected stage-1 recall for an iid row of n distinct values,
-    b dividing n (finite-n reading of Eq. (1), see the module docstring)."""
-    assert n % b == 0
-    s = n // b
-    terms = [_hypergeom_cdf(kb - 1, n - 1, s - 1, i) for i in range(k)]
+    """Exact expected stage-1 recall for an iid row of n distinct values in
+    b interleaved buckets (finite-n reading of Eq. (1), see the module
+    docstring)."""
+    lo, big = n // b, n % b
+    sizes = [(lo + 1, big * (lo + 1) / n), (lo, (b - big) * lo / n)]
+    terms = [w * _hypergeom_cdf(kb - 1, n - 1, s - 1, i) for s, w in sizes if w > 0 for i in range(k)]
     return math.fsum(terms) / k
 
 

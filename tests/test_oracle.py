@@ -242,7 +242,8 @@ def _exhaustive_finite(n, k, b, kb):
     return tot / (cnt * k)
 
 
-@pytest.mark.parametrize("n,k,b,kb", [(8, 3, 2, 1), (8, 4, 4, 1), (9, 4, 3, 2), (12, 5, 4, 2), (12, 6, 3, 3)])
+@pytest.mark.parametrize("n,k,b,kb", [(8, 3, 2, 1), (8, 4, 4, 1), (9, 4, 3, 2), (12, 5, 4, 2), (12, 6, 3, 3),
+                                      (7, 3, 2, 1), (10, 4, 3, 2), (11, 5, 4, 1), (13, 6, 5, 2), (14, 4, 4, 3)])
 def test_eq1_finite_exhaustive(n, k, b, kb):
     assert oracle.eq1_finite(n, k, b, kb) == pytest.approx(float(_exhaustive_finite(n, k, b, kb)), rel=1e-10)
 
