@@ -47,7 +47,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", default="all",
-                    help="all | sel | exact | b64k1 | b128k2 | decode | mha | gqa | sel4k | wide | assign | copy")
+                    help="all | sel | exact | b64k1 | b128k2 | decode | mha | gqa | sel4k | wide | assign | tradeoff | graph "
+                         "| sweep (not in all) | copy")
     ap.add_argument("--no-flush", action="store_true", help="no cache flush before the single-call latency runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
@@ -368,6 +369,156 @@ def assignment_compare(args, timer):
     return out
 
 
+def tradeoff(args, timer):
+    """Runtime against recall of the bucketed top-k at the vocabulary-sampling
+    and knowledge-graph shapes (Figure 4 of the Approximate Top-k page): the
+    exact top-k, then every (b, k_b) of the sweep with the final exact top-k."""
+    import numpy as np
+    import torch
+
+    import top_sparse_attention_exact_amd as atk
+    from top_sparse_attention_exact_amd import workloads
+
+    res = {}
+    for name, c in workloads.TRADEOFF.items():
+        m, n, k = c["m"], c["n"], c["k"]
+        x = workloads.rows_normal(m, n, c["std"], seed=0, device="cuda", workload=name)
+        xs = copies(x, ROTATE_BYTES)
+        torch.cuda.synchronize()
+        _, ex = atk.exact(x, k)
+        ex = ex.cpu().numpy()
+        modes = workloads.tradeoff_modes(k)
+        calls = [("exact", lambda i: atk.exact(xs[i % len(xs)], k))]
+        for b, kb in modes:
+            calls.append(("b%dk%d" % (b, kb), (lambda i, b=b, kb=kb: atk.bucketed(xs[i % len(xs)], k, b, kb, True))))
+        us, info = timer.stream(calls, max(3, min(args.steps, 10)), 2)
+        alg = m * n * 4 + m * k * 8
+        out = {"m": m, "n": n, "k": k, "dtype": "f32", "input_copies": len(xs), "queued_ahead": info["queued_ahead"],
+               "exact": {"us": round(us["exact"], 2), "frac_hbm_peak": alg / (us["exact"] * 1e-6) / 1e9 / HBM_PEAK_GBPS}}
+        for b, kb in modes:
+            nm = "b%dk%d" % (b, kb)
+            _, idx = atk.bucketed(x, k, b, kb, True)
+            got = idx.cpu().numpy()
+            rec = float(np.mean([len(np.intersect1d(a, e)) / k for a, e in zip(got, ex)]))
+            out[nm] = {"us": round(us[nm], 2), "recall": rec,
+                       "frac_hbm_peak": alg / (us[nm] * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+        # The measured chooser at three recall targets (its own timing).
+        out["chooser"] = {}
+        for target in (0.9, 0.95, 0.99):
+            ch = atk.choose(x, k, target)
+            out["chooser"][str(target)] = {"b": ch["b"], "kb": ch["kb"], "expected_recall": ch["recall"],
+                                          "us": round(ch["us"], 2)}
+        res[name] = out
+        del x, xs
+        torch.cuda.empty_cache()
+    return res
+
+
+def sweep(args, timer):
+    """Runtime against n and k at m = 1 and m = 256 (Figures 15-16 of the
+    Approximate Top-k page): the exact top-k and a bucketed top-k with
+    k_b = 1 and b the smallest power of two >= 2k (at most 8192), final
+    exact; torch.topk on the same rows is timed beside them as context."""
+    import torch
+
+    import top_sparse_attention_exact_amd as atk
+    from top_sparse_attention_exact_amd import workloads
+
+    cfg = workloads.SWEEP
+    pts = []
+    for m in cfg["ms"]:
+        for ln in cfg["log2n"]:
+            n = 1 << ln
+            if m * n * 4 > cfg["max_bytes"]:
+                continue
+            x = workloads.rows_normal(m, n, 1.0, seed=ln, device="cuda", workload="sweep")
+            xs = copies(x, min(ROTATE_BYTES, 8 * m * n * 4))
+            torch.cuda.synchronize()
+            for k in cfg["ks"]:
+                b = 1
+                while b < 2 * k:
+                    b *= 2
+                b = min(b, 8192)
+                if k > n or b * 1 < k or b > n:
+                    continue
+                calls = [("exact", lambda i, k=k: atk.exact(xs[i % len(xs)], k)),
+                         ("bucketed", lambda i, k=k, b=b: atk.bucketed(xs[i % len(xs)], k, b, 1, True)),
+                         ("torch.topk", lambda i, k=k: torch.topk(xs[i % len(xs)], k, dim=1))]
+                us, _ = timer.stream(calls, max(3, min(args.steps, 10)), 2)
+                pts.append({"m": m, "n": n, "k": k, "b": b, "exact_us": round(us["exact"], 2),
+                            "bucketed_us": round(us["bucketed"], 2), "torch_topk_us": round(us["torch.topk"], 2)})
+            del x, xs
+            torch.cuda.empty_cache()
+    return pts
+
+
+def graph_leg(args, timer):
+    """The selection step captured in a HIP graph (Figure 9 of the Approximate
+    Top-k page) against the same calls launched one by one: host-side wall
+    time per step with no spin ahead (launch cost included), for the
+    vocab-128k step and the 1 x 4096 selection."""
+    import torch
+
+    import top_sparse_attention_exact_amd as atk
+    from top_sparse_attention_exact_amd import workloads
+
+    res = {}
+    for name in ("vocab-128k", "sel-4k"):
+        c = workloads.SELECTION[name]
+        m, n, k = c["m"], c["n"], c["k"]
+        if name == "vocab-128k":
+            x = workloads.rows_normal_bf16(m, n, 2.0, seed=0, device="cuda")
+        else:
+            x = workloads.rows_uniform(m, n, seed=0, device="cuda")
+        xs = copies(x, ROTATE_BYTES)
+
+        def step(t):
+            atk.exact(t, k)
+            for b, kb, fin in c["modes"]:
+                atk.bucketed(t, k, b, kb, fin)
+
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for t in xs[:2]:
+                step(t)
+        torch.cuda.current_stream().wait_stream(s)
+        graphs = []
+        for t in xs:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(t)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        steps = max(20, args.steps * 10)
+        out = {"m": m, "n": n, "k": k, "modes": ["exact"] + ["b%dk%d%s" % (b, kb, "_final" if f else "")
+                                                            for b, kb, f in c["modes"]]}
+        for mode in ("eager", "graph"):
+            for i in range(3):
+                graphs[i % len(graphs)].replay() if mode == "graph" else step(xs[i % len(xs)])
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            t0 = time.perf_counter()
+            e0.record()
+            for i in range(steps):
+                graphs[i % len(graphs)].replay() if mode == "graph" else step(xs[i % len(xs)])
+            e1.record()
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+            out[mode] = {"wall_us_per_step": wall / steps * 1e6, "gpu_us_per_step": e0.elapsed_time(e1) * 1e3 / steps}
+        # GPU time of the step queued ahead of the GPU (no host gaps), both ways.
+        us, _ = timer.stream([("eager", lambda i: step(xs[i % len(xs)])),
+                              ("graph", lambda i: graphs[i % len(graphs)].replay())], max(3, min(args.steps, 10)), 2)
+        out["eager"]["queued_us_per_step"] = us["eager"]
+        out["graph"]["queued_us_per_step"] = us["graph"]
+        res[name] = out
+        del graphs, x, xs
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return res
+
+
 def copy_calibration(args, timer):
     """A plain elementwise copy (negation) of 256 MiB, the yardstick that
     scales the rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes."""
@@ -436,6 +587,9 @@ def main():
     dec = decode_steps(args, timer) if (not args.no_decode and args.only in ("all", "decode", "mha", "gqa")) else {}
     other = other_selection(args, timer) if args.only in ("all", "sel4k", "wide") else {}
     assign = assignment_compare(args, timer) if args.only in ("all", "assign") else None
+    trade = tradeoff(args, timer) if args.only in ("all", "tradeoff") else None
+    swp = sweep(args, timer) if args.only == "sweep" else None
+    graph = graph_leg(args, timer) if args.only in ("all", "graph") else None
 
     line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
@@ -462,8 +616,10 @@ def main():
                        "wall_ms_per_step_incl_spin": sel["info"]["wall_s"] / args.steps * 1e3,
                        "queued_ahead": sel["info"]["queued_ahead"]},
         })
-    elif assign is not None and not dec and not other:
-        line.update({"value": None, "unit": "elements/s", "ms_per_step": None, "config": {"workload": "vocab-128k"}})
+    elif not dec and not other:
+        line.update({"value": None, "unit": "elements/s", "ms_per_step": None,
+                     "config": {"workload": "vocab-128k" if assign or graph else
+                                ("vocab-sampling, kg-2.65m" if trade else "sweep")}})
     elif dec:
         first = next(iter(dec.values()))
         line.update({"value": first["bucketed"]["scores_per_s"], "unit": "scores/s",
@@ -478,6 +634,12 @@ def main():
         line["other_selection"] = other
     if assign is not None:
         line["assignment"] = assign
+    if trade is not None:
+        line["tradeoff"] = trade
+    if swp is not None:
+        line["sweep"] = swp
+    if graph is not None:
+        line["graph"] = graph
     if sel is not None and not args.no_cpu_baseline:
         cpu, ref = cpu_leg(sel, args.cpu_seconds)
         line["cpu_baseline"] = cpu

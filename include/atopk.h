@@ -55,7 +55,8 @@ enum {
   ATOPK_OK = 0,
   ATOPK_ERR_NULL = 1,        /* a required pointer is NULL                        */
   ATOPK_ERR_SHAPE = 2,       /* m < 0, n < 1, ldx < n, k < 1, k > n, ctx < 1, ...  */
-  ATOPK_ERR_PARAM = 3,       /* b < 1, kb < 1, b*kb < k, kb > floor(n / b), ...    */
+  ATOPK_ERR_PARAM = 3,       /* b < 1, kb < 1, b*kb < k, kb > floor(n / b),
+                                element pointers not aligned to their size, ...   */
   ATOPK_ERR_UNSUPPORTED = 4, /* dtype, d != 128, kb > 16, k > 8192, n >= 2^31, arch */
   ATOPK_ERR_WORKSPACE = 5,   /* ws NULL or smaller than the query says, misaligned */
   ATOPK_ERR_HIP = 6          /* the HIP runtime refused a launch or a query        */
@@ -75,7 +76,9 @@ int atopk_version(void);
  *   x         [m, ldx] row-major, dtype `dtype`; row r is x[r*ldx .. r*ldx+n).
  *   out_vals  [m, k] same dtype as x; out_idx [m, k] int32.  Row r lists the
  *             k largest entries of row r, value descending then index ascending.
- * Limits: 1 <= k <= min(n, 8192), n < 2^31.  m == 0 is a no-op.
+ * Limits: 1 <= k <= min(n, 8192), n < 2^31.  m == 0 is a no-op.  x and
+ * out_vals must be aligned to the element size, out_idx to 4 bytes
+ * (ATOPK_ERR_PARAM otherwise); rows need no further alignment.
  */
 int atopk_exact_workspace(int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k, size_t* ws_bytes);
 int atopk_exact(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k,
@@ -171,6 +174,41 @@ int atopk_sparse_attn_rerank(const void* q, const void* K, const void* V, int64_
                              int64_t ctx, int64_t ctx_stride, int64_t d, float scale, const int32_t* cand,
                              int64_t ncand, int64_t cand_stride, int64_t window, int64_t k_sel, void* out,
                              int32_t* sel_idx, void* stream);
+
+/*
+ * Expected recall of the bucketed top-k ("Approximate Top-k for Increased
+ * Parallelism" (Pith review page), "What carries the argument", Eq. (1)) in
+ * its finite-n form: the expected share of the true top-k kept by stage 1
+ * for an iid row of n distinct values in b interleaved buckets (buckets of
+ * ceil(n/b) or floor(n/b) elements).  Host only.  Needs 1 <= k <= n,
+ * 1 <= b <= n, 1 <= kb <= floor(n / b), b*kb >= k (ATOPK_ERR_SHAPE /
+ * ATOPK_ERR_PARAM otherwise).
+ */
+int atopk_expected_recall(int64_t n, int64_t k, int64_t b, int64_t kb, double* recall);
+
+/*
+ * Measured (b, kb) chooser (same page: "Core claim" and "If this is right" --
+ * the recall model picks (b, kb) for a target accuracy without rerunning the
+ * task; more buckets with kb = 1 when k is small against n, a small kb > 1
+ * with b*kb near k when k is a large fraction of n).  For each kb in
+ * {1, 2, 4, 8, 16} the smallest power-of-two b whose expected recall
+ * (atopk_expected_recall) is >= min_recall, and the next larger b, are
+ * timed on the caller's rows x together with the exact top-k (recall 1);
+ * candidates keep b*kb <= 8192.  The fastest is returned in *b, *kb (the
+ * exact top-k as b = 1, kb = k), its expected recall in *recall and its
+ * measured time per call in *us (both nullable), and out_vals / out_idx
+ * ([m, k], as atopk_bucketed with final_exact) hold its result.
+ * Arguments and limits as atopk_exact, plus 0 <= min_recall <= 1; the
+ * workspace is the largest any candidate needs (atopk_choose_workspace).
+ * BLOCKS the calling thread until the timing launches on `stream` finish
+ * (HIP events), so it cannot be captured into a graph; the caller keeps the
+ * answer for later calls of the same shape.
+ */
+int atopk_choose_workspace(int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k, double min_recall,
+                           size_t* ws_bytes);
+int atopk_choose(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k, double min_recall,
+                 void* out_vals, int32_t* out_idx, void* ws, size_t ws_bytes, void* stream, int64_t* b,
+                 int64_t* kb, double* recall, float* us);
 
 #ifdef __cplusplus
 }

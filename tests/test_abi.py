@@ -33,7 +33,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 14
     handle = ctypes.CDLL(lib_mod.LIB_PATH)
     for name in names:
         assert hasattr(handle, name), name
@@ -77,6 +77,14 @@ def test_exact_validation(L):
     assert L.atopk_exact(FAKE, F32, 4, 100, 100, 10, FAKE, None, None, 0, None) == ENULL
     # m == 0 is a no-op, even with null pointers
     assert L.atopk_exact(None, F32, 0, 100, 100, 10, None, None, None, 0, None) == OK
+    # elements and indices must be aligned to their size
+    odd2, odd1 = ctypes.c_void_p(0x1002), ctypes.c_void_p(0x1001)
+    assert L.atopk_exact(odd2, F32, 4, 100, 100, 10, FAKE, FAKE, None, 0, None) == EPARAM
+    assert L.atopk_exact(FAKE, F32, 4, 100, 100, 10, odd2, FAKE, None, 0, None) == EPARAM
+    assert L.atopk_exact(FAKE, BF16, 4, 100, 100, 10, FAKE, odd2, None, 0, None) == EPARAM
+    assert L.atopk_exact(odd1, BF16, 4, 100, 100, 10, FAKE, FAKE, None, 0, None) == EPARAM
+    assert L.atopk_bucketed(odd2, F32, 2, 100, 100, 4, 4, 1, 1, FAKE, FAKE, None, 0, None) == EPARAM
+    assert L.atopk_bucketed_ex(odd1, BF16, 2, 100, 100, 4, 4, 1, 1, 0, FAKE, FAKE, None, 0, None) == EPARAM
 
 
 def test_exact_workspace_checks(L):
@@ -177,3 +185,44 @@ def test_rerank_validation(L):
     assert call(q=None) == ENULL
     assert call(cand=None) == ENULL
     assert call(q=ctypes.c_void_p(0x1008)) == EUNSUP  # misaligned
+
+
+@pytest.mark.parametrize("n,k,b,kb", [(131072, 64, 64, 1), (131072, 64, 128, 2), (4096, 64, 32, 2), (37, 8, 5, 2),
+                                      (128256, 256, 1024, 1), (128256, 256, 512, 2), (2653751, 100, 2048, 1),
+                                      (2653751, 100, 64, 2), (1 << 20, 8192, 512, 16), (100, 100, 1, 100),
+                                      (1000, 10, 1000, 1)])
+def test_expected_recall_matches_oracle(L, n, k, b, kb):
+    """The library's host recall model against the oracle's finite-n Eq.(1)
+    (itself pinned by exhaustive enumeration)."""
+    import oracle
+
+    r = ctypes.c_double(0.0)
+    assert L.atopk_expected_recall(n, k, b, kb, ctypes.byref(r)) == OK
+    assert r.value == pytest.approx(oracle.eq1_finite(n, k, b, kb), rel=1e-7, abs=1e-9)
+
+
+def test_expected_recall_and_choose_validation(L):
+    r = ctypes.c_double(0.0)
+    assert L.atopk_expected_recall(100, 10, 4, 1, None) == ENULL
+    assert L.atopk_expected_recall(100, 0, 4, 1, ctypes.byref(r)) == ESHAPE
+    assert L.atopk_expected_recall(100, 101, 4, 1, ctypes.byref(r)) == ESHAPE
+    assert L.atopk_expected_recall(100, 10, 4, 2, ctypes.byref(r)) == EPARAM  # b*kb < k
+    assert L.atopk_expected_recall(100, 10, 101, 1, ctypes.byref(r)) == EPARAM
+    assert L.atopk_expected_recall(100, 10, 10, 11, ctypes.byref(r)) == EPARAM  # kb > n/b
+    sz = ctypes.c_size_t(0)
+    assert L.atopk_choose_workspace(F32, 64, 128256, 128256, 256, 0.9, None) == ENULL
+    assert L.atopk_choose_workspace(F32, 64, 128256, 128256, 256, 1.5, ctypes.byref(sz)) == EPARAM
+    assert L.atopk_choose_workspace(F32, 64, 128256, 128256, 256, float("nan"), ctypes.byref(sz)) == EPARAM
+    assert L.atopk_choose_workspace(F32, 64, 128256, 128256, 0, 0.9, ctypes.byref(sz)) == ESHAPE
+    assert L.atopk_choose_workspace(F32, 64, 128256, 128256, 256, 0.9, ctypes.byref(sz)) == OK
+    assert sz.value > 0
+    b, kb = ctypes.c_int64(0), ctypes.c_int64(0)
+    assert L.atopk_choose(None, F32, 64, 128256, 128256, 256, 0.9, FAKE, FAKE, FAKE, sz.value, None,
+                          ctypes.byref(b), ctypes.byref(kb), None, None) == ENULL
+    assert L.atopk_choose(FAKE, F32, 64, 128256, 128256, 256, 0.9, FAKE, FAKE, None, 0, None,
+                          ctypes.byref(b), ctypes.byref(kb), None, None) == EWS
+    assert L.atopk_choose(FAKE, F32, 64, 128256, 128256, 256, 0.9, FAKE, FAKE, FAKE, sz.value, None,
+                          None, ctypes.byref(kb), None, None) == ENULL
+    assert L.atopk_choose(None, F32, 0, 128256, 128256, 256, 0.9, None, None, None, 0, None,
+                          ctypes.byref(b), ctypes.byref(kb), None, None) == OK
+    assert (b.value, kb.value) == (1, 256)

@@ -133,6 +133,25 @@ def test_strided_and_misaligned_rows(gpu):
     check_bucketed(xb, 64, 128, 2, True)
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("off", [1, 2, 3, 5, 7])
+def test_bucketed_row_offsets(gpu, dtype, off):
+    """Rows starting at every element offset from a 16-byte boundary (and an
+    odd row stride, so each row's offset differs): the vectorised stage 1
+    takes the leading elements in a scalar head sweep.  Several (b, k_b),
+    splits of long rows, a row shorter than the head, and b above the
+    vectorised limit (the per-bucket walk)."""
+    base = rand_rows(5, 40011, dtype, 20 + off, gpu)
+    x = base[:, off:off + 39001]
+    for b, kb, fin in [(2, 4, True), (4, 3, True), (64, 1, False), (256, 2, True), (1024, 1, True), (512, 4, False),
+                       (2048, 1, True), (8192, 2, True)]:
+        print("case", dtype, off, b, kb, fin, flush=True)
+        k = min(b * kb, 64)
+        check_bucketed(x, k, b, kb, fin)
+    tiny = base[:, off:off + 3]
+    check_bucketed(tiny, 2, 2, 1, True)
+
+
 def test_single_row_and_empty(gpu):
     x = rand_rows(1, 4096, torch.float32, 9, gpu)
     check_exact(x, 64)
@@ -203,6 +222,63 @@ def test_wide1m_sampled_and_worst_case(gpu):
     assert worst == 64 / 8192
     np.testing.assert_array_equal(r[1::2], worst)  # planted rows: exactly the worst case
     assert abs(r[0::2].mean() - oracle.eq1_finite(n, k, b, kb)) < 0.01
+
+
+@pytest.mark.parametrize("name", ["vocab-sampling", "kg-2.65m"])
+def test_tradeoff_shapes_sampled(gpu, name):
+    """The runtime/accuracy trade-off shapes at full size, in the launches the
+    sweep times: exact top-k and every (b, k_b) of the sweep, final exact, bit
+    for bit against the oracle on sampled rows; the mean recall over all rows
+    within 0.02 of Eq.(1)'s finite-n expectation (iid rows)."""
+    c = workloads.TRADEOFF[name]
+    m, n, k = c["m"], c["n"], c["k"]
+    x = workloads.rows_normal(m, n, c["std"], seed=0, device=gpu, workload=name)
+    rows = [0, m - 1]
+    hx = x[rows].cpu().numpy()
+    ev, ei = atk.exact(x, k)
+    ridx, rv = oracle.exact_topk(hx, k, "f32")
+    np.testing.assert_array_equal(ei[rows].cpu().numpy(), ridx)
+    np.testing.assert_array_equal(ev[rows].cpu().numpy().view(np.uint32), rv.view(np.uint32))
+    ex = ei.cpu().numpy()
+    for b, kb in workloads.tradeoff_modes(k):
+        print("case", name, b, kb, flush=True)
+        bv, bi = atk.bucketed(x, k, b, kb, True)
+        if (b, kb) in ((1024, 1), (512, 2), (8192, 1)):
+            oidx, ov = oracle.bucketed_topk(hx, k, b, kb, True, "f32")
+            np.testing.assert_array_equal(bi[rows].cpu().numpy(), oidx)
+            np.testing.assert_array_equal(bv[rows].cpu().numpy().view(np.uint32), ov.view(np.uint32))
+        r = oracle.recall(bi.cpu().numpy(), ex).mean()
+        assert abs(r - oracle.eq1_finite(n, k, b, kb)) < 0.02, (b, kb, r)
+
+
+@pytest.mark.parametrize("name,dtype", [("vocab-sampling", torch.float32), ("vocab-sampling", torch.bfloat16)])
+def test_choose(gpu, name, dtype):
+    """The measured chooser: its pick meets the recall target by the model,
+    its outputs equal a plain call of the picked (b, k_b) and the oracle on
+    sampled rows, and the measured recall agrees with the model."""
+    c = workloads.TRADEOFF[name]
+    m, n, k = c["m"], c["n"], c["k"]
+    x = workloads.rows_normal(m, n, c["std"], seed=3, device=gpu, workload=name).to(dtype)
+    _, ex = atk.exact(x, k)
+    rows = [0, m - 1]
+    hx, tag = host(x[rows])
+    for target in (0.9, 0.99, 1.0):
+        res = atk.choose(x, k, target)
+        b, kb = res["b"], res["kb"]
+        print("case", name, dtype, target, b, kb, res["us"], flush=True)
+        assert res["recall"] >= target and res["us"] > 0
+        if b == 1:
+            assert kb == k and res["recall"] == 1.0
+        else:
+            assert b * kb <= 8192 and res["recall"] == atk.expected_recall(n, k, b, kb)
+        v, i = atk.bucketed(x, k, b, kb, True)
+        assert torch.equal(v, res["values"]) and torch.equal(i, res["indices"])
+        oidx, ov = oracle.bucketed_topk(hx, k, b, kb, True, tag)
+        np.testing.assert_array_equal(i[rows].cpu().numpy(), oidx)
+        np.testing.assert_array_equal(out_bits(v[rows]), ref_bits(ov, tag))
+        if dtype == torch.float32:
+            r = oracle.recall(i.cpu().numpy(), ex.cpu().numpy()).mean()
+            assert abs(r - res["recall"]) < 0.02
 
 
 # -------------------------------------- wide fp32 rows (two-pass route) ----
@@ -477,3 +553,42 @@ def test_rerank_gqa128k_shape_sampled(gpu):
     g = torch.Generator(device="cpu").manual_seed(7)
     cand = torch.randint(0, c["ctx"], (c["bsz"], c["hq"], 4 * 512), generator=g, dtype=torch.int32).to(gpu)
     _rerank_check(q, K, V, cand, 512, 512, heads=[(0, 0), (1, 7), (3, 31)])
+
+
+# ------------------------------------------------------ HIP graph replay ----
+
+def test_graph_replay_matches_eager(gpu):
+    """Library calls captured in one HIP graph (exact, bucketed with and
+    without the final stage, fp32 and bf16, and a decode) replayed three
+    times; between replays the inputs are rewritten eagerly, and every replay
+    must equal an eager call on the same inputs."""
+    g = torch.Generator(device="cpu").manual_seed(5)
+    xf = torch.randn((3, 70001), generator=g).to(gpu)
+    xb = torch.randn((200, 4096), generator=g).to(torch.bfloat16).to(gpu)
+    q = torch.randn((2, 8, 128), generator=g).to(torch.bfloat16).to(gpu)
+    K = torch.randn((2, 2, 3000, 128), generator=g).to(torch.bfloat16).to(gpu)
+    V = torch.randn((2, 2, 3000, 128), generator=g).to(torch.bfloat16).to(gpu)
+
+    def step():
+        return [atk.exact(xf, 100), atk.bucketed(xf, 100, 512, 1, True), atk.exact(xb, 64),
+                atk.bucketed(xb, 64, 64, 1, False), atk.bucketed(xb, 64, 128, 2, True),
+                atk.sparse_attn_decode(q, K, V, 64, 16, 8, return_sel=True)]
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        captured = step()
+    for rep in range(3):
+        for t in (xf, xb, q, K, V):
+            t.copy_(torch.randn(t.shape, generator=g).to(t.dtype))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        eager = step()
+        for i, (a, b) in enumerate(zip(captured, eager)):
+            for ta, tb in zip(a, b):
+                assert torch.equal(ta, tb), (rep, i)

@@ -13,6 +13,9 @@ library every call raises.
     sparse_attn_decode(q, K, V, k_sel, b, kb) -> out (, sel_idx, scores)
     sparse_attn_rerank(q, K, V, cand, window, k_sel) -> out (, sel_idx)
                                       Top-K over a given candidate set
+    expected_recall(n, k, b, kb)      finite-n Eq. (1) (host)
+    choose(x, k, min_recall)          fastest measured (b, kb) meeting the
+                                      recall target, and its result
 """
 
 import ctypes
@@ -187,3 +190,33 @@ def sparse_attn_rerank(q, K, V, cand, window, k_sel, scale=None, ctx=None, retur
                                         _stream_ptr(q.device))
     check(st, "atopk_sparse_attn_rerank")
     return (out, sel) if return_sel else out
+
+
+def expected_recall(n, k, b, kb):
+    """Expected stage-1 recall of (b, kb) on an iid row of n distinct values
+    (finite-n form of Eq. (1)); computed by the library on the host."""
+    r = ctypes.c_double(0.0)
+    check(lib().atopk_expected_recall(n, k, b, kb, ctypes.byref(r)), "atopk_expected_recall")
+    return r.value
+
+
+def choose(x, k, min_recall):
+    """Time every (b, kb) whose expected recall reaches min_recall (and the
+    exact top-k) on the rows of x and return the fastest:
+    dict(b, kb, recall, us, values, indices) -- values / indices [m, k] are
+    that configuration's sorted result.  Blocks until the timing finishes."""
+    _check_rows(x)
+    m, n = x.shape
+    ldx = x.stride(0) if m > 1 else n
+    size = ctypes.c_size_t(0)
+    check(lib().atopk_choose_workspace(_DTYPES[x.dtype], m, n, ldx, k, float(min_recall), ctypes.byref(size)),
+          "atopk_choose_workspace")
+    ws, nbytes = _workspace(size.value, x.device)
+    vals = torch.empty((m, k), dtype=x.dtype, device=x.device)
+    idx = torch.empty((m, k), dtype=torch.int32, device=x.device)
+    b, kb = ctypes.c_int64(0), ctypes.c_int64(0)
+    rec, us = ctypes.c_double(0.0), ctypes.c_float(0.0)
+    check(lib().atopk_choose(_ptr(x), _DTYPES[x.dtype], m, n, ldx, k, float(min_recall), _ptr(vals), _ptr(idx),
+                             _ptr(ws), nbytes, _stream_ptr(x.device), ctypes.byref(b), ctypes.byref(kb),
+                             ctypes.byref(rec), ctypes.byref(us)), "atopk_choose")
+    return dict(b=b.value, kb=kb.value, recall=rec.value, us=us.value, values=vals, indices=idx)

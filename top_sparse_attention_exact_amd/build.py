@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libatopk.so")
 SOURCES = ["api.cpp", "select_bucket.hip", "select_exact.hip", "select_row.hip", "select_wide.hip", "decode.hip",
-           "decode_fused.hip", "rerank.hip"]
+           "decode_fused.hip", "rerank.hip", "choose.cpp"]
 
 FLAGS = [
     "--offload-arch=gfx950",

@@ -154,6 +154,14 @@ int run_exact(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, int64
 
 bool exact_route(int64_t k, int64_t b, int64_t kb) { return b == 1 && kb == k; }
 
+// Elements (and the int32 indices) must sit at addresses that are multiples
+// of their size.
+bool elems_misaligned(const void* x, const void* out_vals, const int32_t* out_idx, int dtype) {
+  const uintptr_t es = dtype == ATOPK_F32 ? 4 : 2;
+  return ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(out_vals)) & (es - 1)) != 0 ||
+         (reinterpret_cast<uintptr_t>(out_idx) & 3) != 0;
+}
+
 int validate_bucketed(int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k, int64_t b, int64_t kb) {
   if (m < 0 || n < 1 || ldx < n || k < 1 || k > n) return ATOPK_ERR_SHAPE;
   if (b < 1 || b > n || kb < 1 || kb > n / b || b * kb < k) return ATOPK_ERR_PARAM;
@@ -319,6 +327,7 @@ int atopk_exact(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, int
     if (st) return st;
     if (m == 0) return (int)ATOPK_OK;
     if (!x || !out_vals || !out_idx) return (int)ATOPK_ERR_NULL;
+    if (elems_misaligned(x, out_vals, out_idx, dtype)) return (int)ATOPK_ERR_PARAM;
     st = check_ws(ws, ws_bytes, exact_ws_bytes(dtype, m, n, k));
     if (st) return st;
     st = check_device();
@@ -362,6 +371,7 @@ int atopk_bucketed_ex(const void* x, int dtype, int64_t m, int64_t n, int64_t ld
     if (st) return st;
     if (m == 0) return (int)ATOPK_OK;
     if (!x || !out_vals || !out_idx) return (int)ATOPK_ERR_NULL;
+    if (elems_misaligned(x, out_vals, out_idx, dtype)) return (int)ATOPK_ERR_PARAM;
     const bool contig = assignment == ATOPK_CONTIGUOUS && !exact_route(k, b, kb);
     st = check_ws(ws, ws_bytes, contig ? 0 : bucketed_ws_bytes(dtype, m, n, k, b, kb, final_exact));
     if (st) return st;
@@ -384,6 +394,7 @@ int atopk_bucketed(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, 
     if (st) return st;
     if (m == 0) return (int)ATOPK_OK;
     if (!x || !out_vals || !out_idx) return (int)ATOPK_ERR_NULL;
+    if (elems_misaligned(x, out_vals, out_idx, dtype)) return (int)ATOPK_ERR_PARAM;
     st = check_ws(ws, ws_bytes, bucketed_ws_bytes(dtype, m, n, k, b, kb, final_exact));
     if (st) return st;
     st = check_device();

@@ -84,9 +84,14 @@ __global__ __launch_bounds__(kStage1Threads) void bucket_stage1_kernel(const uin
   const int wave = t / kWave;
   const int row = blockIdx.y;
   const int split = blockIdx.x;
-  const int64_t c0 = (int64_t)split * chunk;
-  const int64_t c1 = min((int64_t)n, c0 + chunk);
   const uint8_t* xr = x + (int64_t)row * ld_bytes;
+  // The row's first `a` elements come before its first 16-byte boundary; the
+  // vector loads start there.  Position p of a sweep holds element a + base + p,
+  // so its bucket is (a + p) mod b for every sweep (b divides W).
+  const int a = min((int)((16u - (uint32_t)(reinterpret_cast<uintptr_t>(xr) & 15u)) & 15u) / ES, n);
+  const uint8_t* xv = xr + (int64_t)a * ES;
+  const int64_t c0 = (int64_t)split * chunk;
+  const int64_t c1 = min((int64_t)(n - a), c0 + chunk);
 
   uint64_t q[V][KB];
 #pragma unroll
@@ -94,24 +99,31 @@ __global__ __launch_bounds__(kStage1Threads) void bucket_stage1_kernel(const uin
 #pragma unroll
     for (int j = 0; j < KB; ++j) q[e][j] = 0;
 
+  if (split == 0 && a > 0) {  // head: a partial sweep at base -W, element-wise
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const int i = t * V + e - (W - a);
+      if (i >= 0) queue_insert<KB>(q[e], make_key(ord_f32(load_elem_bits<DT>(xr, i)), (uint32_t)i));
+    }
+  }
   int64_t base = c0;
   for (; base + U * W <= c1; base += U * W) {
     uint4 w[U];
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      w[u] = *reinterpret_cast<const uint4*>(xr + (base + (int64_t)u * W + (int64_t)t * V) * ES);
+      w[u] = *reinterpret_cast<const uint4*>(xv + (base + (int64_t)u * W + (int64_t)t * V) * ES);
 #pragma unroll
-    for (int u = 0; u < U; ++u) consume_vec<DT, KB>(q, w[u], (uint32_t)(base + (int64_t)u * W + t * V));
+    for (int u = 0; u < U; ++u) consume_vec<DT, KB>(q, w[u], (uint32_t)(a + base + (int64_t)u * W + t * V));
   }
   for (; base + W <= c1; base += W) {
-    uint4 w = *reinterpret_cast<const uint4*>(xr + (base + (int64_t)t * V) * ES);
-    consume_vec<DT, KB>(q, w, (uint32_t)(base + t * V));
+    uint4 w = *reinterpret_cast<const uint4*>(xv + (base + (int64_t)t * V) * ES);
+    consume_vec<DT, KB>(q, w, (uint32_t)(a + base + t * V));
   }
   if (base < c1) {  // ragged tail: element-wise, bounds-checked
 #pragma unroll
     for (int e = 0; e < V; ++e) {
-      const int64_t i = base + (int64_t)t * V + e;
-      if (i < c1) queue_insert<KB>(q[e], make_key(ord_f32(load_elem_bits<DT>(xr, i)), (uint32_t)i));
+      const int64_t v = base + (int64_t)t * V + e;
+      if (v < c1) queue_insert<KB>(q[e], make_key(ord_f32(load_elem_bits<DT>(xv, v)), (uint32_t)(a + v)));
     }
   }
 
@@ -146,7 +158,7 @@ __global__ __launch_bounds__(kStage1Threads) void bucket_stage1_kernel(const uin
       const int p = wave * kWave * V + lane * V + e;
       const bool rep = wave_has_all ? (lane * V + e < b) : true;
       const int c = wave_has_all ? wave : p / b;
-      const int r = p % b;
+      const int r = (p + a) % b;
       if (rep) {
 #pragma unroll
         for (int j = 0; j < KB; ++j) lds[((int64_t)c * b + r) * KB + j] = q[e][j];
@@ -173,7 +185,7 @@ __global__ __launch_bounds__(kStage1Threads) void bucket_stage1_kernel(const uin
       const int p = wave * kWave * V + lane * V + e;
       const bool rep = wave_has_all ? (lane * V + e < b) : true;
       const int c = wave_has_all ? wave : p / b;
-      const int r = p % b;
+      const int r = (p + a) % b;
       if (rep) {
         uint64_t* dst = lists + (((int64_t)row * lists_per_row + (int64_t)split * ncopies + c) * b + r) * KB;
 #pragma unroll
@@ -183,7 +195,10 @@ __global__ __launch_bounds__(kStage1Threads) void bucket_stage1_kernel(const uin
   }
 }
 
-// Any b: one thread walks one bucket r, r + b, r + 2b, ... of one row.
+// Any b: one thread walks one bucket r, r + b, r + 2b, ... of one row
+// (neighbouring threads read neighbouring elements), kGenU loads in flight.
+constexpr int kGenU = 8;
+
 template <int DT, int KB>
 __global__ __launch_bounds__(256) void bucket_generic_kernel(const uint8_t* __restrict__ x, int64_t ld_bytes, int n,
                                                             int b, uint64_t* __restrict__ lists) {
@@ -194,7 +209,16 @@ __global__ __launch_bounds__(256) void bucket_generic_kernel(const uint8_t* __re
   uint64_t q[KB];
 #pragma unroll
   for (int j = 0; j < KB; ++j) q[j] = 0;
-  for (int64_t i = r; i < n; i += b) queue_insert<KB>(q, make_key(ord_f32(load_elem_bits<DT>(xr, i)), (uint32_t)i));
+  const int64_t step = (int64_t)kGenU * b;
+  int64_t i0 = r;
+  for (; i0 + (kGenU - 1) * (int64_t)b < n; i0 += step) {
+    uint32_t v[kGenU];
+#pragma unroll
+    for (int u = 0; u < kGenU; ++u) v[u] = load_elem_bits<DT>(xr, i0 + (int64_t)u * b);
+#pragma unroll
+    for (int u = 0; u < kGenU; ++u) queue_insert<KB>(q, make_key(ord_f32(v[u]), (uint32_t)(i0 + (int64_t)u * b)));
+  }
+  for (int64_t i = i0; i < n; i += b) queue_insert<KB>(q, make_key(ord_f32(load_elem_bits<DT>(xr, i)), (uint32_t)i));
   uint64_t* dst = lists + ((int64_t)row * b + r) * KB;
 #pragma unroll
   for (int j = 0; j < KB; ++j) dst[j] = q[j];
@@ -211,7 +235,7 @@ __device__ __forceinline__ void write_result(uint8_t* out_vals, int32_t* out_idx
   }
 }
 
-constexpr int kFinishThreads = 256;
+constexpr int kFinishThreads = 1024;
 
 // mode 0: write the stage-1 candidates bucket-major; mode 1: final exact
 // top-k in LDS; mode 2: write merged candidate keys to cand_out.
@@ -230,12 +254,24 @@ __global__ __launch_bounds__(kFinishThreads) void bucket_finish_kernel(const uin
   const uint8_t* xr = x + (int64_t)row * ld_bytes;
   const int64_t nc = (int64_t)b * kb;
 
+  // Queues of one bucket from the nl lists: LB loads in flight per thread.
+  constexpr int LB = KB >= 8 ? 1 : 8 / KB;
   for (int r = t; r < b; r += T) {
     uint64_t a[KB];
     const uint64_t* src = lists + ((int64_t)row * nl * b + r) * KB;
 #pragma unroll
     for (int j = 0; j < KB; ++j) a[j] = src[j];
-    for (int l = 1; l < nl; ++l) {
+    int l = 1;
+    for (; l + LB <= nl; l += LB) {
+      uint64_t o[LB][KB];
+#pragma unroll
+      for (int u = 0; u < LB; ++u)
+#pragma unroll
+        for (int j = 0; j < KB; ++j) o[u][j] = src[(int64_t)(l + u) * b * KB + j];
+#pragma unroll
+      for (int u = 0; u < LB; ++u) queue_merge<KB>(a, o[u]);
+    }
+    for (; l < nl; ++l) {
       uint64_t o[KB];
       const uint64_t* s2 = src + (int64_t)l * b * KB;
 #pragma unroll
@@ -316,7 +352,8 @@ BucketPlan plan_bucketed(int dtype, int64_t m, int64_t n, int64_t b, int64_t kb,
   const int V = dtype == IN_F32 ? 4 : 8;
   const int W = kStage1Threads * V;
   p.threads = kStage1Threads;
-  p.fast = aligned && is_pow2(b) && b <= W && (int64_t)V * kb_slots(kb) <= 64;
+  (void)aligned;  // misaligned rows take a scalar head sweep
+  p.fast = is_pow2(b) && b <= W && (int64_t)V * kb_slots(kb) <= 64;
   if (!p.fast) {
     p.splits = 1;
     p.chunk = n;

@@ -17,6 +17,12 @@ Workloads (the shapes of the pages' top-k and decode settings, synthetic):
              in the fewest residue classes modulo b (worst case for buckets)
   ar1        fp32 AR(1) Gaussian rows of a chosen correlation (interleaved
              against contiguous bucket assignment)
+  vocab-sampling  64 x 128256 fp32 ~ N(0, 2^2), k = 256 (LLM vocabulary
+             sampling shape of the runtime/accuracy trade-off)
+  kg-2.65m   128 x 2653751 fp32 ~ N(0, 1), k = 100 (knowledge-graph link
+             prediction shape of the same trade-off)
+  sweep      fp32 N(0, 1) rows of the runtime-versus-(n, k) sweep at m = 1
+             and m = 256
 """
 
 import math
@@ -24,7 +30,8 @@ import math
 import numpy as np
 import torch
 
-_WORKLOAD_IDS = {"sel-4k": 1, "vocab-128k": 2, "mha-32k": 3, "gqa-128k": 4, "wide-1m": 5, "ar1": 6, "misc": 9}
+_WORKLOAD_IDS = {"sel-4k": 1, "vocab-128k": 2, "mha-32k": 3, "gqa-128k": 4, "wide-1m": 5, "ar1": 6, "misc": 9,
+                 "vocab-sampling": 10, "kg-2.65m": 11, "sweep": 12}
 
 
 def generator(workload, seed, device="cpu"):
@@ -44,6 +51,13 @@ def rows_normal_bf16(m, n, std, seed, device="cpu", workload="vocab-128k"):
     g = generator(workload, seed, device)
     x = torch.randn((m, n), generator=g, device=device, dtype=torch.float32)
     return (x * std).to(torch.bfloat16)
+
+
+def rows_normal(m, n, std, seed, device="cpu", workload="kg-2.65m"):
+    """[m, n] fp32 draws of std * N(0, 1)."""
+    g = generator(workload, seed, device)
+    x = torch.randn((m, n), generator=g, device=device, dtype=torch.float32)
+    return x.mul_(std) if std != 1.0 else x
 
 
 def rows_planted_residues(m, n, b, k, seed, device="cpu", workload="wide-1m"):
@@ -147,6 +161,28 @@ SELECTION = {
     "vocab-128k": dict(m=256, n=131072, k=64, dtype="bf16", modes=[(64, 1, False), (128, 2, True)]),
     "wide-1m": dict(m=64, n=1 << 20, k=8192, dtype="f32", modes=[(512, 16, True)]),
 }
+# Runtime/accuracy trade-off shapes: every (b, k_b) with k_b in {1, 2} and
+# b * k_b from the smallest power of two >= k up to 8192, final exact top-k.
+TRADEOFF = {
+    "vocab-sampling": dict(m=64, n=128256, k=256, std=2.0),
+    "kg-2.65m": dict(m=128, n=2653751, k=100, std=1.0),
+}
+
+
+def tradeoff_modes(k, max_cand=8192):
+    modes = []
+    for kb in (1, 2):
+        b = 1
+        while b * kb < k:
+            b *= 2
+        while b * kb <= max_cand:
+            modes.append((b, kb))
+            b *= 2
+    return modes
+
+
+# Runtime versus n and k (fp32 N(0, 1) rows).
+SWEEP = dict(ms=(1, 256), log2n=(10, 12, 14, 16, 18, 20, 22), ks=(1, 16, 64, 256, 1024, 4096), max_bytes=1 << 30)
 DECODE = {
     "mha-32k": dict(bsz=16, hq=32, hkv=32, ctx=32768, d=128, k_sel=512, b=256, kb=2),
     "gqa-128k": dict(bsz=4, hq=32, hkv=8, ctx=131072, d=128, k_sel=512, b=512, kb=4),
