@@ -152,6 +152,19 @@ def test_bucketed_row_offsets(gpu, dtype, off):
     check_bucketed(tiny, 2, 2, 1, True)
 
 
+@pytest.mark.parametrize("m,n", [(1, 1 << 20), (3, 777777)])
+def test_bucketed_few_rows_many_splits(gpu, m, n):
+    """Few long rows: stage 1 splits every row over many workgroups (the
+    finish merges up to 1024 lists per bucket through its LDS tree), and
+    the per-bucket walk (b above the vectorised limit, or not a power of
+    two) splits rows too."""
+    x = rand_rows(m, n, torch.float32, 30 + m, gpu)
+    for b, kb, fin, k in [(32, 2, True, 64), (32, 2, False, 64), (4, 4, True, 16), (256, 1, True, 200),
+                          (2048, 1, True, 1000), (3000, 2, True, 64), (4096, 2, False, 64), (1000, 3, True, 300)]:
+        print("case", m, n, b, kb, fin, k, flush=True)
+        check_bucketed(x, k, b, kb, fin)
+
+
 def test_single_row_and_empty(gpu):
     x = rand_rows(1, 4096, torch.float32, 9, gpu)
     check_exact(x, 64)

@@ -12,6 +12,8 @@
 // that share a bucket are merged with cross-lane shuffles, then across the
 // waves of the workgroup in LDS, then across workgroups of a row by the
 // finish kernel.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -198,28 +200,34 @@ __global__ __launch_bounds__(kStage1Threads) void bucket_stage1_kernel(const uin
 // Any b: one thread walks one bucket r, r + b, r + 2b, ... of one row
 // (neighbouring threads read neighbouring elements), kGenU loads in flight.
 constexpr int kGenU = 8;
+constexpr int64_t kGenTargetThreads = 256 * 1024;
 
+// Split s of a row covers elements [s * chunk, (s + 1) * chunk), chunk a
+// multiple of b, and writes list s of the row.
 template <int DT, int KB>
 __global__ __launch_bounds__(256) void bucket_generic_kernel(const uint8_t* __restrict__ x, int64_t ld_bytes, int n,
-                                                            int b, uint64_t* __restrict__ lists) {
+                                                            int b, int64_t chunk, int lists_per_row,
+                                                            uint64_t* __restrict__ lists) {
   const int r = blockIdx.x * 256 + threadIdx.x;
   const int row = blockIdx.y;
+  const int split = blockIdx.z;
   if (r >= b) return;
   const uint8_t* xr = x + (int64_t)row * ld_bytes;
+  const int64_t end = min((int64_t)n, (int64_t)(split + 1) * chunk);
   uint64_t q[KB];
 #pragma unroll
   for (int j = 0; j < KB; ++j) q[j] = 0;
   const int64_t step = (int64_t)kGenU * b;
-  int64_t i0 = r;
-  for (; i0 + (kGenU - 1) * (int64_t)b < n; i0 += step) {
+  int64_t i0 = (int64_t)split * chunk + r;
+  for (; i0 + (kGenU - 1) * (int64_t)b < end; i0 += step) {
     uint32_t v[kGenU];
 #pragma unroll
     for (int u = 0; u < kGenU; ++u) v[u] = load_elem_bits<DT>(xr, i0 + (int64_t)u * b);
 #pragma unroll
     for (int u = 0; u < kGenU; ++u) queue_insert<KB>(q, make_key(ord_f32(v[u]), (uint32_t)(i0 + (int64_t)u * b)));
   }
-  for (int64_t i = i0; i < n; i += b) queue_insert<KB>(q, make_key(ord_f32(load_elem_bits<DT>(xr, i)), (uint32_t)i));
-  uint64_t* dst = lists + ((int64_t)row * b + r) * KB;
+  for (int64_t i = i0; i < end; i += b) queue_insert<KB>(q, make_key(ord_f32(load_elem_bits<DT>(xr, i)), (uint32_t)i));
+  uint64_t* dst = lists + (((int64_t)row * lists_per_row + split) * b + r) * KB;
 #pragma unroll
   for (int j = 0; j < KB; ++j) dst[j] = q[j];
 }
@@ -254,30 +262,60 @@ __global__ __launch_bounds__(kFinishThreads) void bucket_finish_kernel(const uin
   const uint8_t* xr = x + (int64_t)row * ld_bytes;
   const int64_t nc = (int64_t)b * kb;
 
-  // Queues of one bucket from the nl lists: LB loads in flight per thread.
+  // Queue of bucket r merged over lists l0, l0 + P, l0 + 2P, ... < nl, LB
+  // loads in flight.
   constexpr int LB = KB >= 8 ? 1 : 8 / KB;
-  for (int r = t; r < b; r += T) {
-    uint64_t a[KB];
+  auto merge_lists = [&](uint64_t (&a)[KB], int r, int l0, int P) {
     const uint64_t* src = lists + ((int64_t)row * nl * b + r) * KB;
 #pragma unroll
-    for (int j = 0; j < KB; ++j) a[j] = src[j];
-    int l = 1;
-    for (; l + LB <= nl; l += LB) {
+    for (int j = 0; j < KB; ++j) a[j] = 0;
+    int l = l0;
+    for (; l + (LB - 1) * P < nl; l += LB * P) {
       uint64_t o[LB][KB];
 #pragma unroll
       for (int u = 0; u < LB; ++u)
 #pragma unroll
-        for (int j = 0; j < KB; ++j) o[u][j] = src[(int64_t)(l + u) * b * KB + j];
+        for (int j = 0; j < KB; ++j) o[u][j] = src[(int64_t)(l + u * P) * b * KB + j];
 #pragma unroll
       for (int u = 0; u < LB; ++u) queue_merge<KB>(a, o[u]);
     }
-    for (; l < nl; ++l) {
+    for (; l < nl; l += P) {
       uint64_t o[KB];
-      const uint64_t* s2 = src + (int64_t)l * b * KB;
 #pragma unroll
-      for (int j = 0; j < KB; ++j) o[j] = s2[j];
+      for (int j = 0; j < KB; ++j) o[j] = src[(int64_t)l * b * KB + j];
       queue_merge<KB>(a, o);
     }
+  };
+  // Few buckets, many lists: P = 2^h threads share a bucket, each merges
+  // every P-th list, and an LDS tree joins their queues (P * b * KB keys
+  // fit in `cand`).
+  int P = 1;
+  if (KB <= 4 && nl > 1)
+    while (2 * P * b <= T && 2 * P <= nl) P *= 2;
+  for (int r0 = 0; r0 < b; r0 += T) {
+    const int r = P > 1 ? t % b : r0 + t;
+    const int p = P > 1 ? t / b : 0;
+    uint64_t a[KB];
+    if (r < b && p < P) merge_lists(a, r, p, P);
+    if (P > 1) {
+      if (p < P) {
+#pragma unroll
+        for (int j = 0; j < KB; ++j) cand[((int64_t)p * b + r) * KB + j] = a[j];
+      }
+      for (int half = P / 2; half >= 1; half /= 2) {
+        __syncthreads();
+        if (p < half) {
+          uint64_t o[KB];
+#pragma unroll
+          for (int j = 0; j < KB; ++j) o[j] = cand[((int64_t)(p + half) * b + r) * KB + j];
+          queue_merge<KB>(a, o);
+#pragma unroll
+          for (int j = 0; j < KB; ++j) cand[((int64_t)p * b + r) * KB + j] = a[j];
+        }
+      }
+      __syncthreads();  // every partial is read before `cand` takes the candidates
+    }
+    if (r >= b || p != 0) continue;
     if (mode == 0) {
 #pragma unroll
       for (int j = 0; j < KB; ++j)
@@ -331,10 +369,11 @@ hipError_t launch_stage1_dt(const BucketPlan& p, const void* x, int64_t m, int64
     }
 #undef ATOPK_S1
   } else {
-    dim3 grid((unsigned)((b + 255) / 256), (unsigned)m);
-#define ATOPK_G(KBV)                                                                                                   \
-  case KBV:                                                                                                            \
-    hipLaunchKernelGGL((bucket_generic_kernel<DT, KBV>), grid, dim3(256), 0, s, xb, ld_bytes, (int)n, (int)b, lists); \
+    dim3 grid((unsigned)((b + 255) / 256), (unsigned)m, (unsigned)p.splits);
+#define ATOPK_G(KBV)                                                                                       \
+  case KBV:                                                                                                \
+    hipLaunchKernelGGL((bucket_generic_kernel<DT, KBV>), grid, dim3(256), 0, s, xb, ld_bytes, (int)n, (int)b, \
+                       p.chunk, p.lists_per_row, lists);                                                  \
     break;
     switch (kb_slots(kb)) {
       ATOPK_G(1) ATOPK_G(2) ATOPK_G(4) ATOPK_G(8) ATOPK_G(16)
@@ -355,9 +394,17 @@ BucketPlan plan_bucketed(int dtype, int64_t m, int64_t n, int64_t b, int64_t kb,
   (void)aligned;  // misaligned rows take a scalar head sweep
   p.fast = is_pow2(b) && b <= W && (int64_t)V * kb_slots(kb) <= 64;
   if (!p.fast) {
-    p.splits = 1;
-    p.chunk = n;
-    p.lists_per_row = 1;
+    // One thread per (bucket, split): enough splits to give the chip about
+    // kGenTargetThreads threads, while every thread still walks >= 64
+    // elements and the finish merges at most 16 lists per bucket.
+    const int64_t row_threads = (b + 255) / 256 * 256;
+    int64_t splits = (kGenTargetThreads + row_threads * m - 1) / (row_threads * std::max<int64_t>(m, 1));
+    splits = std::min<int64_t>(splits, std::max<int64_t>(1, n / (b * 64)));
+    splits = std::max<int64_t>(1, std::min<int64_t>(splits, 16));
+    const int64_t per = (n + splits - 1) / splits;
+    p.chunk = (per + b - 1) / b * b;
+    p.splits = (int)((n + p.chunk - 1) / p.chunk);
+    p.lists_per_row = p.splits;
     return p;
   }
   // Long chunks amortise the per-workgroup merge; enough of them fill the chip.
