@@ -294,6 +294,49 @@ def test_choose(gpu, name, dtype):
             assert abs(r - res["recall"]) < 0.02
 
 
+# ------------------------------- certified exact (bucketed pass + rescan) ----
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("m,n,k", [(1, 1 << 20, 100), (2, 300007, 256), (64, 128256, 256), (3, 70001, 16),
+                                   (1, 4_000_003, 64), (5, 5000, 300)])
+def test_certified_exact_shapes(gpu, dtype, m, n, k):
+    """Shapes whose exact top-k runs as a bucketed pass plus the finish's
+    certification (k above the one-row kernel's limit, or few long rows)."""
+    x = rand_rows(m, n, dtype, m + n + k, gpu)
+    rows = sorted({0, m - 1})
+    vals, idx = atk.exact(x, k)
+    hx, tag = host(x[rows])
+    ridx, rvals = oracle.exact_topk(hx, k, tag)
+    np.testing.assert_array_equal(idx[rows].cpu().numpy(), ridx)
+    np.testing.assert_array_equal(out_bits(vals[rows]), ref_bits(rvals, tag))
+
+
+def test_certified_exact_rescan_and_fallback(gpu):
+    """Rows that defeat the bucket candidates: row 0 holds 20 large values at
+    multiples of 4096 (one bucket for every power-of-two b <= 4096, so the
+    rescan must bring back all but k_b of them); row 1 lifts every 16th
+    element (with k = 16 the certified plan uses 16 buckets, so one bucket
+    holds 8192 values above the threshold and the pool overflows into the
+    full-row fallback); row 2 has two levels (heavy ties); row 3 is plain."""
+    m, n, k = 4, 131072 + 5, 16
+    g = torch.Generator(device="cpu").manual_seed(77)
+    x = torch.rand((m, n), generator=g)
+    x[0, 0:20 * 4096:4096] = 10.0 + torch.rand(20, generator=g)
+    x[1, 0::16] = 10.0 + torch.rand(x[1, 0::16].shape[0], generator=g)
+    x[2] = torch.floor(torch.rand(n, generator=g) * 2) / 2
+    for kk in (16, 100, 256):
+        xx = x.to(gpu)
+        vals, idx = atk.exact(xx, kk)
+        ridx, rvals = oracle.exact_topk(x.numpy(), kk, "f32")
+        np.testing.assert_array_equal(idx.cpu().numpy(), ridx)
+        np.testing.assert_array_equal(vals.cpu().numpy().view(np.uint32), rvals.view(np.uint32))
+        xb = x.to(torch.bfloat16)
+        vals, idx = atk.exact(xb.to(gpu), kk)
+        ridx, rvals = oracle.exact_topk(bits16(xb), kk, "bf16")
+        np.testing.assert_array_equal(idx.cpu().numpy(), ridx)
+        np.testing.assert_array_equal(bits16(vals), rvals)
+
+
 # -------------------------------------- wide fp32 rows (two-pass route) ----
 
 def quantized_rows(m, n, levels, seed, gpu):

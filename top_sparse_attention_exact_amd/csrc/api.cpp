@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <atomic>
 #include <cstring>
 #include <new>
@@ -119,7 +120,19 @@ int run_wide(const WideLayout& L, const void* x, int64_t m, int64_t n, int64_t l
                                 out_idx, s));
 }
 
+// Certified exact route (defined with the bucketed path below).
+struct CertPlan {
+  bool ok = false;
+  int64_t b = 0, kb = 0;
+};
+CertPlan plan_certified(int dtype, int64_t m, int64_t n, int64_t k);
+size_t certified_ws_bytes(int dtype, int64_t m, int64_t n, const CertPlan& c);
+int run_certified(const CertPlan& c, const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k,
+                  void* out_vals, int32_t* out_idx, void* ws, hipStream_t s);
+
 size_t exact_ws_bytes(int dtype, int64_t m, int64_t n, int64_t k) {
+  const CertPlan cert = plan_certified(dtype, m, n, k);
+  if (cert.ok) return certified_ws_bytes(dtype, m, n, cert);
   if (wide_exact(dtype, m, n, k)) return wide_layout(dtype, m, n, k, 0, 0, true, true).total;
   const ExactPlan p = plan_exact(dtype, m, n, k);
   if (p.splits <= 1) return 0;
@@ -137,6 +150,8 @@ int run_exact(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, int64
   const int64_t es = dtype == ATOPK_F32 ? 4 : 2;
   if (row_exact_ok(dtype, m, n, k, rows_aligned(x, ldx, es)))
     return hip_status(launch_row_exact(x, dtype, m, n, ldx, k, out_vals, out_idx, s));
+  const CertPlan cert = plan_certified(dtype, m, n, k);
+  if (cert.ok) return run_certified(cert, x, dtype, m, n, ldx, k, out_vals, out_idx, ws, s);
   if (wide_exact(dtype, m, n, k))
     return run_wide(wide_layout(dtype, m, n, k, 0, 0, true, true), x, m, n, ldx, k, true, true, out_vals, out_idx, ws,
                     s);
@@ -217,7 +232,7 @@ int run_bucketed(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, in
   uint64_t* lists = reinterpret_cast<uint64_t*>(w + L.lists_off);
   uint64_t* cand = L.cand_bytes ? reinterpret_cast<uint64_t*>(w + L.cand_off) : nullptr;
   if (launch_bucket_stage1(L.plan, x, dtype, m, n, ldx, b, kb, lists, s) != hipSuccess) return ATOPK_ERR_HIP;
-  if (launch_bucket_finish(lists, L.plan.lists_per_row, m, b, kb, k, final_exact, x, dtype, ldx, out_vals, out_idx,
+  if (launch_bucket_finish(lists, L.plan.lists_per_row, m, n, b, kb, k, final_exact, x, dtype, ldx, out_vals, out_idx,
                            cand, s) != hipSuccess)
     return ATOPK_ERR_HIP;
   if (cand) {
@@ -226,6 +241,57 @@ int run_bucketed(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, in
     return hip_status(launch_exact(p2, cand, IN_KEY64, m, nc, nc, k, nullptr, x, dtype, ldx, out_vals, out_idx, s));
   }
   return ATOPK_OK;
+}
+
+// ---- certified exact: bucketed stage 1, then the finish's rescan ------------------
+
+// Expected number of buckets that receive at least kb of the k largest
+// values of an iid row (each lands in one of b buckets with probability 1/b).
+double saturated_buckets(int64_t k, int64_t b, int64_t kb) {
+  const double p = 1.0 / (double)b;
+  double term = std::pow(1.0 - p, (double)k);  // P(X = 0), X ~ Bin(k, p)
+  double cdf = 0.0;
+  for (int64_t j = 0; j < kb && j <= k; ++j) {
+    cdf += term;
+    term *= (double)(k - j) / (double)(j + 1) * p / (1.0 - p);
+  }
+  return (double)b * std::max(0.0, 1.0 - cdf);
+}
+
+// k_b = 4 and the smallest power-of-two b whose expected number of buckets
+// to rescan stays below 1/4 per row and whose expected rescan (that number
+// times a bucket's length) stays below 2048 elements; failing the second,
+// the largest b that meets the first.  b * k_b <= 8192 keeps the candidates
+// in LDS.  Rows far from iid only rescan more buckets, or take the finish's
+// full-row fallback: the result is exact either way.
+CertPlan plan_certified(int dtype, int64_t m, int64_t n, int64_t k) {
+  CertPlan c;
+  if (m < 1 || (dtype != ATOPK_F32 && dtype != ATOPK_BF16)) return c;
+  const int64_t kb = 4;
+  for (int64_t b = std::max<int64_t>(2, pow2_ceil((k + kb - 1) / kb)); b * kb <= kFinishMaxCand; b *= 2) {
+    if (b > n || kb > n / b) break;
+    const double e = saturated_buckets(k, b, kb);
+    if (e <= 0.25) {
+      c.ok = true;
+      c.b = b;
+      c.kb = kb;
+      if (e * (double)((n + b - 1) / b) <= 2048.0) break;
+    }
+  }
+  return c;
+}
+
+size_t certified_ws_bytes(int dtype, int64_t m, int64_t n, const CertPlan& c) {
+  return bucket_layout(dtype, m, n, c.b, c.kb, 1, true).total;
+}
+
+int run_certified(const CertPlan& c, const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k,
+                  void* out_vals, int32_t* out_idx, void* ws, hipStream_t s) {
+  const BucketLayout L = bucket_layout(dtype, m, n, c.b, c.kb, 1, true);
+  uint64_t* lists = reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(ws) + L.lists_off);
+  if (launch_bucket_stage1(L.plan, x, dtype, m, n, ldx, c.b, c.kb, lists, s) != hipSuccess) return ATOPK_ERR_HIP;
+  return hip_status(launch_bucket_finish(lists, L.plan.lists_per_row, m, n, c.b, c.kb, k, kFinishCertified, x, dtype,
+                                         ldx, out_vals, out_idx, nullptr, s));
 }
 
 // ---- decode --------------------------------------------------------------------------

@@ -387,6 +387,115 @@ __device__ int block_compact_ge(uint64_t* keys, int n, uint64_t thr, uint32_t* c
   return cnt;
 }
 
+// Radix select over 32-bit order keys, 8-bit digits from the top: the
+// largest v with #{keys >= v} >= k (the k-th largest key, with
+// multiplicity).  `count(mask, prefix, shift)` histograms, into hist[256],
+// the digit at `shift` of every key whose bits under `mask` equal `prefix`.
+// Returns v; *rem_out = how many copies of v the top k take.
+template <int T, typename Count>
+__device__ uint32_t block_radix_kth32(int k, uint32_t* hist, uint32_t* ctl, Count&& count, int* rem_out) {
+  const int t = threadIdx.x;
+  uint32_t prefix = 0, mask = 0;
+  int rem = k;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = t; i < 256; i += T) hist[i] = 0;
+    __syncthreads();
+    count(mask, prefix, shift);
+    __syncthreads();
+    if (t < kWave) {
+      // lane l owns digits 255-4l .. 252-4l (high to low)
+      uint32_t h[4];
+      int s = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        h[q] = hist[255 - 4 * t - q];
+        s += (int)h[q];
+      }
+      const int incl = wave_incl_scan(s);
+      const int excl = incl - s;
+      if (excl < rem && rem <= incl) {
+        int acc = excl;
+        int d = -1;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (d < 0) {
+            if (acc + (int)h[q] >= rem)
+              d = 255 - 4 * t - q;
+            else
+              acc += (int)h[q];
+          }
+        }
+        ctl[0] = (uint32_t)d;
+        ctl[1] = (uint32_t)(rem - acc);
+      }
+    }
+    __syncthreads();
+    prefix |= ctl[0] << shift;
+    mask |= 255u << shift;
+    rem = (int)ctl[1];
+    __syncthreads();
+  }
+  *rem_out = rem;
+  return prefix;
+}
+
+// Exact top-k of a whole row by radix select over its order keys:
+// ord_at(i) is the order key of element i (0 <= i < n).  The k-th largest
+// order key v, then every element above v (fewer than k) and the
+// lowest-index elements equal to v, in index order.  Leaves the k keys in
+// cand[0..k) (unsorted); hist holds 256 words, ctl 3.
+template <int T, typename Ord>
+__device__ void block_row_topk(Ord&& ord_at, int n, int k, uint64_t* cand, uint32_t* hist, uint32_t* ctl) {
+  const int t = threadIdx.x;
+  int rem;
+  const uint32_t v = block_radix_kth32<T>(
+      k, hist, ctl,
+      [&](uint32_t mask, uint32_t prefix, int shift) {
+        for (int i0 = 0; i0 < n; i0 += T) {
+          const int i = i0 + t;
+          const uint32_t o = i < n ? ord_at(i) : 0u;
+          hist_add(hist, (o >> shift) & 255u, i < n && (o & mask) == prefix);
+        }
+      },
+      &rem);
+  const int above = k - rem;  // elements with order key > v
+  if (t == 0) ctl[2] = 0;
+  __syncthreads();
+  for (int i0 = 0; i0 < n; i0 += T) {
+    const int i = i0 + t;
+    const uint32_t o = i < n ? ord_at(i) : 0u;
+    const bool keep = i < n && o > v;
+    const uint64_t m = __ballot(keep);
+    if (m) {
+      uint32_t pos = 0;
+      if (lane_id() == 0) pos = atomicAdd(&ctl[2], (uint32_t)__popcll(m));
+      pos = __shfl(pos, 0, kWave);
+      if (keep) cand[pos + lanes_below(m)] = make_key(o, (uint32_t)i);
+    }
+  }
+  // ties in index order, one tile of T consecutive elements at a time
+  const int wave = t / kWave;
+  int taken = 0;
+  for (int base = 0; base < n && taken < rem; base += T) {
+    const int i = base + t;
+    const bool eq = i < n && ord_at(i) == v;
+    const uint64_t m = __ballot(eq);
+    if (lane_id() == 0) hist[wave] = (uint32_t)__popcll(m);
+    __syncthreads();
+    int before = 0, total = 0;
+    for (int w = 0; w < T / kWave; ++w) {
+      const int c = (int)hist[w];
+      before += w < wave ? c : 0;
+      total += c;
+    }
+    const int pos = taken + before + (int)lanes_below(m);
+    if (eq && pos < rem) cand[above + pos] = make_key(v, (uint32_t)i);
+    taken += total;
+    __syncthreads();
+  }
+  __syncthreads();
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
   u += 0x7fffu + ((u >> 16) & 1u);

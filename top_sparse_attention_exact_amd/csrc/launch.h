@@ -31,10 +31,13 @@ hipError_t launch_bucket_stage1(const BucketPlan& p, const void* x, int dtype, i
 // Merge the lists of every bucket; then either write the bucket-major
 // candidates (final_exact == 0), or select and sort the final top-k
 // (b * kb <= kFinishMaxCand), or write merged candidates to `cand_out`
-// ([m][b*kb] keys) for the exact path to finish.
+// ([m][b*kb] keys) for the exact path to finish.  final_exact ==
+// kFinishCertified: the exact top-k of the whole row, from the candidates
+// plus a rescan of the buckets that may hide more of it (b*kb <= 8192).
 constexpr int kFinishMaxCand = 8192;
-hipError_t launch_bucket_finish(const uint64_t* lists, int lists_per_row, int64_t m, int64_t b, int64_t kb,
-                                int64_t k, int final_exact, const void* x, int dtype, int64_t ldx,
+constexpr int kFinishCertified = 3;
+hipError_t launch_bucket_finish(const uint64_t* lists, int lists_per_row, int64_t m, int64_t n, int64_t b,
+                                int64_t kb, int64_t k, int final_exact, const void* x, int dtype, int64_t ldx,
                                 void* out_vals, int32_t* out_idx, uint64_t* cand_out, hipStream_t s);
 
 // ---- exact top-k ------------------------------------------------------------

@@ -24,6 +24,7 @@ namespace {
 constexpr int kStage1Threads = 256;
 constexpr int kStage1LdsBytes = 32768;
 constexpr int kTargetBlocks = 1024;
+constexpr int64_t kListBudget = 1 << 17;  // stage-1 list keys per row
 
 // The kernels keep KB = next power of two >= k_b entries per queue; the
 // top-k_b of a bucket is the first k_b of its sorted top-KB, so the finish
@@ -247,16 +248,39 @@ constexpr int kFinishThreads = 1024;
 
 // mode 0: write the stage-1 candidates bucket-major; mode 1: final exact
 // top-k in LDS; mode 2: write merged candidate keys to cand_out.
+// Order key of element i of a row of dtype dt.
+__device__ __forceinline__ uint32_t row_ord(const uint8_t* xr, int dt, int64_t i) {
+  return ord_f32(dt == IN_F32 ? reinterpret_cast<const uint32_t*>(xr)[i]
+                              : (uint32_t)reinterpret_cast<const uint16_t*>(xr)[i] << 16);
+}
+
+__device__ __noinline__ void finish_row_fallback(const uint8_t* xr, int dt, int n, int k, uint64_t* cand,
+                                                 uint32_t* hist, uint32_t* ctl) {
+  block_row_topk<kFinishThreads>([&](int i) { return row_ord(xr, dt, i); }, n, k, cand, hist, ctl);
+}
+
+constexpr int kFlagMax = 256;  // flagged buckets rescanned in LDS; more take the full-row fallback
+
+// mode 3 (certified exact top-k from the bucket candidates).  With T the
+// k-th largest candidate key: a true top-k element e missing from the
+// candidates was dropped by its bucket, so that bucket kept k_b keys above
+// e, all of them true top-k and hence all in the top-k of the candidates;
+// its k_b-th kept key is then >= T.  Rescanning exactly those buckets for
+// the keys between T and their k_b-th kept key (all missing elements lie
+// there: e beats some candidate of the top-k, so key(e) > T) and taking the
+// top-k of the enlarged pool gives the exact top-k.
 template <int KB>
 __global__ __launch_bounds__(kFinishThreads) void bucket_finish_kernel(const uint64_t* __restrict__ lists, int nl,
                                                                       int b, int k, int mode,
                                                                       int kb, const uint8_t* __restrict__ x, int dt,
-                                                                      int64_t ld_bytes, uint8_t* out_vals,
+                                                                      int64_t ld_bytes, int n, uint8_t* out_vals,
                                                                       int32_t* out_idx, uint64_t* cand_out) {
   constexpr int T = kFinishThreads;
   __shared__ uint64_t cand[kFinishMaxCand];
   __shared__ uint32_t hist[256];
   __shared__ uint32_t ctl[8];
+  __shared__ uint32_t flg_r[kFlagMax];
+  __shared__ uint64_t flg_c[kFlagMax];
   const int t = threadIdx.x;
   const int row = blockIdx.x;
   const uint8_t* xr = x + (int64_t)row * ld_bytes;
@@ -320,7 +344,7 @@ __global__ __launch_bounds__(kFinishThreads) void bucket_finish_kernel(const uin
 #pragma unroll
       for (int j = 0; j < KB; ++j)
         if (j < kb) write_result(out_vals, out_idx, (int64_t)row * nc + (int64_t)r * kb + j, xr, dt, a[j]);
-    } else if (mode == 1) {
+    } else if (mode == 1 || mode == 3) {
 #pragma unroll
       for (int j = 0; j < KB; ++j)
         if (j < kb) cand[r * kb + j] = a[j];
@@ -330,10 +354,81 @@ __global__ __launch_bounds__(kFinishThreads) void bucket_finish_kernel(const uin
         if (j < kb) cand_out[(int64_t)row * nc + (int64_t)r * kb + j] = a[j];
     }
   }
-  if (mode != 1) return;
+  if (mode != 1 && mode != 3) return;
   __syncthreads();
   int cnt = (int)nc;
-  if (cnt > k) {
+  if (mode == 3) {
+    const int lane = lane_id();
+    const uint64_t thr = block_kth_key<T>(cand, cnt, k, hist, ctl);
+    if (t == 0) {
+      ctl[5] = 0;
+      ctl[6] = 0;
+    }
+    __syncthreads();
+    for (int r = t; r < b; r += T) {
+      const uint64_t c = cand[r * kb + kb - 1];
+      const int size = (n - r + b - 1) / b;
+      if (size > kb && c >= thr) {
+        const uint32_t f = atomicAdd(&ctl[5], 1u);
+        if (f < (uint32_t)kFlagMax) {
+          flg_r[f] = (uint32_t)r;
+          flg_c[f] = c;
+        }
+      }
+    }
+    cnt = block_compact_ge<T, kFinishMaxCand / T>(cand, cnt, thr, ctl);  // k keys, all >= thr
+    const int nflag = (int)ctl[5];
+    if (nflag > 0) {
+      bool overflow = nflag > kFlagMax;
+      if (!overflow) {
+        // Every thread of the workgroup steps through slot s of the flagged
+        // buckets' elements: bucket f = s / S, element r_f + (s % S) * b, with
+        // S = ceil(n / b) slots per bucket (the last may be past the row).
+        constexpr int U = 4;
+        const int64_t S = ((int64_t)n + b - 1) / b;
+        const int64_t total = (int64_t)nflag * S;
+        for (int64_t s0 = 0; s0 < total; s0 += (int64_t)U * T) {
+          uint32_t o[U];
+          int64_t ii[U];
+          uint64_t cc[U];
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const int64_t sl = s0 + (int64_t)u * T + t;
+            const int f = sl < total ? (int)(sl / S) : 0;
+            ii[u] = sl < total ? (int64_t)flg_r[f] + (sl - (int64_t)f * S) * b : (int64_t)n;
+            cc[u] = flg_c[f];
+            o[u] = ii[u] < n ? row_ord(xr, dt, ii[u]) : 0u;
+          }
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const uint64_t key = make_key(o[u], (uint32_t)ii[u]);
+            const bool keep = ii[u] < n && key > thr && key < cc[u];
+            const uint64_t msk = __ballot(keep);
+            if (msk) {
+              uint32_t pos = 0;
+              if (lane == 0) pos = atomicAdd(&ctl[6], (uint32_t)__popcll(msk));
+              pos = __shfl(pos, 0, kWave);
+              const uint32_t slot = (uint32_t)k + pos + lanes_below(msk);
+              if (keep && slot < (uint32_t)kFinishMaxCand) cand[slot] = key;
+            }
+          }
+        }
+        __syncthreads();
+        const int extra = (int)ctl[6];
+        __syncthreads();
+        overflow = k + extra > kFinishMaxCand;
+        if (!overflow && extra > 0) {
+          cnt = k + extra;
+          const uint64_t thr2 = block_kth_key<T>(cand, cnt, k, hist, ctl);
+          cnt = block_compact_ge<T, kFinishMaxCand / T>(cand, cnt, thr2, ctl);
+        }
+      }
+      if (overflow) {
+        finish_row_fallback(xr, dt, n, k, cand, hist, ctl);
+        cnt = k;
+      }
+    }
+  } else if (cnt > k) {
     const uint64_t thr = block_kth_key<T>(cand, cnt, k, hist, ctl);
     cnt = block_compact_ge<T, kFinishMaxCand / T>(cand, cnt, thr, ctl);
   }
@@ -411,6 +506,8 @@ BucketPlan plan_bucketed(int dtype, int64_t m, int64_t n, int64_t b, int64_t kb,
   const int64_t sweeps = (n + W - 1) / W;
   int64_t splits = (kTargetBlocks + m - 1) / (m > 0 ? m : 1);
   splits = std::min<int64_t>(splits, std::max<int64_t>(1, sweeps / 8));
+  // The finish reads lists_per_row * b queues per row with one workgroup.
+  splits = std::min<int64_t>(splits, std::max<int64_t>(1, kListBudget / (b * kb_slots(kb))));
   splits = std::max<int64_t>(splits, 1);
   const int64_t chunk_sweeps = (sweeps + splits - 1) / splits;
   p.chunk = chunk_sweeps * W;
@@ -428,17 +525,22 @@ hipError_t launch_bucket_stage1(const BucketPlan& p, const void* x, int dtype, i
   return launch_stage1_dt<IN_BF16>(p, x, m, n, ldx, b, kb, lists, s);
 }
 
-hipError_t launch_bucket_finish(const uint64_t* lists, int lists_per_row, int64_t m, int64_t b, int64_t kb, int64_t k,
-                                int final_exact, const void* x, int dtype, int64_t ldx, void* out_vals,
+hipError_t launch_bucket_finish(const uint64_t* lists, int lists_per_row, int64_t m, int64_t n, int64_t b, int64_t kb,
+                                int64_t k, int final_exact, const void* x, int dtype, int64_t ldx, void* out_vals,
                                 int32_t* out_idx, uint64_t* cand_out, hipStream_t s) {
   const int64_t es = dtype == IN_F32 ? 4 : 2;
   int mode = 0;
-  if (final_exact) mode = (b * kb <= kFinishMaxCand) ? 1 : 2;
+  if (final_exact == kFinishCertified) {
+    if (b * kb > kFinishMaxCand || k > b * kb) return hipErrorInvalidValue;
+    mode = 3;
+  } else if (final_exact) {
+    mode = (b * kb <= kFinishMaxCand) ? 1 : 2;
+  }
   dim3 grid((unsigned)m);
 #define ATOPK_F(KBV)                                                                                               \
   case KBV:                                                                                                        \
     hipLaunchKernelGGL((bucket_finish_kernel<KBV>), grid, dim3(kFinishThreads), 0, s, lists, lists_per_row, (int)b, \
-                       (int)k, mode, (int)kb, static_cast<const uint8_t*>(x), dtype, ldx * es,                     \
+                       (int)k, mode, (int)kb, static_cast<const uint8_t*>(x), dtype, ldx * es, (int)n,             \
                        static_cast<uint8_t*>(out_vals), out_idx, cand_out);                                        \
     break;
   switch (kb_slots(kb)) {
