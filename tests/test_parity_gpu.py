@@ -491,6 +491,36 @@ def _clear_gaps(s, k_sel, b, kb, gap=1e-3):
     return len(v) <= k_sel or v[k_sel - 1] - v[k_sel] > gap
 
 
+@pytest.mark.parametrize("hq,hkv,ctx,k_sel,planted", [
+    (2, 2, 3000, 64, "stride256"),    # one query head per KV head: a flagged bucket is rescored
+    (8, 2, 3000, 64, "stride256"),    # query-head groups: rescanned from the written scores
+    (1, 1, 131072, 16, "mod8"),       # one bucket far above the rest: the rescan overflows, full-row fallback
+    (4, 2, 131072, 64, "mod64lt5"),   # the same for query-head groups (5 buckets of 2048 keys)
+])
+def test_decode_exact_certified_planted(gpu, hq, hkv, ctx, k_sel, planted):
+    """Exact Top-K decode on caches that defeat the bucket candidates: keys
+    aligned with a query head planted in positions that share a bucket for
+    every power-of-two b the certified plans use, so buckets are flagged and
+    rescanned (or overflow into the full-row fallback)."""
+    g = torch.Generator(device="cpu").manual_seed(ctx + hq)
+    q = torch.randn((1, hq, 128), generator=g)
+    K = torch.randn((1, hkv, ctx, 128), generator=g) * 0.5
+    V = torch.randn((1, hkv, ctx, 128), generator=g)
+    j = torch.arange(ctx)
+    if planted == "stride256":
+        mask = (j % 256 == 0) & (j < 12 * 256)
+    elif planted == "mod8":
+        mask = j % 8 == 0
+    else:
+        mask = j % 64 < 5
+    G = hq // hkv
+    for h in range(hkv):
+        K[0, h, mask] = 2.0 * q[0, h * G] + 0.05 * torch.randn((int(mask.sum()), 128), generator=g)
+    q, K, V = (t.to(torch.bfloat16).to(gpu) for t in (q, K, V))
+    print("case", hq, hkv, ctx, k_sel, planted, flush=True)
+    _decode_check(q, K, V, k_sel, 1, k_sel)
+
+
 @pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 2), (6, 2)])
 @pytest.mark.parametrize("ctx,k_sel,b,kb", [(3000, 64, 16, 8), (3000, 64, 64, 1), (3000, 64, 1, 64),
                                             (4096, 256, 128, 2), (5000, 100, 7, 16)])

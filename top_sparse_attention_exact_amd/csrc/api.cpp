@@ -309,17 +309,52 @@ int validate_decode(int64_t batch, int64_t hq, int64_t hkv, int64_t ctx, int64_t
 
 struct DecodeLayout {
   DecodePlan plan;
+  bool certified;                                          // exact Top-K from a fused bucketed pass
+  int64_t cb, ckb;                                         // its (b, kb)
+  int cmode;                                               // 1: scores written and rescanned, 2: recomputed
   size_t partial_off;                                      // fused path
-  size_t scores_off, vals_off, idx_off, sel_ws_off;        // separate passes
+  size_t scores_off, vals_off, idx_off, sel_ws_off;        // separate passes (scores_off also certified)
   size_t sel_ws_bytes;
   size_t total;
 };
 
+// The exact Top-K of a decode as a fused bucketed pass plus the finish's
+// certification.  Query-head groups (scores on the matrix cores): k_b = 4,
+// every score written out and rescanned from there; the smallest b the
+// fused kernels take whose expected rescan (buckets to rescan times keys
+// per bucket, on iid scores) stays below 4096 scores per head.  One query
+// head per KV head: k_b = 8 and no score write; the finish recomputes a
+// flagged bucket's scores, so b is the smallest whose expected number of
+// flagged buckets stays below 1/16 per head.
+bool plan_decode_certified(int64_t batch, int64_t hq, int64_t hkv, int64_t ctx, int64_t k_sel, int64_t* b_out,
+                           int64_t* kb_out, int* mode) {
+  const bool groups = hq / hkv >= 2;
+  const int64_t kb = groups ? 4 : 8;
+  for (int64_t b = std::max<int64_t>(2, pow2_ceil((k_sel + kb - 1) / kb)); b * kb <= kFinishMaxCand; b *= 2) {
+    if (b > ctx || kb > ctx / b) break;
+    if (!plan_decode(batch, hq, hkv, ctx, k_sel, b, kb).fused) break;
+    const double e = saturated_buckets(k_sel, b, kb);
+    const bool ok = groups ? (e <= 16.0 && e * (double)((ctx + b - 1) / b) <= 4096.0) : e <= 1.0 / 16.0;
+    if (ok) {
+      *b_out = b;
+      *kb_out = kb;
+      *mode = groups ? 1 : 2;
+      return true;
+    }
+  }
+  return false;
+}
+
 DecodeLayout decode_layout(int64_t batch, int64_t hq, int64_t hkv, int64_t ctx, int64_t k_sel, int64_t b, int64_t kb) {
   DecodeLayout L{};
-  L.plan = plan_decode(batch, hq, hkv, ctx, k_sel, b, kb);
+  L.certified =
+      exact_route(k_sel, b, kb) && plan_decode_certified(batch, hq, hkv, ctx, k_sel, &L.cb, &L.ckb, &L.cmode);
+  L.plan = L.certified ? plan_decode(batch, hq, hkv, ctx, k_sel, L.cb, L.ckb) : plan_decode(batch, hq, hkv, ctx, k_sel, b, kb);
   Carve c;
-  if (L.plan.fused) {
+  if (L.certified) {
+    L.partial_off = c.take(L.plan.partial_bytes);
+    L.scores_off = c.take((size_t)batch * hq * ctx * 4);
+  } else if (L.plan.fused) {
     L.partial_off = c.take(L.plan.partial_bytes);
   } else {
     const int64_t rows = batch * hq;
@@ -502,10 +537,17 @@ int atopk_sparse_attn_decode(const void* q, const void* K, const void* V, int64_
     const uint16_t* q16 = static_cast<const uint16_t*>(q);
     const uint16_t* k16 = static_cast<const uint16_t*>(K);
     const uint16_t* v16 = static_cast<const uint16_t*>(V);
+    if (L.certified) {
+      float* buf = scores ? scores : reinterpret_cast<float*>(w + L.scores_off);
+      return hip_status(launch_decode_fused(L.plan, q16, k16, v16, batch, hq, hkv, ctx, ctx_stride, scale, k_sel, L.cb,
+                                            L.ckb, reinterpret_cast<uint64_t*>(w + L.partial_off),
+                                            static_cast<uint16_t*>(out), sel_idx, L.cmode == 1 ? buf : scores, L.cmode,
+                                            buf, s));
+    }
     if (L.plan.fused) {
       return hip_status(launch_decode_fused(L.plan, q16, k16, v16, batch, hq, hkv, ctx, ctx_stride, scale, k_sel, b,
                                             kb, reinterpret_cast<uint64_t*>(w + L.partial_off),
-                                            static_cast<uint16_t*>(out), sel_idx, scores, s));
+                                            static_cast<uint16_t*>(out), sel_idx, scores, 0, nullptr, s));
     }
     float* sc = scores ? scores : reinterpret_cast<float*>(w + L.scores_off);
     float* vals = reinterpret_cast<float*>(w + L.vals_off);

@@ -58,6 +58,27 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
+// Staged scores of one step (G head rows of nk keys from key s0) to
+// scores[row0 + g][s0 + li]: 16-byte stores when the rows allow them.
+template <int T>
+__device__ __forceinline__ void dump_scores(float* __restrict__ scores, int64_t row0, int ctx, int s0, int G, int nk,
+                                            const float (*scb)[kSubPad]) {
+  const int t = threadIdx.x;
+  if (nk == kSub && (ctx & 3) == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0) {
+    constexpr int Q = kSub / 4;
+    for (int i = t; i < G * Q; i += T) {
+      const int g = i / Q, li = (i - g * Q) * 4;
+      const float4 v = make_float4(scb[g][li], scb[g][li + 1], scb[g][li + 2], scb[g][li + 3]);
+      *reinterpret_cast<float4*>(scores + (row0 + g) * ctx + s0 + li) = v;
+    }
+  } else {
+    for (int i = t; i < G * nk; i += T) {
+      const int g = i / nk, li = i - g * nk;
+      scores[(row0 + g) * ctx + s0 + li] = scb[g][li];
+    }
+  }
+}
+
 // PPT (head, bucket) pairs per thread, KB queue slots per pair.
 template <int PPT, int KB>
 __global__ __launch_bounds__(kT1) void decode_select_kernel(const uint16_t* __restrict__ q,
@@ -121,12 +142,7 @@ __global__ __launch_bounds__(kT1) void decode_select_kernel(const uint16_t* __re
     }
     lds_barrier();
     const int nk = s1 - s0;
-    if (scores != nullptr) {  // debug dump, coalesced
-      for (int i = t; i < G * nk; i += kT1) {
-        const int g = i / nk, li = i - g * nk;
-        scores[(int64_t)(bi * hq + h * G + g) * ctx + s0 + li] = sc[buf][g][li];
-      }
-    }
+    if (scores != nullptr) dump_scores<kT1>(scores, (int64_t)(bi * hq + h * G), ctx, s0, G, nk, sc[buf]);
     // fold the staged scores of the owned (head, bucket) pairs: bucket r
     // holds keys j with j mod b == r
     const int rs = b > 0 ? s0 % b : 0;  // b == 0: scores only
@@ -239,12 +255,7 @@ __global__ __launch_bounds__(kT1M, 2) void decode_select_mfma_kernel(const uint1
     }
     lds_barrier();
     const int nk = s1 - s0;
-    if (scores != nullptr) {  // debug dump, coalesced
-      for (int i = t; i < G * nk; i += kT1M) {
-        const int g = i / nk, li = i - g * nk;
-        scores[(int64_t)(bi * hq + h * G + g) * ctx + s0 + li] = sc[buf][g][li];
-      }
-    }
+    if (scores != nullptr) dump_scores<kT1M>(scores, (int64_t)(bi * hq + h * G), ctx, s0, G, nk, sc[buf]);
     // fold the staged scores of the owned (head, bucket) pairs: bucket r
     // holds keys j with j mod b == r
     const int rs = b > 0 ? s0 % b : 0;  // b == 0: scores only
@@ -279,15 +290,55 @@ constexpr int kT2 = 512;
 constexpr int kMaxCand = 8192;
 constexpr int kVGroups = kT2 / 16;  // 16-lane groups gathering V rows
 
+constexpr int kFlagMax = 256;  // flagged buckets rescanned in LDS; more take the full-row fallback
+
+__device__ __noinline__ void decode_row_fallback(const float* srow, int ctx, int k, uint64_t* cand, uint32_t* hist,
+                                                 uint32_t* ctl) {
+  block_row_topk<kT2>([&](int i) { return ord_f32(__float_as_uint(srow[i])); }, ctx, k, cand, hist, ctl);
+}
+
+// Without stored scores (one query head per KV head), for a rescan that
+// overflows: the workgroup recomputes every score of its head exactly as the
+// scoring kernel does (16-lane groups) into its own row `srow` of the
+// workspace, then selects from that row.
+__device__ __noinline__ void decode_fill_scores(const uint16_t* qrow, const uint16_t* krow, float scale, int ctx,
+                                                float* srow) {
+  const int t = threadIdx.x;
+  const int grp = t >> 4, sub = t & 15;
+  const uint4 qv = *reinterpret_cast<const uint4*>(qrow + sub * 8);
+  for (int j0 = 0; j0 < ctx; j0 += kVGroups) {
+    const int j = j0 + grp;
+    const uint4 kv = j < ctx ? *reinterpret_cast<const uint4*>(krow + (int64_t)j * kD + sub * 8) : make_uint4(0, 0, 0, 0);
+    const float sc = row16_sum(dot8_bf16(kv, qv)) * scale;
+    if (sub == 0 && j < ctx) srow[j] = sc;
+  }
+  __threadfence_block();
+  __syncthreads();
+}
+
+// certify != 0 makes the Top-K exact over every score of the head: with T
+// the k_sel-th candidate key, a bucket that kept k_b keys all >= T may hide
+// more of the Top-K (any missing key beats T); those buckets are rescanned
+// for keys between T and their k_b-th kept key, and the Top-K of the
+// enlarged pool is the exact one.  certify == 1: the scores of the head are
+// in `scores` ([B*Hq, ctx]); certify == 2 (one query head per KV head): the
+// rescan recomputes them from q and K with the scoring kernel's own
+// arithmetic (16-lane packed bf16 dot products, the same row sum, the same
+// scaling), so they are bit-identical to the ones that were ranked.
 template <int KB>
 __global__ __launch_bounds__(kT2) void decode_finish_kernel(const uint64_t* __restrict__ partial, int nchunks, int hq,
                                                            int hkv, int b, int kb, int k_sel,
                                                            const uint16_t* __restrict__ V, int64_t ctx_stride,
-                                                           uint16_t* __restrict__ out, int32_t* __restrict__ sel_idx) {
+                                                           uint16_t* __restrict__ out, int32_t* __restrict__ sel_idx,
+                                                           int certify, float* __restrict__ scores, int ctx,
+                                                           const uint16_t* __restrict__ q,
+                                                           const uint16_t* __restrict__ K, float scale) {
   constexpr int T = kT2;
   __shared__ uint64_t cand[kMaxCand];
   __shared__ uint32_t hist[256];
   __shared__ uint32_t ctl[8];
+  __shared__ uint32_t flg_r[kFlagMax];
+  __shared__ uint64_t flg_c[kFlagMax];
   __shared__ float acc_lds[kVGroups][kD];
   __shared__ float w_lds[kVGroups];
   __shared__ float red[T / kWave];
@@ -330,7 +381,99 @@ __global__ __launch_bounds__(kT2) void decode_finish_kernel(const uint64_t* __re
   }
   __syncthreads();
   int n = b * kb;
-  if (n > k_sel) {
+  if (certify) {
+    const uint64_t thr = block_kth_key<T>(cand, n, k_sel, hist, ctl);
+    if (t == 0) {
+      ctl[5] = 0;
+      ctl[6] = 0;
+    }
+    __syncthreads();
+    for (int r = t; r < b; r += T) {
+      const uint64_t c = cand[r * kb + kb - 1];
+      if ((ctx - r + b - 1) / b > kb && c >= thr) {
+        const uint32_t f = atomicAdd(&ctl[5], 1u);
+        if (f < (uint32_t)kFlagMax) {
+          flg_r[f] = (uint32_t)r;
+          flg_c[f] = c;
+        }
+      }
+    }
+    n = block_compact_ge<T, kMaxCand / T>(cand, n, thr, ctl);  // k_sel keys
+    const int nflag = (int)ctl[5];
+    const float* srow = scores + (int64_t)r_out * ctx;
+    if (nflag > 0) {
+      bool overflow = nflag > kFlagMax || (certify == 2 && G != 1);  // recompute is for G == 1 only
+      if (!overflow && certify == 2) {
+        // 16-lane groups recompute the flagged buckets' scores
+        const int grp = t >> 4, sub = t & 15;
+        const uint4 qv = *reinterpret_cast<const uint4*>(q + (int64_t)r_out * kD + sub * 8);
+        const uint16_t* kh = K + (int64_t)bh * ctx_stride * kD + sub * 8;
+        const int S = (ctx + b - 1) / b;
+        const int total = nflag * S;
+        for (int s0 = 0; s0 < total; s0 += kVGroups) {
+          const int sl = s0 + grp;
+          const int f = sl < total ? sl / S : 0;
+          const int j = sl < total ? (int)flg_r[f] + (sl - f * S) * b : ctx;
+          const uint4 kv = j < ctx ? *reinterpret_cast<const uint4*>(kh + (int64_t)j * kD) : make_uint4(0, 0, 0, 0);
+          const float sc = row16_sum(dot8_bf16(kv, qv)) * scale;
+          const uint64_t key = j < ctx ? make_key(ord_f32(__float_as_uint(sc)), (uint32_t)j) : 0;
+          const bool keep = sub == 0 && j < ctx && key > thr && key < flg_c[f];
+          const uint64_t msk = __ballot(keep);
+          if (msk) {
+            uint32_t pos = 0;
+            if (lane_id() == 0) pos = atomicAdd(&ctl[6], (uint32_t)__popcll(msk));
+            pos = __shfl(pos, 0, kWave);
+            const uint32_t slot = (uint32_t)k_sel + pos + lanes_below(msk);
+            if (keep && slot < (uint32_t)kMaxCand) cand[slot] = key;
+          }
+        }
+        __syncthreads();
+        const int extra = (int)ctl[6];
+        __syncthreads();
+        overflow = k_sel + extra > kMaxCand;
+        if (!overflow && extra > 0) {
+          n = k_sel + extra;
+          const uint64_t thr2 = block_kth_key<T>(cand, n, k_sel, hist, ctl);
+          n = block_compact_ge<T, kMaxCand / T>(cand, n, thr2, ctl);
+        }
+      } else if (!overflow) {
+        // every thread steps through slot s of the flagged buckets' keys:
+        // bucket f = s / S, key r_f + (s % S) * b, S = ceil(ctx / b)
+        const int S = (ctx + b - 1) / b;
+        const int total = nflag * S;
+        for (int s0 = 0; s0 < total; s0 += T) {
+          const int sl = s0 + t;
+          const int f = sl < total ? sl / S : 0;
+          const int j = sl < total ? (int)flg_r[f] + (sl - f * S) * b : ctx;
+          const uint64_t key = j < ctx ? make_key(ord_f32(__float_as_uint(srow[j])), (uint32_t)j) : 0;
+          const bool keep = j < ctx && key > thr && key < flg_c[f];
+          const uint64_t msk = __ballot(keep);
+          if (msk) {
+            uint32_t pos = 0;
+            if (lane_id() == 0) pos = atomicAdd(&ctl[6], (uint32_t)__popcll(msk));
+            pos = __shfl(pos, 0, kWave);
+            const uint32_t slot = (uint32_t)k_sel + pos + lanes_below(msk);
+            if (keep && slot < (uint32_t)kMaxCand) cand[slot] = key;
+          }
+        }
+        __syncthreads();
+        const int extra = (int)ctl[6];
+        __syncthreads();
+        overflow = k_sel + extra > kMaxCand;
+        if (!overflow && extra > 0) {
+          n = k_sel + extra;
+          const uint64_t thr2 = block_kth_key<T>(cand, n, k_sel, hist, ctl);
+          n = block_compact_ge<T, kMaxCand / T>(cand, n, thr2, ctl);
+        }
+      }
+      if (overflow) {
+        float* row = scores + (int64_t)r_out * ctx;
+        if (certify == 2) decode_fill_scores(q + (int64_t)r_out * kD, K + (int64_t)bh * ctx_stride * kD, scale, ctx, row);
+        decode_row_fallback(row, ctx, k_sel, cand, hist, ctl);
+        n = k_sel;
+      }
+    }
+  } else if (n > k_sel) {
     const uint64_t thr = block_kth_key<T>(cand, n, k_sel, hist, ctl);
     n = block_compact_ge<T, kMaxCand / T>(cand, n, thr, ctl);
   }
@@ -452,7 +595,9 @@ hipError_t launch_decode_scores(const uint16_t* q, const uint16_t* K, int64_t ba
 hipError_t launch_decode_fused(const DecodePlan& p, const uint16_t* q, const uint16_t* K, const uint16_t* V,
                                int64_t batch, int64_t hq, int64_t hkv, int64_t ctx, int64_t ctx_stride, float scale,
                                int64_t k_sel, int64_t b, int64_t kb, uint64_t* partial, uint16_t* out,
-                               int32_t* sel_idx, float* scores, hipStream_t s) {
+                               int32_t* sel_idx, float* scores, int certify, float* cert_buf, hipStream_t s) {
+  if (certify && cert_buf == nullptr) return hipErrorInvalidValue;
+  if (certify == 1 && scores != cert_buf) return hipErrorInvalidValue;
   const int kbs = kb_pow2(kb);
   dim3 g1((unsigned)p.nchunks, (unsigned)(batch * hkv));
 #define ATOPK_D1(P, KBV)                                                                                            \
@@ -476,7 +621,8 @@ hipError_t launch_decode_fused(const DecodePlan& p, const uint16_t* q, const uin
 #define ATOPK_D2(KBV)                                                                                              \
   case KBV:                                                                                                        \
     hipLaunchKernelGGL((decode_finish_kernel<KBV>), g2, dim3(kT2), 0, s, partial, p.nchunks, (int)hq, (int)hkv,     \
-                       (int)b, (int)kb, (int)k_sel, V, ctx_stride, out, sel_idx);                                  \
+                       (int)b, (int)kb, (int)k_sel, V, ctx_stride, out, sel_idx, certify, cert_buf, (int)ctx, q, K, \
+                       scale);                                                                                      \
     break;
   switch (kbs) {
     ATOPK_D2(1) ATOPK_D2(2) ATOPK_D2(4) ATOPK_D2(8) ATOPK_D2(16)

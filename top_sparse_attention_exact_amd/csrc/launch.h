@@ -115,10 +115,16 @@ struct DecodePlan {
   size_t partial_bytes;  // per-chunk k_b-lists
 };
 DecodePlan plan_decode(int64_t batch, int64_t hq, int64_t hkv, int64_t ctx, int64_t k_sel, int64_t b, int64_t kb);
+// certify != 0: (b, kb) is a certified plan for the exact Top-K and
+// cert_buf a [B*Hq, ctx] fp32 buffer.  certify == 1: every score goes to
+// cert_buf (scores must equal it) and the finish rescans from there;
+// certify == 2 (one query head per KV head): the finish recomputes the
+// scores it rescans, and cert_buf is scratch for its rare full-row fallback.
+// scores (nullable otherwise): every score, when the caller asks for them.
 hipError_t launch_decode_fused(const DecodePlan& p, const uint16_t* q, const uint16_t* K, const uint16_t* V,
                                int64_t batch, int64_t hq, int64_t hkv, int64_t ctx, int64_t ctx_stride, float scale,
                                int64_t k_sel, int64_t b, int64_t kb, uint64_t* partial, uint16_t* out,
-                               int32_t* sel_idx, float* scores, hipStream_t s);
+                               int32_t* sel_idx, float* scores, int certify, float* cert_buf, hipStream_t s);
 
 // Candidate-set rerank decode: per query head the given indices united with
 // the last `window` keys, exact scores, Top-K, softmax-V.
