@@ -168,12 +168,16 @@ int atopk_sparse_attn_decode(const void* q, const void* K, const void* V, int64_
  *           padded with -1 when the set holds fewer than k_sel keys.
  * Requires d == 128, hq % hkv == 0, 1 <= ctx <= 262144, ctx_stride >= ctx,
  * 1 <= window <= ctx, 0 <= ncand <= cand_stride, ncand + window <= 8192,
- * 1 <= k_sel <= 8192, 16-byte aligned q, K, V.  No workspace.
+ * 1 <= k_sel <= 8192, 16-byte aligned q, K, V.  The workspace (size from
+ * atopk_sparse_attn_rerank_workspace, 256-byte aligned) holds the scored
+ * candidate keys between the scoring and the selection kernels.
  */
+int atopk_sparse_attn_rerank_workspace(int64_t batch, int64_t hq, int64_t hkv, int64_t ctx, int64_t ncand,
+                                       int64_t window, size_t* ws_bytes);
 int atopk_sparse_attn_rerank(const void* q, const void* K, const void* V, int64_t batch, int64_t hq, int64_t hkv,
                              int64_t ctx, int64_t ctx_stride, int64_t d, float scale, const int32_t* cand,
                              int64_t ncand, int64_t cand_stride, int64_t window, int64_t k_sel, void* out,
-                             int32_t* sel_idx, void* stream);
+                             int32_t* sel_idx, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Expected recall of the bucketed top-k ("Approximate Top-k for Increased

@@ -33,7 +33,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 15
     handle = ctypes.CDLL(lib_mod.LIB_PATH)
     for name in names:
         assert hasattr(handle, name), name
@@ -167,9 +167,9 @@ def test_decode_validation(L):
 
 def test_rerank_validation(L):
     def call(bsz=2, hq=8, hkv=2, ctx=4096, stride=4096, d=128, cand=FAKE, ncand=100, cstride=128, window=64,
-             k=64, q=FAKE, out=FAKE):
+             k=64, q=FAKE, out=FAKE, ws=FAKE, ws_bytes=1 << 30):
         return L.atopk_sparse_attn_rerank(q, FAKE, FAKE, bsz, hq, hkv, ctx, stride, d, 0.1, cand, ncand, cstride,
-                                          window, k, out, None, None)
+                                          window, k, out, None, ws, ws_bytes, None)
     assert call(hq=6, hkv=4) == ESHAPE          # hq % hkv
     assert call(stride=100) == ESHAPE           # ctx_stride < ctx
     assert call(cstride=50) == ESHAPE           # cand_stride < ncand
@@ -185,6 +185,15 @@ def test_rerank_validation(L):
     assert call(q=None) == ENULL
     assert call(cand=None) == ENULL
     assert call(q=ctypes.c_void_p(0x1008)) == EUNSUP  # misaligned
+    sz = ctypes.c_size_t(0)
+    assert L.atopk_sparse_attn_rerank_workspace(2, 8, 2, 4096, 100, 64, None) == ENULL
+    assert L.atopk_sparse_attn_rerank_workspace(2, 8, 2, 4096, 100, 0, ctypes.byref(sz)) == EPARAM
+    assert L.atopk_sparse_attn_rerank_workspace(2, 8, 2, 4096, 8150, 64, ctypes.byref(sz)) == EUNSUP
+    assert L.atopk_sparse_attn_rerank_workspace(2, 8, 2, 4096, 100, 64, ctypes.byref(sz)) == OK
+    assert sz.value >= 2 * 8 * (100 + 64) * 8
+    assert call(ws=None, ws_bytes=0) == EWS
+    assert call(ws_bytes=sz.value - 1) == EWS
+    assert call(ws=ctypes.c_void_p(0x1008)) == EWS  # not 256-byte aligned
 
 
 @pytest.mark.parametrize("n,k,b,kb", [(131072, 64, 64, 1), (131072, 64, 128, 2), (4096, 64, 32, 2), (37, 8, 5, 2),

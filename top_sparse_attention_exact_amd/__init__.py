@@ -162,7 +162,7 @@ def sparse_attn_decode(q, K, V, k_sel, b=1, kb=None, scale=None, ctx=None, retur
     return res[0] if len(res) == 1 else tuple(res)
 
 
-def sparse_attn_rerank(q, K, V, cand, window, k_sel, scale=None, ctx=None, return_sel=False):
+def sparse_attn_rerank(q, K, V, cand, window, k_sel, scale=None, ctx=None, return_sel=False, workspace=None):
     """Candidate-set rerank decode.  q [B, Hq, D], K/V [B, Hkv, Lmax, D] bf16;
     cand [B, Hq, C] int32 candidate key indices per query head (entries
     outside [0, ctx) are skipped, repeats count once); the last `window` keys
@@ -184,9 +184,13 @@ def sparse_attn_rerank(q, K, V, cand, window, k_sel, scale=None, ctx=None, retur
     out = torch.empty((bsz, hq, d), dtype=torch.bfloat16, device=q.device)
     sel = torch.empty((bsz, hq, k_sel), dtype=torch.int32, device=q.device) if return_sel else None
     ncand = cand.shape[2]
+    size = ctypes.c_size_t(0)
+    check(lib().atopk_sparse_attn_rerank_workspace(bsz, hq, hkv, ctx, ncand, window, ctypes.byref(size)),
+          "atopk_sparse_attn_rerank_workspace")
+    ws, nbytes = (workspace, workspace.numel()) if workspace is not None else _workspace(size.value, q.device)
     st = lib().atopk_sparse_attn_rerank(_ptr(q), _ptr(K), _ptr(V), bsz, hq, hkv, ctx, lmax, d, float(scale),
                                         _ptr(cand) if ncand > 0 else ctypes.c_void_p(0), ncand,
-                                        ncand, window, k_sel, _ptr(out), _ptr(sel),
+                                        ncand, window, k_sel, _ptr(out), _ptr(sel), _ptr(ws), nbytes,
                                         _stream_ptr(q.device))
     check(st, "atopk_sparse_attn_rerank")
     return (out, sel) if return_sel else out

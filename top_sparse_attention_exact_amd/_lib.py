@@ -38,10 +38,12 @@ _SIGNATURES = {
         [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, ctypes.c_float, _c_i64, _c_i64, _c_i64,
          _c_vp, _c_vp, _c_vp, _c_vp, ctypes.c_size_t, _c_vp],
     ),
+    "atopk_sparse_attn_rerank_workspace": (
+        _c_int, [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, ctypes.POINTER(ctypes.c_size_t)]),
     "atopk_sparse_attn_rerank": (
         _c_int,
         [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, ctypes.c_float, _c_vp, _c_i64, _c_i64,
-         _c_i64, _c_i64, _c_vp, _c_vp, _c_vp],
+         _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, ctypes.c_size_t, _c_vp],
     ),
     "atopk_expected_recall": (_c_int, [_c_i64, _c_i64, _c_i64, _c_i64, ctypes.POINTER(ctypes.c_double)]),
     "atopk_choose_workspace": (

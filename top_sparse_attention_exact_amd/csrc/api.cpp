@@ -384,6 +384,17 @@ int guarded(F&& f) {
   }
 }
 
+int validate_rerank(int64_t batch, int64_t hq, int64_t hkv, int64_t ctx, int64_t ctx_stride, int64_t d, int64_t k_sel,
+                    int64_t ncand, int64_t cand_stride, int64_t window) {
+  if (batch < 0 || hq < 1 || hkv < 1 || hq % hkv != 0 || ctx < 1 || ctx_stride < ctx || d < 1 || k_sel < 1 ||
+      ncand < 0 || cand_stride < ncand)
+    return ATOPK_ERR_SHAPE;
+  if (window < 1 || window > ctx) return ATOPK_ERR_PARAM;
+  if (d != 128 || ctx > kRerankMaxCtx || ncand + window > kRerankMaxCand || k_sel > ATOPK_MAX_K)
+    return ATOPK_ERR_UNSUPPORTED;
+  return ATOPK_OK;
+}
+
 int validate_assignment(int dtype, int64_t n, int64_t k, int64_t b, int64_t kb, int final_exact, int assignment) {
   if (assignment != ATOPK_INTERLEAVED && assignment != ATOPK_CONTIGUOUS) return ATOPK_ERR_PARAM;
   if (assignment == ATOPK_CONTIGUOUS && !exact_route(k, b, kb) && !row_contig_ok(n, b, kb, final_exact))
@@ -562,26 +573,35 @@ int atopk_sparse_attn_decode(const void* q, const void* K, const void* V, int64_
   });
 }
 
+int atopk_sparse_attn_rerank_workspace(int64_t batch, int64_t hq, int64_t hkv, int64_t ctx, int64_t ncand,
+                                       int64_t window, size_t* ws_bytes) {
+  return guarded([&] {
+    if (ws_bytes == nullptr) return (int)ATOPK_ERR_NULL;
+    int st = validate_rerank(batch, hq, hkv, ctx, ctx, 128, 1, ncand, ncand, window);
+    if (st) return st;
+    *ws_bytes = batch == 0 ? 0 : rerank_ws_bytes(batch, hq, ncand, window);
+    return (int)ATOPK_OK;
+  });
+}
+
 int atopk_sparse_attn_rerank(const void* q, const void* K, const void* V, int64_t batch, int64_t hq, int64_t hkv,
                              int64_t ctx, int64_t ctx_stride, int64_t d, float scale, const int32_t* cand,
                              int64_t ncand, int64_t cand_stride, int64_t window, int64_t k_sel, void* out,
-                             int32_t* sel_idx, void* stream) {
+                             int32_t* sel_idx, void* ws, size_t ws_bytes, void* stream) {
   return guarded([&] {
-    if (batch < 0 || hq < 1 || hkv < 1 || hq % hkv != 0 || ctx < 1 || ctx_stride < ctx || d < 1 || k_sel < 1 ||
-        ncand < 0 || cand_stride < ncand)
-      return (int)ATOPK_ERR_SHAPE;
-    if (window < 1 || window > ctx) return (int)ATOPK_ERR_PARAM;
-    if (d != 128 || ctx > kRerankMaxCtx || ncand + window > kRerankMaxCand || k_sel > ATOPK_MAX_K)
-      return (int)ATOPK_ERR_UNSUPPORTED;
+    int st = validate_rerank(batch, hq, hkv, ctx, ctx_stride, d, k_sel, ncand, cand_stride, window);
+    if (st) return st;
     if (batch == 0) return (int)ATOPK_OK;
     if (!q || !K || !V || !out || (ncand > 0 && !cand)) return (int)ATOPK_ERR_NULL;
     if (((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(K) | reinterpret_cast<uintptr_t>(V)) & 15) != 0)
       return (int)ATOPK_ERR_UNSUPPORTED;
-    int st = check_device();
+    st = check_ws(ws, ws_bytes, rerank_ws_bytes(batch, hq, ncand, window));
+    if (st) return st;
+    st = check_device();
     if (st) return st;
     return hip_status(launch_rerank(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(K),
                                     static_cast<const uint16_t*>(V), batch, hq, hkv, ctx, ctx_stride, scale, cand,
-                                    ncand, cand_stride, window, k_sel, static_cast<uint16_t*>(out), sel_idx,
+                                    ncand, cand_stride, window, k_sel, static_cast<uint16_t*>(out), sel_idx, ws,
                                     static_cast<hipStream_t>(stream)));
   });
 }

@@ -130,10 +130,11 @@ hipError_t launch_decode_fused(const DecodePlan& p, const uint16_t* q, const uin
 // the last `window` keys, exact scores, Top-K, softmax-V.
 constexpr int kRerankMaxCand = 8192;   // ncand + window
 constexpr int kRerankMaxCtx = 262144;  // context covered by the LDS bitmap
+size_t rerank_ws_bytes(int64_t batch, int64_t hq, int64_t ncand, int64_t window);
 hipError_t launch_rerank(const uint16_t* q, const uint16_t* K, const uint16_t* V, int64_t batch, int64_t hq,
                          int64_t hkv, int64_t ctx, int64_t ctx_stride, float scale, const int32_t* cand, int64_t ncand,
                          int64_t cand_stride, int64_t window, int64_t k_sel, uint16_t* out, int32_t* sel_idx,
-                         hipStream_t s);
+                         void* ws, hipStream_t s);
 
 // out[r] = softmax(sel_vals[r]) @ V[sel_idx[r]] for r = i*hq + h.
 hipError_t launch_sparse_softmax_v(const float* sel_vals, const int32_t* sel_idx, const uint16_t* V,

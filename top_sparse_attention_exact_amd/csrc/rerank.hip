@@ -8,16 +8,21 @@
 // This is that inner step (the cache of query / support pairs and the
 // fallback policy stay with the caller).
 //
-// One workgroup per query head:
-//  1. candidate set: the head's given indices inside [0, ctx) and the last
-//     `window` positions, made unique with an LDS bitmap (one bit per key);
-//  2. scores: 16 lanes read one 256-byte key row with 16-byte loads and form
+// Two kernels:
+//  1. (query head, split) workgroups: the candidates in the split's position
+//     range -- the head's given indices inside [0, ctx) and the last `window`
+//     positions -- made unique with an LDS bitmap over the range; their
+//     scores: 16 lanes read one 256-byte key row with 16-byte loads and form
 //     its dot product with the query (packed bf16 dot products, fp32
-//     accumulation, DPP row sums), scaled in fp32;
-//  3. exact Top-K of the set by (score desc, index asc) -- radix select on
-//     the keys in LDS -- or the whole set when it holds fewer than K keys;
-//  4. softmax over the selected scores (maximum subtracted) and the weighted
-//     sum of their V rows, rounded to bf16.
+//     accumulation, DPP row sums), scaled in fp32; keys to the workspace.
+//     Splitting by position keeps every workgroup's bitmap small and puts
+//     the whole chip on the gather when there are few heads.
+//  2. one workgroup per query head: exact Top-K of its keys by (score desc,
+//     index asc) -- radix select in LDS -- or the whole set when it holds
+//     fewer than K keys; softmax over the selected scores (maximum
+//     subtracted) and the weighted sum of their V rows, rounded to bf16.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -28,6 +33,7 @@ namespace {
 constexpr int kD = 128;
 constexpr int kRT = 512;
 constexpr int kGroups = kRT / 16;
+constexpr int64_t kRerankTargetBlocks = 512;  // scoring workgroups to aim for
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -48,52 +54,57 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
-__global__ __launch_bounds__(kRT) void rerank_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ K,
-                                                    const uint16_t* __restrict__ V, int hq, int hkv, int ctx,
-                                                    int64_t ctx_stride, float scale,
-                                                    const int32_t* __restrict__ cand, int ncand, int64_t cand_stride,
-                                                    int window, int k_sel, uint16_t* __restrict__ out,
-                                                    int32_t* __restrict__ sel_idx) {
+// Kernel 1: workgroup (head, split) takes the candidates whose positions fall
+// in the split's range [lo, hi) (so every position has one owner and the
+// bitmap only covers the range), makes them unique, scores them and writes
+// their keys to keys_out[(head * S + split) * cap ...], count to cnt_out.
+__global__ __launch_bounds__(kRT) void rerank_score_kernel(const uint16_t* __restrict__ q,
+                                                          const uint16_t* __restrict__ K, int hq, int hkv, int ctx,
+                                                          int64_t ctx_stride, float scale,
+                                                          const int32_t* __restrict__ cand, int ncand,
+                                                          int64_t cand_stride, int window, int range,
+                                                          uint64_t* __restrict__ keys_out,
+                                                          int* __restrict__ cnt_out) {
   constexpr int T = kRT;
-  __shared__ uint64_t keys[kRerankMaxCand];
-  __shared__ uint32_t list[kRerankMaxCand];      // the candidate indices
-  __shared__ uint32_t bits[kRerankMaxCtx / 32];  // candidate bitmap, then the V partial sums
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t ctl[8];
-  __shared__ float w_lds[kGroups];
-  __shared__ float red[T / kWave];
-  float* acc_lds = reinterpret_cast<float*>(bits);  // [kGroups][kD] after the bitmap is done
-  static_assert(kRerankMaxCtx / 32 >= kGroups * kD, "the V partial sums live in the bitmap's words");
+  __shared__ uint32_t list[kRerankMaxCand];
+  __shared__ uint32_t bits[kRerankMaxCtx / 32];
+  __shared__ uint32_t ctl[1];
 
   const int t = threadIdx.x;
   const int r_out = blockIdx.x;  // = bi * hq + h
+  const int sp = blockIdx.y;
+  const int S = gridDim.y;
   const int bi = r_out / hq;
   const int h = r_out - bi * hq;
   const int kvh = h / (hq / hkv);
   const int64_t bh = (int64_t)bi * hkv + kvh;
+  const int lo = sp * range;
+  const int hi = min(ctx, lo + range);
 
-  // 1. candidate set
-  const int words = (ctx + 31) / 32;
+  // 1. the split's candidates, made unique
+  const int words = (max(hi - lo, 0) + 31) / 32;
   for (int i = t; i < words; i += T) bits[i] = 0;
-  if (t == 0) ctl[7] = 0;
+  if (t == 0) ctl[0] = 0;
   __syncthreads();
   const int32_t* cr = cand + (int64_t)r_out * cand_stride;
   const int total = ncand + window;
   for (int i = t; i < total; i += T) {
     const int j = i < ncand ? cr[i] : ctx - window + (i - ncand);
-    if (j >= 0 && j < ctx) {
-      const uint32_t bit = 1u << (j & 31);
-      if ((atomicOr(&bits[j >> 5], bit) & bit) == 0) list[atomicAdd(&ctl[7], 1u)] = (uint32_t)j;
+    if (j >= lo && j < hi) {
+      const int jl = j - lo;
+      const uint32_t bit = 1u << (jl & 31);
+      if ((atomicOr(&bits[jl >> 5], bit) & bit) == 0) list[atomicAdd(&ctl[0], 1u)] = (uint32_t)j;
     }
   }
   __syncthreads();
-  const int nc = (int)ctl[7];  // <= ncand + window <= kRerankMaxCand
+  const int nc = (int)ctl[0];  // <= ncand + window
 
   // 2. scores
   const int group = t >> 4;
   const int sub = t & 15;
   const uint4 qv = *reinterpret_cast<const uint4*>(q + (int64_t)r_out * kD + sub * 8);
   const uint16_t* kh = K + bh * ctx_stride * kD + sub * 8;
+  uint64_t* dst = keys_out + ((int64_t)r_out * S + sp) * total;
   constexpr int U = 8;
   for (int i0 = 0; i0 < nc; i0 += kGroups * U) {
     uint32_t jj[U];
@@ -111,14 +122,49 @@ __global__ __launch_bounds__(kRT) void rerank_kernel(const uint16_t* __restrict_
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = i0 + group + kGroups * u;
-      const float s = row16_sum(dot8_bf16(kv[u], qv)) * scale;
-      if (i < nc && sub == 0) keys[i] = make_key(ord_f32(__float_as_uint(s)), jj[u]);
+      const float sc = row16_sum(dot8_bf16(kv[u], qv)) * scale;
+      if (i < nc && sub == 0) dst[i] = make_key(ord_f32(__float_as_uint(sc)), jj[u]);
     }
+  }
+  if (t == 0) cnt_out[(int64_t)r_out * S + sp] = nc;
+}
+
+// Kernel 2, one workgroup per query head: the keys of its S splits, the
+// exact Top-K of them (all of them when fewer), softmax and the weighted sum
+// of the selected V rows.
+constexpr int kST = 1024;              // select kernel threads
+constexpr int kSGroups = kST / 16;
+
+__global__ __launch_bounds__(kST) void rerank_select_kernel(const uint64_t* __restrict__ keys_in,
+                                                           const int* __restrict__ cnt_in, int S, int total,
+                                                           int hq, int hkv, int64_t ctx_stride,
+                                                           const uint16_t* __restrict__ V, int k_sel,
+                                                           uint16_t* __restrict__ out, int32_t* __restrict__ sel_idx) {
+  constexpr int T = kST;
+  __shared__ uint64_t keys[kRerankMaxCand];
+  __shared__ float acc_lds[kSGroups][kD];
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t ctl[8];
+  __shared__ float w_lds[kSGroups];
+  __shared__ float red[T / kWave];
+
+  const int t = threadIdx.x;
+  const int r_out = blockIdx.x;
+  const int bi = r_out / hq;
+  const int h = r_out - bi * hq;
+  const int kvh = h / (hq / hkv);
+  const int64_t bh = (int64_t)bi * hkv + kvh;
+
+  int n = 0;
+  for (int sp = 0; sp < S; ++sp) {
+    const int c = cnt_in[(int64_t)r_out * S + sp];
+    const uint64_t* src = keys_in + ((int64_t)r_out * S + sp) * total;
+    for (int i = t; i < c; i += T) keys[n + i] = src[i];
+    n += c;  // <= total <= kRerankMaxCand (positions are unique across splits)
   }
   __syncthreads();
 
   // 3. exact Top-K of the set (the whole set when it is smaller)
-  int n = nc;
   if (n > k_sel) {
     const uint64_t thr = block_kth_key<T>(keys, n, k_sel, hist, ctl);
     n = block_compact_ge<T, kRerankMaxCand / T>(keys, n, thr, ctl);
@@ -143,17 +189,20 @@ __global__ __launch_bounds__(kRT) void rerank_kernel(const uint16_t* __restrict_
 #pragma unroll
   for (int w = 1; w < T / kWave; ++w) mx = fmaxf(mx, red[w]);
 
+  constexpr int U = 8;
+  const int group = t >> 4;
+  const int sub = t & 15;
   const uint16_t* vh = V + bh * ctx_stride * kD + sub * 8;
   float acc[8];
 #pragma unroll
   for (int d = 0; d < 8; ++d) acc[d] = 0.0f;
   float wsum = 0.0f;
-  for (int i = group; i < n; i += kGroups * U) {
+  for (int i = group; i < n; i += kSGroups * U) {
     uint4 v[U];
     float w[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int ii = i + kGroups * u;
+      const int ii = i + kSGroups * u;
       if (ii < n) {
         const uint64_t key = keys[ii];
         v[u] = *reinterpret_cast<const uint4*>(vh + (int64_t)key_idx(key) * kD);
@@ -175,14 +224,14 @@ __global__ __launch_bounds__(kRT) void rerank_kernel(const uint16_t* __restrict_
     }
   }
 #pragma unroll
-  for (int d = 0; d < 8; ++d) acc_lds[group * kD + sub * 8 + d] = acc[d];
+  for (int d = 0; d < 8; ++d) acc_lds[group][sub * 8 + d] = acc[d];
   if (sub == 0) w_lds[group] = wsum;
   __syncthreads();
   if (t < kD) {
     float s = 0.0f, wt = 0.0f;
 #pragma unroll
-    for (int gg = 0; gg < kGroups; ++gg) {
-      s += acc_lds[gg * kD + t];
+    for (int gg = 0; gg < kSGroups; ++gg) {
+      s += acc_lds[gg][t];
       wt += w_lds[gg];
     }
     out[(int64_t)r_out * kD + t] = f32_to_bf16_rne(s / wt);
@@ -191,12 +240,36 @@ __global__ __launch_bounds__(kRT) void rerank_kernel(const uint16_t* __restrict_
 
 }  // namespace
 
+int rerank_splits(int64_t batch, int64_t hq, int64_t ncand, int64_t window) {
+  const int64_t heads = std::max<int64_t>(1, batch * hq);
+  int64_t S = (kRerankTargetBlocks + heads - 1) / heads;
+  S = std::min<int64_t>(S, std::max<int64_t>(1, (ncand + window) / 256));
+  return (int)std::max<int64_t>(1, std::min<int64_t>(S, 8));
+}
+
+size_t rerank_ws_bytes(int64_t batch, int64_t hq, int64_t ncand, int64_t window) {
+  const int64_t rows = batch * hq * rerank_splits(batch, hq, ncand, window);
+  const size_t keys = ((size_t)rows * (ncand + window) * 8 + 255) / 256 * 256;
+  return keys + (size_t)rows * 4;
+}
+
 hipError_t launch_rerank(const uint16_t* q, const uint16_t* K, const uint16_t* V, int64_t batch, int64_t hq,
                          int64_t hkv, int64_t ctx, int64_t ctx_stride, float scale, const int32_t* cand, int64_t ncand,
                          int64_t cand_stride, int64_t window, int64_t k_sel, uint16_t* out, int32_t* sel_idx,
-                         hipStream_t s) {
-  hipLaunchKernelGGL(rerank_kernel, dim3((unsigned)(batch * hq)), dim3(kRT), 0, s, q, K, V, (int)hq, (int)hkv,
-                     (int)ctx, ctx_stride, scale, cand, (int)ncand, cand_stride, (int)window, (int)k_sel, out, sel_idx);
+                         void* ws, hipStream_t s) {
+  const int S = rerank_splits(batch, hq, ncand, window);
+  const int64_t rows = batch * hq * S;
+  const int64_t total = ncand + window;
+  uint64_t* keys = static_cast<uint64_t*>(ws);
+  int* cnt = reinterpret_cast<int*>(static_cast<uint8_t*>(ws) + ((size_t)rows * total * 8 + 255) / 256 * 256);
+  int range = (int)((ctx + S - 1) / S);
+  range = (range + 31) / 32 * 32;
+  hipLaunchKernelGGL(rerank_score_kernel, dim3((unsigned)(batch * hq), (unsigned)S), dim3(kRT), 0, s, q, K, (int)hq,
+                     (int)hkv, (int)ctx, ctx_stride, scale, cand, (int)ncand, cand_stride, (int)window, range, keys, cnt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(rerank_select_kernel, dim3((unsigned)(batch * hq)), dim3(kST), 0, s, keys, cnt, S, (int)total,
+                     (int)hq, (int)hkv, ctx_stride, V, (int)k_sel, out, sel_idx);
   return hipGetLastError();
 }
 
