@@ -248,7 +248,7 @@ __global__ __launch_bounds__(kWave * kMaxChunks) void wide_collect_exact_kernel(
     const float* __restrict__ x, int64_t ldx, int n, int b, int groups, int spc, const float* __restrict__ rowthr,
     int* __restrict__ row_cnt, uint64_t* __restrict__ row_keys) {
   __shared__ uint64_t wbuf[kMaxChunks][kFlush];
-  const Unit u = unit_of(n, b, groups, spc, true);
+  const Unit u = unit_of(n, b, groups, spc, false);
   uint64_t* buf = wbuf[threadIdx.x / kWave];
   const int lane = lane_id();
   const float* xr = x + (int64_t)u.row * ldx + u.r;
@@ -279,25 +279,20 @@ __global__ __launch_bounds__(kWave * kMaxChunks) void wide_collect_exact_kernel(
       if (fill > kFlush - kWave) flush();
     }
   };
-  // Walk the chunk from its end: the values pass read those sweeps last, so
-  // they are the ones still in the Infinity Cache.
-  const int fs = max(u.full, u.s0);  // sweeps [fs, s1) may be partial
-  for (int s = u.s1 - 1; s >= fs; --s) {
+  // sweeps [s0, fe) hold an element of every bucket; the rest may not
+  const int fe = u.full > u.s0 ? u.full : u.s0;
+  int s = u.s0;
+  for (; s + kWideU <= fe; s += kWideU) {
+    float w[kWideU];
+#pragma unroll
+    for (int v = 0; v < kWideU; ++v) w[v] = xr[(int64_t)(s + v) * b];
+#pragma unroll
+    for (int v = 0; v < kWideU; ++v) see(w[v] >= th, w[v], s + v);
+  }
+  for (; s < u.s1; ++s) {
     const bool in = (int64_t)s * b + u.r < n;
     const float v = in ? xr[(int64_t)s * b] : -INFINITY;
     see(in && v >= th, v, s);
-  }
-  int s = fs;
-  for (; s - kWideU >= u.s0; s -= kWideU) {
-    float w[kWideU];
-#pragma unroll
-    for (int v = 0; v < kWideU; ++v) w[v] = xr[(int64_t)(s - 1 - v) * b];
-#pragma unroll
-    for (int v = 0; v < kWideU; ++v) see(w[v] >= th, w[v], s - 1 - v);
-  }
-  for (--s; s >= u.s0; --s) {
-    const float v = xr[(int64_t)s * b];
-    see(v >= th, v, s);
   }
   if (fill > 0) flush();
 }
@@ -360,12 +355,13 @@ __device__ void block_sort_desc_regs(uint64_t (&key)[P], uint64_t* lds) {
 }
 
 // Sort cand[0..cnt) (LDS, cnt <= kFinMax, unique nonzero keys) descending.
-// Counting sort on the value: kFinMax bins spread evenly over the order-key
-// range of the candidates (bin 0 = largest values), a scan and a scatter;
-// then every key's place is its bin's start plus the number of larger keys
-// in its bin.  A bin above kBinRank keys (heavy ties) sends the whole set
-// to the bitonic sort.  `bins` holds kFinMax words, `red` 64.
+// Counting sort on the value over equi-depth bins (bin 0 = largest values;
+// see below), a scan and a scatter; then every key's place is its bin's
+// start plus the number of larger keys in its bin.  A bin above kBinRank
+// keys (heavy ties) sends the whole set to the bitonic sort.  `bins` holds
+// kFinMax words, `red` 64 + 2 * kCoarse.
 constexpr int kBinRank = 256;
+constexpr int kCoarse = 256;
 
 __device__ bool block_sort_desc_binned(uint64_t* cand, int cnt, uint32_t* bins, uint32_t* red) {
   constexpr int T = kFinT, P = kFinP;
@@ -402,10 +398,47 @@ __device__ bool block_sort_desc_binned(uint64_t* cand, int cnt, uint32_t* bins, 
     hi = max(hi, red[16 + w]);
   }
   const uint64_t span = (uint64_t)(hi - lo) + 1;
+  // Equi-depth bins: a coarse histogram (kCoarse bins evenly over the
+  // order-key range), then each coarse bin is cut into as many fine bins as
+  // it holds keys, evenly over its own range -- about one key per fine bin
+  // even when a few outliers stretch the range.  red[64 ..) holds the coarse
+  // counts, then their exclusive scan.
+  uint32_t* coarse = red + 64;
+  for (int j = t; j < kCoarse; j += T) coarse[j] = 0;
+  __syncthreads();
+  uint32_t cb[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    cb[p] = (uint32_t)(((uint64_t)(hi - key_ord(key[p])) * kCoarse) / span);
+    hist_add(coarse, cb[p], t * P + p < cnt);
+  }
+  __syncthreads();
+  if (t < kWave) {  // lane l scans coarse bins [4l, 4l + 4)
+    uint32_t c4[4], s4 = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      c4[j] = coarse[4 * t + j];
+      s4 += c4[j];
+    }
+    uint32_t run = (uint32_t)wave_incl_scan((int)s4) - s4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      coarse[kCoarse + 4 * t + j] = run;  // start of coarse bin j
+      run += c4[j];
+    }
+  }
+  __syncthreads();
   uint32_t bin[P];
 #pragma unroll
   for (int p = 0; p < P; ++p) {
-    bin[p] = (uint32_t)(((uint64_t)(hi - key_ord(key[p])) * (uint64_t)kFinMax) / span);
+    const uint64_t rel = hi - key_ord(key[p]);
+    const uint32_t c = cb[p];
+    // coarse bin c covers rel in [ceil(c * span / K), ceil((c + 1) * span / K))
+    const uint64_t c_lo = (c * span + kCoarse - 1) / kCoarse;
+    const uint64_t c_hi = ((c + 1) * span + kCoarse - 1) / kCoarse;
+    const uint32_t cn = coarse[c];
+    const uint32_t f = (uint32_t)(((rel - c_lo) * cn) / max<uint64_t>(c_hi - c_lo, 1));
+    bin[p] = coarse[kCoarse + c] + min(f, cn > 0 ? cn - 1 : 0u);
     hist_add(bins, bin[p], t * P + p < cnt);
   }
   __syncthreads();
@@ -487,7 +520,10 @@ __device__ void sort_and_write(uint64_t* cand, int cnt, int k, const float* __re
     uint32_t idx = key_idx(cand[i]);
     idx = idx < (uint32_t)n ? idx : 0u;  // only reachable with NaN inputs
     out_idx[i] = (int32_t)idx;
-    reinterpret_cast<uint32_t*>(out_vals)[i] = reinterpret_cast<const uint32_t*>(xr)[idx];
+    // the order key gives the value back, except the sign of a zero
+    const uint32_t o = key_ord(cand[i]);
+    reinterpret_cast<uint32_t*>(out_vals)[i] =
+        o == 0x80000000u ? reinterpret_cast<const uint32_t*>(xr)[idx] : bits_from_ord(o);
   }
 }
 
@@ -510,7 +546,7 @@ __global__ __launch_bounds__(kFinT) void wide_final_kernel(const float* __restri
   constexpr int T = kFinT;
   __shared__ uint64_t cand[kFinMax];
   __shared__ uint32_t bins[kFinMax];
-  __shared__ uint32_t red[64];
+  __shared__ uint32_t red[64 + 2 * kCoarse];
   uint32_t* hist = bins;  // the radix selects run before the sort
   uint32_t* ctl = bins + 256;
   const int t = threadIdx.x;
