@@ -488,27 +488,34 @@ __global__ __launch_bounds__(kRowT) void row_exact_kernel(const uint8_t* __restr
     }
   };
 
+  // Full tiles through two register sets: the next tile's loads are always
+  // in flight while a tile is filtered.  The prefetch is unconditional (past
+  // the last full tile it re-reads tile 0) so that the code stays straight
+  // and the wait before a tile covers only that tile's own loads.
   const int nfull = n / TILE;
-  uint4 w[U];
+  uint4 wa[U], wb[U];
+  auto load_full = [&](uint4 (&w)[U], int it) {
+    const int64_t base = (int64_t)(it < nfull ? it : 0) * TILE;
+#pragma unroll
+    for (int u = 0; u < U; ++u) w[u] = *reinterpret_cast<const uint4*>(xr + (base + (int64_t)u * T * V + t * V) * ES);
+  };
+  int it = 0;
   if (nfull > 0) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) w[u] = *reinterpret_cast<const uint4*>(xr + ((int64_t)u * T * V + t * V) * ES);
-  }
-  for (int it = 0; it < nfull; ++it) {
-    const int64_t base = (int64_t)it * TILE;
-    uint4 wn[U];
-    if (it + 1 < nfull) {
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        wn[u] = *reinterpret_cast<const uint4*>(xr + (base + TILE + (int64_t)u * T * V + t * V) * ES);
+    load_full(wa, 0);
+    for (; it + 1 < nfull; it += 2) {
+      load_full(wb, it + 1);
+      tile(wa, (int64_t)it * TILE, std::true_type{});
+      load_full(wa, it + 2);
+      tile(wb, (int64_t)(it + 1) * TILE, std::true_type{});
     }
-    tile(w, base, std::true_type{});
-#pragma unroll
-    for (int u = 0; u < U; ++u) w[u] = wn[u];
+    if (it < nfull) {
+      tile(wa, (int64_t)it * TILE, std::true_type{});
+      ++it;
+    }
   }
   if ((int64_t)nfull * TILE < n) {
-    load_tile<DT, T>(xr, (int64_t)nfull * TILE, n, t, w);
-    tile(w, (int64_t)nfull * TILE, std::false_type{});
+    load_tile<DT, T>(xr, (int64_t)nfull * TILE, n, t, wa);
+    tile(wa, (int64_t)nfull * TILE, std::false_type{});
   }
 
   // Each wave reduces its region to its top-min(k, cnt), sorted: a run of 64;
