@@ -432,6 +432,13 @@ __global__ __launch_bounds__(kFinishThreads) void bucket_finish_kernel(const uin
     const uint64_t thr = block_kth_key<T>(cand, cnt, k, hist, ctl);
     cnt = block_compact_ge<T, kFinishMaxCand / T>(cand, cnt, thr, ctl);
   }
+  if (cnt <= kWave) {  // one wave sorts the (at most 64) keys in registers
+    if (t < kWave) {
+      const uint64_t key = wave_sort64_desc(t < cnt ? cand[t] : 0);
+      if (t < k) write_result(out_vals, out_idx, (int64_t)row * k + t, xr, dt, key);
+    }
+    return;
+  }
   int npow = 1;
   while (npow < k) npow <<= 1;
   for (int i = cnt + t; i < npow; i += T) cand[i] = 0;
