@@ -489,28 +489,32 @@ __global__ __launch_bounds__(kRowT) void row_exact_kernel(const uint8_t* __restr
   };
 
   // Full tiles through two register sets: the next tile's loads are always
-  // in flight while a tile is filtered.  The prefetch is unconditional (past
-  // the last full tile it re-reads tile 0) so that the code stays straight
-  // and the wait before a tile covers only that tile's own loads.
+  // in flight while a tile is filtered.  Inside the loop the prefetch is
+  // unconditional (the loop stops while tile it + 2 still exists), so the
+  // code stays straight and the wait before a tile covers only that tile's
+  // own loads; the last one or two tiles are handled after the loop.
   const int nfull = n / TILE;
   uint4 wa[U], wb[U];
   auto load_full = [&](uint4 (&w)[U], int it) {
-    const int64_t base = (int64_t)(it < nfull ? it : 0) * TILE;
+    const int64_t base = (int64_t)it * TILE;
 #pragma unroll
     for (int u = 0; u < U; ++u) w[u] = *reinterpret_cast<const uint4*>(xr + (base + (int64_t)u * T * V + t * V) * ES);
   };
-  int it = 0;
   if (nfull > 0) {
+    int it = 0;
     load_full(wa, 0);
-    for (; it + 1 < nfull; it += 2) {
+    for (; it + 2 < nfull; it += 2) {
       load_full(wb, it + 1);
       tile(wa, (int64_t)it * TILE, std::true_type{});
       load_full(wa, it + 2);
       tile(wb, (int64_t)(it + 1) * TILE, std::true_type{});
     }
-    if (it < nfull) {
+    if (it + 1 < nfull) {
+      load_full(wb, it + 1);
       tile(wa, (int64_t)it * TILE, std::true_type{});
-      ++it;
+      tile(wb, (int64_t)(it + 1) * TILE, std::true_type{});
+    } else {
+      tile(wa, (int64_t)it * TILE, std::true_type{});
     }
   }
   if ((int64_t)nfull * TILE < n) {
