@@ -532,6 +532,22 @@ def test_decode_small(gpu, hq, hkv, ctx, k_sel, b, kb):
     _decode_check(q, K, V, k_sel, b, kb)
 
 
+@pytest.mark.parametrize("hq,hkv,ctx,k_sel,b,kb", [
+    (8, 1, 3007, 100, 1, 100),    # the largest query-head group (G = 8), exact Top-K (certified)
+    (16, 2, 2049, 64, 32, 4),     # G = 8, bucketed with the final stage, ragged context
+    (8, 1, 777, 77, 11, 7),       # G = 8, non-power-of-two b and k_b
+    (2, 2, 65, 64, 1, 64),        # context barely above K
+    (4, 4, 5000, 1, 1, 1),        # K = 1: the arg-max key
+])
+def test_decode_groups_and_edges(gpu, hq, hkv, ctx, k_sel, b, kb):
+    g = torch.Generator(device="cpu").manual_seed(ctx + hq + k_sel)
+    q = torch.randn((2, hq, 128), generator=g).to(torch.bfloat16).to(gpu)
+    K = torch.randn((2, hkv, ctx, 128), generator=g).to(torch.bfloat16).to(gpu)
+    V = torch.randn((2, hkv, ctx, 128), generator=g).to(torch.bfloat16).to(gpu)
+    print("case", hq, hkv, ctx, k_sel, b, kb, flush=True)
+    _decode_check(q, K, V, k_sel, b, kb)
+
+
 def test_decode_ctx_stride(gpu):
     g = torch.Generator(device="cpu").manual_seed(3)
     q = torch.randn((1, 4, 128), generator=g).to(torch.bfloat16).to(gpu)
