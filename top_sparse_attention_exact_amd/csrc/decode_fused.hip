@@ -226,36 +226,46 @@ __global__ __launch_bounds__(kT1M, 2) void decode_select_mfma_kernel(const uint1
     for (int j = 0; j < KB; ++j) qq[i][j] = 0;
   const int npairs = G * b;
 
+  // 16-key groups through two register sets: a group's loads are in flight
+  // while the previous group is on the matrix cores, and the next step's
+  // first group loads during this step's fold (after the score stores, which
+  // share the load counter).  Loads past the chunk are masked off.
+  static_assert(GR == 4, "the group schedule below is written for 4 groups per wave and step");
+  uint4 kv0[KS], kv1[KS];
+  auto load_grp = [&](uint4 (&kv)[KS], int s0x, int gi) {
+    const int s1x = min(j1, s0x + kSub);
+    const int jj = s0x + (wave * GR + gi) * 16 + col;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kv[ks] = jj < s1x ? *reinterpret_cast<const uint4*>(kh + (int64_t)jj * kD + 32 * ks) : make_uint4(0, 0, 0, 0);
+  };
   int buf = 0;
+  auto mma_grp = [&](const uint4 (&kv)[KS], int gi) {
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], __builtin_bit_cast(bf16x8_t, kv[ks]), acc, 0, 0, 0);
+    const int li = (wave * GR + gi) * 16 + col;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int g = 4 * (lane >> 4) + i;
+      if (g < G) sc[buf][g][li] = acc[i] * scale;
+    }
+  };
+  load_grp(kv0, j0, 0);
   for (int s0 = j0; s0 < j1; s0 += kSub) {
     const int s1 = min(j1, s0 + kSub);
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {  // two 16-key groups in flight: fewer registers
-      uint4 kv[GR / 2][KS];
-#pragma unroll
-      for (int gh = 0; gh < GR / 2; ++gh) {
-        const int jj = s0 + (wave * GR + half * (GR / 2) + gh) * 16 + col;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          kv[gh][ks] = jj < s1 ? *reinterpret_cast<const uint4*>(kh + (int64_t)jj * kD + 32 * ks) : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int gh = 0; gh < GR / 2; ++gh) {
-        f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], __builtin_bit_cast(bf16x8_t, kv[gh][ks]), acc, 0, 0, 0);
-        const int li = (wave * GR + half * (GR / 2) + gh) * 16 + col;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int g = 4 * (lane >> 4) + i;
-          if (g < G) sc[buf][g][li] = acc[i] * scale;
-        }
-      }
-    }
+    load_grp(kv1, s0, 1);
+    mma_grp(kv0, 0);
+    load_grp(kv0, s0, 2);
+    mma_grp(kv1, 1);
+    load_grp(kv1, s0, 3);
+    mma_grp(kv0, 2);
+    mma_grp(kv1, 3);
     lds_barrier();
     const int nk = s1 - s0;
     if (scores != nullptr) dump_scores<kT1M>(scores, (int64_t)(bi * hq + h * G), ctx, s0, G, nk, sc[buf]);
+    load_grp(kv0, s0 + kSub, 0);
     // fold the staged scores of the owned (head, bucket) pairs: bucket r
     // holds keys j with j mod b == r
     const int rs = b > 0 ? s0 % b : 0;  // b == 0: scores only
