@@ -548,6 +548,17 @@ def test_decode_groups_and_edges(gpu, hq, hkv, ctx, k_sel, b, kb):
     _decode_check(q, K, V, k_sel, b, kb)
 
 
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 2)])
+def test_decode_exact_large_k(gpu, hq, hkv):
+    """Exact Top-K with K = ctx / 2: no certified plan fits, so the decode runs
+    as separate passes (all scores, exact selection, softmax-V)."""
+    g = torch.Generator(device="cpu").manual_seed(hq * 7 + hkv)
+    q = torch.randn((1, hq, 128), generator=g).to(torch.bfloat16).to(gpu)
+    K = torch.randn((1, hkv, 4096, 128), generator=g).to(torch.bfloat16).to(gpu)
+    V = torch.randn((1, hkv, 4096, 128), generator=g).to(torch.bfloat16).to(gpu)
+    _decode_check(q, K, V, 2048, 1, 2048)
+
+
 def test_decode_ctx_stride(gpu):
     g = torch.Generator(device="cpu").manual_seed(3)
     q = torch.randn((1, 4, 128), generator=g).to(torch.bfloat16).to(gpu)
