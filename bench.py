@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", default="all",
                     help="all | sel | exact | b64k1 | b128k2 | decode | mha | gqa | sel4k | wide | assign | tradeoff | graph "
-                         "| sweep (not in all) | copy")
+                         "| stream | sweep (not in all) | copy")
     ap.add_argument("--no-flush", action="store_true", help="no cache flush before the single-call latency runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
@@ -214,6 +214,7 @@ def selection_step(args, timer):
         modes[name] = {
             "us": round(us[name], 2),
             "us_cold": round(float(np.mean(cold[name])), 2),
+            "us_cold_median": round(float(np.median(cold[name])), 2),
             "us_cold_p10": round(float(np.percentile(cold[name], 10)), 2),
             "us_cold_p90": round(float(np.percentile(cold[name], 90)), 2),
             "elements_per_s": m * n / t,
@@ -519,6 +520,51 @@ def graph_leg(args, timer):
     return res
 
 
+STREAM_SIZES = (("64MiB", 64 << 20), ("256MiB", 256 << 20), ("1GiB", 1 << 30), ("4GiB", 4 << 30))
+
+
+def stream_calibration(args, timer):
+    """A plain streaming-read kernel (calib/stream_read.hip) at the input
+    sizes of the workloads, best over five grid sizes: the rate a kernel
+    that only reads its input reaches on this GPU, the practical ceiling the
+    kernels are compared with beside the 8 TB/s peak.  Buffers below 640 MB
+    rotate over copies (no launch finds its input in the Infinity Cache)."""
+    import ctypes
+
+    import torch
+
+    from top_sparse_attention_exact_amd import build as _build
+
+    calib = ctypes.CDLL(_build.CALIB)
+    calib.atopk_calib_stream_read.restype = ctypes.c_int
+    calib.atopk_calib_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                               ctypes.c_void_p]
+    block_counts = (1024, 2048, 4096, 8192, 16384)
+    sink = torch.empty(max(block_counts), dtype=torch.int32, device="cuda")
+    res = {}
+    for name, nbytes in STREAM_SIZES:
+        x = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+        xs = copies(x, ROTATE_BYTES)
+
+        def call(i, xs=xs, nbytes=nbytes, blocks=1024):
+            st = calib.atopk_calib_stream_read(ctypes.c_void_p(xs[i % len(xs)].data_ptr()), nbytes, blocks,
+                                               ctypes.c_void_p(sink.data_ptr()),
+                                               ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            if st != 0:
+                raise RuntimeError("stream read launch failed: %d" % st)
+
+        calls = [("b%d" % nb, (lambda i, nb=nb: call(i, blocks=nb))) for nb in block_counts]
+        us, _ = timer.stream(calls, max(3, min(args.steps, 10)), 2)
+        best = min(us, key=us.get)
+        res[name] = {"bytes": nbytes, "us": round(us[best], 2), "workgroups": int(best[1:]),
+                     "gbps": nbytes / (us[best] * 1e-6) / 1e9,
+                     "frac_hbm_peak": nbytes / (us[best] * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                     "us_by_workgroups": {k[1:]: round(v, 2) for k, v in us.items()}}
+        del x, xs
+        torch.cuda.empty_cache()
+    return res
+
+
 def copy_calibration(args, timer):
     """A plain elementwise copy (negation) of 256 MiB, the yardstick that
     scales the rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes."""
@@ -590,6 +636,7 @@ def main():
     trade = tradeoff(args, timer) if args.only in ("all", "tradeoff") else None
     swp = sweep(args, timer) if args.only == "sweep" else None
     graph = graph_leg(args, timer) if args.only in ("all", "graph") else None
+    stream = stream_calibration(args, timer) if args.only in ("all", "stream") else None
 
     line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
@@ -619,7 +666,7 @@ def main():
     elif not dec and not other:
         line.update({"value": None, "unit": "elements/s", "ms_per_step": None,
                      "config": {"workload": "vocab-128k" if assign or graph else
-                                ("vocab-sampling, kg-2.65m" if trade else "sweep")}})
+                                ("vocab-sampling, kg-2.65m" if trade else ("stream read" if stream else "sweep"))}})
     elif dec:
         first = next(iter(dec.values()))
         line.update({"value": first["bucketed"]["scores_per_s"], "unit": "scores/s",
@@ -640,6 +687,10 @@ def main():
         line["sweep"] = swp
     if graph is not None:
         line["graph"] = graph
+    if stream is not None:
+        line["stream_read"] = stream
+        if "roofline" in line:
+            line["roofline"]["stream_read_64MiB_gbps"] = stream["64MiB"]["gbps"]
     if sel is not None and not args.no_cpu_baseline:
         cpu, ref = cpu_leg(sel, args.cpu_seconds)
         line["cpu_baseline"] = cpu

@@ -35,9 +35,15 @@ def hipcc():
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose=False):
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + FLAGS + ["-I", INCLUDE, "-I", CSRC] + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
+# The streaming-read yardstick bench.py measures the kernels against (not
+# part of the library).
+CALIB = os.path.join(HERE, "libatopk_calib.so")
+CALIB_SOURCES = [os.path.join(HERE, "calib", "stream_read.hip")]
+
+
+def _compile(out, sources, includes, verbose):
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [hipcc()] + FLAGS + [a for inc in includes for a in ("-I", inc)] + sources + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -45,8 +51,13 @@ def build(verbose=False):
         sys.stderr.write(res.stdout + res.stderr)
         if os.path.exists(tmp):
             os.remove(tmp)
-        raise RuntimeError("hipcc failed building libatopk.so")
-    os.replace(tmp, LIB)
+        raise RuntimeError("hipcc failed building " + os.path.basename(out))
+    os.replace(tmp, out)
+
+
+def build(verbose=False):
+    _compile(LIB, [os.path.join(CSRC, s) for s in SOURCES], [INCLUDE, CSRC], verbose)
+    _compile(CALIB, CALIB_SOURCES, [], verbose)
     return LIB
 
 
