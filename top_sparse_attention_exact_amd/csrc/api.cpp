@@ -231,7 +231,11 @@ int run_bucketed(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, in
   uint8_t* w = static_cast<uint8_t*>(ws);
   uint64_t* lists = reinterpret_cast<uint64_t*>(w + L.lists_off);
   uint64_t* cand = L.cand_bytes ? reinterpret_cast<uint64_t*>(w + L.cand_off) : nullptr;
-  if (launch_bucket_stage1(L.plan, x, dtype, m, n, ldx, b, kb, lists, s) != hipSuccess) return ATOPK_ERR_HIP;
+  bool direct = false;
+  if (launch_bucket_stage1(L.plan, x, dtype, m, n, ldx, b, kb, lists, s, k, final_exact, out_vals, out_idx,
+                           cand ? nullptr : &direct) != hipSuccess)
+    return ATOPK_ERR_HIP;
+  if (direct) return ATOPK_OK;
   if (launch_bucket_finish(lists, L.plan.lists_per_row, m, n, b, kb, k, final_exact, x, dtype, ldx, out_vals, out_idx,
                            cand, s) != hipSuccess)
     return ATOPK_ERR_HIP;

@@ -25,8 +25,14 @@ struct BucketPlan {
 };
 BucketPlan plan_bucketed(int dtype, int64_t m, int64_t n, int64_t b, int64_t kb, bool aligned);
 
+// With direct_done non-null, stage 1 may write the result itself (one split
+// per row, lists merged in LDS: the bucket-major candidates, or the sorted
+// top-k when b * kb <= 64); *direct_done then tells the caller to skip the
+// finish.
 hipError_t launch_bucket_stage1(const BucketPlan& p, const void* x, int dtype, int64_t m, int64_t n,
-                                int64_t ldx, int64_t b, int64_t kb, uint64_t* lists, hipStream_t s);
+                                int64_t ldx, int64_t b, int64_t kb, uint64_t* lists, hipStream_t s, int64_t k = 0,
+                                int final_exact = 0, void* out_vals = nullptr, int32_t* out_idx = nullptr,
+                                bool* direct_done = nullptr);
 
 // Merge the lists of every bucket; then either write the bucket-major
 // candidates (final_exact == 0), or select and sort the final top-k

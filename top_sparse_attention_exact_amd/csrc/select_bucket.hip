@@ -69,11 +69,28 @@ __device__ __forceinline__ void consume_vec(uint64_t (&q)[VecOf<DT>::V][KB], con
   for (int e = 0; e < VecOf<DT>::V; ++e) queue_insert<KB>(q[e], make_key(ord_f32(elem_bits<DT>(w, e)), idx0 + e));
 }
 
+__device__ __forceinline__ void write_result(uint8_t* out_vals, int32_t* out_idx, int64_t o, const uint8_t* xr,
+                                             int dt, uint64_t key) {
+  const uint32_t idx = key_idx(key);
+  out_idx[o] = (int32_t)idx;
+  if (dt == IN_F32) {
+    reinterpret_cast<uint32_t*>(out_vals)[o] = reinterpret_cast<const uint32_t*>(xr)[idx];
+  } else {
+    reinterpret_cast<uint16_t*>(out_vals)[o] = reinterpret_cast<const uint16_t*>(xr)[idx];
+  }
+}
+
 template <int DT, int KB>
+// direct != 0 (one split per row, queues merged in LDS): the workgroup
+// writes the row's result itself instead of its lists -- direct == 1 the
+// bucket-major candidates (slot r * kb + j), direct == 2 the sorted top-k of
+// the b * kb <= 64 candidates (one wave sorts them in registers).
 __global__ __launch_bounds__(kStage1Threads) void bucket_stage1_kernel(const uint8_t* __restrict__ x, int64_t ld_bytes,
                                                                       int n, int b, int64_t chunk, int lds_merge,
                                                                       int lists_per_row,
-                                                                      uint64_t* __restrict__ lists) {
+                                                                      uint64_t* __restrict__ lists, int direct, int kb,
+                                                                      int k, uint8_t* __restrict__ out_vals,
+                                                                      int32_t* __restrict__ out_idx) {
   constexpr int T = kStage1Threads;
   constexpr int V = VecOf<DT>::V;
   constexpr int ES = VecOf<DT>::ES;
@@ -168,6 +185,35 @@ __global__ __launch_bounds__(kStage1Threads) void bucket_stage1_kernel(const uin
       }
     }
     __syncthreads();
+    constexpr int ES_ = VecOf<DT>::ES;
+    if (direct == 2) {  // b * kb <= 64 < T: thread r merges bucket r
+      uint64_t m[KB];
+#pragma unroll
+      for (int j = 0; j < KB; ++j) m[j] = 0;
+      if (t < b) {
+#pragma unroll
+        for (int j = 0; j < KB; ++j) m[j] = lds[(int64_t)t * KB + j];
+        for (int c = 1; c < ncopies; ++c) {
+          uint64_t o[KB];
+#pragma unroll
+          for (int j = 0; j < KB; ++j) o[j] = lds[((int64_t)c * b + t) * KB + j];
+          queue_merge<KB>(m, o);
+        }
+      }
+      __syncthreads();
+      if (t < b) {
+#pragma unroll
+        for (int j = 0; j < KB; ++j)
+          if (j < kb) lds[t * kb + j] = m[j];
+      }
+      __syncthreads();
+      if (t < kWave) {
+        const uint64_t key = wave_sort64_desc(t < b * kb ? lds[t] : 0);
+        if (t < k) write_result(out_vals, out_idx, (int64_t)row * k + t, xr, DT, key);
+      }
+      (void)ES_;
+      return;
+    }
     for (int r = t; r < b; r += T) {
       uint64_t a[KB];
 #pragma unroll
@@ -177,6 +223,13 @@ __global__ __launch_bounds__(kStage1Threads) void bucket_stage1_kernel(const uin
 #pragma unroll
         for (int j = 0; j < KB; ++j) o[j] = lds[((int64_t)c * b + r) * KB + j];
         queue_merge<KB>(a, o);
+      }
+      if (direct == 1) {
+        const int64_t nc = (int64_t)b * kb;
+#pragma unroll
+        for (int j = 0; j < KB; ++j)
+          if (j < kb) write_result(out_vals, out_idx, (int64_t)row * nc + (int64_t)r * kb + j, xr, DT, a[j]);
+        continue;
       }
       uint64_t* dst = lists + (((int64_t)row * lists_per_row + split) * b + r) * KB;
 #pragma unroll
@@ -233,16 +286,6 @@ __global__ __launch_bounds__(256) void bucket_generic_kernel(const uint8_t* __re
   for (int j = 0; j < KB; ++j) dst[j] = q[j];
 }
 
-__device__ __forceinline__ void write_result(uint8_t* out_vals, int32_t* out_idx, int64_t o, const uint8_t* xr,
-                                             int dt, uint64_t key) {
-  const uint32_t idx = key_idx(key);
-  out_idx[o] = (int32_t)idx;
-  if (dt == IN_F32) {
-    reinterpret_cast<uint32_t*>(out_vals)[o] = reinterpret_cast<const uint32_t*>(xr)[idx];
-  } else {
-    reinterpret_cast<uint16_t*>(out_vals)[o] = reinterpret_cast<const uint16_t*>(xr)[idx];
-  }
-}
 
 constexpr int kFinishThreads = 1024;
 
@@ -450,7 +493,8 @@ bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 
 template <int DT>
 hipError_t launch_stage1_dt(const BucketPlan& p, const void* x, int64_t m, int64_t n, int64_t ldx, int64_t b,
-                            int64_t kb, uint64_t* lists, hipStream_t s) {
+                            int64_t kb, uint64_t* lists, hipStream_t s, int64_t k, int final_exact, void* out_vals,
+                            int32_t* out_idx, bool* direct_done) {
   const int64_t ld_bytes = ldx * VecOf<DT>::ES;
   const uint8_t* xb = static_cast<const uint8_t*>(x);
   if (p.fast) {
@@ -459,11 +503,19 @@ hipError_t launch_stage1_dt(const BucketPlan& p, const void* x, int64_t m, int64
     const bool wave_has_all = kWave * V >= b;
     const int ncopies = wave_has_all ? kStage1Threads / kWave : (int)(W / b);
     const int lds_merge = (int64_t)ncopies * b * kb_slots(kb) * 8 <= kStage1LdsBytes;
+    int direct = 0;
+    if (direct_done != nullptr && p.splits == 1 && lds_merge) {
+      if (!final_exact) direct = 1;
+      else if (b * kb <= kWave && k <= kWave && k <= b * kb) direct = 2;
+    }
+    if (direct_done != nullptr) *direct_done = direct != 0;
+    uint8_t* ov = static_cast<uint8_t*>(out_vals);
     dim3 grid((unsigned)p.splits, (unsigned)m);
 #define ATOPK_S1(KBV)                                                                                          \
   case KBV:                                                                                                    \
     hipLaunchKernelGGL((bucket_stage1_kernel<DT, KBV>), grid, dim3(kStage1Threads), 0, s, xb, ld_bytes, (int)n, \
-                       (int)b, p.chunk, lds_merge, p.lists_per_row, lists);                                   \
+                       (int)b, p.chunk, lds_merge, p.lists_per_row, lists, direct, (int)kb, (int)k, ov,       \
+                       out_idx);                                                                              \
     break;
     switch (kb_slots(kb)) {
       ATOPK_S1(1) ATOPK_S1(2) ATOPK_S1(4) ATOPK_S1(8) ATOPK_S1(16)
@@ -527,9 +579,12 @@ BucketPlan plan_bucketed(int dtype, int64_t m, int64_t n, int64_t b, int64_t kb,
 }
 
 hipError_t launch_bucket_stage1(const BucketPlan& p, const void* x, int dtype, int64_t m, int64_t n, int64_t ldx,
-                                int64_t b, int64_t kb, uint64_t* lists, hipStream_t s) {
-  if (dtype == IN_F32) return launch_stage1_dt<IN_F32>(p, x, m, n, ldx, b, kb, lists, s);
-  return launch_stage1_dt<IN_BF16>(p, x, m, n, ldx, b, kb, lists, s);
+                                int64_t b, int64_t kb, uint64_t* lists, hipStream_t s, int64_t k, int final_exact,
+                                void* out_vals, int32_t* out_idx, bool* direct_done) {
+  if (direct_done != nullptr) *direct_done = false;
+  if (dtype == IN_F32)
+    return launch_stage1_dt<IN_F32>(p, x, m, n, ldx, b, kb, lists, s, k, final_exact, out_vals, out_idx, direct_done);
+  return launch_stage1_dt<IN_BF16>(p, x, m, n, ldx, b, kb, lists, s, k, final_exact, out_vals, out_idx, direct_done);
 }
 
 hipError_t launch_bucket_finish(const uint64_t* lists, int lists_per_row, int64_t m, int64_t n, int64_t b, int64_t kb,
