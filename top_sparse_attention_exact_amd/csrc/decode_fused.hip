@@ -349,7 +349,6 @@ __global__ __launch_bounds__(kT2) void decode_finish_kernel(const uint64_t* __re
   __shared__ uint32_t ctl[8];
   __shared__ uint32_t flg_r[kFlagMax];
   __shared__ uint64_t flg_c[kFlagMax];
-  __shared__ float acc_lds[kVGroups][kD];
   __shared__ float w_lds[kVGroups];
   __shared__ float red[T / kWave];
 
@@ -541,6 +540,10 @@ __global__ __launch_bounds__(kT2) void decode_finish_kernel(const uint64_t* __re
       wsum += w[u];
     }
   }
+  // the selected keys are no longer read: their LDS takes the partial sums
+  __syncthreads();
+  float (*acc_lds)[kD] = reinterpret_cast<float (*)[kD]>(cand);
+  static_assert(sizeof(cand) >= sizeof(float) * kVGroups * kD, "the partial sums fit in the key array");
 #pragma unroll
   for (int d = 0; d < 8; ++d) acc_lds[group][sub * 8 + d] = acc[d];
   if (sub == 0) w_lds[group] = wsum;

@@ -142,7 +142,6 @@ __global__ __launch_bounds__(kST) void rerank_select_kernel(const uint64_t* __re
                                                            uint16_t* __restrict__ out, int32_t* __restrict__ sel_idx) {
   constexpr int T = kST;
   __shared__ uint64_t keys[kRerankMaxCand];
-  __shared__ float acc_lds[kSGroups][kD];
   __shared__ uint32_t hist[256];
   __shared__ uint32_t ctl[8];
   __shared__ float w_lds[kSGroups];
@@ -223,6 +222,10 @@ __global__ __launch_bounds__(kST) void rerank_select_kernel(const uint64_t* __re
       wsum += w[u];
     }
   }
+  // the selected keys are no longer read: their LDS takes the partial sums
+  __syncthreads();
+  float (*acc_lds)[kD] = reinterpret_cast<float (*)[kD]>(keys);
+  static_assert(sizeof(keys) >= sizeof(float) * kSGroups * kD, "the partial sums fit in the key array");
 #pragma unroll
   for (int d = 0; d < 8; ++d) acc_lds[group][sub * 8 + d] = acc[d];
   if (sub == 0) w_lds[group] = wsum;
