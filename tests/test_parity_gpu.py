@@ -493,7 +493,7 @@ def _clear_gaps(s, k_sel, b, kb, gap=1e-3):
 
 @pytest.mark.parametrize("hq,hkv,ctx,k_sel,planted", [
     (2, 2, 3000, 64, "stride256"),    # one query head per KV head: a flagged bucket is rescored
-    (8, 2, 3000, 64, "stride256"),    # query-head groups: rescanned from the written scores
+    (8, 2, 3000, 64, "stride256"),    # query-head groups: a flagged bucket is rescored on the matrix cores
     (1, 1, 131072, 16, "mod8"),       # one bucket far above the rest: the rescan overflows, full-row fallback
     (4, 2, 131072, 64, "mod64lt5"),   # the same for query-head groups (5 buckets of 2048 keys)
 ])
@@ -519,6 +519,33 @@ def test_decode_exact_certified_planted(gpu, hq, hkv, ctx, k_sel, planted):
     q, K, V = (t.to(torch.bfloat16).to(gpu) for t in (q, K, V))
     print("case", hq, hkv, ctx, k_sel, planted, flush=True)
     _decode_check(q, K, V, k_sel, 1, k_sel)
+
+
+def test_decode_scores_position_invariant(gpu):
+    """The matrix-core scores of query-head groups do not depend on where a key
+    sits among the 16 columns of an MFMA tile, or in which step or chunk it is
+    scored: copies of a key row at other positions get bit-identical scores.
+    The certified exact decode relies on it when it rescores flagged buckets
+    with their keys in other columns; the copies here are the top keys, so
+    their exact ties decide the Top-K and are rescanned."""
+    g = torch.Generator(device="cpu").manual_seed(11)
+    hq, hkv, ctx, k_sel = 8, 2, 6000, 64
+    G = hq // hkv
+    q = torch.randn((1, hq, 128), generator=g)
+    K = torch.randn((1, hkv, ctx, 128), generator=g) * 0.5
+    V = torch.randn((1, hkv, ctx, 128), generator=g)
+    src = torch.arange(40) * 37 + 5
+    offs = [1, 3, 6, 16, 529, 4103]
+    for h in range(hkv):
+        K[0, h, src] = 2.0 * q[0, h * G + 1] + 0.3 * torch.randn((len(src), 128), generator=g)
+        for o in offs:
+            K[0, h, src + o] = K[0, h, src]
+    q, K, V = (t.to(torch.bfloat16).to(gpu) for t in (q, K, V))
+    for b, kb in [(1, k_sel), (16, 8)]:
+        _, _, sc = _decode_check(q, K, V, k_sel, b, kb)
+        s = sc[0].cpu().numpy().view(np.uint32)
+        for o in offs:
+            np.testing.assert_array_equal(s[:, src.numpy() + o], s[:, src.numpy()])
 
 
 @pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 2), (6, 2)])

@@ -315,31 +315,29 @@ struct DecodeLayout {
   DecodePlan plan;
   bool certified;                                          // exact Top-K from a fused bucketed pass
   int64_t cb, ckb;                                         // its (b, kb)
-  int cmode;                                               // 1: scores written and rescanned, 2: recomputed
+  int cmode;                                               // rescan on the matrix cores (1) or dot products (2)
   size_t partial_off;                                      // fused path
-  size_t scores_off, vals_off, idx_off, sel_ws_off;        // separate passes (scores_off also certified)
+  size_t scores_off, vals_off, idx_off, sel_ws_off;        // separate passes; scores_off also the certified fallback rows
   size_t sel_ws_bytes;
   size_t total;
 };
 
 // The exact Top-K of a decode as a fused bucketed pass plus the finish's
-// certification.  Query-head groups (scores on the matrix cores): k_b = 4,
-// every score written out and rescanned from there; the smallest b the
-// fused kernels take whose expected rescan (buckets to rescan times keys
-// per bucket, on iid scores) stays below 4096 scores per head.  One query
-// head per KV head: k_b = 8 and no score write; the finish recomputes a
-// flagged bucket's scores, so b is the smallest whose expected number of
-// flagged buckets stays below 1/16 per head.
+// certification: k_b = 8 and the smallest b the fused kernels take whose
+// expected number of flagged buckets (on iid scores) stays at most one per
+// head and whose expected rescan (that number times a bucket's length) stays
+// at most 1024 keys.  No score is written: the finish recomputes a flagged
+// bucket's scores with the scoring kernel's arithmetic (matrix cores for
+// query-head groups, mode 1; 16-lane dot products otherwise, mode 2).
 bool plan_decode_certified(int64_t batch, int64_t hq, int64_t hkv, int64_t ctx, int64_t k_sel, int64_t* b_out,
                            int64_t* kb_out, int* mode) {
   const bool groups = hq / hkv >= 2;
-  const int64_t kb = groups ? 4 : 8;
+  const int64_t kb = 8;
   for (int64_t b = std::max<int64_t>(2, pow2_ceil((k_sel + kb - 1) / kb)); b * kb <= kFinishMaxCand; b *= 2) {
     if (b > ctx || kb > ctx / b) break;
     if (!plan_decode(batch, hq, hkv, ctx, k_sel, b, kb).fused) break;
     const double e = saturated_buckets(k_sel, b, kb);
-    const bool ok = groups ? (e <= 16.0 && e * (double)((ctx + b - 1) / b) <= 4096.0) : e <= 1.0 / 16.0;
-    if (ok) {
+    if (e <= 1.0 && e * (double)((ctx + b - 1) / b) <= 1024.0) {
       *b_out = b;
       *kb_out = kb;
       *mode = groups ? 1 : 2;
@@ -556,8 +554,7 @@ int atopk_sparse_attn_decode(const void* q, const void* K, const void* V, int64_
       float* buf = scores ? scores : reinterpret_cast<float*>(w + L.scores_off);
       return hip_status(launch_decode_fused(L.plan, q16, k16, v16, batch, hq, hkv, ctx, ctx_stride, scale, k_sel, L.cb,
                                             L.ckb, reinterpret_cast<uint64_t*>(w + L.partial_off),
-                                            static_cast<uint16_t*>(out), sel_idx, L.cmode == 1 ? buf : scores, L.cmode,
-                                            buf, s));
+                                            static_cast<uint16_t*>(out), sel_idx, scores, L.cmode, buf, s));
     }
     if (L.plan.fused) {
       return hip_status(launch_decode_fused(L.plan, q16, k16, v16, batch, hq, hkv, ctx, ctx_stride, scale, k_sel, b,

@@ -103,6 +103,10 @@ __device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// Lane 0's value for the whole wave (a scalar read, no LDS round trip; lane
+// 0 must be active).
+__device__ __forceinline__ uint32_t wave_lane0(uint32_t v) { return (uint32_t)__builtin_amdgcn_readlane((int)v, 0); }
+
 // Inclusive prefix sum over the wave.
 __device__ __forceinline__ int wave_incl_scan(int v) {
   const int l = lane_id();
@@ -273,8 +277,10 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool add)
 }
 
 // The threshold key t such that exactly k of the n unique keys in `keys`
-// (LDS) are >= t (radix select, 8-bit digits from the top).  `hist` is a
-// 256-entry LDS array, `ctl` 4 LDS words.
+// (LDS) are >= t (radix select, 8-bit digits from the top).  Once at most 64
+// keys share the selected prefix, they are gathered into `hist` and one wave
+// ranks them, which ends the select in place of the remaining digit passes.
+// `hist` is a 256-entry LDS array, `ctl` 4 LDS words.
 template <int T>
 __device__ uint64_t block_kth_key(const uint64_t* keys, int n, int k, uint32_t* hist, uint32_t* ctl) {
   const int tid = threadIdx.x;
@@ -284,11 +290,18 @@ __device__ uint64_t block_kth_key(const uint64_t* keys, int n, int k, uint32_t* 
     for (int i = tid; i < 256; i += T) hist[i] = 0;
     __syncthreads();
     const uint64_t hi_prefix = (shift == 56) ? 0 : (prefix >> (shift + 8));
-    for (int i0 = 0; i0 < n; i0 += T) {
-      const int i = i0 + tid;
-      const uint64_t key = i < n ? keys[i] : 0;
-      const bool match = i < n && ((shift == 56) || ((key >> (shift + 8)) == hi_prefix));
-      hist_add(hist, (uint32_t)(key >> shift) & 255u, match);
+    for (int i0 = 0; i0 < n; i0 += 2 * T) {
+      uint64_t kk[2];  // two loads in flight
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int i = i0 + u * T + tid;
+        kk[u] = i < n ? keys[i] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const bool match = i0 + u * T + tid < n && ((shift == 56) || ((kk[u] >> (shift + 8)) == hi_prefix));
+        hist_add(hist, (uint32_t)(kk[u] >> shift) & 255u, match);
+      }
     }
     __syncthreads();
     if (tid < kWave) {
@@ -318,6 +331,7 @@ __device__ uint64_t block_kth_key(const uint64_t* keys, int n, int k, uint32_t* 
         ctl[0] = (uint32_t)(d - 1);
         ctl[1] = (uint32_t)(rem - acc);
         ctl[2] = cnt;
+        ctl[3] = 0;
       }
     }
     __syncthreads();
@@ -328,6 +342,49 @@ __device__ uint64_t block_kth_key(const uint64_t* keys, int n, int k, uint32_t* 
     prefix |= (uint64_t)digit << shift;
     rem = new_rem;
     if ((int)cnt == rem) break;  // every key with this prefix is in
+    if (cnt <= (uint32_t)kWave && shift > 0) {
+      // gather the keys with the prefix (two 32-bit words each)
+      const uint64_t want = prefix >> shift;
+      for (int i0 = 0; i0 < n; i0 += T) {
+        const int i = i0 + tid;
+        const uint64_t key = i < n ? keys[i] : 0;
+        const bool m = i < n && (key >> shift) == want;
+        const uint64_t msk = __ballot(m);
+        if (msk) {
+          uint32_t pos = 0;
+          if (lane_id() == 0) pos = atomicAdd(&ctl[3], (uint32_t)__popcll(msk));
+          pos = wave_lane0(pos);
+          if (m) {
+            const uint32_t slot = pos + lanes_below(msk);
+            hist[2 * slot] = (uint32_t)key;
+            hist[2 * slot + 1] = (uint32_t)(key >> 32);
+          }
+        }
+      }
+      __syncthreads();
+      if (tid < kWave) {
+        // lane l holds gathered key l; the rem-th largest has fewer than rem
+        // keys above it and at least rem at or above it
+        const bool own = tid < (int)cnt;
+        const uint32_t lo = own ? hist[2 * tid] : 0u, hi = own ? hist[2 * tid + 1] : 0u;
+        const uint64_t mine = ((uint64_t)hi << 32) | lo;
+        int above = 0, same = 0;
+        for (int j = 0; j < (int)cnt; ++j) {
+          const uint64_t o = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, j) << 32) |
+                             (uint32_t)__builtin_amdgcn_readlane((int)lo, j);
+          above += o > mine;
+          same += o == mine;
+        }
+        if (own && above < rem && rem <= above + same) {
+          ctl[0] = lo;
+          ctl[1] = hi;
+        }
+      }
+      __syncthreads();
+      const uint64_t t = ((uint64_t)ctl[1] << 32) | ctl[0];
+      __syncthreads();
+      return t;
+    }
   }
   return prefix;
 }
@@ -370,15 +427,25 @@ __device__ int block_compact_ge(uint64_t* keys, int n, uint64_t thr, uint32_t* c
   }
   if (tid == 0) ctl[0] = 0;
   __syncthreads();
+  // one LDS atomic per wave for every four slots' kept keys
 #pragma unroll
-  for (int j = 0; j < MAXPER; ++j) {
-    bool keep = v[j] != 0 && v[j] >= thr;
-    uint64_t mask = __ballot(keep);
-    if (mask) {
+  for (int j0 = 0; j0 < MAXPER; j0 += 4) {
+    uint64_t masks[4];
+    uint32_t total = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      masks[j] = j0 + j < MAXPER ? __ballot(v[j0 + j] != 0 && v[j0 + j] >= thr) : 0;
+      total += (uint32_t)__popcll(masks[j]);
+    }
+    if (total) {
       uint32_t pos = 0;
-      if (lane_id() == 0) pos = atomicAdd(&ctl[0], (uint32_t)__popcll(mask));
-      pos = __shfl(pos, 0, kWave);
-      if (keep) keys[pos + lanes_below(mask)] = v[j];
+      if (lane_id() == 0) pos = atomicAdd(&ctl[0], total);
+      pos = wave_lane0(pos);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if ((masks[j] >> lane_id()) & 1) keys[pos + lanes_below(masks[j])] = v[j0 + j];
+        pos += (uint32_t)__popcll(masks[j]);
+      }
     }
   }
   __syncthreads();
@@ -469,7 +536,7 @@ __device__ void block_row_topk(Ord&& ord_at, int n, int k, uint64_t* cand, uint3
     if (m) {
       uint32_t pos = 0;
       if (lane_id() == 0) pos = atomicAdd(&ctl[2], (uint32_t)__popcll(m));
-      pos = __shfl(pos, 0, kWave);
+      pos = wave_lane0(pos);
       if (keep) cand[pos + lanes_below(m)] = make_key(o, (uint32_t)i);
     }
   }

@@ -307,10 +307,10 @@ __device__ __noinline__ void decode_row_fallback(const float* srow, int ctx, int
   block_row_topk<kT2>([&](int i) { return ord_f32(__float_as_uint(srow[i])); }, ctx, k, cand, hist, ctl);
 }
 
-// Without stored scores (one query head per KV head), for a rescan that
-// overflows: the workgroup recomputes every score of its head exactly as the
-// scoring kernel does (16-lane groups) into its own row `srow` of the
-// workspace, then selects from that row.
+// For a rescan that overflows (one query head per KV head): the workgroup
+// recomputes every score of its head exactly as the scoring kernel does
+// (16-lane groups) into its own row `srow` of the workspace, then selects
+// from that row.
 __device__ __noinline__ void decode_fill_scores(const uint16_t* qrow, const uint16_t* krow, float scale, int ctx,
                                                 float* srow) {
   const int t = threadIdx.x;
@@ -326,15 +326,150 @@ __device__ __noinline__ void decode_fill_scores(const uint16_t* qrow, const uint
   __syncthreads();
 }
 
+// Matrix-core counterpart of decode_fill_scores for query-head groups: the
+// scoring kernel's own v_mfma_f32_16x16x32_bf16 chain (the G query rows of
+// the KV head as A rows 0..G-1, 16 keys as B, the k steps in order from a zero
+// accumulator, then the scaling), row g of the result to `srow`.
+__device__ __noinline__ void decode_fill_scores_mfma(const uint16_t* qg, int G, int g, const uint16_t* kh, float scale,
+                                                     int ctx, float* srow) {
+  constexpr int KS = kD / 32;
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int col = lane & 15, kq = 8 * (lane >> 4);
+  bf16x8_t qa[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    qa[ks] = __builtin_bit_cast(bf16x8_t, col < G ? *reinterpret_cast<const uint4*>(qg + (int64_t)col * kD + 32 * ks + kq)
+                                                  : make_uint4(0, 0, 0, 0));
+  const bool mine = (lane >> 4) == (g >> 2);  // the lanes that hold C row g
+  for (int j0 = 0; j0 < ctx; j0 += kT2 / kWave * 16) {
+    const int j = j0 + wave * 16 + col;
+    uint4 kv[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kv[ks] = j < ctx ? *reinterpret_cast<const uint4*>(kh + (int64_t)j * kD + 32 * ks + kq) : make_uint4(0, 0, 0, 0);
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], __builtin_bit_cast(bf16x8_t, kv[ks]), acc, 0, 0, 0);
+    if (mine && j < ctx) srow[j] = acc[g & 3] * scale;
+  }
+  __threadfence_block();
+  __syncthreads();
+}
+
+// Keys that a rescan keeps go after the k_sel selected ones (ctl[6] counts
+// them; slots past the LDS array are dropped and the count reports the
+// overflow).  Called by every lane of the wave.
+__device__ __forceinline__ void append_kept(bool keep, uint64_t key, int k_sel, uint64_t* cand, uint32_t* ctl) {
+  const uint64_t msk = __ballot(keep);
+  if (msk) {
+    uint32_t pos = 0;
+    if (lane_id() == 0) pos = atomicAdd(&ctl[6], (uint32_t)__popcll(msk));
+    pos = wave_lane0(pos);
+    const uint32_t slot = (uint32_t)k_sel + pos + lanes_below(msk);
+    if (keep && slot < (uint32_t)kMaxCand) cand[slot] = key;
+  }
+}
+
+// Slot sl of the flagged buckets' keys: bucket f = sl / S, key
+// r_f + (sl % S) * b with S = ceil(ctx / b); ctx for a slot past the list or
+// past the context.
+__device__ __forceinline__ int flagged_key(int sl, int total, int S, int b, const uint32_t* flg_r, int* f) {
+  *f = sl < total ? sl / S : 0;
+  return sl < total ? (int)flg_r[*f] + (sl - *f * S) * b : INT32_MAX;
+}
+
+// Rescan of the flagged buckets with one query head per KV head: 16-lane
+// groups recompute the scores with the scoring kernel's arithmetic (packed
+// bf16 dot products, the same row sum, the same scaling), U keys per group
+// and step so that their loads are in flight together.
+__device__ __forceinline__ void decode_rescan_dot(const uint16_t* qrow, const uint16_t* kh, float scale, int ctx, int b,
+                                                  int nflag, const uint32_t* flg_r, const uint64_t* flg_c,
+                                                  uint64_t thr, int k_sel, uint64_t* cand, uint32_t* ctl) {
+  constexpr int U = 4;
+  const int t = threadIdx.x;
+  const int grp = t >> 4, sub = t & 15;
+  const uint4 qv = *reinterpret_cast<const uint4*>(qrow + sub * 8);
+  const int S = (ctx + b - 1) / b;
+  const int total = nflag * S;
+  for (int s0 = 0; s0 < total; s0 += kVGroups * U) {
+    int jj[U], ff[U];
+    uint4 kv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      jj[u] = flagged_key(s0 + u * kVGroups + grp, total, S, b, flg_r, &ff[u]);
+      kv[u] = jj[u] < ctx ? *reinterpret_cast<const uint4*>(kh + (int64_t)jj[u] * kD + sub * 8) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = jj[u];
+      const float sc = row16_sum(dot8_bf16(kv[u], qv)) * scale;
+      const uint64_t key = j < ctx ? make_key(ord_f32(__float_as_uint(sc)), (uint32_t)j) : 0;
+      append_kept(sub == 0 && j < ctx && key > thr && key < flg_c[ff[u]], key, k_sel, cand, ctl);
+    }
+  }
+}
+
+// Rescan of the flagged buckets for query-head groups: every wave recomputes
+// 16 keys per MFMA chain, two chains per step, with the scoring kernel's
+// operands in the same places (the G query rows as A rows 0..G-1, the k
+// steps in order from a zero accumulator, then the scaling).  A result
+// element of v_mfma depends only on its own A row, B column and accumulator
+// element, so the recomputed scores are the ones that were ranked, wherever
+// a key sits among the 16 columns.
+__device__ __forceinline__ void decode_rescan_mfma(const uint16_t* qg, int G, int g, const uint16_t* kh, float scale,
+                                                int ctx, int b, int nflag, const uint32_t* flg_r,
+                                                const uint64_t* flg_c, uint64_t thr, int k_sel, uint64_t* cand,
+                                                uint32_t* ctl) {
+  constexpr int KS = kD / 32;
+  constexpr int GR = 2;
+  constexpr int STEP = kT2 / kWave * 16 * GR;
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int col = lane & 15, kq = 8 * (lane >> 4);
+  bf16x8_t qa[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    qa[ks] = __builtin_bit_cast(bf16x8_t, col < G ? *reinterpret_cast<const uint4*>(qg + (int64_t)col * kD + 32 * ks + kq)
+                                                  : make_uint4(0, 0, 0, 0));
+  const bool mine = (lane >> 4) == (g >> 2);
+  const int S = (ctx + b - 1) / b;
+  const int total = nflag * S;
+  for (int s0 = 0; s0 < total; s0 += STEP) {
+    uint4 kv[GR][KS];
+    int jj[GR], ff[GR];
+#pragma unroll
+    for (int gi = 0; gi < GR; ++gi) {
+      jj[gi] = flagged_key(s0 + (wave * GR + gi) * 16 + col, total, S, b, flg_r, &ff[gi]);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kv[gi][ks] = jj[gi] < ctx ? *reinterpret_cast<const uint4*>(kh + (int64_t)jj[gi] * kD + 32 * ks + kq)
+                                  : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int gi = 0; gi < GR; ++gi) {
+      f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], __builtin_bit_cast(bf16x8_t, kv[gi][ks]), acc, 0, 0, 0);
+      const int j = jj[gi];
+      const float sc = acc[g & 3] * scale;
+      const uint64_t key = j < ctx ? make_key(ord_f32(__float_as_uint(sc)), (uint32_t)j) : 0;
+      append_kept(mine && j < ctx && key > thr && key < flg_c[ff[gi]], key, k_sel, cand, ctl);
+    }
+  }
+}
+
 // certify != 0 makes the Top-K exact over every score of the head: with T
 // the k_sel-th candidate key, a bucket that kept k_b keys all >= T may hide
 // more of the Top-K (any missing key beats T); those buckets are rescanned
 // for keys between T and their k_b-th kept key, and the Top-K of the
-// enlarged pool is the exact one.  certify == 1: the scores of the head are
-// in `scores` ([B*Hq, ctx]); certify == 2 (one query head per KV head): the
-// rescan recomputes them from q and K with the scoring kernel's own
-// arithmetic (16-lane packed bf16 dot products, the same row sum, the same
-// scaling), so they are bit-identical to the ones that were ranked.
+// enlarged pool is the exact one.  The rescan recomputes the flagged
+// buckets' scores from q and K with the scoring kernel's own arithmetic, so
+// they are bit-identical to the ones that were ranked: certify == 1 (query-
+// head groups) on the matrix cores, certify == 2 (one query head per KV head)
+// with the 16-lane dot products.  Past kFlagMax flagged buckets, or past the
+// LDS candidate array, the workgroup recomputes every score of its head into
+// its row of `scores` ([B*Hq, ctx] workspace) and selects from that row.
 template <int KB>
 __global__ __launch_bounds__(kT2) void decode_finish_kernel(const uint64_t* __restrict__ partial, int nchunks, int hq,
                                                            int hkv, int b, int kb, int k_sel,
@@ -409,62 +544,15 @@ __global__ __launch_bounds__(kT2) void decode_finish_kernel(const uint64_t* __re
     }
     n = block_compact_ge<T, kMaxCand / T>(cand, n, thr, ctl);  // k_sel keys
     const int nflag = (int)ctl[5];
-    const float* srow = scores + (int64_t)r_out * ctx;
     if (nflag > 0) {
-      bool overflow = nflag > kFlagMax || (certify == 2 && G != 1);  // recompute is for G == 1 only
-      if (!overflow && certify == 2) {
-        // 16-lane groups recompute the flagged buckets' scores
-        const int grp = t >> 4, sub = t & 15;
-        const uint4 qv = *reinterpret_cast<const uint4*>(q + (int64_t)r_out * kD + sub * 8);
-        const uint16_t* kh = K + (int64_t)bh * ctx_stride * kD + sub * 8;
-        const int S = (ctx + b - 1) / b;
-        const int total = nflag * S;
-        for (int s0 = 0; s0 < total; s0 += kVGroups) {
-          const int sl = s0 + grp;
-          const int f = sl < total ? sl / S : 0;
-          const int j = sl < total ? (int)flg_r[f] + (sl - f * S) * b : ctx;
-          const uint4 kv = j < ctx ? *reinterpret_cast<const uint4*>(kh + (int64_t)j * kD) : make_uint4(0, 0, 0, 0);
-          const float sc = row16_sum(dot8_bf16(kv, qv)) * scale;
-          const uint64_t key = j < ctx ? make_key(ord_f32(__float_as_uint(sc)), (uint32_t)j) : 0;
-          const bool keep = sub == 0 && j < ctx && key > thr && key < flg_c[f];
-          const uint64_t msk = __ballot(keep);
-          if (msk) {
-            uint32_t pos = 0;
-            if (lane_id() == 0) pos = atomicAdd(&ctl[6], (uint32_t)__popcll(msk));
-            pos = __shfl(pos, 0, kWave);
-            const uint32_t slot = (uint32_t)k_sel + pos + lanes_below(msk);
-            if (keep && slot < (uint32_t)kMaxCand) cand[slot] = key;
-          }
-        }
-        __syncthreads();
-        const int extra = (int)ctl[6];
-        __syncthreads();
-        overflow = k_sel + extra > kMaxCand;
-        if (!overflow && extra > 0) {
-          n = k_sel + extra;
-          const uint64_t thr2 = block_kth_key<T>(cand, n, k_sel, hist, ctl);
-          n = block_compact_ge<T, kMaxCand / T>(cand, n, thr2, ctl);
-        }
-      } else if (!overflow) {
-        // every thread steps through slot s of the flagged buckets' keys:
-        // bucket f = s / S, key r_f + (s % S) * b, S = ceil(ctx / b)
-        const int S = (ctx + b - 1) / b;
-        const int total = nflag * S;
-        for (int s0 = 0; s0 < total; s0 += T) {
-          const int sl = s0 + t;
-          const int f = sl < total ? sl / S : 0;
-          const int j = sl < total ? (int)flg_r[f] + (sl - f * S) * b : ctx;
-          const uint64_t key = j < ctx ? make_key(ord_f32(__float_as_uint(srow[j])), (uint32_t)j) : 0;
-          const bool keep = j < ctx && key > thr && key < flg_c[f];
-          const uint64_t msk = __ballot(keep);
-          if (msk) {
-            uint32_t pos = 0;
-            if (lane_id() == 0) pos = atomicAdd(&ctl[6], (uint32_t)__popcll(msk));
-            pos = __shfl(pos, 0, kWave);
-            const uint32_t slot = (uint32_t)k_sel + pos + lanes_below(msk);
-            if (keep && slot < (uint32_t)kMaxCand) cand[slot] = key;
-          }
-        }
+      bool overflow = nflag > kFlagMax;
+      const uint16_t* kh = K + (int64_t)bh * ctx_stride * kD;
+      const uint16_t* qg = q + (int64_t)(r_out - g) * kD;  // the G query rows of the KV head
+      if (!overflow) {
+        if (certify == 1)
+          decode_rescan_mfma(qg, G, g, kh, scale, ctx, b, nflag, flg_r, flg_c, thr, k_sel, cand, ctl);
+        else
+          decode_rescan_dot(q + (int64_t)r_out * kD, kh, scale, ctx, b, nflag, flg_r, flg_c, thr, k_sel, cand, ctl);
         __syncthreads();
         const int extra = (int)ctl[6];
         __syncthreads();
@@ -477,7 +565,10 @@ __global__ __launch_bounds__(kT2) void decode_finish_kernel(const uint64_t* __re
       }
       if (overflow) {
         float* row = scores + (int64_t)r_out * ctx;
-        if (certify == 2) decode_fill_scores(q + (int64_t)r_out * kD, K + (int64_t)bh * ctx_stride * kD, scale, ctx, row);
+        if (certify == 1)
+          decode_fill_scores_mfma(qg, G, g, kh, scale, ctx, row);
+        else
+          decode_fill_scores(q + (int64_t)r_out * kD, kh, scale, ctx, row);
         decode_row_fallback(row, ctx, k_sel, cand, hist, ctl);
         n = k_sel;
       }
@@ -610,7 +701,7 @@ hipError_t launch_decode_fused(const DecodePlan& p, const uint16_t* q, const uin
                                int64_t k_sel, int64_t b, int64_t kb, uint64_t* partial, uint16_t* out,
                                int32_t* sel_idx, float* scores, int certify, float* cert_buf, hipStream_t s) {
   if (certify && cert_buf == nullptr) return hipErrorInvalidValue;
-  if (certify == 1 && scores != cert_buf) return hipErrorInvalidValue;
+  if (certify && certify != (p.mfma ? 1 : 2)) return hipErrorInvalidValue;  // the rescan repeats kernel 1's arithmetic
   const int kbs = kb_pow2(kb);
   dim3 g1((unsigned)p.nchunks, (unsigned)(batch * hkv));
 #define ATOPK_D1(P, KBV)                                                                                            \

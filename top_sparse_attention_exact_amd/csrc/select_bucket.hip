@@ -450,7 +450,7 @@ __global__ __launch_bounds__(kFinishThreads) void bucket_finish_kernel(const uin
             if (msk) {
               uint32_t pos = 0;
               if (lane == 0) pos = atomicAdd(&ctl[6], (uint32_t)__popcll(msk));
-              pos = __shfl(pos, 0, kWave);
+              pos = wave_lane0(pos);
               const uint32_t slot = (uint32_t)k + pos + lanes_below(msk);
               if (keep && slot < (uint32_t)kFinishMaxCand) cand[slot] = key;
             }

@@ -118,7 +118,7 @@ __global__ __launch_bounds__(kExactThreads) void exact_filter_kernel(
       if (mask) {
         uint32_t pos = 0;
         if (lane == 0) pos = atomicAdd(ctr, (uint32_t)__popcll(mask));
-        pos = __shfl(pos, 0, kWave);
+        pos = wave_lane0(pos);
         if (pass) buf[count + pos + lanes_below(mask)] = key[s];
       }
     }

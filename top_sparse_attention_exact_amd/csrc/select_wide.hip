@@ -261,7 +261,7 @@ __global__ __launch_bounds__(kWave * kMaxChunks) void wide_collect_exact_kernel(
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     int base = 0;
     if (lane == 0) base = atomicAdd(&row_cnt[u.row], fill);
-    base = __shfl(base, 0, kWave);
+    base = (int)wave_lane0((uint32_t)base);
     for (int j = lane; j < fill; j += kWave)
       if (base + j < kRowCap) out[base + j] = buf[j];
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -574,7 +574,7 @@ __global__ __launch_bounds__(kFinT) void wide_final_kernel(const float* __restri
       if (m) {
         uint32_t pos = 0;
         if (lane_id() == 0) pos = atomicAdd(&ctl[4], (uint32_t)__popcll(m));
-        pos = __shfl(pos, 0, kWave);
+        pos = wave_lane0(pos);
         const uint32_t slot = pos + lanes_below(m);
         if (keep && slot < (uint32_t)kFinMax) cand[slot] = key;
       }
