@@ -358,7 +358,7 @@ __device__ __forceinline__ void load_tile(const uint8_t* xr, int64_t base, int n
 // Lower bounds of the row's k-th largest value are shared through LDS
 // without synchronisation (each published value is valid whenever read).
 constexpr int kRowExactMaxK = 64;
-constexpr int kWaveRegion = kRowLds / 8 / kRowWaves;  // keys per wave (256)
+constexpr int kWaveRegion = kRowLds / 8 / kRowWaves;  // keys per wave (512)
 
 // Keep the wave's top-k of its region (cnt keys) at the front; return the
 // order key of the k-th (the wave's new lower bound) -- wave-synchronous.
@@ -414,6 +414,7 @@ __global__ __launch_bounds__(kRowT) void row_exact_kernel(const uint8_t* __restr
   // barriers: relaxed workgroup-scope atomics (a volatile access would also
   // wait for the next tile's loads in flight).
   __shared__ uint32_t pub[kRowWaves];
+  __shared__ uint32_t packed;  // keys in the final run
   auto pub_store = [&](int w2, uint32_t v) {
     __hip_atomic_store(&pub[w2], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   };
@@ -522,29 +523,39 @@ __global__ __launch_bounds__(kRowT) void row_exact_kernel(const uint8_t* __restr
     tile(wa, (int64_t)nfull * TILE, std::false_type{});
   }
 
-  // Each wave reduces its region to its top-min(k, cnt), sorted: a run of 64;
-  // a tree of pairwise top-64 merges across the waves leaves the row's top-k
-  // (k <= 64) in wave 0, lane = rank.
+  // Each wave reduces its region to at most k keys (its top-k when it holds
+  // more than a wave's worth).  Once every wave has streamed, the published
+  // bounds are final and their minimum bounds the row's k-th largest from
+  // below (as in the first tile), far tighter than the bounds the keys were
+  // admitted with: the keys that reach it are packed into one run at the
+  // front of `buf`, and each key's rank in that run -- its output position
+  // -- is counted directly.
   if (cnt > kWave) {
     wave_compact_region(mine, cnt, k);
     cnt = k;
   }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
-  uint64_t key = lane < cnt ? mine[lane] : 0;
-  key = wave_sort64_desc(key);
-  uint64_t* runs = buf;  // run w at buf[64 w]
+  const uint64_t key = lane < cnt ? mine[lane] : 0;
+  if (t == 0) packed = 0;
   __syncthreads();
-  for (int st = kRowWaves / 2; st >= 1; st >>= 1) {
-    if (wave >= st && wave < 2 * st) runs[(wave - st) * kWave + lane] = key;
-    __syncthreads();
-    if (wave < st) key = wave_merge_top64(key, runs + wave * kWave);
-    __syncthreads();
+  uint32_t bound = 0xffffffffu;
+#pragma unroll
+  for (int w2 = 0; w2 < kRowWaves; ++w2) bound = min(bound, pub_load(w2));
+  const bool keep = key != 0 && key_ord(key) >= bound;
+  const uint64_t kmask = __ballot(keep);
+  if (kmask) {
+    uint32_t pos = 0;
+    if (lane == 0) pos = atomicAdd(&packed, (uint32_t)__popcll(kmask));
+    pos = wave_lane0(pos);
+    if (keep) buf[pos + lanes_below(kmask)] = key;
   }
-  if (wave == 0 && lane < k && key != 0) {
+  __syncthreads();
+  const int total = (int)packed;
+  block_rank_final(buf, total, k, [&](int i, uint64_t kk) {
     // the order key gives the value back, except the sign of a zero
-    const uint32_t idx = key_idx(key);
-    const uint32_t o = key_ord(key);
-    const int64_t at = (int64_t)row * k + lane;
+    const uint32_t idx = key_idx(kk);
+    const uint32_t o = key_ord(kk);
+    const int64_t at = (int64_t)row * k + i;
     out_idx[at] = (int32_t)idx;
     if constexpr (DT == IN_F32) {
       reinterpret_cast<uint32_t*>(out_vals)[at] =
@@ -554,7 +565,7 @@ __global__ __launch_bounds__(kRowT) void row_exact_kernel(const uint8_t* __restr
       reinterpret_cast<uint16_t*>(out_vals)[at] =
           o16 == 0x8000u ? reinterpret_cast<const uint16_t*>(xr)[idx] : bf16_from_ord16(o16);
     }
-  }
+  });
 }
 
 // ------------------------------------------------------------ contiguous ----
