@@ -257,11 +257,21 @@ __device__ void block_sortmerge_final(const uint64_t* cand, uint64_t* runs, int 
   }
 }
 
-// hist[bin] += 1 for every active lane with `add`.  Keys near a selection
-// threshold share their high digits, and per-lane LDS atomics on one
-// address serialise, so the first few distinct bins of the wave take one
-// atomic each (count = lanes in that bin); the rest go lane by lane.
+// hist[bin] += 1 for every active lane with `add`: one LDS atomic per lane.
+// Lanes that hit one address serialise inside the LDS unit, which still
+// costs less than folding equal bins first: that takes a shuffle, two
+// ballots and an LDS round trip per distinct bin, all on the vector and
+// scalar units every wave shares (measured at 2048 keys: 6.1 against 3.6 us
+// per radix select, the keys of the first digit in a few bins).
 __device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool add) {
+  if (add) atomicAdd(&hist[bin], 1u);
+}
+
+// The same where most lanes of most waves fall into one or two bins for
+// several digits in a row (the largest values of a uniform row): the first
+// few distinct bins of the wave take one atomic each (count = lanes in that
+// bin), the rest go lane by lane.
+__device__ __forceinline__ void hist_add_grouped(uint32_t* hist, uint32_t bin, bool add) {
   uint64_t todo = __ballot(add);
 #pragma unroll
   for (int it = 0; it < 4; ++it) {

@@ -167,7 +167,7 @@ __global__ __launch_bounds__(kExactB) void wide_exact_threshold_kernel(const flo
       k, hist, ctl,
       [&](uint32_t mask, uint32_t prefix, int shift) {
 #pragma unroll
-        for (int j = 0; j < KB; ++j) hist_add(hist, (o[j] >> shift) & 255u, (o[j] & mask) == prefix);
+        for (int j = 0; j < KB; ++j) hist_add_grouped(hist, (o[j] >> shift) & 255u, (o[j] & mask) == prefix);
       },
       &rem);
   if (threadIdx.x == 0) {
