@@ -56,7 +56,7 @@ __device__ __forceinline__ void fnet_insert(float (&q)[KB], float x) {
 // [w * spc, (w + 1) * spc).  Workgroups go round-robin to the 8 XCDs, so
 // when the rows split evenly the map puts all groups of a row -- the
 // workgroups that read the same sweeps -- on one XCD.  `rev` walks the
-// workgroups in reverse launch order: the collect pass then starts on the
+// workgroups in reverse launch order: the collect passes then start on the
 // data the values pass read last, which is still in the Infinity Cache.
 constexpr int kXcds = 8;
 
@@ -243,13 +243,19 @@ __global__ __launch_bounds__(kWave * kMaxChunks) void wide_collect_bucket_kernel
 
 // 2b. exact collect: element >= T -> the row's key list (kRowCap entries;
 //     the count keeps growing past the cap).  Keys gather in a per-wave LDS
-//     buffer that is flushed with one atomic per ~kFlush keys.
+//     buffer; a full buffer is flushed with one atomic of its own, and the
+//     last keys of all the workgroup's waves with one atomic between them
+//     (per-wave atomics on the row's one counter serialise: they doubled the
+//     pass).
 __global__ __launch_bounds__(kWave * kMaxChunks) void wide_collect_exact_kernel(
     const float* __restrict__ x, int64_t ldx, int n, int b, int groups, int spc, const float* __restrict__ rowthr,
     int* __restrict__ row_cnt, uint64_t* __restrict__ row_keys) {
   __shared__ uint64_t wbuf[kMaxChunks][kFlush];
-  const Unit u = unit_of(n, b, groups, spc, false);
-  uint64_t* buf = wbuf[threadIdx.x / kWave];
+  __shared__ uint32_t wg_off[kMaxChunks];
+  __shared__ uint32_t wg_base;
+  const Unit u = unit_of(n, b, groups, spc, true);
+  const int wave = threadIdx.x / kWave;
+  uint64_t* buf = wbuf[wave];
   const int lane = lane_id();
   const float* xr = x + (int64_t)u.row * ldx + u.r;
   const float th = rowthr[u.row];
@@ -282,19 +288,57 @@ __global__ __launch_bounds__(kWave * kMaxChunks) void wide_collect_exact_kernel(
   // sweeps [s0, fe) hold an element of every bucket; the rest may not
   const int fe = u.full > u.s0 ? u.full : u.s0;
   int s = u.s0;
-  for (; s + kWideU <= fe; s += kWideU) {
-    float w[kWideU];
+  // groups of kWideU sweeps through two register sets: the next group's
+  // loads are in flight while a group is filtered
+  const int ng = (fe - s) / kWideU;
+  float wa[kWideU], wb[kWideU];
+  auto load = [&](float (&w)[kWideU], int s0) {
 #pragma unroll
-    for (int v = 0; v < kWideU; ++v) w[v] = xr[(int64_t)(s + v) * b];
+    for (int v = 0; v < kWideU; ++v) w[v] = xr[(int64_t)(s0 + v) * b];
+  };
+  auto filt = [&](const float (&w)[kWideU], int s0) {
 #pragma unroll
-    for (int v = 0; v < kWideU; ++v) see(w[v] >= th, w[v], s + v);
+    for (int v = 0; v < kWideU; ++v) see(w[v] >= th, w[v], s0 + v);
+  };
+  if (ng > 0) {
+    int g = 0;
+    load(wa, s);
+    for (; g + 2 < ng; g += 2) {
+      load(wb, s + (g + 1) * kWideU);
+      filt(wa, s + g * kWideU);
+      load(wa, s + (g + 2) * kWideU);
+      filt(wb, s + (g + 1) * kWideU);
+    }
+    if (g + 1 < ng) {
+      load(wb, s + (g + 1) * kWideU);
+      filt(wa, s + g * kWideU);
+      filt(wb, s + (g + 1) * kWideU);
+    } else {
+      filt(wa, s + g * kWideU);
+    }
+    s += ng * kWideU;
   }
   for (; s < u.s1; ++s) {
     const bool in = (int64_t)s * b + u.r < n;
     const float v = in ? xr[(int64_t)s * b] : -INFINITY;
     see(in && v >= th, v, s);
   }
-  if (fill > 0) flush();
+  // the waves' last keys: offsets inside the workgroup, one atomic in all
+  if (lane == 0) wg_off[wave] = (uint32_t)fill;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t tot = 0;
+    for (int w2 = 0; w2 < (int)(blockDim.x / kWave); ++w2) {
+      const uint32_t c = wg_off[w2];
+      wg_off[w2] = tot;
+      tot += c;
+    }
+    wg_base = tot ? (uint32_t)atomicAdd(&row_cnt[u.row], (int)tot) : 0u;
+  }
+  __syncthreads();
+  const int base = (int)(wg_base + wg_off[wave]);
+  for (int j = lane; j < fill; j += kWave)
+    if (base + j < kRowCap) out[base + j] = buf[j];
 }
 
 // Bitonic sort (descending) of T*P keys held P per thread, key index
