@@ -107,6 +107,21 @@ __device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
 // 0 must be active).
 __device__ __forceinline__ uint32_t wave_lane0(uint32_t v) { return (uint32_t)__builtin_amdgcn_readlane((int)v, 0); }
 
+// Bitwise AND and OR over the wave: DPP inside each row of 16 lanes (two
+// quad swaps and two mirrors reach every lane of the row), then the 4 rows.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce_dpp(uint32_t v, Op op) {
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xb1, 0xf, 0xf, true));   // quad_perm 1,0,3,2
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4e, 0xf, 0xf, true));   // quad_perm 2,3,0,1
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xf, 0xf, true));  // row_half_mirror
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xf, 0xf, true));  // row_mirror
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return op(op(a, b), op(c, d));
+}
+
 // Inclusive prefix sum over the wave.
 __device__ __forceinline__ int wave_incl_scan(int v) {
   const int l = lane_id();
@@ -293,10 +308,37 @@ __device__ __forceinline__ void hist_add_grouped(uint32_t* hist, uint32_t bin, b
 // `hist` is a 256-entry LDS array, `ctl` 4 LDS words.
 template <int T>
 __device__ uint64_t block_kth_key(const uint64_t* keys, int n, int k, uint32_t* hist, uint32_t* ctl) {
+  static_assert(T / kWave <= 64, "per-wave words fit the histogram array");
   const int tid = threadIdx.x;
-  uint64_t prefix = 0;
+  // Leading bytes that every key shares (where the AND and the OR of the
+  // keys' order words agree) need no histogram pass: candidates near a
+  // threshold often share their sign and exponent byte.
+  uint32_t wa = 0xffffffffu, wo = 0;
+  for (int i = tid; i < n; i += T) {
+    const uint32_t o = key_ord(keys[i]);
+    wa &= o;
+    wo |= o;
+  }
+  wa = wave_reduce_dpp(wa, [](uint32_t x, uint32_t y) { return x & y; });
+  wo = wave_reduce_dpp(wo, [](uint32_t x, uint32_t y) { return x | y; });
+  if (lane_id() == 0) {
+    hist[2 * (tid / kWave)] = wa;
+    hist[2 * (tid / kWave) + 1] = wo;
+  }
+  __syncthreads();
+  wa = 0xffffffffu;
+  wo = 0;
+#pragma unroll
+  for (int w = 0; w < T / kWave; ++w) {
+    wa &= hist[2 * w];
+    wo |= hist[2 * w + 1];
+  }
+  __syncthreads();
+  const uint32_t diff = wa ^ wo;
+  const int common = diff == 0 ? 4 : __builtin_clz(diff) / 8;  // shared leading bytes of the order word
+  uint64_t prefix = common == 0 ? 0 : ((uint64_t)(wa & (0xffffffffu << (32 - 8 * common))) << 32);
   int rem = k;
-  for (int shift = 56; shift >= 0; shift -= 8) {
+  for (int shift = 56 - 8 * common; shift >= 0; shift -= 8) {
     for (int i = tid; i < 256; i += T) hist[i] = 0;
     __syncthreads();
     const uint64_t hi_prefix = (shift == 56) ? 0 : (prefix >> (shift + 8));
