@@ -122,11 +122,12 @@ struct DecodePlan {
 };
 DecodePlan plan_decode(int64_t batch, int64_t hq, int64_t hkv, int64_t ctx, int64_t k_sel, int64_t b, int64_t kb);
 // certify != 0: (b, kb) is a certified plan for the exact Top-K and
-// cert_buf a [B*Hq, ctx] fp32 buffer.  certify == 1: every score goes to
-// cert_buf (scores must equal it) and the finish rescans from there;
-// certify == 2 (one query head per KV head): the finish recomputes the
-// scores it rescans, and cert_buf is scratch for its rare full-row fallback.
-// scores (nullable otherwise): every score, when the caller asks for them.
+// cert_buf a [B*Hq, ctx] fp32 buffer, scratch for the finish's rare
+// full-row fallback.  The finish recomputes the scores of the buckets it
+// rescans with kernel 1's arithmetic: certify == 1 for query-head groups
+// (matrix cores), certify == 2 with one query head per KV head (packed dot
+// products); any other pairing is rejected.  scores (nullable): every
+// score, when the caller asks for them.
 hipError_t launch_decode_fused(const DecodePlan& p, const uint16_t* q, const uint16_t* K, const uint16_t* V,
                                int64_t batch, int64_t hq, int64_t hkv, int64_t ctx, int64_t ctx_stride, float scale,
                                int64_t k_sel, int64_t b, int64_t kb, uint64_t* partial, uint16_t* out,
