@@ -305,10 +305,15 @@ __device__ __forceinline__ void hist_add_grouped(uint32_t* hist, uint32_t bin, b
 // (LDS) are >= t (radix select, 8-bit digits from the top).  Once at most 64
 // keys share the selected prefix, they are gathered into `hist` and one wave
 // ranks them, which ends the select in place of the remaining digit passes.
-// `hist` is a 256-entry LDS array, `ctl` 4 LDS words.
-template <int T>
+// With SUB > 1 lane l counts into copy l mod SUB of the histogram, so keys
+// of one digit hit SUB addresses instead of one.  `hist` is a 256 * SUB
+// entry LDS array, `ctl` 4 LDS words.
+constexpr int kKthSub = 4;  // histogram copies for candidate sets, which crowd few digits
+
+template <int T, int SUB = 1>
 __device__ uint64_t block_kth_key(const uint64_t* keys, int n, int k, uint32_t* hist, uint32_t* ctl) {
   static_assert(T / kWave <= 64, "per-wave words fit the histogram array");
+  static_assert(SUB == 1 || SUB == 2 || SUB == 4, "lanes spread over 1, 2 or 4 histogram copies");
   const int tid = threadIdx.x;
   // Leading bytes that every key shares (where the AND and the OR of the
   // keys' order words agree) need no histogram pass: candidates near a
@@ -339,8 +344,9 @@ __device__ uint64_t block_kth_key(const uint64_t* keys, int n, int k, uint32_t* 
   uint64_t prefix = common == 0 ? 0 : ((uint64_t)(wa & (0xffffffffu << (32 - 8 * common))) << 32);
   int rem = k;
   for (int shift = 56 - 8 * common; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += T) hist[i] = 0;
+    for (int i = tid; i < 256 * SUB; i += T) hist[i] = 0;
     __syncthreads();
+    uint32_t* hsub = hist + 256 * (lane_id() % SUB);  // keys of one digit in a wave hit SUB addresses
     const uint64_t hi_prefix = (shift == 56) ? 0 : (prefix >> (shift + 8));
     for (int i0 = 0; i0 < n; i0 += 2 * T) {
       uint64_t kk[2];  // two loads in flight
@@ -352,7 +358,7 @@ __device__ uint64_t block_kth_key(const uint64_t* keys, int n, int k, uint32_t* 
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const bool match = i0 + u * T + tid < n && ((shift == 56) || ((kk[u] >> (shift + 8)) == hi_prefix));
-        hist_add(hist, (uint32_t)(kk[u] >> shift) & 255u, match);
+        hist_add(hsub, (uint32_t)(kk[u] >> shift) & 255u, match);
       }
     }
     __syncthreads();
@@ -363,6 +369,8 @@ __device__ uint64_t block_kth_key(const uint64_t* keys, int n, int k, uint32_t* 
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         h[j] = hist[255 - 4 * tid - j];
+#pragma unroll
+        for (int c = 1; c < SUB; ++c) h[j] += hist[256 * c + 255 - 4 * tid - j];
         s += (int)h[j];
       }
       int incl = wave_incl_scan(s);  // keys in digits above this lane's low end

@@ -480,7 +480,7 @@ __global__ __launch_bounds__(kT2) void decode_finish_kernel(const uint64_t* __re
                                                            const uint16_t* __restrict__ K, float scale) {
   constexpr int T = kT2;
   __shared__ uint64_t cand[kMaxCand];
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[256 * kKthSub];
   __shared__ uint32_t ctl[8];
   __shared__ uint32_t flg_r[kFlagMax];
   __shared__ uint64_t flg_c[kFlagMax];
@@ -526,7 +526,7 @@ __global__ __launch_bounds__(kT2) void decode_finish_kernel(const uint64_t* __re
   __syncthreads();
   int n = b * kb;
   if (certify) {
-    const uint64_t thr = block_kth_key<T>(cand, n, k_sel, hist, ctl);
+    const uint64_t thr = block_kth_key<T, kKthSub>(cand, n, k_sel, hist, ctl);
     if (t == 0) {
       ctl[5] = 0;
       ctl[6] = 0;
@@ -559,7 +559,7 @@ __global__ __launch_bounds__(kT2) void decode_finish_kernel(const uint64_t* __re
         overflow = k_sel + extra > kMaxCand;
         if (!overflow && extra > 0) {
           n = k_sel + extra;
-          const uint64_t thr2 = block_kth_key<T>(cand, n, k_sel, hist, ctl);
+          const uint64_t thr2 = block_kth_key<T, kKthSub>(cand, n, k_sel, hist, ctl);
           n = block_compact_ge<T, kMaxCand / T>(cand, n, thr2, ctl);
         }
       }
@@ -574,7 +574,7 @@ __global__ __launch_bounds__(kT2) void decode_finish_kernel(const uint64_t* __re
       }
     }
   } else if (n > k_sel) {
-    const uint64_t thr = block_kth_key<T>(cand, n, k_sel, hist, ctl);
+    const uint64_t thr = block_kth_key<T, kKthSub>(cand, n, k_sel, hist, ctl);
     n = block_compact_ge<T, kMaxCand / T>(cand, n, thr, ctl);
   }
   if (sel_idx != nullptr) {

@@ -142,7 +142,7 @@ __global__ __launch_bounds__(kST) void rerank_select_kernel(const uint64_t* __re
                                                            uint16_t* __restrict__ out, int32_t* __restrict__ sel_idx) {
   constexpr int T = kST;
   __shared__ uint64_t keys[kRerankMaxCand];
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[256 * kKthSub];
   __shared__ uint32_t ctl[8];
   __shared__ float w_lds[kSGroups];
   __shared__ float red[T / kWave];
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(kST) void rerank_select_kernel(const uint64_t* __re
 
   // 3. exact Top-K of the set (the whole set when it is smaller)
   if (n > k_sel) {
-    const uint64_t thr = block_kth_key<T>(keys, n, k_sel, hist, ctl);
+    const uint64_t thr = block_kth_key<T, kKthSub>(keys, n, k_sel, hist, ctl);
     n = block_compact_ge<T, kRerankMaxCand / T>(keys, n, thr, ctl);
   }
   if (sel_idx != nullptr) {

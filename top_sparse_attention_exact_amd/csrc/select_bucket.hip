@@ -320,7 +320,7 @@ __global__ __launch_bounds__(kFinishThreads) void bucket_finish_kernel(const uin
                                                                       int32_t* out_idx, uint64_t* cand_out) {
   constexpr int T = kFinishThreads;
   __shared__ uint64_t cand[kFinishMaxCand];
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[256 * kKthSub];
   __shared__ uint32_t ctl[8];
   __shared__ uint32_t flg_r[kFlagMax];
   __shared__ uint64_t flg_c[kFlagMax];
@@ -402,7 +402,7 @@ __global__ __launch_bounds__(kFinishThreads) void bucket_finish_kernel(const uin
   int cnt = (int)nc;
   if (mode == 3) {
     const int lane = lane_id();
-    const uint64_t thr = block_kth_key<T>(cand, cnt, k, hist, ctl);
+    const uint64_t thr = block_kth_key<T, kKthSub>(cand, cnt, k, hist, ctl);
     if (t == 0) {
       ctl[5] = 0;
       ctl[6] = 0;
@@ -462,7 +462,7 @@ __global__ __launch_bounds__(kFinishThreads) void bucket_finish_kernel(const uin
         overflow = k + extra > kFinishMaxCand;
         if (!overflow && extra > 0) {
           cnt = k + extra;
-          const uint64_t thr2 = block_kth_key<T>(cand, cnt, k, hist, ctl);
+          const uint64_t thr2 = block_kth_key<T, kKthSub>(cand, cnt, k, hist, ctl);
           cnt = block_compact_ge<T, kFinishMaxCand / T>(cand, cnt, thr2, ctl);
         }
       }
@@ -472,7 +472,7 @@ __global__ __launch_bounds__(kFinishThreads) void bucket_finish_kernel(const uin
       }
     }
   } else if (cnt > k) {
-    const uint64_t thr = block_kth_key<T>(cand, cnt, k, hist, ctl);
+    const uint64_t thr = block_kth_key<T, kKthSub>(cand, cnt, k, hist, ctl);
     cnt = block_compact_ge<T, kFinishMaxCand / T>(cand, cnt, thr, ctl);
   }
   if (cnt <= kWave) {  // one wave sorts the (at most 64) keys in registers
