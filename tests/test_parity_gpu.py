@@ -118,6 +118,9 @@ def test_all_equal_rows(gpu):
     for dtype in (torch.float32, torch.bfloat16):
         x = torch.full((2, 5000), 1.5, dtype=dtype, device=gpu)
         check_exact(x, 700)
+        # k <= 64: every wave keeps a full region of ties, the final ranks 16 x 64 keys by index
+        check_exact(x, 64)
+        check_exact(x, 1)
         check_bucketed(x, 64, 32, 2, True)
         check_bucketed(x, 64, 32, 2, False)
 
