@@ -669,9 +669,12 @@ DecodePlan plan_decode(int64_t batch, int64_t hq, int64_t hkv, int64_t ctx, int6
   p.ppt = ppt;
   p.fused = !(b == 1 && kb == k_sel) && ppt <= 8 && (int64_t)ppt * kbs <= 64 && b * kb <= kMaxCand && kbs <= 16;
   // chunks: enough workgroups to fill the chip, long enough that the lists
-  // written per chunk stay small next to the K bytes read
+  // written per chunk stay small next to the K bytes read.  The matrix-core
+  // kernel streams as fast with one 512-thread workgroup per CU as with two,
+  // and half the chunks halve the lists the finish merges (gqa-128k: 215 ->
+  // 211 us per call).
   const int64_t heads = batch * hkv;
-  const int64_t target = 512;  // workgroups
+  const int64_t target = p.mfma ? 256 : 512;  // workgroups
   int64_t nchunks = std::max<int64_t>(1, (target + heads - 1) / std::max<int64_t>(heads, 1));
   nchunks = std::min<int64_t>(nchunks, std::max<int64_t>(1, ctx / 4096));
   int64_t chunk = (ctx + nchunks - 1) / nchunks;
