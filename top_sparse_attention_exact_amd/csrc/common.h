@@ -302,12 +302,12 @@ __device__ __forceinline__ void hist_add_grouped(uint32_t* hist, uint32_t bin, b
 }
 
 // The threshold key t such that exactly k of the n unique keys in `keys`
-// (LDS) are >= t (radix select, 8-bit digits from the top).  Once at most 64
-// keys share the selected prefix, they are gathered into `hist` and one wave
-// ranks them, which ends the select in place of the remaining digit passes.
-// With SUB > 1 lane l counts into copy l mod SUB of the histogram, so keys
-// of one digit hit SUB addresses instead of one.  `hist` is a 256 * SUB
-// entry LDS array, `ctl` 4 LDS words.
+// (LDS) are >= t: radix select, 8-bit digits from the first byte the keys do
+// not all share.  Once at most 64 keys share the selected prefix, they are
+// gathered into `hist` and one wave ranks them, which ends the select in
+// place of the remaining digit passes.  With SUB > 1 lane l counts into copy
+// l mod SUB of the histogram, so keys of one digit hit SUB addresses instead
+// of one.  `hist` is a 256 * SUB entry LDS array, `ctl` 4 LDS words.
 constexpr int kKthSub = 4;  // histogram copies for candidate sets, which crowd few digits
 
 template <int T, int SUB = 1>
