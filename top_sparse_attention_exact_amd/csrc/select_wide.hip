@@ -423,11 +423,8 @@ __device__ bool block_sort_desc_binned(uint64_t* cand, int cnt, uint32_t* bins, 
       hi = max(hi, key_ord(key[p]));
     }
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    lo = min(lo, (uint32_t)__shfl_xor((int)lo, o, kWave));
-    hi = max(hi, (uint32_t)__shfl_xor((int)hi, o, kWave));
-  }
+  lo = wave_reduce_dpp(lo, [](uint32_t x, uint32_t y) { return min(x, y); });
+  hi = wave_reduce_dpp(hi, [](uint32_t x, uint32_t y) { return max(x, y); });
   if (lane == 0) {
     red[wave] = lo;
     red[16 + wave] = hi;
@@ -481,7 +478,11 @@ __device__ bool block_sort_desc_binned(uint64_t* cand, int cnt, uint32_t* bins, 
     const uint64_t c_lo = (c * span + kCoarse - 1) / kCoarse;
     const uint64_t c_hi = ((c + 1) * span + kCoarse - 1) / kCoarse;
     const uint32_t cn = coarse[c];
-    const uint32_t f = (uint32_t)(((rel - c_lo) * cn) / max<uint64_t>(c_hi - c_lo, 1));
+    // a monotone map of rel inside the coarse bin (the rank step below only
+    // needs the bins in value order), in fp32: rel - c_lo and the bin width
+    // stay below 2^24 + 1, so both convert exactly
+    const uint32_t f =
+        (uint32_t)((float)(uint32_t)(rel - c_lo) * (float)cn / (float)(uint32_t)max<uint64_t>(c_hi - c_lo, 1));
     bin[p] = coarse[kCoarse + c] + min(f, cn > 0 ? cn - 1 : 0u);
     hist_add(bins, bin[p], t * P + p < cnt);
   }
