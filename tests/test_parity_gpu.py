@@ -589,6 +589,29 @@ def test_decode_exact_large_k(gpu, hq, hkv):
     _decode_check(q, K, V, 2048, 1, 2048)
 
 
+@pytest.mark.parametrize("hq,hkv,planted", [(8, 2, "mod64lt5"), (8, 2, "none"), (2, 2, "mod64lt5")])
+def test_decode_exact_without_scores_matches(gpu, hq, hkv, planted):
+    """The certified exact decode without a score output (its rescans and any
+    fallback row use the workspace alone) selects and outputs exactly what it
+    does with one."""
+    g = torch.Generator(device="cpu").manual_seed(hq * 31 + hkv)
+    ctx = 40000
+    q = torch.randn((2, hq, 128), generator=g)
+    K = torch.randn((2, hkv, ctx, 128), generator=g) * 0.5
+    V = torch.randn((2, hkv, ctx, 128), generator=g)
+    if planted == "mod64lt5":  # five buckets far above the rest: flagged and rescanned
+        mask = torch.arange(ctx) % 64 < 5
+        G = hq // hkv
+        for b in range(2):
+            for h in range(hkv):
+                K[b, h, mask] = 2.0 * q[b, h * G] + 0.05 * torch.randn((int(mask.sum()), 128), generator=g)
+    q, K, V = (t.to(torch.bfloat16).to(gpu) for t in (q, K, V))
+    out1, sel1, _ = atk.sparse_attn_decode(q, K, V, 64, return_sel=True, return_scores=True)
+    out2, sel2 = atk.sparse_attn_decode(q, K, V, 64, return_sel=True)
+    assert torch.equal(sel1, sel2)
+    assert torch.equal(out1, out2)
+
+
 def test_decode_ctx_stride(gpu):
     g = torch.Generator(device="cpu").manual_seed(3)
     q = torch.randn((1, 4, 128), generator=g).to(torch.bfloat16).to(gpu)
