@@ -65,11 +65,13 @@ __device__ __forceinline__ void block_rank_final(const uint64_t* cand, int n, in
     // keys per step: distinct banks, each broadcast to its group
     int cnt0 = 0, cnt1 = 0, cnt2 = 0, cnt3 = 0;
     int j = part;
-    for (; j + 3 * per < n; j += 4 * per) {
-      cnt0 += cand[j] > key ? 1 : 0;
-      cnt1 += cand[j + per] > key ? 1 : 0;
-      cnt2 += cand[j + 2 * per] > key ? 1 : 0;
-      cnt3 += cand[j + 3 * per] > key ? 1 : 0;
+    for (; j + 7 * per < n; j += 8 * per) {  // eight reads in flight
+      const uint64_t a0 = cand[j], a1 = cand[j + per], a2 = cand[j + 2 * per], a3 = cand[j + 3 * per];
+      const uint64_t a4 = cand[j + 4 * per], a5 = cand[j + 5 * per], a6 = cand[j + 6 * per], a7 = cand[j + 7 * per];
+      cnt0 += (a0 > key ? 1 : 0) + (a4 > key ? 1 : 0);
+      cnt1 += (a1 > key ? 1 : 0) + (a5 > key ? 1 : 0);
+      cnt2 += (a2 > key ? 1 : 0) + (a6 > key ? 1 : 0);
+      cnt3 += (a3 > key ? 1 : 0) + (a7 > key ? 1 : 0);
     }
     for (; j < n; j += per) cnt0 += cand[j] > key ? 1 : 0;
     int cnt = cnt0 + cnt1 + cnt2 + cnt3;
