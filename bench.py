@@ -1,26 +1,33 @@
 #!/usr/bin/env python3
-"""Benchmark of the top-k selection hot path on one MI355X.
+"""Benchmark of the top-k selection / top-K sparse-attention decode hot path
+on one MI355X.
 
-Workload (one "step"): the 256 x 131072 bf16 vocabulary-sampling batch
-(N(0, 2^2) logits, k = 64) through every selection mode of the path:
-exact top-64, bucketed (b, k_b) = (64, 1) without the final stage, and
-bucketed (128, 2) with the final exact top-64.  Inputs are resident in HBM
-before timing starts.
+Headline ("value", one "step"): one top-K sparse-attention decode step of
+the mha-32k workload -- B16 H32 D128, context 32768, bf16 q, K, V ~ N(0, 1)
+with 64 planted keys per head, scores q K^T / sqrt(128) in fp32, Top-512 via
+(b, k_b) = (256, 2), softmax-V over the selected keys -- the largest of the
+workloads (4.36 GB of algorithmic bytes per step).  value = scores per second
+(B * H * L / step time); ms_per_step is the decode time of one step.
 
-Throughput ("value", "us" per mode): K launches per mode back to back on one
-stream, queued behind a spin kernel so that the GPU never waits for the
-host, bracketed by HIP events on that stream; the launches rotate over
-enough copies of the batch (640 MB) that no launch finds its input in the
-256 MB Infinity Cache.  Latency ("us_cold"): single calls with HIP events
-around each, after a 1 GiB read that evicts the L2 and the Infinity Cache
-(timing protocol after the benchmark protocol printed with "Approximate
-Top-k for Increased Parallelism": warm-up, then events around each top-k
-launch queued behind a short spin kernel).
+The same run measures every other workload of the path the same way and
+reports each under "workloads": vocab-128k (256 x 131072 bf16, k = 64:
+exact, (64, 1), (128, 2) + final), gqa-128k (B4 Hq32 Hkv8, context 131072,
+Top-512 via (512, 4) + final, exact and rerank), wide-1m (64 x 2^20 fp32,
+k = 8192: exact and (512, 16) + final) and sel-4k (1 x 4096 fp32, k = 64).
 
-The same run also times the sparse-attention decode steps (scoring, Top-K
-selection, softmax-V) of the two decode workloads, the small-row and
-wide-row selection workloads, and the CPU oracle on a bounded sample of the
-selection batch.
+Timing: K calls per mode back to back on torch's stream (the library's
+stream), queued behind a spin kernel so that the GPU never waits for the
+host, bracketed by HIP events on that stream; selection inputs rotate over
+enough copies (640 MB) that no call finds its input in the 256 MB Infinity
+Cache (decode caches are larger than it).  Per-kernel times (the stages of a
+call: scoring + stage 1, stage 2 + softmax-V, ...) come from HIP events the
+library records after each of its kernels (atopk_stage_events) in a second
+pass of the same calls.  "roofline" gives, per workload, the dominant
+kernel's algorithmic bytes per launch over its event-timed launch duration
+against the 8 TB/s HBM peak, and the HBM traffic rocprofv3 counted for it
+(profiles/traffic_*.md) while its sources are unchanged.  The CPU oracle
+(numpy, float64 for the decode) runs on a bounded sample of every workload
+in a process pool over the host cores.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--only MODE]
 """
@@ -30,7 +37,6 @@ import hashlib
 import json
 import math
 import os
-import platform
 import sys
 import time
 
@@ -39,6 +45,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "top-k score elements/s + HBM GB/s vs peak; recall vs Eq.(1); decode µs/step"
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+CSRC = os.path.join(ROOT, "top_sparse_attention_exact_amd", "csrc")
 
 
 def parse():
@@ -47,30 +54,29 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", default="all",
-                    help="all | sel | exact | b64k1 | b128k2 | decode | mha | gqa | sel4k | wide | assign | tradeoff | graph "
-                         "| stream | sweep (not in all) | copy")
+                    help="all | core (the five workloads, no secondary legs) | mha | gqa | vocab | wide | sel4k | "
+                         "assign | tradeoff | graph | stream | sweep (not in all) | copy")
     ap.add_argument("--no-flush", action="store_true", help="no cache flush before the single-call latency runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-stages", action="store_true", help="skip the per-kernel (stage) timing pass")
+    ap.add_argument("--cpu-seconds", type=float, default=5.0, help="CPU oracle budget per workload (wall seconds)")
     return ap.parse_args()
 
 
-# Sources the selection kernels of the step are compiled from.
-KERNEL_SOURCES = ("common.h", "select_row.hip")
+# ------------------------------------------------------------ traffic ----
 
-
-def kernel_source_hash():
+def source_hash(sources):
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "top_sparse_attention_exact_amd", "csrc", name), "rb") as f:
+    for name in sources:
+        with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
 def recorded_traffic(name):
-    """HBM bytes per launch from the committed rocprofv3 counter summary of
-    the named kernel, if the kernel sources still hash the same."""
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    profiles/traffic_<name>.md, if the sources it lists still hash the
+    same (null once the kernel changed since the counters were taken)."""
     path = os.path.join(ROOT, "profiles", "traffic_%s.md" % name)
     if not os.path.exists(path):
         return None
@@ -79,7 +85,8 @@ def recorded_traffic(name):
         if ":" in line and line.strip().startswith("- "):
             key, val = line.strip()[2:].split(":", 1)
             fields[key.strip()] = val.strip().strip("`")
-    if fields.get("kernel_source_hash") != kernel_source_hash():
+    sources = [s.strip() for s in fields.get("kernel_sources", "").split(",") if s.strip()]
+    if not sources or fields.get("kernel_source_hash") != source_hash(sources):
         return None
     try:
         return int(fields["hbm_bytes_per_launch"])
@@ -176,159 +183,351 @@ def copies(x, min_bytes):
 ROTATE_BYTES = 640 << 20
 
 
-def selection_step(args, timer):
+def stage_split(fn, steps, spin):
+    """Per-kernel durations of a library call: the caller records an event
+    before the call and the library records one after each of its kernels
+    (atopk_stage_events), all on torch's current stream, the calls queued
+    behind a spin kernel.  Returns (mean µs per kernel, per-call lists)."""
+    import numpy as np
+    import torch
+
+    import top_sparse_attention_exact_amd as atk
+
+    probe = [torch.cuda.Event(enable_timing=True) for _ in range(64)]
+    for e in probe:
+        e.record()
+    torch.cuda.synchronize()
+    atk.stage_events(probe)
+    fn(0)
+    nk = min(atk.stage_count(), len(probe))
+    atk.stage_events(None)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(steps)]
+    for row in evs:
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+    torch.cuda._sleep(spin)
+    for s in range(steps):
+        evs[s][0].record()
+        atk.stage_events(evs[s][1:])
+        fn(s)
+    atk.stage_events(None)
+    torch.cuda.synchronize()
+    per = [[evs[s][j].elapsed_time(evs[s][j + 1]) * 1e3 for j in range(nk)] for s in range(steps)]
+    return [float(np.mean([p[j] for p in per])) for j in range(nk)], per
+
+
+def describe_stages(names, alg, us):
+    """Stage list of one call: kernel names (when the call launched the
+    expected number of kernels), algorithmic bytes and event-timed µs."""
+    if len(names) != len(us):
+        names = ["kernel %d" % j for j in range(len(us))]
+        alg = [None] * len(us)
+    out = []
+    for nm, a, t in zip(names, alg, us):
+        d = {"kernel": nm, "us": round(t, 2)}
+        if a is not None:
+            d["alg_bytes"] = a
+            d["gbps"] = a / (t * 1e-6) / 1e9
+            d["frac_hbm_peak"] = d["gbps"] / HBM_PEAK_GBPS
+        out.append(d)
+    return out
+
+
+def roofline_block(stages, call_alg, call_us, traffic_name):
+    """Roofline of one call: its dominant kernel (the one with the largest
+    share of the call's kernel time) when that kernel carries algorithmic
+    bytes of its own and at least 80% of the time, else the whole call."""
+    total = sum(s["us"] for s in stages) if stages else call_us
+    dom = max(stages, key=lambda s: s["us"]) if stages else None
+    if dom is not None and "alg_bytes" in dom and dom["us"] >= 0.8 * total:
+        kernel, alg, us = dom["kernel"], dom["alg_bytes"], dom["us"]
+    else:
+        kernel = " + ".join(s["kernel"] for s in stages) if stages else "whole call"
+        alg, us = call_alg, (total if stages else call_us)
+    achieved = alg / (us * 1e-6) / 1e9
+    return {"bound": "hbm", "kernel": kernel, "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS, "traffic": recorded_traffic(traffic_name),
+            "alg_bytes_per_launch": alg, "launch_us": round(us, 2), "call_us": round(call_us, 2)}
+
+
+def cold_stats(vals):
+    import numpy as np
+
+    return {"us_cold_median": round(float(np.median(vals)), 2), "us_cold_p10": round(float(np.percentile(vals, 10)), 2),
+            "us_cold_p90": round(float(np.percentile(vals, 90)), 2)}
+
+
+# Kernels each call launches, in order, with the algorithmic bytes each one
+# carries: the input read goes to the kernel that reads it first, the output
+# write to the kernel that writes it; work the path adds on top of the
+# definition (a re-read, lists in the workspace) carries none.
+def selection_kernels(workload, mode, m, n, k, es, width):
+    read, write = m * n * es, m * width * (es + 4)
+    if workload == "vocab-128k":
+        name = {"exact": "row_exact_kernel<1>", "b64k1": "row_bucket_bf16_kernel<1, false>",
+                "b128k2_final": "row_bucket_bf16_kernel<2, true>"}[mode]
+        return [name], [read + write]
+    if workload == "wide-1m":
+        if mode == "exact":
+            return (["wide_values_kernel<16>", "wide_exact_threshold_kernel", "wide_collect_exact_kernel",
+                     "wide_final_kernel"], [read, 0, 0, write])
+        return (["wide_values_kernel<16>", "wide_collect_bucket_kernel<16>", "wide_final_kernel"], [read, 0, write])
+    return [], []
+
+
+def decode_kernels(c, mode, group):
+    kbytes = c["bsz"] * c["hkv"] * c["ctx"] * c["d"] * 2
+    qbytes = c["bsz"] * c["hq"] * c["d"] * 2
+    vbytes = c["bsz"] * c["hq"] * c["k_sel"] * c["d"] * 2
+    score = ("decode_select_mfma_kernel<%d, %d>" if group > 1 else "decode_select_kernel<%d, %d>")
+    if mode == "bucketed":
+        names = [score % (group, c["kb"]), "decode_finish_kernel<%d>" % c["kb"]]
+    else:
+        names = [score % (group, 8), "decode_finish_kernel<8>"]
+    return names, [kbytes + qbytes, vbytes + qbytes]
+
+
+def run_selection(args, timer, name):
+    """One selection workload: every mode timed back to back over rotating
+    copies, single-call latency after a cache flush, per-kernel stages."""
     import numpy as np
     import torch
 
     import top_sparse_attention_exact_amd as atk
     from top_sparse_attention_exact_amd import workloads
 
-    cfg = workloads.SELECTION["vocab-128k"]
-    m, n, k = cfg["m"], cfg["n"], cfg["k"]
-    x = workloads.rows_normal_bf16(m, n, 2.0, seed=0, device="cuda")
+    c = workloads.SELECTION[name]
+    m, n, k = c["m"], c["n"], c["k"]
+    if name == "vocab-128k":
+        x = workloads.rows_normal_bf16(m, n, 2.0, seed=0, device="cuda")
+    elif name == "wide-1m":
+        x = workloads.rows_planted_residues(m, n, 512, k, seed=0, device="cuda")
+    else:
+        x = workloads.rows_uniform(m, n, seed=0, device="cuda")
+    es = x.element_size()
     xs = copies(x, ROTATE_BYTES)
     torch.cuda.synchronize()
     outs = {}
 
-    def mk(name, f):
+    def mk(mode, f):
         def call(i):
-            outs[name] = f(xs[i % len(xs)])
-        return name, call
+            outs[mode] = f(xs[i % len(xs)])
+        return mode, call
 
-    calls = []
-    if args.only in ("all", "sel", "exact"):
-        calls.append(mk("exact", lambda t: atk.exact(t, k)))
-    if args.only in ("all", "sel", "b64k1"):
-        calls.append(mk("b64k1", lambda t: atk.bucketed(t, k, 64, 1, False)))
-    if args.only in ("all", "sel", "b128k2"):
-        calls.append(mk("b128k2", lambda t: atk.bucketed(t, k, 128, 2, True)))
-    if not calls:
-        return None
-    us, info = timer.stream(calls, args.steps, args.warmup)
+    calls = [mk("exact", lambda t: atk.exact(t, k))]
+    widths = {"exact": k}
+    for b, kb, fin in c["modes"]:
+        mode = "b%dk%d%s" % (b, kb, "_final" if fin else "")
+        calls.append(mk(mode, lambda t, b=b, kb=kb, fin=fin: atk.bucketed(t, k, b, kb, fin)))
+        widths[mode] = k if fin else b * kb
+    steps = args.steps if name == "vocab-128k" else max(3, min(args.steps, 10))
+    us, info = timer.stream(calls, steps, args.warmup)
     cold = timer.cold(calls, max(3, min(args.steps, 10)), 1)
-    width = {"exact": k, "b64k1": 64, "b128k2": k}
-    modes = {}
-    for name, _ in calls:
-        t = us[name] * 1e-6
-        alg = m * n * 2 + m * width[name] * (2 + 4)
-        modes[name] = {
-            "us": round(us[name], 2),
-            "us_cold": round(float(np.mean(cold[name])), 2),
-            "us_cold_median": round(float(np.median(cold[name])), 2),
-            "us_cold_p10": round(float(np.percentile(cold[name], 10)), 2),
-            "us_cold_p90": round(float(np.percentile(cold[name], 90)), 2),
-            "elements_per_s": m * n / t,
-            "alg_bytes": alg,
-            "gbps": alg / t / 1e9,
-            "frac_hbm_peak": alg / t / 1e9 / HBM_PEAK_GBPS,
-        }
-    recall = {}
+    res = {"m": m, "n": n, "k": k, "dtype": "bf16" if es == 2 else "f32", "input_copies": len(xs),
+           "queued_ahead": info["queued_ahead"], "modes": {}}
+    for mode, fn in calls:
+        t = us[mode] * 1e-6
+        alg = m * n * es + m * widths[mode] * (es + 4)
+        d = {"us": round(us[mode], 2), "elements_per_s": m * n / t, "rows_per_s": m / t, "alg_bytes": alg,
+             "gbps": alg / t / 1e9, "frac_hbm_peak": alg / t / 1e9 / HBM_PEAK_GBPS,
+             "us_cold": round(float(np.mean(cold[mode])), 2), **cold_stats(cold[mode])}
+        if not args.no_stages and name != "sel-4k":
+            st_us, _ = stage_split(fn, max(3, min(args.steps, 10)), timer.spin)
+            names, algs = selection_kernels(name, mode, m, n, k, es, widths[mode])
+            d["stages"] = describe_stages(names, algs, st_us)
+        res["modes"][mode] = d
+    # recall of the bucketed modes against the exact result (index recall and,
+    # for ties at the k-th value, value recall), with the recall models
     if "exact" in outs:
-        ex = outs["exact"][1].cpu().numpy()
-        for name in ("b64k1", "b128k2"):
-            if name in outs:
-                got = outs[name][1].cpu().numpy()
-                r = [len(np.intersect1d(a, e)) / k for a, e in zip(got, ex)]
-                recall[name] = float(np.mean(r))
-    step_s = sum(modes[nm]["us"] for nm in modes) * 1e-6
-    return dict(m=m, n=n, k=k, modes=modes, step_s=step_s, info=info, recall=recall, x=x, copies=len(xs))
+        import oracle
+
+        ev, ei = outs["exact"]
+        ex = ei.cpu().numpy()
+        exv = ev.float().cpu().numpy().astype(np.float64)
+        rec = {}
+        for b, kb, fin in c["modes"]:
+            mode = "b%dk%d%s" % (b, kb, "_final" if fin else "")
+            bv, bi = outs[mode]
+            got = bi.cpu().numpy()
+            r = {"index_recall": float(np.mean([len(np.intersect1d(a, e)) / k for a, e in zip(got, ex)])),
+                 "value_recall": float(oracle.value_recall(bv.float().cpu().numpy().astype(np.float64), exv).mean()),
+                 "eq1": oracle.eq1(k, b, kb), "eq1_finite_n": oracle.eq1_finite(n, k, b, kb)}
+            if name == "wide-1m":
+                rr = oracle.recall(got, ex)
+                r["index_recall_iid_rows"] = float(rr[0::2].mean())
+                r["index_recall_adversarial_rows"] = float(rr[1::2].mean())
+                r["eq2_worst_case"] = oracle.eq2(n, k, b, kb)
+            rec[mode] = r
+        res["recall"] = rec
+    res["_x"] = x
+    del xs
+    return res
+
+
+def run_decode(args, timer, name):
+    """One decode workload: bucketed and exact Top-K (and, on gqa-128k, the
+    candidate rerank) timed back to back, per-kernel stages."""
+    import numpy as np
+    import torch
+
+    import top_sparse_attention_exact_amd as atk
+    from top_sparse_attention_exact_amd import workloads
+
+    c = workloads.DECODE[name]
+    if name == "mha-32k":
+        q, K, V, _ = workloads.decode_mha(c["bsz"], c["hq"], c["ctx"], c["d"], 64, 0.8, seed=0, device="cuda")
+    else:
+        q, K, V, _ = workloads.decode_gqa(c["bsz"], c["hq"], c["hkv"], c["ctx"], c["d"], 0.01, 3.0, seed=0,
+                                          device="cuda")
+    torch.cuda.synchronize()
+    group = c["hq"] // c["hkv"]
+    modes = [("bucketed", c["b"], c["kb"]), ("exact", 1, c["k_sel"])]
+    calls = [(mode, (lambda i, b=b, kb=kb: atk.sparse_attn_decode(q, K, V, c["k_sel"], b, kb)))
+             for mode, b, kb in modes]
+    cand = None
+    if name == "gqa-128k":
+        # Candidate rerank on the same cache: per query head 4 retrieved
+        # supports of K_sel positions (seeded uniform draws, repeats allowed)
+        # united with the last K_sel keys, exact Top-K_sel inside.
+        g = torch.Generator(device="cpu").manual_seed(11)
+        ncand = RERANK_SUPPORTS * c["k_sel"]
+        cand = torch.randint(0, c["ctx"], (c["bsz"], c["hq"], ncand), generator=g, dtype=torch.int32).cuda()
+        calls.append(("rerank", lambda i: atk.sparse_attn_rerank(q, K, V, cand, c["k_sel"], c["k_sel"])))
+    steps = max(3, min(args.steps, 10))
+    us, info = timer.stream(calls, steps, 2)
+    kbytes = K.numel() * 2
+    alg = kbytes + q.numel() * 2 + c["bsz"] * c["hq"] * c["k_sel"] * c["d"] * 2 + q.numel() * 2
+    res = {"B": c["bsz"], "Hq": c["hq"], "Hkv": c["hkv"], "L": c["ctx"], "D": c["d"], "K_sel": c["k_sel"],
+           "b": c["b"], "kb": c["kb"], "alg_bytes": alg, "queued_ahead": info["queued_ahead"], "modes": {}}
+    for mode, fn in calls:
+        if mode == "rerank":
+            continue
+        t = us[mode] * 1e-6
+        d = {"us_per_step": round(us[mode], 1), "gbps": alg / t / 1e9, "frac_hbm_peak": alg / t / 1e9 / HBM_PEAK_GBPS,
+             "scores_per_s": c["bsz"] * c["hq"] * c["ctx"] / t}
+        if not args.no_stages:
+            st_us, _ = stage_split(fn, steps, timer.spin)
+            names, algs = decode_kernels(c, mode, group)
+            d["stages"] = describe_stages(names, algs, st_us)
+        res["modes"][mode] = d
+    if cand is not None:
+        heads = c["bsz"] * c["hq"]
+        nuniq = sum(len(np.union1d(row, np.arange(c["ctx"] - c["k_sel"], c["ctx"])))
+                    for row in cand.view(heads, -1).cpu().numpy())
+        ralg = nuniq * c["d"] * 2 + heads * (c["k_sel"] * c["d"] * 2 + cand.shape[2] * 4 + 2 * c["d"] * 2)
+        t = us["rerank"] * 1e-6
+        res["modes"]["rerank"] = {"us_per_step": round(us["rerank"], 1), "supports": RERANK_SUPPORTS,
+                                  "window": c["k_sel"], "mean_candidates": nuniq / heads, "alg_bytes": ralg,
+                                  "gbps": ralg / t / 1e9, "frac_hbm_peak": ralg / t / 1e9 / HBM_PEAK_GBPS,
+                                  "speedup_vs_exact": us["exact"] / us["rerank"]}
+    res["_qkv"] = (q, K, V)
+    return res
 
 
 RERANK_SUPPORTS = 4
 
 
-def decode_steps(args, timer):
+# ------------------------------------------------------ CPU oracle leg ----
+# Run in a process pool created before the GPU is touched ("spawn": fresh
+# interpreters that import numpy and the oracle only).
+
+def cpu_cores():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or platform.machine()
+
+
+def _cpu_selection_task(task):
+    """Oracle on one block of rows, every mode of the workload."""
+    import oracle
+
+    rows, tag, k, modes = task
+    oracle.exact_topk(rows, k, tag)
+    for b, kb, fin in modes:
+        oracle.bucketed_topk(rows, k, b, kb, fin, tag)
+    return rows.shape[0] * rows.shape[1] * (1 + len(modes))
+
+
+def _cpu_decode_task(task):
+    """float64 dense-then-masked decode of the query heads that share one KV
+    head, in the workload's (b, k_b) mode."""
+    import oracle
+
+    q_bits, k_bits, v_bits, scale, k_sel, b, kb = task
+    oracle.attn_decode(q_bits[None], k_bits[None, None], v_bits[None, None], scale, k_sel, b, kb)
+    return q_bits.shape[0] * k_bits.shape[0]
+
+
+def cpu_run(pool, cores, fn, tasks, seconds):
+    """Tasks in waves of `cores` until the time budget is spent (at least one
+    wave).  Returns (units per second, tasks done, wall seconds)."""
+    t0 = time.perf_counter()
+    done = units = 0
+    while done < len(tasks) and (done == 0 or time.perf_counter() - t0 < seconds):
+        wave = tasks[done:done + cores]
+        units += sum(pool.map(fn, wave))
+        done += len(wave)
+    dt = time.perf_counter() - t0
+    return units / dt, done, dt
+
+
+def cpu_leg(pool, cores, sel, dec, seconds):
+    """The CPU oracle (as it stands) on the same bytes as the GPU runs, per
+    workload, over `cores` worker processes."""
     import numpy as np
     import torch
 
-    import top_sparse_attention_exact_amd as atk
     from top_sparse_attention_exact_amd import workloads
 
-    res = {}
-    todo = [w for w in ("mha", "gqa") if args.only in ("all", "decode", w)]
-    for w in todo:
-        if w == "mha":
-            c = workloads.DECODE["mha-32k"]
-            q, K, V, _ = workloads.decode_mha(c["bsz"], c["hq"], c["ctx"], c["d"], 64, 0.8, seed=0, device="cuda")
+    out = {}
+    for name, r in sel.items():
+        c = workloads.SELECTION[name]
+        x = r["_x"]
+        per = 1 if c["n"] >= 1 << 20 else (4 if c["n"] >= 1 << 16 else 64)
+        rows = min(c["m"], per * cores * 8)
+        if x.dtype == torch.bfloat16:
+            hx, tag = x[:rows].cpu().view(torch.int16).numpy().view(np.uint16), "bf16"
         else:
-            c = workloads.DECODE["gqa-128k"]
-            q, K, V, _ = workloads.decode_gqa(c["bsz"], c["hq"], c["hkv"], c["ctx"], c["d"], 0.01, 3.0, seed=0,
-                                              device="cuda")
-        torch.cuda.synchronize()
-        modes = [("bucketed", c["b"], c["kb"]), ("exact", 1, c["k_sel"])]
-        calls = [(name, (lambda i, b=b, kb=kb: atk.sparse_attn_decode(q, K, V, c["k_sel"], b, kb)))
-                 for name, b, kb in modes]
-        if w == "gqa":
-            # Candidate rerank on the same cache: per query head, 4 retrieved
-            # supports of K_sel positions each (seeded uniform draws; repeats
-            # allowed) united with the last K_sel keys, exact Top-K_sel inside.
-            g = torch.Generator(device="cpu").manual_seed(11)
-            ncand = RERANK_SUPPORTS * c["k_sel"]
-            cand = torch.randint(0, c["ctx"], (c["bsz"], c["hq"], ncand), generator=g, dtype=torch.int32).cuda()
-            calls.append(("rerank", lambda i: atk.sparse_attn_rerank(q, K, V, cand, c["k_sel"], c["k_sel"])))
-        us, info = timer.stream(calls, max(3, min(args.steps, 10)), 2)
-        kbytes = K.numel() * 2
-        alg = kbytes + q.numel() * 2 + c["bsz"] * c["hq"] * c["k_sel"] * c["d"] * 2 + q.numel() * 2
-        out = {"workload": "%s-%dk" % (w, c["ctx"] // 1024), "B": c["bsz"], "Hq": c["hq"], "Hkv": c["hkv"],
-               "L": c["ctx"], "K_sel": c["k_sel"], "b": c["b"], "kb": c["kb"], "alg_bytes": alg,
-               "queued_ahead": info["queued_ahead"]}
-        for name, _, _ in modes:
-            t = us[name] * 1e-6
-            out[name] = {"us_per_step": round(us[name], 1), "gbps": alg / t / 1e9,
-                         "frac_hbm_peak": alg / t / 1e9 / HBM_PEAK_GBPS,
-                         "scores_per_s": c["bsz"] * c["hq"] * c["ctx"] / t}
-        if w == "gqa":
-            # Each head reads its unique candidates' K rows, its K_sel V rows
-            # and its candidate list (plus q and out).
-            heads = c["bsz"] * c["hq"]
-            nuniq = sum(len(np.union1d(row, np.arange(c["ctx"] - c["k_sel"], c["ctx"])))
-                        for row in cand.view(heads, -1).cpu().numpy())
-            ralg = nuniq * c["d"] * 2 + heads * (c["k_sel"] * c["d"] * 2 + ncand * 4 + 2 * c["d"] * 2)
-            t = us["rerank"] * 1e-6
-            out["rerank"] = {"us_per_step": round(us["rerank"], 1), "supports": RERANK_SUPPORTS,
-                             "window": c["k_sel"], "mean_candidates": nuniq / heads, "alg_bytes": ralg,
-                             "gbps": ralg / t / 1e9, "frac_hbm_peak": ralg / t / 1e9 / HBM_PEAK_GBPS,
-                             "speedup_vs_exact": us["exact"] / us["rerank"]}
-        res[out["workload"]] = out
-        del q, K, V
-        torch.cuda.empty_cache()
-    return res
-
-
-def other_selection(args, timer):
-    """The 1 x 4096 fp32 and 64 x 2^20 fp32 selection workloads (secondary)."""
-    import torch
-
-    import top_sparse_attention_exact_amd as atk
-    from top_sparse_attention_exact_amd import workloads
-
-    res = {}
-    todo = [w for w in ("sel4k", "wide") if args.only in ("all", w)]
-    for w in todo:
-        if w == "sel4k":
-            c = workloads.SELECTION["sel-4k"]
-            x = workloads.rows_uniform(c["m"], c["n"], seed=0, device="cuda")
-        else:
-            c = workloads.SELECTION["wide-1m"]
-            x = workloads.rows_planted_residues(c["m"], c["n"], 512, c["k"], seed=0, device="cuda")
-        xs = copies(x, ROTATE_BYTES)
-        m, n, k = c["m"], c["n"], c["k"]
-        calls = [("exact", lambda i: atk.exact(xs[i % len(xs)], k))]
-        for b, kb, fin in c["modes"]:
-            calls.append(("b%dk%d%s" % (b, kb, "_final" if fin else ""),
-                          (lambda i, b=b, kb=kb, fin=fin: atk.bucketed(xs[i % len(xs)], k, b, kb, fin))))
-        torch.cuda.synchronize()
-        us, info = timer.stream(calls, max(3, min(args.steps, 10)), 2)
-        out = {"m": m, "n": n, "k": k, "dtype": "f32", "queued_ahead": info["queued_ahead"]}
-        for name, _ in calls:
-            t = us[name] * 1e-6
-            alg = m * n * 4 + m * k * 8
-            out[name] = {"us": round(us[name], 2), "elements_per_s": m * n / t, "gbps": alg / t / 1e9,
-                         "frac_hbm_peak": alg / t / 1e9 / HBM_PEAK_GBPS}
-        res["sel-4k" if w == "sel4k" else "wide-1m"] = out
-        del x, xs
-        torch.cuda.empty_cache()
-    return res
+            hx, tag = x[:rows].cpu().numpy(), "f32"
+        if name == "sel-4k":  # one row at the workload's size: more seeded rows of the same recipe
+            hx = workloads.rows_uniform(per * cores * 4, c["n"], seed=1, device="cpu").numpy()
+        tasks = [(hx[i:i + per], tag, c["k"], c["modes"]) for i in range(0, hx.shape[0], per)]
+        rate, done, dt = cpu_run(pool, cores, _cpu_selection_task, tasks, seconds)
+        out[name] = {"value": rate, "unit": "elements/s", "cores": cores, "kind": "oracle",
+                     "sample": "%d rows x %d, exact + %d bucketed modes per row, %.1f s wall" % (
+                         min(done * per, hx.shape[0]), c["n"], len(c["modes"]), dt)}
+    for name, r in dec.items():
+        c = workloads.DECODE[name]
+        q, K, V = r["_qkv"]
+        g = c["hq"] // c["hkv"]
+        scale = float(np.float32(1.0 / math.sqrt(c["d"])))
+        per_wave = cores
+        groups = [(i, h) for i in range(c["bsz"]) for h in range(c["hkv"])][:per_wave * 4]
+        b16 = lambda t: t.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)  # noqa: E731
+        tasks = [(b16(q[i, h * g:(h + 1) * g]), b16(K[i, h]), b16(V[i, h]), scale, c["k_sel"], c["b"], c["kb"])
+                 for i, h in groups]
+        rate, done, dt = cpu_run(pool, cores, _cpu_decode_task, tasks, seconds)
+        out[name] = {"value": rate, "unit": "scores/s", "cores": cores, "kind": "oracle",
+                     "sample": "%d of %d query heads (float64 dense-then-masked decode, (b, k_b) = (%d, %d)), "
+                               "%.1f s wall" % (done * g, c["bsz"] * c["hq"], c["b"], c["kb"], dt)}
+    return out
 
 
 def assignment_compare(args, timer):
@@ -578,42 +777,10 @@ def copy_calibration(args, timer):
             "gbps": 2 * nbytes / us["copy"] / 1e3}
 
 
-def cpu_leg(sel, seconds):
-    """The CPU oracle (as it stands) on a bounded sample of the same batch."""
-    import numpy as np
-    import torch
-
-    import oracle
-
-    x = sel["x"]
-    m, n, k = sel["m"], sel["n"], sel["k"]
-    hx = x.cpu().view(torch.int16).numpy().view(np.uint16)
-    rows = 0
-    t0 = time.perf_counter()
-    while rows < m and (rows < 8 or time.perf_counter() - t0 < seconds):
-        r = hx[rows:rows + 1]
-        oracle.exact_topk(r, k, "bf16")
-        oracle.bucketed_topk(r, k, 64, 1, False, "bf16")
-        oracle.bucketed_topk(r, k, 128, 2, True, "bf16")
-        rows += 1
-    dt = time.perf_counter() - t0
-    ref = {
-        "b64k1": {"eq1": oracle.eq1(k, 64, 1), "eq1_finite_n": oracle.eq1_finite(n, k, 64, 1)},
-        "b128k2": {"eq1": oracle.eq1(k, 128, 2), "eq1_finite_n": oracle.eq1_finite(n, k, 128, 2)},
-    }
-    return {
-        "value": rows * n * 3 / dt,
-        "unit": "elements/s",
-        "cores": 1,
-        "kind": "oracle",
-        "sample": "%d of %d rows of the step's batch, all three modes (numpy, one thread, %s)" % (
-            rows, m, platform.processor() or platform.machine()),
-    }, ref
-
-
-# The kernel each selection mode of the step launches (one launch per call).
-MODE_KERNEL = {"exact": "row_exact_kernel", "b64k1": "row_bucket_bf16_kernel<1, false>",
-               "b128k2": "row_bucket_bf16_kernel<2, true>"}
+TRAFFIC_NAME = {("vocab-128k", "exact"): "vocab128k_exact", ("vocab-128k", "b64k1"): "vocab128k_b64k1",
+                ("vocab-128k", "b128k2_final"): "vocab128k_b128k2", ("wide-1m", "b512k16_final"): "wide1m_b512k16",
+                ("wide-1m", "exact"): "wide1m_exact", ("mha-32k", "bucketed"): "mha32k_bucketed",
+                ("gqa-128k", "bucketed"): "gqa128k_bucketed"}
 
 
 def main():
@@ -622,63 +789,102 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path (rows and heads shard with no "
               "communication across GPUs). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    only = args.only
+    core = only in ("all", "core")
+    want = {w: core or only == key for w, key in (("mha-32k", "mha"), ("gqa-128k", "gqa"), ("vocab-128k", "vocab"),
+                                                  ("wide-1m", "wide"), ("sel-4k", "sel4k"))}
+    pool = cores = None
+    if not args.no_cpu_baseline and any(want.values()):
+        import multiprocessing
+
+        cores = cpu_cores()
+        pool = multiprocessing.get_context("spawn").Pool(cores)  # before the GPU is touched
     import torch
 
     torch.cuda.set_device(0)
     timer = EventTimer(flush=not args.no_flush)
-    if args.only == "copy":
+    if only == "copy":
         print(json.dumps({"copy_calibration": copy_calibration(args, timer)}), flush=True)
         return
-    sel = selection_step(args, timer) if args.only in ("all", "sel", "exact", "b64k1", "b128k2") else None
-    dec = decode_steps(args, timer) if (not args.no_decode and args.only in ("all", "decode", "mha", "gqa")) else {}
-    other = other_selection(args, timer) if args.only in ("all", "sel4k", "wide") else {}
-    assign = assignment_compare(args, timer) if args.only in ("all", "assign") else None
-    trade = tradeoff(args, timer) if args.only in ("all", "tradeoff") else None
-    swp = sweep(args, timer) if args.only == "sweep" else None
-    graph = graph_leg(args, timer) if args.only in ("all", "graph") else None
-    stream = stream_calibration(args, timer) if args.only in ("all", "stream") else None
+    dec, sel = {}, {}
+    for w in ("mha-32k", "gqa-128k"):
+        if want[w]:
+            dec[w] = run_decode(args, timer, w)
+    for w in ("vocab-128k", "wide-1m", "sel-4k"):
+        if want[w]:
+            sel[w] = run_selection(args, timer, w)
+    cpu = cpu_leg(pool, cores, sel, dec, args.cpu_seconds) if pool is not None else {}
+    if pool is not None:
+        pool.close()
+        pool.join()
+    for r in list(dec.values()) + list(sel.values()):
+        r.pop("_x", None)
+        r.pop("_qkv", None)
+    torch.cuda.empty_cache()
+    assign = assignment_compare(args, timer) if only in ("all", "assign") else None
+    trade = tradeoff(args, timer) if only in ("all", "tradeoff") else None
+    swp = sweep(args, timer) if only == "sweep" else None
+    graph = graph_leg(args, timer) if only in ("all", "graph") else None
+    stream = stream_calibration(args, timer) if only in ("all", "stream") else None
+
+    # roofline per workload: the mode the workload names (bucketed decode,
+    # the slowest vocab-128k mode, (512, 16) + final on wide-1m)
+    roofs = {}
+    for w, r in dec.items():
+        d = r["modes"]["bucketed"]
+        roofs[w] = roofline_block(d.get("stages", []), r["alg_bytes"], d["us_per_step"], TRAFFIC_NAME[(w, "bucketed")])
+        roofs[w]["mode"] = "bucketed (%d, %d)%s" % (r["b"], r["kb"], " + final" if r["b"] * r["kb"] > r["K_sel"] else "")
+    for w, r in sel.items():
+        if w == "sel-4k":
+            continue
+        modes = r["modes"]
+        mode = max(modes, key=lambda nm: modes[nm]["us"]) if w == "vocab-128k" else "b512k16_final"
+        d = modes[mode]
+        roofs[w] = roofline_block(d.get("stages", []), d["alg_bytes"], d["us"], TRAFFIC_NAME[(w, mode)])
+        roofs[w]["mode"] = mode
+    if stream is not None:
+        sizes = {"vocab-128k": "64MiB", "wide-1m": "256MiB", "gqa-128k": "1GiB", "mha-32k": "4GiB"}
+        for w, rf in roofs.items():
+            rf["stream_read_gbps_same_size"] = stream[sizes[w]]["gbps"]
 
     line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
-    if sel is not None:
-        modes = sel["modes"]
-        passes = len(modes)
-        value = passes * sel["m"] * sel["n"] / sel["step_s"]
-        dom = max(modes, key=lambda nm: modes[nm]["us"])
+    if "mha-32k" in dec:
+        r = dec["mha-32k"]
+        d = r["modes"]["bucketed"]
         line.update({
-            "value": value,
-            "unit": "elements/s",
-            "ms_per_step": sel["step_s"] * 1e3,
-            "config": {"workload": "vocab-128k: 256 x 131072 bf16 ~ N(0, 2^2), k = 64; one step = " +
-                                   " + ".join(modes) + " (value counts m*n elements per mode)",
-                       "m": sel["m"], "n": sel["n"], "k": sel["k"], "modes": list(modes),
-                       "input_copies": sel["copies"]},
-            "roofline": {"bound": "hbm", "kernel": MODE_KERNEL[dom] + " (" + dom + ")",
-                         "achieved": modes[dom]["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": modes[dom]["gbps"] / HBM_PEAK_GBPS, "traffic": recorded_traffic(dom),
-                         "alg_bytes_per_launch": modes[dom]["alg_bytes"], "launch_us": modes[dom]["us"]},
-            "modes": modes,
-            "recall": sel["recall"],
-            "timing": {"gpu_ms_per_step": sel["info"]["gpu_s"] / args.steps * 1e3,
-                       "wall_ms_per_step_incl_spin": sel["info"]["wall_s"] / args.steps * 1e3,
-                       "queued_ahead": sel["info"]["queued_ahead"]},
+            "value": d["scores_per_s"], "unit": "scores/s", "ms_per_step": d["us_per_step"] / 1e3,
+            "config": {"workload": "mha-32k: Top-K sparse-attention decode, B16 H32 D128, context 32768, bf16 q/K/V "
+                                   "~ N(0,1) with 64 keys per head planted at cosine 0.8; fp32 scores q.K/sqrt(128); "
+                                   "Top-512 via (b, k_b) = (256, 2); softmax-V over the selected keys; one step = one "
+                                   "decode call over all 512 heads (value = B*H*L scores per second)",
+                       "B": r["B"], "H": r["Hq"], "D": r["D"], "L": r["L"], "K_sel": r["K_sel"], "b": r["b"],
+                       "kb": r["kb"], "alg_bytes_per_step": r["alg_bytes"]},
+            "roofline": roofs["mha-32k"],
         })
-    elif not dec and not other:
-        line.update({"value": None, "unit": "elements/s", "ms_per_step": None,
-                     "config": {"workload": "vocab-128k" if assign or graph else
-                                ("vocab-sampling, kg-2.65m" if trade else ("stream read" if stream else "sweep"))}})
-    elif dec:
-        first = next(iter(dec.values()))
-        line.update({"value": first["bucketed"]["scores_per_s"], "unit": "scores/s",
-                     "ms_per_step": first["bucketed"]["us_per_step"] / 1e3, "config": {"workload": first["workload"]}})
+    elif sel or dec:
+        w, r = next(iter({**dec, **sel}.items()))
+        if w in dec:
+            d = r["modes"]["bucketed"]
+            line.update({"value": d["scores_per_s"], "unit": "scores/s", "ms_per_step": d["us_per_step"] / 1e3})
+        else:
+            d = r["modes"]["exact"]
+            line.update({"value": d["elements_per_s"], "unit": "elements/s", "ms_per_step": d["us"] / 1e3})
+        line["config"] = {"workload": w}
+        if w in roofs:
+            line["roofline"] = roofs[w]
     else:
-        name, first = next(iter(other.items()))
-        line.update({"value": first["exact"]["elements_per_s"], "unit": "elements/s",
-                     "ms_per_step": first["exact"]["us"] / 1e3, "config": {"workload": name}})
-    if dec:
-        line["decode"] = dec
-    if other:
-        line["other_selection"] = other
+        line.update({"value": None, "unit": None, "ms_per_step": None, "config": {"workload": only}})
+    if roofs:
+        line["rooflines"] = roofs
+    if dec or sel:
+        line["workloads"] = {**dec, **sel}
+    if cpu:
+        head = "mha-32k" if "mha-32k" in cpu else next(iter(cpu))
+        line["cpu_baseline"] = dict(cpu[head])
+        line["cpu_baseline"]["cpu_model"] = cpu_model()
+        line["cpu_baseline"]["by_workload"] = {w: {k: v for k, v in c.items() if k in ("value", "unit", "sample")}
+                                               for w, c in cpu.items()}
     if assign is not None:
         line["assignment"] = assign
     if trade is not None:
@@ -689,14 +895,6 @@ def main():
         line["graph"] = graph
     if stream is not None:
         line["stream_read"] = stream
-        if "roofline" in line:
-            line["roofline"]["stream_read_64MiB_gbps"] = stream["64MiB"]["gbps"]
-    if sel is not None and not args.no_cpu_baseline:
-        cpu, ref = cpu_leg(sel, args.cpu_seconds)
-        line["cpu_baseline"] = cpu
-        for nm, r in ref.items():
-            if nm in line["recall"]:
-                line["recall"][nm] = {"measured": line["recall"][nm], **r}
     print(json.dumps(line), flush=True)
 
 

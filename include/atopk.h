@@ -4,17 +4,17 @@
  *
  * What is computed (pages cited by title and section):
  *  - "Approximate Top-k for Increased Parallelism" (Pith review page),
- *    "The reading": exact top-k finds the k largest entries of a vector.
- *    "What carries the argument": the two-stage bucketed top-k splits the n
- *    inputs into b interleaved buckets, takes an exact top-k_b inside every
- *    bucket, and, when the b*k_b candidates exceed k, an exact top-k of them.
- *    Benchmark protocol (reference list): x has shape (m, n).
+ *    "The reading" and "What carries the argument": the exact top-k of a row,
+ *    and the two-stage approximation of it -- positions dealt round-robin
+ *    into b buckets, the k_b best of each bucket kept, and the best k of
+ *    those b*k_b survivors taken when there are more than k of them.  The
+ *    benchmark protocol in the reference list works on an (m, n) matrix x.
  *  - "Recall Before You Rank: Similarity-Guided Top-K Reuse ..." (fugumt
- *    page), Abstract: Top-K sparse attention scores the current query against
- *    the full KV cache, selects a global Top-K, and runs softmax and value
- *    aggregation over that subset only.
- *  - STARC (Pith review page), Figure 3 caption: q in R^{1 x d_h} and
- *    K, V in R^{L x d_h} per attention head.
+ *    page), Abstract: the decode step of Top-K sparse attention -- every
+ *    cached key is scored against the new query, the K best are kept, and
+ *    the softmax-weighted sum of values runs over those K keys alone.
+ *  - STARC (Pith review page), Figure 3 caption: per head the query is one
+ *    row of d_h values, the keys and values L such rows.
  *
  * Conventions shared by every entry point
  *  - Order: value descending, ties to the LOWER index.  -0.0 equals +0.0.
@@ -70,6 +70,25 @@ const char* atopk_status_str(int status);
 
 /* Library version as 10000*major + 100*minor + patch. */
 int atopk_version(void);
+
+/*
+ * Measurement aid for benchmarks and profilers (not needed to use the
+ * library).  After atopk_stage_events(events, count), the calling thread's
+ * following entry-point calls record events[j] (caller-created hipEvent_t
+ * handles, cast to void*) on their stream right after enqueuing their j-th
+ * kernel, counting from 0 across calls until the next atopk_stage_events;
+ * marks beyond `count` are counted but record nothing.  With an event
+ * recorded by the caller before the call, the differences of consecutive
+ * events give each kernel's duration (the stages of the path: scoring and
+ * stage 1, stage 2, softmax-V).  count == 0 (events may be NULL) turns it
+ * off.  atopk_stage_count() returns the number of marks since the last
+ * atopk_stage_events on this thread.  The array must stay valid while on.
+ * Recording events between kernels adds a little time to a call; the
+ * library's results do not change.  ATOPK_ERR_PARAM for count < 0 or a
+ * NULL array with count > 0.
+ */
+int atopk_stage_events(void* const* events, int count);
+int atopk_stage_count(void);
 
 /*
  * Exact top-k of every row of x.
@@ -166,6 +185,9 @@ int atopk_sparse_attn_decode(const void* q, const void* K, const void* V, int64_
  *   softmax and value aggregation over it.
  *   sel_idx [batch, hq, k_sel] int32, nullable: selected keys, score desc,
  *           padded with -1 when the set holds fewer than k_sel keys.
+ *   scores  [batch, hq, ctx] fp32, nullable: the score of every candidate
+ *           key written at its position (other positions are not written;
+ *           a debug dump, as in atopk_sparse_attn_decode).
  * Requires d == 128, hq % hkv == 0, 1 <= ctx <= 262144, ctx_stride >= ctx,
  * 1 <= window <= ctx, 0 <= ncand <= cand_stride, ncand + window <= 8192,
  * 1 <= k_sel <= 8192, 16-byte aligned q, K, V.  The workspace (size from
@@ -177,7 +199,7 @@ int atopk_sparse_attn_rerank_workspace(int64_t batch, int64_t hq, int64_t hkv, i
 int atopk_sparse_attn_rerank(const void* q, const void* K, const void* V, int64_t batch, int64_t hq, int64_t hkv,
                              int64_t ctx, int64_t ctx_stride, int64_t d, float scale, const int32_t* cand,
                              int64_t ncand, int64_t cand_stride, int64_t window, int64_t k_sel, void* out,
-                             int32_t* sel_idx, void* ws, size_t ws_bytes, void* stream);
+                             int32_t* sel_idx, float* scores, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Expected recall of the bucketed top-k ("Approximate Top-k for Increased

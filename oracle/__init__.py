@@ -28,7 +28,6 @@ from .topk import (  # noqa: F401
     bucketed_topk,
     bucket_members,
     contiguous_members,
-    bucket_of,
 )
 from .recall import (  # noqa: F401
     recall,

@@ -47,9 +47,9 @@ def _rank_order(vals, idx):
 def exact_topk(x, k, dtype="f32"):
     """Exact top-k of every row of x (shape [m, n]).
 
-    The k largest entries of each row ("finding the k largest entries of a
-    vector", Approximate Top-k page, "The reading"), ordered by value
-    descending and then by index ascending.
+    The k largest entries of each row (the exact problem stated in the
+    Approximate Top-k page, "The reading"), ordered by value descending and
+    then by index ascending.
 
     Returns (idx [m, k] int64, vals [m, k] in x's own dtype / bit pattern).
     """
@@ -91,22 +91,12 @@ def contiguous_members(n, b, r):
     return i[(i * b) // n == r]
 
 
-def bucket_of(i, n, b, assignment="interleaved"):
-    """Bucket of position i under either assignment."""
-    i = np.asarray(i, dtype=np.int64)
-    if assignment == "interleaved":
-        return i % b
-    if assignment == "contiguous":
-        return (i * b) // n
-    raise ValueError(assignment)
-
-
 def bucketed_topk(x, k, b, kb, final_exact, dtype="f32", assignment="interleaved"):
     """Two-stage bucketed top-k (Approximate Top-k page, "What carries the
-    argument"): split the n inputs into b interleaved buckets, take an exact
-    top-k_b inside every bucket, and optionally take an exact top-k of the
-    b * k_b concatenated candidates.  assignment="contiguous" uses the
-    contiguous buckets of contiguous_members instead.
+    argument"): position i belongs to bucket i mod b; stage 1 keeps the k_b
+    best of every bucket on its own; stage 2, when asked for, is the exact
+    top-k over the b * k_b stage-1 survivors.  assignment="contiguous" uses
+    the contiguous buckets of contiguous_members instead.
 
     Stage 1 output (final_exact False): [m, b * kb], bucket-major, slot
     r * kb + j holding the j-th best element of bucket r.

@@ -33,7 +33,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 17
     handle = ctypes.CDLL(lib_mod.LIB_PATH)
     for name in names:
         assert hasattr(handle, name), name
@@ -45,6 +45,19 @@ def test_status_strings(L):
         assert L.atopk_status_str(s)
     assert L.atopk_status_str(99) == b"unknown status"
     assert L.atopk_version() >= 100
+
+
+def test_stage_events_arguments(L):
+    """The measurement hook validates its arguments, counts marks only from
+    entry points that launch, and turns off with count 0 (no HIP call)."""
+    assert L.atopk_stage_events(None, -1) == EPARAM
+    assert L.atopk_stage_events(None, 3) == EPARAM
+    assert L.atopk_stage_events(None, 0) == OK
+    assert L.atopk_stage_count() == 0
+    # a call that fails validation launches nothing, so marks nothing
+    sz = ctypes.c_size_t(0)
+    assert L.atopk_exact(None, F32, 1, 10, 10, 5, None, None, None, 0, None) == ENULL
+    assert L.atopk_stage_count() == 0
 
 
 def _ws_exact(L, dt, m, n, ldx, k):
@@ -169,7 +182,7 @@ def test_rerank_validation(L):
     def call(bsz=2, hq=8, hkv=2, ctx=4096, stride=4096, d=128, cand=FAKE, ncand=100, cstride=128, window=64,
              k=64, q=FAKE, out=FAKE, ws=FAKE, ws_bytes=1 << 30):
         return L.atopk_sparse_attn_rerank(q, FAKE, FAKE, bsz, hq, hkv, ctx, stride, d, 0.1, cand, ncand, cstride,
-                                          window, k, out, None, ws, ws_bytes, None)
+                                          window, k, out, None, None, ws, ws_bytes, None)
     assert call(hq=6, hkv=4) == ESHAPE          # hq % hkv
     assert call(stride=100) == ESHAPE           # ctx_stride < ctx
     assert call(cstride=50) == ESHAPE           # cand_stride < ncand

@@ -123,6 +123,48 @@ def test_fig2_toy_golden():
     assert Fraction(oracle.eq1(k, b, kb)).limit_denominator(1000) == Fraction(gd["eq1_numerator"], gd["eq1_denominator"])
 
 
+def test_value_recall_golden_ties():
+    """value_recall on hand-derived bf16 rows with ties at the k-th value
+    (tests/golden/value_recall_ties.json): index recall counts a tie at a
+    higher index as a miss, value recall does not."""
+    with open(os.path.join(HERE, "golden", "value_recall_ties.json")) as f:
+        gd = json.load(f)
+    for case in gd["cases"]:
+        bits = (np.array([case["x"]], dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        assert np.array_equal((bits.astype(np.uint32) << 16).view(np.float32), np.array([case["x"]], np.float32))
+        k, b, kb = case["k"], case["b"], case["kb"]
+        ex, exv = oracle.exact_topk(bits, k, "bf16")
+        np.testing.assert_array_equal(ex[0], case["exact_idx"])
+        for stage, final in (("stage1", False), ("final", True)):
+            idx, vals = oracle.bucketed_topk(bits, k, b, kb, final, "bf16")
+            np.testing.assert_array_equal(idx[0], case["%s_idx" % stage])
+            assert oracle.recall(idx, ex)[0] == case["recall_%s" % stage]
+            vr = oracle.value_recall(oracle.to_f64(vals, "bf16"), oracle.to_f64(exv, "bf16"))[0]
+            assert vr == case["value_recall_%s" % stage], (case["name"], stage)
+
+
+def test_value_recall_bounds_index_recall():
+    """Every output index in the exact set has a value >= the k-th exact
+    value, so value recall >= index recall; with distinct values the two are
+    equal; the exact result itself has value recall 1."""
+    rng = np.random.default_rng(12)
+    tied = rng.integers(0, 5, size=(40, 300)).astype(np.float32)
+    distinct = rng.permutation(40 * 300).reshape(40, 300).astype(np.float32)
+    for x, same in ((tied, False), (distinct, True)):
+        ex, exv = oracle.exact_topk(x, 24, "f32")
+        exv64 = oracle.to_f64(exv, "f32")
+        assert (oracle.value_recall(exv64, exv64) == 1.0).all()
+        for b, kb, final in ((8, 3, True), (16, 2, False), (6, 4, True)):
+            idx, vals = oracle.bucketed_topk(x, 24, b, kb, final, "f32")
+            r = oracle.recall(idx, ex)
+            vr = oracle.value_recall(oracle.to_f64(vals, "f32"), exv64)
+            assert (vr >= r - 1e-12).all()
+            if same:
+                np.testing.assert_allclose(vr, r, rtol=0, atol=1e-12)
+            else:
+                assert (vr > r).any()
+
+
 def test_bucketed_reduces_to_exact():
     rng = np.random.default_rng(4)
     x = rng.integers(0, 6, size=(6, 48)).astype(np.float32)  # many ties

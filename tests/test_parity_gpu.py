@@ -9,6 +9,8 @@ selection crosses has a score gap above 1e-3; the bf16 output within 2e-2
 """
 
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
@@ -56,6 +58,35 @@ def check_bucketed(x, k, b, kb, final, assignment="interleaved"):
     ridx, rvals = oracle.bucketed_topk(hx, k, b, kb, final, tag, assignment=assignment)
     np.testing.assert_array_equal(idx.cpu().numpy(), ridx)
     np.testing.assert_array_equal(out_bits(vals), ref_bits(rvals, tag))
+
+
+def host_pool():
+    """Threads for the oracle side of the full-size checks (numpy releases
+    the GIL in its sorts and products)."""
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 4
+    return ThreadPoolExecutor(max(1, min(16, cores)))
+
+
+def check_rows_all(x, k, runs):
+    """Every row of a large batch against the oracle, rows spread over host
+    threads.  runs: list of (name, gpu (vals, idx), oracle function of one
+    host row block -> (idx, vals))."""
+    hx, tag = host(x)
+    got = [(name, idx.cpu().numpy(), out_bits(vals), fn) for name, (vals, idx), fn in runs]
+    chunk = 4
+
+    def one(r0):
+        rows = slice(r0, min(r0 + chunk, hx.shape[0]))
+        for name, gi, gv, fn in got:
+            ridx, rvals = fn(hx[rows], tag)
+            np.testing.assert_array_equal(gi[rows], ridx, err_msg="%s rows %s" % (name, rows))
+            np.testing.assert_array_equal(gv[rows], ref_bits(rvals, tag), err_msg="%s rows %s" % (name, rows))
+
+    with host_pool() as pool:
+        list(pool.map(one, range(0, hx.shape[0], chunk)))
 
 
 def rand_rows(m, n, dtype, seed, gpu):
@@ -221,18 +252,22 @@ def test_vocab128k_full(gpu):
         np.testing.assert_array_equal(bits16(bv), ov)
 
 
-def test_wide1m_sampled_and_worst_case(gpu):
+@pytest.mark.timeout(600)
+def test_wide1m_all_rows_and_worst_case(gpu):
+    """The 64 x 2^20 fp32 batch with k = 8192 in the launches the benchmark
+    times: exact, (512, 16) + final and (512, 16) stage 1 alone, every row
+    bit for bit against the oracle; the adversarial rows' recall is exactly
+    the Eq. (2) worst case."""
     m, n, b, kb, k = 64, 1 << 20, 512, 16, 8192
     x = workloads.rows_planted_residues(m, n, b, k, seed=0, device=gpu)
     bv, bi = atk.bucketed(x, k, b, kb, True)
     ev, ei = atk.exact(x, k)
-    rows = [0, 1, 2, 3, 62, 63]
-    hx = x[rows].cpu().numpy()
-    ridx, rv = oracle.exact_topk(hx, k, "f32")
-    np.testing.assert_array_equal(ei[rows].cpu().numpy(), ridx)
-    np.testing.assert_array_equal(ev[rows].cpu().numpy().view(np.uint32), rv.view(np.uint32))
-    bidx, bvals = oracle.bucketed_topk(hx, k, b, kb, True, "f32")
-    np.testing.assert_array_equal(bi[rows].cpu().numpy(), bidx)
+    sv, si = atk.bucketed(x, k, b, kb, False)
+    check_rows_all(x, k, [
+        ("exact", (ev, ei), lambda h, tag: oracle.exact_topk(h, k, tag)),
+        ("b512k16_final", (bv, bi), lambda h, tag: oracle.bucketed_topk(h, k, b, kb, True, tag)),
+        ("b512k16", (sv, si), lambda h, tag: oracle.bucketed_topk(h, k, b, kb, False, tag)),
+    ])
     r = oracle.recall(bi.cpu().numpy(), ei.cpu().numpy())
     worst = oracle.eq2(n, k, b, kb)
     assert worst == 64 / 8192
@@ -240,44 +275,40 @@ def test_wide1m_sampled_and_worst_case(gpu):
     assert abs(r[0::2].mean() - oracle.eq1_finite(n, k, b, kb)) < 0.01
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["vocab-sampling", "kg-2.65m"])
-def test_tradeoff_shapes_sampled(gpu, name):
+def test_tradeoff_shapes_all_rows(gpu, name):
     """The runtime/accuracy trade-off shapes at full size, in the launches the
-    sweep times: exact top-k and every (b, k_b) of the sweep, final exact, bit
-    for bit against the oracle on sampled rows; the mean recall over all rows
-    within 0.02 of Eq.(1)'s finite-n expectation (iid rows)."""
+    sweep times: exact top-k and three (b, k_b) of the sweep, final exact, bit
+    for bit against the oracle on every row; for every (b, k_b) the mean
+    recall over all rows within 0.02 of Eq.(1)'s finite-n expectation (iid
+    rows)."""
     c = workloads.TRADEOFF[name]
     m, n, k = c["m"], c["n"], c["k"]
     x = workloads.rows_normal(m, n, c["std"], seed=0, device=gpu, workload=name)
-    rows = [0, m - 1]
-    hx = x[rows].cpu().numpy()
     ev, ei = atk.exact(x, k)
-    ridx, rv = oracle.exact_topk(hx, k, "f32")
-    np.testing.assert_array_equal(ei[rows].cpu().numpy(), ridx)
-    np.testing.assert_array_equal(ev[rows].cpu().numpy().view(np.uint32), rv.view(np.uint32))
+    runs = [("exact", (ev, ei), lambda h, tag: oracle.exact_topk(h, k, tag))]
     ex = ei.cpu().numpy()
     for b, kb in workloads.tradeoff_modes(k):
         print("case", name, b, kb, flush=True)
         bv, bi = atk.bucketed(x, k, b, kb, True)
         if (b, kb) in ((1024, 1), (512, 2), (8192, 1)):
-            oidx, ov = oracle.bucketed_topk(hx, k, b, kb, True, "f32")
-            np.testing.assert_array_equal(bi[rows].cpu().numpy(), oidx)
-            np.testing.assert_array_equal(bv[rows].cpu().numpy().view(np.uint32), ov.view(np.uint32))
+            runs.append(("b%dk%d" % (b, kb), (bv, bi),
+                         lambda h, tag, b=b, kb=kb: oracle.bucketed_topk(h, k, b, kb, True, tag)))
         r = oracle.recall(bi.cpu().numpy(), ex).mean()
         assert abs(r - oracle.eq1_finite(n, k, b, kb)) < 0.02, (b, kb, r)
+    check_rows_all(x, k, runs)
 
 
 @pytest.mark.parametrize("name,dtype", [("vocab-sampling", torch.float32), ("vocab-sampling", torch.bfloat16)])
 def test_choose(gpu, name, dtype):
     """The measured chooser: its pick meets the recall target by the model,
     its outputs equal a plain call of the picked (b, k_b) and the oracle on
-    sampled rows, and the measured recall agrees with the model."""
+    every row, and the measured recall agrees with the model."""
     c = workloads.TRADEOFF[name]
     m, n, k = c["m"], c["n"], c["k"]
     x = workloads.rows_normal(m, n, c["std"], seed=3, device=gpu, workload=name).to(dtype)
     _, ex = atk.exact(x, k)
-    rows = [0, m - 1]
-    hx, tag = host(x[rows])
     for target in (0.9, 0.99, 1.0):
         res = atk.choose(x, k, target)
         b, kb = res["b"], res["kb"]
@@ -289,9 +320,8 @@ def test_choose(gpu, name, dtype):
             assert b * kb <= 8192 and res["recall"] == atk.expected_recall(n, k, b, kb)
         v, i = atk.bucketed(x, k, b, kb, True)
         assert torch.equal(v, res["values"]) and torch.equal(i, res["indices"])
-        oidx, ov = oracle.bucketed_topk(hx, k, b, kb, True, tag)
-        np.testing.assert_array_equal(i[rows].cpu().numpy(), oidx)
-        np.testing.assert_array_equal(out_bits(v[rows]), ref_bits(ov, tag))
+        check_rows_all(x, k, [("chosen", (v, i), lambda h, tag, b=b, kb=kb: oracle.bucketed_topk(h, k, b, kb, True,
+                                                                                               tag))])
         if dtype == torch.float32:
             r = oracle.recall(i.cpu().numpy(), ex.cpu().numpy()).mean()
             assert abs(r - res["recall"]) < 0.02
@@ -450,33 +480,59 @@ def test_contiguous_recall_under_correlation(gpu):
 # --------------------------------------------------------------- decode ----
 
 def _decode_check(q, K, V, k_sel, b, kb, rows=None):
+    """The decode in three forms: the call as the benchmark times it (output
+    only), with the selection, and with the selection and the score dump.
+    All three must agree bit for bit (the dump and the selection output do
+    not change what is computed).  Then, for every (batch, query head) -- or
+    the given pairs -- against the float64 oracle: scores within
+    1e-3 * max(1, |s|); the selection bit-exact against the oracle's
+    selection on the GPU's own fp32 scores, and equal as a set to the float64
+    selection where every crossed boundary has a clear gap; the output within
+    2e-2 of the float64 softmax over the GPU's set."""
+    out_t = atk.sparse_attn_decode(q, K, V, k_sel, b, kb)
+    out_s, sel_s = atk.sparse_attn_decode(q, K, V, k_sel, b, kb, return_sel=True)
     out, sel, sc = atk.sparse_attn_decode(q, K, V, k_sel, b, kb, return_sel=True, return_scores=True)
+    assert torch.equal(out_t, out), "the output-only call differs from the dumping call"
+    assert torch.equal(out_s, out) and torch.equal(sel_s, sel), "the selection call differs from the dumping call"
     bsz, hq, d = q.shape
     hkv = K.shape[1]
     g = hq // hkv
-    scale = 1.0 / math.sqrt(d)
-    scale32 = float(np.float32(scale))
+    scale32 = float(np.float32(1.0 / math.sqrt(d)))
     pairs = rows if rows is not None else [(i, h) for i in range(bsz) for h in range(hq)]
+    groups = {}
     for (i, h) in pairs:
-        qb = bits16(q[i:i + 1, h:h + 1])
-        kb_bits = bits16(K[i:i + 1, h // g:h // g + 1])
-        ref_s = oracle.decode_scores(qb, kb_bits, scale32)[0, 0]
-        gpu_s = sc[i, h].cpu().numpy()
-        assert np.all(np.abs(gpu_s - ref_s) <= 1e-3 * np.maximum(1.0, np.abs(ref_s)))
-        gsel = sel[i, h].cpu().numpy()
-        # selection on the GPU's own scores: bit-exact
-        ssel = oracle.attention.select(gpu_s[None, :].astype(np.float64), k_sel, b, kb)[0]
-        np.testing.assert_array_equal(gsel, ssel)
-        # against the float64 selection where every crossed boundary has a clear
-        # gap: the selected set is then fixed (the order inside it is not, where
-        # two selected scores sit within fp32 rounding of each other)
-        fsel = oracle.attention.select(ref_s[None, :], k_sel, b, kb)[0]
-        if _clear_gaps(ref_s, k_sel, b, kb):
-            np.testing.assert_array_equal(np.sort(gsel), np.sort(fsel))
-        vv = oracle.bf16_bits_to_f64(bits16(V[i, h // g]))
-        ref_o = oracle.softmax_v_subset(ref_s, gsel, vv)
-        got_o = out[i, h].float().cpu().numpy()
-        assert np.max(np.abs(got_o - ref_o)) <= 2e-2
+        groups.setdefault((i, h // g), []).append(h)
+    q_h = bits16(q)
+    sel_h = sel.cpu().numpy()
+    out_h = out.float().cpu().numpy()
+
+    def one(item):
+        (i, kvh), heads = item
+        kb_bits = bits16(K[i:i + 1, kvh:kvh + 1])
+        vv = oracle.bf16_bits_to_f64(bits16(V[i, kvh]))
+        ref = oracle.decode_scores(q_h[i:i + 1, heads[0]:heads[-1] + 1], kb_bits, scale32)[0]
+        gpu = sc[i, heads[0]:heads[-1] + 1].cpu().numpy()
+        for h in heads:
+            ref_s = ref[h - heads[0]]
+            gpu_s = gpu[h - heads[0]]
+            assert np.all(np.abs(gpu_s - ref_s) <= 1e-3 * np.maximum(1.0, np.abs(ref_s))), (i, h)
+            gsel = sel_h[i, h]
+            # selection on the GPU's own scores: bit-exact
+            ssel = oracle.attention.select(gpu_s[None, :].astype(np.float64), k_sel, b, kb)[0]
+            np.testing.assert_array_equal(gsel, ssel, err_msg="head %d,%d" % (i, h))
+            # against the float64 selection where every crossed boundary has a
+            # clear gap: the selected set is then fixed (the order inside it is
+            # not, where two selected scores sit within fp32 rounding)
+            if _clear_gaps(ref_s, k_sel, b, kb):
+                fsel = oracle.attention.select(ref_s[None, :], k_sel, b, kb)[0]
+                np.testing.assert_array_equal(np.sort(gsel), np.sort(fsel), err_msg="head %d,%d" % (i, h))
+            ref_o = oracle.softmax_v_subset(ref_s, gsel, vv)
+            assert np.max(np.abs(out_h[i, h] - ref_o)) <= 2e-2, (i, h)
+        return len(heads)
+
+    with host_pool() as pool:
+        done = sum(pool.map(one, sorted(groups.items())))
+    assert done == len(pairs)
     return out, sel, sc
 
 
@@ -625,10 +681,14 @@ def test_decode_ctx_stride(gpu):
     assert torch.equal(out, ref)
 
 
-def test_decode_mha32k_sampled(gpu):
+@pytest.mark.timeout(900)
+def test_decode_mha32k_all_heads(gpu):
+    """B16 H32 L32768, Top-512 via (256, 2): all 512 heads, in the call the
+    benchmark times and with the dumps (see _decode_check); then the exact
+    Top-512 (certified route) on all heads as well."""
     c = workloads.DECODE["mha-32k"]
     q, K, V, planted = workloads.decode_mha(c["bsz"], c["hq"], c["ctx"], c["d"], 64, 0.8, seed=0, device=gpu)
-    out, sel, sc = _decode_check(q, K, V, c["k_sel"], c["b"], c["kb"], rows=[(0, 0), (3, 17), (15, 31)])
+    out, sel, sc = _decode_check(q, K, V, c["k_sel"], c["b"], c["kb"])
     # Planted keys outscore every other key, so stage 1 keeps exactly
     # min(k_b, t_r) of the t_r planted keys that fall in bucket r.
     s = sel.cpu().numpy()
@@ -638,50 +698,73 @@ def test_decode_mha32k_sampled(gpu):
             kept = len(set(p[i, h].tolist()) & set(s[i, h].tolist()))
             t = np.bincount(p[i, h] % c["b"], minlength=c["b"])
             assert kept == np.minimum(t, c["kb"]).sum()
+    del out, sel, sc
+    _decode_check(q, K, V, c["k_sel"], 1, c["k_sel"])
 
 
-def test_decode_gqa128k_sampled(gpu):
+@pytest.mark.timeout(900)
+def test_decode_gqa128k_all_heads(gpu):
+    """B4 Hq32 Hkv8 L131072, Top-512 via (512, 4) + final and exact: all 128
+    query heads in both modes, in the calls the benchmark times and with the
+    dumps (see _decode_check)."""
     c = workloads.DECODE["gqa-128k"]
     q, K, V, _ = workloads.decode_gqa(c["bsz"], c["hq"], c["hkv"], c["ctx"], c["d"], 0.01, 3.0, seed=0, device=gpu)
-    _decode_check(q, K, V, c["k_sel"], c["b"], c["kb"], rows=[(0, 0), (1, 5), (3, 31)])
-    _decode_check(q, K, V, c["k_sel"], 1, c["k_sel"], rows=[(2, 9)])
+    _decode_check(q, K, V, c["k_sel"], c["b"], c["kb"])
+    _decode_check(q, K, V, c["k_sel"], 1, c["k_sel"])
 
 
 # ------------------------------------------------------ candidate rerank ----
 
 def _rerank_check(q, K, V, cand, window, k_sel, heads=None):
-    """GPU rerank against the float64 oracle: the selected set equals the
-    oracle's wherever the K-th / (K+1)-th candidate scores differ by more than
-    1e-3, and is a valid Top-K within that tolerance elsewhere; the output is
-    within 2e-2 of the float64 softmax over the GPU's own selection."""
-    out, sel = atk.sparse_attn_rerank(q, K, V, cand, window, k_sel, return_sel=True)
+    """GPU rerank against the float64 oracle.  The call without dumps must
+    equal the dumping call bit for bit.  Per head: the dumped fp32 scores of
+    the candidates within 1e-3 * max(1, |s|) of float64; the selection
+    bit-exact (order included) against the oracle's Top-K of the candidate
+    set on the GPU's own scores; equal as a set to the float64 selection where
+    the K-th / (K+1)-th float64 scores differ by more than 1e-3; the output
+    within 2e-2 of the float64 softmax over the GPU's selection."""
+    out_t = atk.sparse_attn_rerank(q, K, V, cand, window, k_sel)
+    out, sel, scd = atk.sparse_attn_rerank(q, K, V, cand, window, k_sel, return_sel=True, return_scores=True)
+    assert torch.equal(out_t, out), "the output-only call differs from the dumping call"
     bsz, hq, d = q.shape
     g = hq // K.shape[1]
     length = K.shape[2]
-    scale = 1.0 / math.sqrt(d)
+    scale = float(np.float32(1.0 / math.sqrt(d)))
     cand_h = cand.cpu().numpy()
     sel_h = sel.cpu().numpy()
     out_h = out.float().cpu().numpy()
-    for (i, h) in (heads or [(i, h) for i in range(bsz) for h in range(hq)]):
-        qb = bits16(q[i:i + 1, h:h + 1])
+    q_h = bits16(q)
+    todo = heads or [(i, h) for i in range(bsz) for h in range(hq)]
+
+    def one(ih):
+        i, h = ih
         kb = bits16(K[i:i + 1, h // g:h // g + 1])
-        vb = bits16(V[i:i + 1, h // g:h // g + 1])
+        vb = bits16(V[i, h // g])
         c = oracle.rerank_candidates(cand_h[i, h], window, length)
-        sc = oracle.decode_scores(qb, kb, scale)[0, 0]
+        sc = oracle.decode_scores(q_h[i:i + 1, h:h + 1], kb, scale)[0, 0]
+        gs = scd[i, h].cpu().numpy()
+        assert not np.isnan(gs[c]).any(), (i, h)
+        assert np.all(np.abs(gs[c] - sc[c]) <= 1e-3 * np.maximum(1.0, np.abs(sc[c]))), (i, h)
         kk = min(k_sel, len(c))
         got = sel_h[i, h]
         assert (got[kk:] == -1).all()
         got = got[:kk]
-        assert len(set(got.tolist())) == kk and set(got.tolist()) <= set(c.tolist())
+        # the oracle's Top-K of the set on the GPU's own scores: bit-exact
+        own = np.full(len(gs), -np.inf)
+        own[c] = gs[c]
+        _, ref_own, _ = oracle.rerank_decode(None, None, vb[None, None], scale, cand_h[i:i + 1, h:h + 1], window,
+                                             k_sel, scores=own[None, None])
+        np.testing.assert_array_equal(got, ref_own[0, 0, :kk], err_msg="head %d,%d" % (i, h))
         cs = np.sort(sc[c])[::-1]
         if kk < len(c) and cs[kk - 1] - cs[kk] > 1e-3:
-            _, ref_sel, _ = oracle.rerank_decode(qb, kb, vb, scale, cand_h[i:i + 1, h:h + 1], window, k_sel)
+            _, ref_sel, _ = oracle.rerank_decode(None, None, vb[None, None], scale, cand_h[i:i + 1, h:h + 1], window,
+                                                 k_sel, scores=sc[None, None])
             assert set(got.tolist()) == set(ref_sel[0, 0, :kk].tolist()), (i, h)
-        elif kk < len(c):
-            rest = np.setdiff1d(c, got)
-            assert sc[got].min() >= sc[rest].max() - 2e-3
-        ref = oracle.softmax_v_subset(sc, got, oracle.bf16_bits_to_f64(vb)[0, 0])
+        ref = oracle.softmax_v_subset(sc, got, oracle.bf16_bits_to_f64(vb))
         assert np.abs(out_h[i, h] - ref).max() <= 2e-2, (i, h)
+
+    with host_pool() as pool:
+        list(pool.map(one, todo))
 
 
 def _rerank_inputs(bsz, hq, hkv, length, ncand, seed, gpu):
@@ -711,14 +794,15 @@ def test_rerank_whole_cache_matches_exact_decode(gpu):
     assert (out.float() - out2.float()).abs().max().item() <= 1e-2
 
 
-def test_rerank_gqa128k_shape_sampled(gpu):
+@pytest.mark.timeout(900)
+def test_rerank_gqa128k_shape_all_heads(gpu):
     """The long-context shape: 4 retrieved supports of 512 keys per head plus
-    a 512-key window, Top-512, at B4 Hq32 Hkv8 L131072."""
+    a 512-key window, Top-512, at B4 Hq32 Hkv8 L131072, every query head."""
     c = workloads.DECODE["gqa-128k"]
     q, K, V, _ = workloads.decode_gqa(c["bsz"], c["hq"], c["hkv"], c["ctx"], c["d"], 0.01, 3.0, seed=0, device=gpu)
     g = torch.Generator(device="cpu").manual_seed(7)
     cand = torch.randint(0, c["ctx"], (c["bsz"], c["hq"], 4 * 512), generator=g, dtype=torch.int32).to(gpu)
-    _rerank_check(q, K, V, cand, 512, 512, heads=[(0, 0), (1, 7), (3, 31)])
+    _rerank_check(q, K, V, cand, 512, 512)
 
 
 # ------------------------------------------------------ HIP graph replay ----

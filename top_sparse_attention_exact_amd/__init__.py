@@ -162,12 +162,14 @@ def sparse_attn_decode(q, K, V, k_sel, b=1, kb=None, scale=None, ctx=None, retur
     return res[0] if len(res) == 1 else tuple(res)
 
 
-def sparse_attn_rerank(q, K, V, cand, window, k_sel, scale=None, ctx=None, return_sel=False, workspace=None):
+def sparse_attn_rerank(q, K, V, cand, window, k_sel, scale=None, ctx=None, return_sel=False, return_scores=False,
+                       workspace=None):
     """Candidate-set rerank decode.  q [B, Hq, D], K/V [B, Hkv, Lmax, D] bf16;
     cand [B, Hq, C] int32 candidate key indices per query head (entries
     outside [0, ctx) are skipped, repeats count once); the last `window` keys
     are candidates too.  Returns out [B, Hq, D] bf16 (plus int32 sel_idx
-    [B, Hq, k_sel], -1 padded, when asked)."""
+    [B, Hq, k_sel], -1 padded, and fp32 scores [B, Hq, ctx] -- NaN except at
+    the candidates' positions -- when asked)."""
     for t in (q, K, V):
         if t.dtype != torch.bfloat16 or not t.is_cuda:
             raise TypeError("q, K, V must be bf16 GPU tensors")
@@ -183,6 +185,7 @@ def sparse_attn_rerank(q, K, V, cand, window, k_sel, scale=None, ctx=None, retur
     scale = (1.0 / d ** 0.5) if scale is None else scale
     out = torch.empty((bsz, hq, d), dtype=torch.bfloat16, device=q.device)
     sel = torch.empty((bsz, hq, k_sel), dtype=torch.int32, device=q.device) if return_sel else None
+    scores = torch.full((bsz, hq, ctx), float("nan"), dtype=torch.float32, device=q.device) if return_scores else None
     ncand = cand.shape[2]
     size = ctypes.c_size_t(0)
     check(lib().atopk_sparse_attn_rerank_workspace(bsz, hq, hkv, ctx, ncand, window, ctypes.byref(size)),
@@ -190,10 +193,37 @@ def sparse_attn_rerank(q, K, V, cand, window, k_sel, scale=None, ctx=None, retur
     ws, nbytes = (workspace, workspace.numel()) if workspace is not None else _workspace(size.value, q.device)
     st = lib().atopk_sparse_attn_rerank(_ptr(q), _ptr(K), _ptr(V), bsz, hq, hkv, ctx, lmax, d, float(scale),
                                         _ptr(cand) if ncand > 0 else ctypes.c_void_p(0), ncand,
-                                        ncand, window, k_sel, _ptr(out), _ptr(sel), _ptr(ws), nbytes,
+                                        ncand, window, k_sel, _ptr(out), _ptr(sel), _ptr(scores), _ptr(ws), nbytes,
                                         _stream_ptr(q.device))
     check(st, "atopk_sparse_attn_rerank")
-    return (out, sel) if return_sel else out
+    res = [out] + ([sel] if return_sel else []) + ([scores] if return_scores else [])
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+_stage_array = None
+
+
+def stage_events(events):
+    """Measurement aid (atopk_stage_events): after this, the calling thread's
+    library calls record events[j] on their stream right after enqueuing
+    their j-th kernel (counting across calls).  `events` are
+    torch.cuda.Event objects created with enable_timing=True and recorded
+    once already (so that the HIP event exists); None or [] turns it off.
+    Returns nothing; stage_count() gives the marks made so far."""
+    global _stage_array
+    if not events:
+        _stage_array = None
+        check(lib().atopk_stage_events(None, 0), "atopk_stage_events")
+        return
+    arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    if any(not e.cuda_event for e in events):
+        raise ValueError("record each event once before handing it to the library")
+    _stage_array = arr
+    check(lib().atopk_stage_events(arr, len(events)), "atopk_stage_events")
+
+
+def stage_count():
+    return lib().atopk_stage_count()
 
 
 def expected_recall(n, k, b, kb):

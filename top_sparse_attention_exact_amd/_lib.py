@@ -14,6 +14,8 @@ _c_size_p = ctypes.POINTER(ctypes.c_size_t)
 _SIGNATURES = {
     "atopk_status_str": (ctypes.c_char_p, [_c_int]),
     "atopk_version": (_c_int, []),
+    "atopk_stage_events": (_c_int, [ctypes.POINTER(_c_vp), _c_int]),
+    "atopk_stage_count": (_c_int, []),
     "atopk_exact_workspace": (_c_int, [_c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_size_p]),
     "atopk_exact": (_c_int, [_c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, ctypes.c_size_t, _c_vp]),
     "atopk_bucketed_workspace": (_c_int, [_c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_int, _c_size_p]),
@@ -43,7 +45,7 @@ _SIGNATURES = {
     "atopk_sparse_attn_rerank": (
         _c_int,
         [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, ctypes.c_float, _c_vp, _c_i64, _c_i64,
-         _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, ctypes.c_size_t, _c_vp],
+         _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp, ctypes.c_size_t, _c_vp],
     ),
     "atopk_expected_recall": (_c_int, [_c_i64, _c_i64, _c_i64, _c_i64, ctypes.POINTER(ctypes.c_double)]),
     "atopk_choose_workspace": (

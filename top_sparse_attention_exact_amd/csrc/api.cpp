@@ -15,6 +15,20 @@
 
 using namespace atopk;
 
+// ---- stage events (measurement aid) -------------------------------------------
+
+namespace {
+thread_local void* const* t_stage_events = nullptr;
+thread_local int t_stage_cap = 0;
+thread_local int t_stage_marks = 0;
+}  // namespace
+
+void atopk::stage_mark(hipStream_t s) {
+  if (t_stage_events != nullptr && t_stage_marks < t_stage_cap)
+    (void)hipEventRecord(static_cast<hipEvent_t>(t_stage_events[t_stage_marks]), s);
+  ++t_stage_marks;
+}
+
 namespace {
 
 constexpr int64_t kMaxN = (int64_t)1 << 31;  // indices are int32
@@ -422,7 +436,17 @@ const char* atopk_status_str(int status) {
   }
 }
 
-int atopk_version(void) { return 10000 * 0 + 100 * 1 + 0; }
+int atopk_version(void) { return 10000 * 0 + 100 * 2 + 0; }
+
+int atopk_stage_events(void* const* events, int count) {
+  if (count < 0 || (count > 0 && events == nullptr)) return ATOPK_ERR_PARAM;
+  t_stage_events = count > 0 ? events : nullptr;
+  t_stage_cap = count;
+  t_stage_marks = 0;
+  return ATOPK_OK;
+}
+
+int atopk_stage_count(void) { return t_stage_marks; }
 
 int atopk_exact_workspace(int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k, size_t* ws_bytes) {
   return guarded([&] {
@@ -588,7 +612,7 @@ int atopk_sparse_attn_rerank_workspace(int64_t batch, int64_t hq, int64_t hkv, i
 int atopk_sparse_attn_rerank(const void* q, const void* K, const void* V, int64_t batch, int64_t hq, int64_t hkv,
                              int64_t ctx, int64_t ctx_stride, int64_t d, float scale, const int32_t* cand,
                              int64_t ncand, int64_t cand_stride, int64_t window, int64_t k_sel, void* out,
-                             int32_t* sel_idx, void* ws, size_t ws_bytes, void* stream) {
+                             int32_t* sel_idx, float* scores, void* ws, size_t ws_bytes, void* stream) {
   return guarded([&] {
     int st = validate_rerank(batch, hq, hkv, ctx, ctx_stride, d, k_sel, ncand, cand_stride, window);
     if (st) return st;
@@ -602,7 +626,7 @@ int atopk_sparse_attn_rerank(const void* q, const void* K, const void* V, int64_
     if (st) return st;
     return hip_status(launch_rerank(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(K),
                                     static_cast<const uint16_t*>(V), batch, hq, hkv, ctx, ctx_stride, scale, cand,
-                                    ncand, cand_stride, window, k_sel, static_cast<uint16_t*>(out), sel_idx, ws,
+                                    ncand, cand_stride, window, k_sel, static_cast<uint16_t*>(out), sel_idx, scores, ws,
                                     static_cast<hipStream_t>(stream)));
   });
 }

@@ -96,7 +96,7 @@ hipError_t launch_sparse_softmax_v(const float* sel_vals, const int32_t* sel_idx
                                    int64_t hq, int64_t hkv, int64_t ctx_stride, int64_t k_sel, uint16_t* out,
                                    hipStream_t s) {
   dim3 grid((unsigned)(batch * hq));
-  hipLaunchKernelGGL(sparse_softmax_v_kernel, grid, dim3(kDecThreads), 0, s, sel_vals, sel_idx, V, (int)hq, (int)hkv,
+  ATOPK_LAUNCH(sparse_softmax_v_kernel, grid, dim3(kDecThreads), 0, s, sel_vals, sel_idx, V, (int)hq, (int)hkv,
                      ctx_stride, (int)k_sel, out);
   return hipGetLastError();
 }

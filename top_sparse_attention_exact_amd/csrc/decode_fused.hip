@@ -2,11 +2,12 @@
 // pass over K, then per query head the merge, the final exact Top-K and the
 // softmax / value aggregation over the selected keys.
 //
-// "Recall Before You Rank ..." (fugumt page), Abstract: score the current
-// query against the full KV cache, select a global Top-K, run softmax and
-// value aggregation over that subset only.  "Approximate Top-k for Increased
-// Parallelism" (Pith review page), "What carries the argument": the bucketed
-// two-stage selection that replaces the single global Top-K.
+// "Recall Before You Rank ..." (fugumt page), Abstract: every cached key is
+// scored against the new query, the K best keys are kept, and the attention
+// softmax and the weighted value sum run over those K keys only.
+// "Approximate Top-k for Increased Parallelism" (Pith review page), "What
+// carries the argument": the two-stage bucketed selection stands in for the
+// single global Top-K.
 //
 // Kernel 1 (grid: context chunks x (batch, KV head)): 16 lanes read one
 // 256-byte key row with 16-byte loads and form its dot products with the g
@@ -691,10 +692,10 @@ hipError_t launch_decode_scores(const uint16_t* q, const uint16_t* K, int64_t ba
   const DecodePlan p = plan_decode(batch, hq, hkv, ctx, 1, 1, 1);
   dim3 g1((unsigned)p.nchunks, (unsigned)(batch * hkv));
   if (p.mfma)
-    hipLaunchKernelGGL((decode_select_mfma_kernel<1, 1>), g1, dim3(kT1M), 0, s, q, K, (int)hq, (int)hkv, (int)ctx,
+    ATOPK_LAUNCH((decode_select_mfma_kernel<1, 1>), g1, dim3(kT1M), 0, s, q, K, (int)hq, (int)hkv, (int)ctx,
                        ctx_stride, scale, 0, p.chunk, p.nchunks, nullptr, scores);
   else
-    hipLaunchKernelGGL((decode_select_kernel<1, 1>), g1, dim3(kT1), 0, s, q, K, (int)hq, (int)hkv, (int)ctx,
+    ATOPK_LAUNCH((decode_select_kernel<1, 1>), g1, dim3(kT1), 0, s, q, K, (int)hq, (int)hkv, (int)ctx,
                        ctx_stride, scale, 0, p.chunk, p.nchunks, nullptr, scores);
   return hipGetLastError();
 }
@@ -710,10 +711,10 @@ hipError_t launch_decode_fused(const DecodePlan& p, const uint16_t* q, const uin
 #define ATOPK_D1(P, KBV)                                                                                            \
   if (p.ppt == P && kbs == KBV) {                                                                                   \
     if (p.mfma)                                                                                                     \
-      hipLaunchKernelGGL((decode_select_mfma_kernel<P, KBV>), g1, dim3(kT1M), 0, s, q, K, (int)hq, (int)hkv,         \
+      ATOPK_LAUNCH((decode_select_mfma_kernel<P, KBV>), g1, dim3(kT1M), 0, s, q, K, (int)hq, (int)hkv,         \
                          (int)ctx, ctx_stride, scale, (int)b, p.chunk, p.nchunks, partial, scores);                  \
     else                                                                                                            \
-      hipLaunchKernelGGL((decode_select_kernel<P, KBV>), g1, dim3(kT1), 0, s, q, K, (int)hq, (int)hkv, (int)ctx,     \
+      ATOPK_LAUNCH((decode_select_kernel<P, KBV>), g1, dim3(kT1), 0, s, q, K, (int)hq, (int)hkv, (int)ctx,     \
                          ctx_stride, scale, (int)b, p.chunk, p.nchunks, partial, scores);                            \
   } else
   ATOPK_D1(1, 1) ATOPK_D1(1, 2) ATOPK_D1(1, 4) ATOPK_D1(1, 8) ATOPK_D1(1, 16)
@@ -727,7 +728,7 @@ hipError_t launch_decode_fused(const DecodePlan& p, const uint16_t* q, const uin
   dim3 g2((unsigned)(batch * hq));
 #define ATOPK_D2(KBV)                                                                                              \
   case KBV:                                                                                                        \
-    hipLaunchKernelGGL((decode_finish_kernel<KBV>), g2, dim3(kT2), 0, s, partial, p.nchunks, (int)hq, (int)hkv,     \
+    ATOPK_LAUNCH((decode_finish_kernel<KBV>), g2, dim3(kT2), 0, s, partial, p.nchunks, (int)hq, (int)hkv,     \
                        (int)b, (int)kb, (int)k_sel, V, ctx_stride, out, sel_idx, certify, cert_buf, (int)ctx, q, K, \
                        scale);                                                                                      \
     break;

@@ -8,6 +8,18 @@
 
 namespace atopk {
 
+// Measurement aid behind atopk_stage_events: records the calling thread's
+// next stage event (if any) on the stream after a kernel launch.
+void stage_mark(hipStream_t s);
+
+// Every kernel launch of the library goes through this: the launch, then the
+// stage mark.
+#define ATOPK_LAUNCH(kernel, grid, block, shmem, stream, ...)                 \
+  do {                                                                       \
+    hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);     \
+    ::atopk::stage_mark(stream);                                             \
+  } while (0)
+
 // Element types (match atopk_dtype) plus pre-built 64-bit keys.
 enum InKind { IN_F32 = 0, IN_BF16 = 1, IN_KEY64 = 2 };
 
@@ -141,7 +153,7 @@ size_t rerank_ws_bytes(int64_t batch, int64_t hq, int64_t ncand, int64_t window)
 hipError_t launch_rerank(const uint16_t* q, const uint16_t* K, const uint16_t* V, int64_t batch, int64_t hq,
                          int64_t hkv, int64_t ctx, int64_t ctx_stride, float scale, const int32_t* cand, int64_t ncand,
                          int64_t cand_stride, int64_t window, int64_t k_sel, uint16_t* out, int32_t* sel_idx,
-                         void* ws, hipStream_t s);
+                         float* scores, void* ws, hipStream_t s);
 
 // out[r] = softmax(sel_vals[r]) @ V[sel_idx[r]] for r = i*hq + h.
 hipError_t launch_sparse_softmax_v(const float* sel_vals, const int32_t* sel_idx, const uint16_t* V,

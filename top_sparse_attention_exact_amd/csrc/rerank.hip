@@ -14,7 +14,8 @@
 //     positions -- made unique with an LDS bitmap over the range; their
 //     scores: 16 lanes read one 256-byte key row with 16-byte loads and form
 //     its dot product with the query (packed bf16 dot products, fp32
-//     accumulation, DPP row sums), scaled in fp32; keys to the workspace.
+//     accumulation, DPP row sums), scaled in fp32; keys to the workspace
+//     (and, when asked, each score to its position in a [heads, ctx] dump).
 //     Splitting by position keeps every workgroup's bitmap small and puts
 //     the whole chip on the gather when there are few heads.
 //  2. one workgroup per query head: exact Top-K of its keys by (score desc,
@@ -64,7 +65,7 @@ __global__ __launch_bounds__(kRT) void rerank_score_kernel(const uint16_t* __res
                                                           const int32_t* __restrict__ cand, int ncand,
                                                           int64_t cand_stride, int window, int range,
                                                           uint64_t* __restrict__ keys_out,
-                                                          int* __restrict__ cnt_out) {
+                                                          int* __restrict__ cnt_out, float* __restrict__ scores) {
   constexpr int T = kRT;
   __shared__ uint32_t list[kRerankMaxCand];
   __shared__ uint32_t bits[kRerankMaxCtx / 32];
@@ -123,7 +124,10 @@ __global__ __launch_bounds__(kRT) void rerank_score_kernel(const uint16_t* __res
     for (int u = 0; u < U; ++u) {
       const int i = i0 + group + kGroups * u;
       const float sc = row16_sum(dot8_bf16(kv[u], qv)) * scale;
-      if (i < nc && sub == 0) dst[i] = make_key(ord_f32(__float_as_uint(sc)), jj[u]);
+      if (i < nc && sub == 0) {
+        dst[i] = make_key(ord_f32(__float_as_uint(sc)), jj[u]);
+        if (scores != nullptr) scores[(int64_t)r_out * ctx + jj[u]] = sc;
+      }
     }
   }
   if (t == 0) cnt_out[(int64_t)r_out * S + sp] = nc;
@@ -259,7 +263,7 @@ size_t rerank_ws_bytes(int64_t batch, int64_t hq, int64_t ncand, int64_t window)
 hipError_t launch_rerank(const uint16_t* q, const uint16_t* K, const uint16_t* V, int64_t batch, int64_t hq,
                          int64_t hkv, int64_t ctx, int64_t ctx_stride, float scale, const int32_t* cand, int64_t ncand,
                          int64_t cand_stride, int64_t window, int64_t k_sel, uint16_t* out, int32_t* sel_idx,
-                         void* ws, hipStream_t s) {
+                         float* scores, void* ws, hipStream_t s) {
   const int S = rerank_splits(batch, hq, ncand, window);
   const int64_t rows = batch * hq * S;
   const int64_t total = ncand + window;
@@ -267,11 +271,11 @@ hipError_t launch_rerank(const uint16_t* q, const uint16_t* K, const uint16_t* V
   int* cnt = reinterpret_cast<int*>(static_cast<uint8_t*>(ws) + ((size_t)rows * total * 8 + 255) / 256 * 256);
   int range = (int)((ctx + S - 1) / S);
   range = (range + 31) / 32 * 32;
-  hipLaunchKernelGGL(rerank_score_kernel, dim3((unsigned)(batch * hq), (unsigned)S), dim3(kRT), 0, s, q, K, (int)hq,
-                     (int)hkv, (int)ctx, ctx_stride, scale, cand, (int)ncand, cand_stride, (int)window, range, keys, cnt);
+  ATOPK_LAUNCH(rerank_score_kernel, dim3((unsigned)(batch * hq), (unsigned)S), dim3(kRT), 0, s, q, K, (int)hq,
+                     (int)hkv, (int)ctx, ctx_stride, scale, cand, (int)ncand, cand_stride, (int)window, range, keys, cnt, scores);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(rerank_select_kernel, dim3((unsigned)(batch * hq)), dim3(kST), 0, s, keys, cnt, S, (int)total,
+  ATOPK_LAUNCH(rerank_select_kernel, dim3((unsigned)(batch * hq)), dim3(kST), 0, s, keys, cnt, S, (int)total,
                      (int)hq, (int)hkv, ctx_stride, V, (int)k_sel, out, sel_idx);
   return hipGetLastError();
 }

@@ -2,9 +2,9 @@
 // buckets) and the merge / final stage.
 //
 // "Approximate Top-k for Increased Parallelism" (Pith review page), "What
-// carries the argument": split the n inputs into b interleaved buckets,
-// take an exact top-k_b in each bucket independently, and, if the b*k_b
-// candidates exceed k, take an exact top-k of them.  The pages' kernel keeps
+// carries the argument": position i goes to bucket i mod b, each bucket keeps
+// its own k_b best independently of the others, and when more than k
+// survivors result, an exact top-k over them follows.  The pages' kernel keeps
 // one small priority queue per thread in registers (k_b <= 4); here every
 // lane keeps one sorted k_b-queue per element slot of its 16-byte loads, so
 // a sweep of the workgroup over T*V consecutive elements (a multiple of b)
@@ -513,7 +513,7 @@ hipError_t launch_stage1_dt(const BucketPlan& p, const void* x, int64_t m, int64
     dim3 grid((unsigned)p.splits, (unsigned)m);
 #define ATOPK_S1(KBV)                                                                                          \
   case KBV:                                                                                                    \
-    hipLaunchKernelGGL((bucket_stage1_kernel<DT, KBV>), grid, dim3(kStage1Threads), 0, s, xb, ld_bytes, (int)n, \
+    ATOPK_LAUNCH((bucket_stage1_kernel<DT, KBV>), grid, dim3(kStage1Threads), 0, s, xb, ld_bytes, (int)n, \
                        (int)b, p.chunk, lds_merge, p.lists_per_row, lists, direct, (int)kb, (int)k, ov,       \
                        out_idx);                                                                              \
     break;
@@ -526,7 +526,7 @@ hipError_t launch_stage1_dt(const BucketPlan& p, const void* x, int64_t m, int64
     dim3 grid((unsigned)((b + 255) / 256), (unsigned)m, (unsigned)p.splits);
 #define ATOPK_G(KBV)                                                                                       \
   case KBV:                                                                                                \
-    hipLaunchKernelGGL((bucket_generic_kernel<DT, KBV>), grid, dim3(256), 0, s, xb, ld_bytes, (int)n, (int)b, \
+    ATOPK_LAUNCH((bucket_generic_kernel<DT, KBV>), grid, dim3(256), 0, s, xb, ld_bytes, (int)n, (int)b, \
                        p.chunk, p.lists_per_row, lists);                                                  \
     break;
     switch (kb_slots(kb)) {
@@ -601,7 +601,7 @@ hipError_t launch_bucket_finish(const uint64_t* lists, int lists_per_row, int64_
   dim3 grid((unsigned)m);
 #define ATOPK_F(KBV)                                                                                               \
   case KBV:                                                                                                        \
-    hipLaunchKernelGGL((bucket_finish_kernel<KBV>), grid, dim3(kFinishThreads), 0, s, lists, lists_per_row, (int)b, \
+    ATOPK_LAUNCH((bucket_finish_kernel<KBV>), grid, dim3(kFinishThreads), 0, s, lists, lists_per_row, (int)b, \
                        (int)k, mode, (int)kb, static_cast<const uint8_t*>(x), dtype, ldx * es, (int)n,             \
                        static_cast<uint8_t*>(out_vals), out_idx, cand_out);                                        \
     break;

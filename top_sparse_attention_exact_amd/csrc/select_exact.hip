@@ -163,12 +163,12 @@ hipError_t launch_exact_in(const ExactPlan& p, const void* x, int64_t m, int64_t
   dim3 grid((unsigned)p.splits, (unsigned)m);
   const int aligned = ((reinterpret_cast<uintptr_t>(x) | (uintptr_t)ld_bytes) & 15) == 0;
   if (p.cap == 4096) {
-    hipLaunchKernelGGL((exact_filter_kernel<IN, 4096>), grid, dim3(kExactThreads), 0, s,
+    ATOPK_LAUNCH((exact_filter_kernel<IN, 4096>), grid, dim3(kExactThreads), 0, s,
                        static_cast<const uint8_t*>(x), ld_bytes, (int)n, (int)k, p.chunk, p.splits, aligned, part,
                        static_cast<const uint8_t*>(src), src_ld_bytes, src_dtype,
                        static_cast<uint8_t*>(out_vals), out_idx);
   } else {
-    hipLaunchKernelGGL((exact_filter_kernel<IN, 10240>), grid, dim3(kExactThreads), 0, s,
+    ATOPK_LAUNCH((exact_filter_kernel<IN, 10240>), grid, dim3(kExactThreads), 0, s,
                        static_cast<const uint8_t*>(x), ld_bytes, (int)n, (int)k, p.chunk, p.splits, aligned, part,
                        static_cast<const uint8_t*>(src), src_ld_bytes, src_dtype,
                        static_cast<uint8_t*>(out_vals), out_idx);

@@ -730,7 +730,7 @@ hipError_t launch_row_bucket(const void* x, int dtype, int64_t m, int64_t n, int
   dim3 grid((unsigned)m);
   const int kbs = kb <= 1 ? 1 : kb <= 2 ? 2 : 4;
 #define ATOPK_RB(KBV, FIN)                                                                                  \
-  hipLaunchKernelGGL((row_bucket_bf16_kernel<KBV, FIN>), grid, dim3(kRowT), 0, s, xb, ld_bytes, (int)n, \
+  ATOPK_LAUNCH((row_bucket_bf16_kernel<KBV, FIN>), grid, dim3(kRowT), 0, s, xb, ld_bytes, (int)n, \
                      (int)b, (int)kb, (int)k, ov, out_idx)
   if (final_exact) {
     if (kbs == 1) ATOPK_RB(1, true);
@@ -754,12 +754,12 @@ void launch_contig_t(dim3 grid, hipStream_t s, const uint8_t* xb, int64_t ld_byt
                      int64_t k, int vec, bool pack, uint8_t* ov, int32_t* out_idx) {
   if constexpr (DT == IN_BF16) {
     if (pack) {
-      hipLaunchKernelGGL((row_contig_kernel<DT, KB, FIN, true>), grid, dim3(kRowT), 0, s, xb, ld_bytes, (int)n, (int)b,
+      ATOPK_LAUNCH((row_contig_kernel<DT, KB, FIN, true>), grid, dim3(kRowT), 0, s, xb, ld_bytes, (int)n, (int)b,
                          (int)kb, (int)k, vec, ov, out_idx);
       return;
     }
   }
-  hipLaunchKernelGGL((row_contig_kernel<DT, KB, FIN, false>), grid, dim3(kRowT), 0, s, xb, ld_bytes, (int)n, (int)b,
+  ATOPK_LAUNCH((row_contig_kernel<DT, KB, FIN, false>), grid, dim3(kRowT), 0, s, xb, ld_bytes, (int)n, (int)b,
                      (int)kb, (int)k, vec, ov, out_idx);
 }
 
@@ -800,9 +800,9 @@ hipError_t launch_row_exact(const void* x, int dtype, int64_t m, int64_t n, int6
   const uint8_t* xb = static_cast<const uint8_t*>(x);
   uint8_t* ov = static_cast<uint8_t*>(out_vals);
   if (dtype == IN_F32) {
-    hipLaunchKernelGGL((row_exact_kernel<IN_F32>), grid, dim3(kRowT), 0, s, xb, ldx * 4, (int)n, (int)k, ov, out_idx);
+    ATOPK_LAUNCH((row_exact_kernel<IN_F32>), grid, dim3(kRowT), 0, s, xb, ldx * 4, (int)n, (int)k, ov, out_idx);
   } else {
-    hipLaunchKernelGGL((row_exact_kernel<IN_BF16>), grid, dim3(kRowT), 0, s, xb, ldx * 2, (int)n, (int)k, ov, out_idx);
+    ATOPK_LAUNCH((row_exact_kernel<IN_BF16>), grid, dim3(kRowT), 0, s, xb, ldx * 2, (int)n, (int)k, ov, out_idx);
   }
   return hipGetLastError();
 }

@@ -676,27 +676,27 @@ hipError_t launch_wide(const WidePlan& p, const float* x, int64_t m, int64_t n, 
   const int b = (int)p.b, kb = (int)p.kb;
   const dim3 grid((unsigned)p.blocks), block((unsigned)(kWave * p.nchunks));
   if (p.kbn == 8)
-    hipLaunchKernelGGL(wide_values_kernel<8>, grid, block, 0, s, x, ldx, (int)n, b, kb, (int)p.groups,
+    ATOPK_LAUNCH(wide_values_kernel<8>, grid, block, 0, s, x, ldx, (int)n, b, kb, (int)p.groups,
                        p.sweeps_per_chunk, exact ? 1 : 0, w.thr, w.need, w.vals);
   else
-    hipLaunchKernelGGL(wide_values_kernel<kWideKB>, grid, block, 0, s, x, ldx, (int)n, b, kb, (int)p.groups,
+    ATOPK_LAUNCH(wide_values_kernel<kWideKB>, grid, block, 0, s, x, ldx, (int)n, b, kb, (int)p.groups,
                        p.sweeps_per_chunk, exact ? 1 : 0, w.thr, w.need, w.vals);
   if (exact) {
-    hipLaunchKernelGGL(wide_exact_threshold_kernel, dim3((unsigned)m), dim3(kExactB), 0, s, w.vals, (int)k, w.rowthr,
+    ATOPK_LAUNCH(wide_exact_threshold_kernel, dim3((unsigned)m), dim3(kExactB), 0, s, w.vals, (int)k, w.rowthr,
                        w.row_cnt);
-    hipLaunchKernelGGL(wide_collect_exact_kernel, grid, block, 0, s, x, ldx, (int)n, b, (int)p.groups,
+    ATOPK_LAUNCH(wide_collect_exact_kernel, grid, block, 0, s, x, ldx, (int)n, b, (int)p.groups,
                        p.sweeps_per_chunk, w.rowthr, w.row_cnt, w.row_keys);
   } else if (p.kbn == 8) {
-    hipLaunchKernelGGL(wide_collect_bucket_kernel<8>, grid, block, 0, s, x, ldx, (int)n, b, kb, (int)p.groups,
+    ATOPK_LAUNCH(wide_collect_bucket_kernel<8>, grid, block, 0, s, x, ldx, (int)n, b, kb, (int)p.groups,
                        p.sweeps_per_chunk, final_exact ? 1 : 0, w.thr, w.need, w.cand,
                        static_cast<float*>(out_vals), out_idx);
   } else {
-    hipLaunchKernelGGL(wide_collect_bucket_kernel<kWideKB>, grid, block, 0, s, x, ldx, (int)n, b, kb, (int)p.groups,
+    ATOPK_LAUNCH(wide_collect_bucket_kernel<kWideKB>, grid, block, 0, s, x, ldx, (int)n, b, kb, (int)p.groups,
                        p.sweeps_per_chunk, final_exact ? 1 : 0, w.thr, w.need, w.cand,
                        static_cast<float*>(out_vals), out_idx);
   }
   if (exact || final_exact)
-    hipLaunchKernelGGL(wide_final_kernel, dim3((unsigned)m), dim3(kFinT), 0, s, x, ldx, (int)n, b, kb, (int)k,
+    ATOPK_LAUNCH(wide_final_kernel, dim3((unsigned)m), dim3(kFinT), 0, s, x, ldx, (int)n, b, kb, (int)k,
                        exact ? 1 : 0, w.cand, w.row_cnt, w.row_keys, static_cast<float*>(out_vals), out_idx);
   return hipGetLastError();
 }
