@@ -472,6 +472,28 @@ __device__ void block_sort_desc(uint64_t* keys, int n_pow2) {
   __syncthreads();
 }
 
+// The n unique nonzero keys of keys[0..n) (LDS, capacity cap >= 2T, a power
+// of two) in descending order, returned as a pointer into keys: for n <= T
+// every wave sorts a run of 64 and each key's rank, found by binary search
+// in the other runs, is its place in keys[T..T+n); beyond that the keys are
+// sorted in place (bitonic).  Ends with a barrier.  Reductions over the
+// selected keys read them in this order, so their floating-point result does
+// not depend on the order in which a compaction left the keys.
+template <int T>
+__device__ uint64_t* block_order_desc(uint64_t* keys, int n, int cap) {
+  if (n <= T) {
+    uint64_t* dst = keys + T;
+    block_sortmerge_final<T>(keys, keys, n, n, [&](int r, uint64_t key) { dst[r] = key; });
+    __syncthreads();
+    return dst;
+  }
+  int npow = 1;
+  while (npow < n) npow <<= 1;
+  for (int i = n + (int)threadIdx.x; i < npow && i < cap; i += T) keys[i] = 0;
+  block_sort_desc<T>(keys, npow);
+  return keys;
+}
+
 // Keep the keys >= thr of keys[0..n) at the front (order not kept) and
 // return their count to every thread.  n <= T * MAXPER: every thread first
 // reads its MAXPER slots into registers, so the in-place writes cannot

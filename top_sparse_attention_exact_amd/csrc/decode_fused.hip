@@ -578,18 +578,15 @@ __global__ __launch_bounds__(kT2) void decode_finish_kernel(const uint64_t* __re
     const uint64_t thr = block_kth_key<T, kKthSub>(cand, n, k_sel, hist, ctl);
     n = block_compact_ge<T, kMaxCand / T>(cand, n, thr, ctl);
   }
-  if (sel_idx != nullptr) {
-    int npow = 1;
-    while (npow < n) npow <<= 1;
-    for (int i = n + t; i < npow; i += T) cand[i] = 0;
-    block_sort_desc<T>(cand, npow);
-    for (int i = t; i < n; i += T) sel_idx[(int64_t)r_out * k_sel + i] = (int32_t)key_idx(cand[i]);
-  }
-  __syncthreads();
+  // the selection in descending order: the output, and the order of the
+  // softmax-V sums whether or not the selection is written
+  const uint64_t* sel = block_order_desc<T>(cand, n, kMaxCand);
+  if (sel_idx != nullptr)
+    for (int i = t; i < n; i += T) sel_idx[(int64_t)r_out * k_sel + i] = (int32_t)key_idx(sel[i]);
 
   // softmax over the selected scores, weighted sum of their V rows
   float mx = -INFINITY;
-  for (int i = t; i < n; i += T) mx = fmaxf(mx, key_value_f32(cand[i]));
+  for (int i = t; i < n; i += T) mx = fmaxf(mx, key_value_f32(sel[i]));
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
   if (lane_id() == 0) red[t / kWave] = mx;
@@ -613,7 +610,7 @@ __global__ __launch_bounds__(kT2) void decode_finish_kernel(const uint64_t* __re
     for (int u = 0; u < U; ++u) {
       const int ii = i + kVGroups * u;
       if (ii < n) {
-        const uint64_t key = cand[ii];
+        const uint64_t key = sel[ii];
         v[u] = *reinterpret_cast<const uint4*>(vh + (int64_t)key_idx(key) * kD);
         w[u] = expf(key_value_f32(key) - mx);
       } else {
