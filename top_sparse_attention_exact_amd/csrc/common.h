@@ -449,6 +449,117 @@ __device__ uint64_t block_kth_key(const uint64_t* keys, int n, int k, uint32_t* 
   return prefix;
 }
 
+// The k-th largest of n unique keys in LDS (1 <= k <= n), for candidate
+// sets whose order words spread over a range: 512 equal-width bins over
+// [min, max] of the order words (bin 0 holds the largest), one LDS atomic per
+// key, a block scan of the bin counts for the bin holding the k-th key, and
+// one wave ranking the keys of that bin.  When every key has the same order
+// word, or that bin holds more than 64 keys, the radix select above decides
+// instead.  `hist` holds 1024 words and `ctl` 8; both are overwritten.
+template <int T>
+__device__ __forceinline__ uint64_t block_kth_key_binned(const uint64_t* keys, int n, int k, uint32_t* hist, uint32_t* ctl) {
+  constexpr int NB = 512;
+  constexpr int NW = T / kWave;
+  static_assert(T >= NB && NW <= 32, "one bin per thread of the first 512");
+  uint32_t* mm = hist + NB;            // [NW] minima, [NW] maxima, [8] scan totals
+  uint32_t* gath = hist + NB + 2 * NW + 8;  // up to 64 gathered keys (two words each)
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid / kWave;
+  uint32_t lo = 0xffffffffu, hi = 0;
+  for (int i = tid; i < n; i += T) {
+    const uint32_t o = key_ord(keys[i]);
+    lo = min(lo, o);
+    hi = max(hi, o);
+  }
+  lo = wave_reduce_dpp(lo, [](uint32_t x, uint32_t y) { return min(x, y); });
+  hi = wave_reduce_dpp(hi, [](uint32_t x, uint32_t y) { return max(x, y); });
+  if (lane == 0) {
+    mm[wave] = lo;
+    mm[NW + wave] = hi;
+  }
+  if (tid < NB) hist[tid] = 0;
+  if (tid == 0) ctl[3] = 0;
+  __syncthreads();
+  lo = 0xffffffffu;
+  hi = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    lo = min(lo, mm[w]);
+    hi = max(hi, mm[NW + w]);
+  }
+  const uint32_t range = hi - lo;
+  if (range == 0) {
+    __syncthreads();
+    return block_kth_key<T, kKthSub>(keys, n, k, hist, ctl);
+  }
+  // bin of order word o: (hi - o) scaled to [0, NB), monotone in o
+  const uint64_t inv = ((uint64_t)NB << 32) / ((uint64_t)range + 1);
+  for (int i = tid; i < n; i += T) {
+    const uint32_t d = hi - key_ord(keys[i]);
+    atomicAdd(&hist[(uint32_t)(((uint64_t)d * inv) >> 32)], 1u);
+  }
+  __syncthreads();
+  // the bin where the running count from the top reaches k
+  const int c = tid < NB ? (int)hist[tid] : 0;
+  const int incl = wave_incl_scan(c);
+  if (lane == kWave - 1 && tid < NB) mm[2 * NW + wave] = (uint32_t)incl;
+  __syncthreads();
+  if (tid < NB) {
+    int before = incl - c;
+#pragma unroll
+    for (int w = 0; w < NB / kWave; ++w) before += w < wave ? (int)mm[2 * NW + w] : 0;
+    if (before < k && k <= before + c) {
+      ctl[0] = (uint32_t)tid;
+      ctl[1] = (uint32_t)(k - before);
+      ctl[2] = (uint32_t)c;
+    }
+  }
+  __syncthreads();
+  const uint32_t bin = ctl[0];
+  const int rem = (int)ctl[1];
+  const int cnt = (int)ctl[2];
+  if (cnt > kWave) {
+    __syncthreads();
+    return block_kth_key<T, kKthSub>(keys, n, k, hist, ctl);
+  }
+  for (int i0 = 0; i0 < n; i0 += T) {
+    const int i = i0 + tid;
+    const uint64_t key = i < n ? keys[i] : 0;
+    const bool m = i < n && (uint32_t)(((uint64_t)(hi - key_ord(key)) * inv) >> 32) == bin;
+    const uint64_t msk = __ballot(m);
+    if (msk) {
+      uint32_t pos = 0;
+      if (lane == 0) pos = atomicAdd(&ctl[3], (uint32_t)__popcll(msk));
+      pos = wave_lane0(pos);
+      if (m) {
+        const uint32_t slot = pos + lanes_below(msk);
+        gath[2 * slot] = (uint32_t)key;
+        gath[2 * slot + 1] = (uint32_t)(key >> 32);
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < kWave) {
+    // lane l holds gathered key l; the rem-th largest has rem - 1 above it
+    const bool own = tid < cnt;
+    const uint32_t klo = own ? gath[2 * tid] : 0u, khi = own ? gath[2 * tid + 1] : 0u;
+    const uint64_t mine = ((uint64_t)khi << 32) | klo;
+    int above = 0;
+    for (int j = 0; j < cnt; ++j) {
+      const uint64_t o = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)khi, j) << 32) |
+                         (uint32_t)__builtin_amdgcn_readlane((int)klo, j);
+      above += o > mine;
+    }
+    if (own && above == rem - 1) {
+      ctl[4] = klo;
+      ctl[5] = khi;
+    }
+  }
+  __syncthreads();
+  return ((uint64_t)ctl[5] << 32) | ctl[4];
+}
+
 // Sort keys[0..n_pow2) descending in LDS (bitonic network).
 template <int T>
 __device__ void block_sort_desc(uint64_t* keys, int n_pow2) {
@@ -472,18 +583,30 @@ __device__ void block_sort_desc(uint64_t* keys, int n_pow2) {
   __syncthreads();
 }
 
-// The n unique nonzero keys of keys[0..n) (LDS, capacity cap >= 2T, a power
-// of two) in descending order, returned as a pointer into keys: for n <= T
-// every wave sorts a run of 64 and each key's rank, found by binary search
-// in the other runs, is its place in keys[T..T+n); beyond that the keys are
+// The n unique nonzero keys of keys[0..n) (LDS, capacity cap >= 2048, a
+// power of two) in descending order, returned as a pointer into keys: for
+// n <= 1024 each key's rank -- the number of larger keys, counted over the
+// whole set -- is its place in keys[cap/2 ..]; beyond that the keys are
 // sorted in place (bitonic).  Ends with a barrier.  Reductions over the
 // selected keys read them in this order, so their floating-point result does
-// not depend on the order in which a compaction left the keys.
+// not depend on the order in which the keys arrived.
 template <int T>
 __device__ uint64_t* block_order_desc(uint64_t* keys, int n, int cap) {
-  if (n <= T) {
-    uint64_t* dst = keys + T;
-    block_sortmerge_final<T>(keys, keys, n, n, [&](int r, uint64_t key) { dst[r] = key; });
+  if (n <= 1024) {
+    uint64_t* dst = keys + cap / 2;
+    for (int c = (int)threadIdx.x; c < n; c += T) {
+      const uint64_t key = keys[c];
+      int c0 = 0, c1 = 0, c2 = 0, c3 = 0;
+      int j = 0;
+      for (; j + 4 <= n; j += 4) {
+        c0 += keys[j] > key ? 1 : 0;
+        c1 += keys[j + 1] > key ? 1 : 0;
+        c2 += keys[j + 2] > key ? 1 : 0;
+        c3 += keys[j + 3] > key ? 1 : 0;
+      }
+      for (; j < n; ++j) c0 += keys[j] > key ? 1 : 0;
+      dst[c0 + c1 + c2 + c3] = key;
+    }
     __syncthreads();
     return dst;
   }
@@ -492,6 +615,55 @@ __device__ uint64_t* block_order_desc(uint64_t* keys, int n, int cap) {
   for (int i = n + (int)threadIdx.x; i < npow && i < cap; i += T) keys[i] = 0;
   block_sort_desc<T>(keys, npow);
   return keys;
+}
+
+// Keep the keys >= thr of keys[0..n) at the front IN THEIR ORDER and return
+// their count to every thread.  Slot i = j*T + tid is read into registers
+// first (n <= T * MAXPER), each wave counts its kept keys of every j into
+// `scratch` (MAXPER * T/64 LDS words), and a key's place is the number of
+// kept keys at smaller slots.  The result depends only on the input order,
+// never on the order in which waves arrive.
+template <int T, int MAXPER>
+__device__ __forceinline__ int block_compact_ge_stable(uint64_t* keys, int n, uint64_t thr, uint32_t* scratch) {
+  constexpr int NW = T / kWave;
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int jn = (n + T - 1) / T;  // block-uniform
+  uint64_t v[MAXPER];
+  uint64_t msk[MAXPER];
+#pragma unroll
+  for (int j = 0; j < MAXPER; ++j) {
+    const int i = j * T + tid;
+    v[j] = (j < jn && i < n) ? keys[i] : 0;
+    msk[j] = 0;
+    if (j < jn) {
+      msk[j] = __ballot(i < n && v[j] >= thr);
+      if (lane_id() == 0) scratch[j * NW + wave] = (uint32_t)__popcll(msk[j]);
+    }
+  }
+  __syncthreads();
+  int total = 0;
+  int pos[MAXPER];
+#pragma unroll
+  for (int j = 0; j < MAXPER; ++j) {
+    pos[j] = 0;
+    if (j < jn) {
+      int before = 0, all = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const int c = (int)scratch[j * NW + w];
+        before += w < wave ? c : 0;
+        all += c;
+      }
+      pos[j] = total + before;
+      total += all;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < MAXPER; ++j)
+    if (j < jn && ((msk[j] >> lane_id()) & 1)) keys[pos[j] + lanes_below(msk[j])] = v[j];
+  __syncthreads();
+  return total;
 }
 
 // Keep the keys >= thr of keys[0..n) at the front (order not kept) and

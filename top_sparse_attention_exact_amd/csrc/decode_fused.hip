@@ -80,12 +80,59 @@ __device__ __forceinline__ void dump_scores(float* __restrict__ scores, int64_t 
   }
 }
 
-// PPT (head, bucket) pairs per thread, KB queue slots per pair.
+// Bucket-range mode: a workgroup owns the R buckets [r0, r0 + R) (R a power
+// of two dividing kSub) of one (batch, KV head) over the whole context; step
+// s stages the keys of sweeps m = s*M .. s*M + M - 1 (M = kSub / R): slot li
+// is key m*b + r0 + (li mod R) of sweep m = s*M + li / R, live when it is
+// below ctx.  A thread folds the slots of its (head, bucket) pair.
+__device__ __forceinline__ int brange_key(int s, int li, int lgR, int b, int r0) {
+  const int M = kSub >> lgR;
+  return (s * M + (li >> lgR)) * b + r0 + (li & ((1 << lgR) - 1));
+}
+
+template <int T>
+__device__ __forceinline__ void dump_scores_brange(float* __restrict__ scores, int64_t row0, int ctx, int s, int lgR,
+                                                   int b, int r0, int G, const float (*scb)[kSubPad]) {
+  for (int i = threadIdx.x; i < G * kSub; i += T) {
+    const int g = i / kSub, li = i - g * kSub;
+    const int j = brange_key(s, li, lgR, b, r0);
+    if (j < ctx) scores[(row0 + g) * ctx + j] = scb[g][li];
+  }
+}
+
+// Fold of one step in bucket-range mode: the thread's pair (g, rl) takes the
+// slots li = mm*R + rl, mm = part, part + tpp, ... < M.
+template <int KB>
+__device__ __forceinline__ void fold_brange(uint64_t (&qq)[KB], const float (*scb)[kSubPad], int g, int rl, int part,
+                                            int tpp, int s, int lgR, int b, int r0, int ctx) {
+  const int M = kSub >> lgR;
+  for (int mm = part; mm < M; mm += tpp) {
+    const int li = (mm << lgR) + rl;
+    const int j = brange_key(s, li, lgR, b, r0);
+    if (j < ctx) queue_insert<KB>(qq, make_key(ord_f32(__float_as_uint(scb[g][li])), (uint32_t)j));
+  }
+}
+
+// The tpp partial queues of a pair (consecutive lanes) merged into lane
+// part 0's.
+template <int KB>
+__device__ __forceinline__ void merge_parts(uint64_t (&qq)[KB], int tpp) {
+  for (int o = 1; o < tpp; o <<= 1) {
+    uint64_t other[KB];
+#pragma unroll
+    for (int j = 0; j < KB; ++j) other[j] = shfl_xor_u64(qq[j], o);
+    queue_merge<KB>(qq, other);
+  }
+}
+
+// PPT (head, bucket) pairs per thread, KB queue slots per pair.  Context
+// chunks (lgR < 0) or bucket ranges (lgR >= 0, tpp threads per pair), as in
+// decode_select_mfma_kernel below.
 template <int PPT, int KB>
 __global__ __launch_bounds__(kT1) void decode_select_kernel(const uint16_t* __restrict__ q,
                                                            const uint16_t* __restrict__ K, int hq, int hkv,
                                                            int ctx, int64_t ctx_stride, float scale, int b,
-                                                           int64_t chunk, int nchunks,
+                                                           int64_t chunk, int nchunks, int lgR, int tpp,
                                                            uint64_t* __restrict__ partial,
                                                            float* __restrict__ scores) {
   constexpr int U = 8;                 // keys in flight per 16-lane group
@@ -100,8 +147,11 @@ __global__ __launch_bounds__(kT1) void decode_select_kernel(const uint16_t* __re
   const int h = bh - bi * hkv;
   const int G = hq / hkv;
   const int c = blockIdx.x;
-  const int j0 = (int)(c * chunk);
-  const int j1 = (int)min((int64_t)ctx, (int64_t)j0 + chunk);
+  const bool brange = lgR >= 0;
+  const int j0 = brange ? 0 : (int)(c * chunk);
+  const int j1 = brange ? ctx : (int)min((int64_t)ctx, (int64_t)j0 + chunk);
+  const int r0 = brange ? (c << lgR) : 0;
+  const int nsteps = brange ? ((ctx + b - 1) / b + (kSub >> lgR) - 1) / (kSub >> lgR) : (j1 - j0 + kSub - 1) / kSub;
 
   uint4 qv[kMaxG];
 #pragma unroll
@@ -115,19 +165,24 @@ __global__ __launch_bounds__(kT1) void decode_select_kernel(const uint16_t* __re
   for (int i = 0; i < PPT; ++i)
 #pragma unroll
     for (int j = 0; j < KB; ++j) qq[i][j] = 0;
-  const int npairs = G * b;
+  const int npairs = G * (brange ? (1 << lgR) : b);
+  const int bpr = brange ? t / tpp : 0;
+  const int bpart = brange ? t - bpr * tpp : 0;
 
   int buf = 0;
-  for (int s0 = j0; s0 < j1; s0 += kSub) {
+  for (int st = 0; st < nsteps; ++st) {
+    const int s0 = j0 + st * kSub;
     const int s1 = min(j1, s0 + kSub);
-    // score keys s0 + slot + 16 * (u + U * p)
+    // score the staged slots li = slot + 16 * (u + U * p)
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
       uint4 kv[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int jj = s0 + slot + 16 * (u + U * p);
-        kv[u] = jj < s1 ? *reinterpret_cast<const uint4*>(kh + (int64_t)jj * kD) : make_uint4(0, 0, 0, 0);
+        const int li = slot + 16 * (u + U * p);
+        const int jj = brange ? brange_key(st, li, lgR, b, r0) : s0 + li;
+        kv[u] = jj < (brange ? ctx : s1) ? *reinterpret_cast<const uint4*>(kh + (int64_t)jj * kD)
+                                         : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -142,24 +197,40 @@ __global__ __launch_bounds__(kT1) void decode_select_kernel(const uint16_t* __re
       }
     }
     lds_barrier();
-    const int nk = s1 - s0;
-    if (scores != nullptr) dump_scores<kT1>(scores, (int64_t)(bi * hq + h * G), ctx, s0, G, nk, sc[buf]);
-    // fold the staged scores of the owned (head, bucket) pairs: bucket r
-    // holds keys j with j mod b == r
-    const int rs = b > 0 ? s0 % b : 0;  // b == 0: scores only
+    if (brange) {
+      if (scores != nullptr) dump_scores_brange<kT1>(scores, (int64_t)(bi * hq + h * G), ctx, st, lgR, b, r0, G, sc[buf]);
+      if (bpr < npairs) fold_brange<KB>(qq[0], sc[buf], bpr >> lgR, bpr & ((1 << lgR) - 1), bpart, tpp, st, lgR, b, r0, ctx);
+    } else {
+      const int nk = s1 - s0;
+      if (scores != nullptr) dump_scores<kT1>(scores, (int64_t)(bi * hq + h * G), ctx, s0, G, nk, sc[buf]);
+      // fold the staged scores of the owned (head, bucket) pairs: bucket r
+      // holds keys j with j mod b == r
+      const int rs = b > 0 ? s0 % b : 0;  // b == 0: scores only
 #pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int pr = t + kT1 * i;
-      if (pr < npairs) {
-        const int g = pr / b;
-        const int r = pr - g * b;
-        for (int li = r - rs + (r < rs ? b : 0); li < nk; li += b) {
-          const uint32_t bits = __float_as_uint(sc[buf][g][li]);
-          queue_insert<KB>(qq[i], make_key(ord_f32(bits), (uint32_t)(s0 + li)));
+      for (int i = 0; i < PPT; ++i) {
+        const int pr = t + kT1 * i;
+        if (pr < npairs) {
+          const int g = pr / b;
+          const int r = pr - g * b;
+          for (int li = r - rs + (r < rs ? b : 0); li < nk; li += b) {
+            const uint32_t bits = __float_as_uint(sc[buf][g][li]);
+            queue_insert<KB>(qq[i], make_key(ord_f32(bits), (uint32_t)(s0 + li)));
+          }
         }
       }
     }
     buf ^= 1;
+  }
+  if (brange) {
+    merge_parts<KB>(qq[0], tpp);
+    if (bpr < npairs && bpart == 0) {
+      const int g = bpr >> lgR;
+      const int r = r0 + (bpr & ((1 << lgR) - 1));
+      uint64_t* dst = partial + (((int64_t)bh * G + g) * b + r) * KB;
+#pragma unroll
+      for (int j = 0; j < KB; ++j) dst[j] = qq[0][j];
+    }
+    return;
   }
 #pragma unroll
   for (int i = 0; i < PPT; ++i) {
@@ -190,7 +261,7 @@ template <int PPT, int KB>
 __global__ __launch_bounds__(kT1M, 2) void decode_select_mfma_kernel(const uint16_t* __restrict__ q,
                                                                  const uint16_t* __restrict__ K, int hq, int hkv,
                                                                  int ctx, int64_t ctx_stride, float scale, int b,
-                                                                 int64_t chunk, int nchunks,
+                                                                 int64_t chunk, int nchunks, int lgR, int tpp,
                                                                  uint64_t* __restrict__ partial,
                                                                  float* __restrict__ scores) {
   constexpr int NW = kT1M / kWave;  // 8 waves
@@ -206,8 +277,13 @@ __global__ __launch_bounds__(kT1M, 2) void decode_select_mfma_kernel(const uint1
   const int h = bh - bi * hkv;
   const int G = hq / hkv;
   const int c = blockIdx.x;
-  const int j0 = (int)(c * chunk);
-  const int j1 = (int)min((int64_t)ctx, (int64_t)j0 + chunk);
+  // context-chunk mode (lgR < 0): keys [j0, j1); bucket-range mode: buckets
+  // [r0, r0 + 2^lgR) over the whole context, nsteps steps
+  const bool brange = lgR >= 0;
+  const int j0 = brange ? 0 : (int)(c * chunk);
+  const int j1 = brange ? ctx : (int)min((int64_t)ctx, (int64_t)j0 + chunk);
+  const int r0 = brange ? (c << lgR) : 0;
+  const int nsteps = brange ? ((ctx + b - 1) / b + (kSub >> lgR) - 1) / (kSub >> lgR) : (j1 - j0 + kSub - 1) / kSub;
 
   const int col = lane & 15;         // A row (query head) / B column (key)
   const int kq = 8 * (lane >> 4);    // k offset inside a k step
@@ -225,20 +301,26 @@ __global__ __launch_bounds__(kT1M, 2) void decode_select_mfma_kernel(const uint1
   for (int i = 0; i < PPT; ++i)
 #pragma unroll
     for (int j = 0; j < KB; ++j) qq[i][j] = 0;
-  const int npairs = G * b;
+  const int npairs = G * (brange ? (1 << lgR) : b);
 
+  // key of staged slot li in step st (ctx or beyond when it is not live)
+  auto key_of = [&](int st, int li) {
+    if (brange) return brange_key(st, li, lgR, b, r0);
+    const int jj = j0 + st * kSub + li;
+    return jj < j1 ? jj : ctx;
+  };
   // 16-key groups through two register sets: a group's loads are in flight
   // while the previous group is on the matrix cores, and the next step's
   // first group loads during this step's fold (after the score stores, which
-  // share the load counter).  Loads past the chunk are masked off.
+  // share the load counter).  Loads of keys that are not live are masked off.
   static_assert(GR == 4, "the group schedule below is written for 4 groups per wave and step");
   uint4 kv0[KS], kv1[KS];
-  auto load_grp = [&](uint4 (&kv)[KS], int s0x, int gi) {
-    const int s1x = min(j1, s0x + kSub);
-    const int jj = s0x + (wave * GR + gi) * 16 + col;
+  auto load_grp = [&](uint4 (&kv)[KS], int st, int gi) {
+    const int jj = key_of(st, (wave * GR + gi) * 16 + col);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      kv[ks] = jj < s1x ? *reinterpret_cast<const uint4*>(kh + (int64_t)jj * kD + 32 * ks) : make_uint4(0, 0, 0, 0);
+      kv[ks] = (st < nsteps && jj < ctx) ? *reinterpret_cast<const uint4*>(kh + (int64_t)jj * kD + 32 * ks)
+                                         : make_uint4(0, 0, 0, 0);
   };
   int buf = 0;
   auto mma_grp = [&](const uint4 (&kv)[KS], int gi) {
@@ -253,36 +335,57 @@ __global__ __launch_bounds__(kT1M, 2) void decode_select_mfma_kernel(const uint1
       if (g < G) sc[buf][g][li] = acc[i] * scale;
     }
   };
-  load_grp(kv0, j0, 0);
-  for (int s0 = j0; s0 < j1; s0 += kSub) {
-    const int s1 = min(j1, s0 + kSub);
-    load_grp(kv1, s0, 1);
+  // fold ownership: chunk mode, PPT pairs per thread; bucket-range mode,
+  // tpp threads per pair (PPT == 1), each taking every tpp-th sweep
+  const int bpr = brange ? t / tpp : 0;
+  const int bpart = brange ? t - bpr * tpp : 0;
+  load_grp(kv0, 0, 0);
+  for (int st = 0; st < nsteps; ++st) {
+    load_grp(kv1, st, 1);
     mma_grp(kv0, 0);
-    load_grp(kv0, s0, 2);
+    load_grp(kv0, st, 2);
     mma_grp(kv1, 1);
-    load_grp(kv1, s0, 3);
+    load_grp(kv1, st, 3);
     mma_grp(kv0, 2);
     mma_grp(kv1, 3);
     lds_barrier();
-    const int nk = s1 - s0;
-    if (scores != nullptr) dump_scores<kT1M>(scores, (int64_t)(bi * hq + h * G), ctx, s0, G, nk, sc[buf]);
-    load_grp(kv0, s0 + kSub, 0);
-    // fold the staged scores of the owned (head, bucket) pairs: bucket r
-    // holds keys j with j mod b == r
-    const int rs = b > 0 ? s0 % b : 0;  // b == 0: scores only
+    if (brange) {
+      if (scores != nullptr) dump_scores_brange<kT1M>(scores, (int64_t)(bi * hq + h * G), ctx, st, lgR, b, r0, G, sc[buf]);
+      load_grp(kv0, st + 1, 0);
+      if (bpr < npairs) fold_brange<KB>(qq[0], sc[buf], bpr >> lgR, bpr & ((1 << lgR) - 1), bpart, tpp, st, lgR, b, r0, ctx);
+    } else {
+      const int s0 = j0 + st * kSub;
+      const int nk = min(j1, s0 + kSub) - s0;
+      if (scores != nullptr) dump_scores<kT1M>(scores, (int64_t)(bi * hq + h * G), ctx, s0, G, nk, sc[buf]);
+      load_grp(kv0, st + 1, 0);
+      // fold the staged scores of the owned (head, bucket) pairs: bucket r
+      // holds keys j with j mod b == r
+      const int rs = b > 0 ? s0 % b : 0;  // b == 0: scores only
 #pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int pr = t + kT1M * i;
-      if (pr < npairs) {
-        const int g = pr / b;
-        const int r = pr - g * b;
-        for (int li = r - rs + (r < rs ? b : 0); li < nk; li += b) {
-          const uint32_t bits = __float_as_uint(sc[buf][g][li]);
-          queue_insert<KB>(qq[i], make_key(ord_f32(bits), (uint32_t)(s0 + li)));
+      for (int i = 0; i < PPT; ++i) {
+        const int pr = t + kT1M * i;
+        if (pr < npairs) {
+          const int g = pr / b;
+          const int r = pr - g * b;
+          for (int li = r - rs + (r < rs ? b : 0); li < nk; li += b) {
+            const uint32_t bits = __float_as_uint(sc[buf][g][li]);
+            queue_insert<KB>(qq[i], make_key(ord_f32(bits), (uint32_t)(s0 + li)));
+          }
         }
       }
     }
     buf ^= 1;
+  }
+  if (brange) {
+    merge_parts<KB>(qq[0], tpp);
+    if (bpr < npairs && bpart == 0) {
+      const int g = bpr >> lgR;
+      const int r = r0 + (bpr & ((1 << lgR) - 1));
+      uint64_t* dst = partial + (((int64_t)bh * G + g) * b + r) * KB;
+#pragma unroll
+      for (int j = 0; j < KB; ++j) dst[j] = qq[0][j];
+    }
+    return;
   }
 #pragma unroll
   for (int i = 0; i < PPT; ++i) {
@@ -299,6 +402,7 @@ __global__ __launch_bounds__(kT1M, 2) void decode_select_mfma_kernel(const uint1
 
 constexpr int kT2 = 512;
 constexpr int kMaxCand = 8192;
+constexpr int kStableMax = 1024;  // selections up to this size are summed in compaction order
 constexpr int kVGroups = kT2 / 16;  // 16-lane groups gathering V rows
 
 constexpr int kFlagMax = 256;  // flagged buckets rescanned in LDS; more take the full-row fallback
@@ -472,7 +576,7 @@ __device__ __forceinline__ void decode_rescan_mfma(const uint16_t* qg, int G, in
 // LDS candidate array, the workgroup recomputes every score of its head into
 // its row of `scores` ([B*Hq, ctx] workspace) and selects from that row.
 template <int KB>
-__global__ __launch_bounds__(kT2) void decode_finish_kernel(const uint64_t* __restrict__ partial, int nchunks, int hq,
+__global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(4))) void decode_finish_kernel(const uint64_t* __restrict__ partial, int nchunks, int hq,
                                                            int hkv, int b, int kb, int k_sel,
                                                            const uint16_t* __restrict__ V, int64_t ctx_stride,
                                                            uint16_t* __restrict__ out, int32_t* __restrict__ sel_idx,
@@ -489,36 +593,49 @@ __global__ __launch_bounds__(kT2) void decode_finish_kernel(const uint64_t* __re
   __shared__ float red[T / kWave];
 
   const int t = threadIdx.x;
-  const int r_out = blockIdx.x;  // = bi * hq + hh
+  const int G = hq / hkv;
+  // r_out = bi * hq + hh.  Workgroups are dealt to the 8 XCDs round-robin by
+  // id: the G query heads of one KV head go to one XCD, where the V rows
+  // they share meet in one L2.
+  int r_out = blockIdx.x;
+  if (G > 1 && gridDim.x % (8 * G) == 0) {
+    const int x = blockIdx.x & 7, kk = blockIdx.x >> 3;
+    r_out = ((kk / G) * 8 + x) * G + kk % G;
+  }
   const int bi = r_out / hq;
   const int hh = r_out - bi * hq;
-  const int G = hq / hkv;
   const int kvh = hh / G;
   const int g = hh - kvh * G;
   const int bh = bi * hkv + kvh;
 
-  // merge the chunk lists of every bucket
+  // merge the chunk lists of every bucket, every list of a batch in flight
+  // at once (lists past the last chunk read as empty and change nothing)
+  constexpr int kLB = KB >= 16 ? 2 : 32 / KB;  // lists per batch: 32 keys in registers
   for (int r = t; r < b; r += T) {
-    uint64_t a[KB];
     const uint64_t* src = partial + ((((int64_t)bh * nchunks) * G + g) * b + r) * KB;
     const int64_t cstride = (int64_t)G * b * KB;
+    uint64_t a[KB];
 #pragma unroll
-    for (int j = 0; j < KB; ++j) a[j] = src[j];
-    int c = 1;
-    for (; c + 4 <= nchunks; c += 4) {  // four lists in flight
-      uint64_t o[4][KB];
+    for (int j = 0; j < KB; ++j) a[j] = 0;
+    for (int c0 = 0; c0 < nchunks; c0 += kLB) {
+      uint64_t o[kLB][KB];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < kLB; ++u) {
+        const bool live = c0 + u < nchunks;
+        const uint64_t* p = src + (int64_t)(c0 + u) * cstride;
+        if constexpr (KB >= 2) {
 #pragma unroll
-        for (int j = 0; j < KB; ++j) o[u][j] = src[(c + u) * cstride + j];
+          for (int j = 0; j < KB; j += 2) {
+            const uint4 w = live ? *reinterpret_cast<const uint4*>(p + j) : make_uint4(0, 0, 0, 0);
+            o[u][j] = ((uint64_t)w.y << 32) | w.x;
+            o[u][j + 1] = ((uint64_t)w.w << 32) | w.z;
+          }
+        } else {
+          o[u][0] = live ? p[0] : 0;
+        }
+      }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) queue_merge<KB>(a, o[u]);
-    }
-    for (; c < nchunks; ++c) {
-      uint64_t o[KB];
-#pragma unroll
-      for (int j = 0; j < KB; ++j) o[j] = src[c * cstride + j];
-      queue_merge<KB>(a, o);
+      for (int u = 0; u < kLB; ++u) queue_merge<KB>(a, o[u]);
     }
 #pragma unroll
     for (int j = 0; j < KB; ++j)
@@ -526,8 +643,13 @@ __global__ __launch_bounds__(kT2) void decode_finish_kernel(const uint64_t* __re
   }
   __syncthreads();
   int n = b * kb;
+  // Order of the selection for the softmax-V sums (and its ranks for
+  // sel_idx): the stable compaction's order -- a function of the candidates
+  // alone -- or, after a rescan or a fallback (which append keys in arrival
+  // order) and for selections above kStableMax keys, descending order.
+  bool sorted = false;
   if (certify) {
-    const uint64_t thr = block_kth_key<T, kKthSub>(cand, n, k_sel, hist, ctl);
+    const uint64_t thr = block_kth_key_binned<T>(cand, n, k_sel, hist, ctl);
     if (t == 0) {
       ctl[5] = 0;
       ctl[6] = 0;
@@ -543,9 +665,10 @@ __global__ __launch_bounds__(kT2) void decode_finish_kernel(const uint64_t* __re
         }
       }
     }
-    n = block_compact_ge<T, kMaxCand / T>(cand, n, thr, ctl);  // k_sel keys
+    n = block_compact_ge_stable<T, kMaxCand / T>(cand, n, thr, hist);  // k_sel keys
     const int nflag = (int)ctl[5];
     if (nflag > 0) {
+      sorted = true;
       bool overflow = nflag > kFlagMax;
       const uint16_t* kh = K + (int64_t)bh * ctx_stride * kD;
       const uint16_t* qg = q + (int64_t)(r_out - g) * kD;  // the G query rows of the KV head
@@ -561,7 +684,7 @@ __global__ __launch_bounds__(kT2) void decode_finish_kernel(const uint64_t* __re
         if (!overflow && extra > 0) {
           n = k_sel + extra;
           const uint64_t thr2 = block_kth_key<T, kKthSub>(cand, n, k_sel, hist, ctl);
-          n = block_compact_ge<T, kMaxCand / T>(cand, n, thr2, ctl);
+          n = block_compact_ge_stable<T, kMaxCand / T>(cand, n, thr2, hist);
         }
       }
       if (overflow) {
@@ -575,14 +698,32 @@ __global__ __launch_bounds__(kT2) void decode_finish_kernel(const uint64_t* __re
       }
     }
   } else if (n > k_sel) {
-    const uint64_t thr = block_kth_key<T, kKthSub>(cand, n, k_sel, hist, ctl);
-    n = block_compact_ge<T, kMaxCand / T>(cand, n, thr, ctl);
+    const uint64_t thr = block_kth_key_binned<T>(cand, n, k_sel, hist, ctl);
+    n = block_compact_ge_stable<T, kMaxCand / T>(cand, n, thr, hist);
   }
-  // the selection in descending order: the output, and the order of the
-  // softmax-V sums whether or not the selection is written
-  const uint64_t* sel = block_order_desc<T>(cand, n, kMaxCand);
-  if (sel_idx != nullptr)
-    for (int i = t; i < n; i += T) sel_idx[(int64_t)r_out * k_sel + i] = (int32_t)key_idx(sel[i]);
+  sorted = sorted || n > kStableMax;
+  const uint64_t* sel = sorted ? block_order_desc<T>(cand, n, kMaxCand) : cand;
+  if (sel_idx != nullptr) {
+    int32_t* dst = sel_idx + (int64_t)r_out * k_sel;
+    if (sorted) {
+      for (int i = t; i < n; i += T) dst[i] = (int32_t)key_idx(sel[i]);
+    } else {
+      // a key's place in descending order: the number of larger keys
+      for (int c = t; c < n; c += T) {
+        const uint64_t key = sel[c];
+        int c0 = 0, c1 = 0, c2 = 0, c3 = 0;
+        int j = 0;
+        for (; j + 4 <= n; j += 4) {
+          c0 += sel[j] > key ? 1 : 0;
+          c1 += sel[j + 1] > key ? 1 : 0;
+          c2 += sel[j + 2] > key ? 1 : 0;
+          c3 += sel[j + 3] > key ? 1 : 0;
+        }
+        for (; j < n; ++j) c0 += sel[j] > key ? 1 : 0;
+        dst[c0 + c1 + c2 + c3] = (int32_t)key_idx(key);
+      }
+    }
+  }
 
   // softmax over the selected scores, weighted sum of their V rows
   float mx = -INFINITY;
@@ -595,7 +736,9 @@ __global__ __launch_bounds__(kT2) void decode_finish_kernel(const uint64_t* __re
 #pragma unroll
   for (int w = 1; w < T / kWave; ++w) mx = fmaxf(mx, red[w]);
 
-  constexpr int U = 8;
+  // lane group `group` takes rows group, group + kVGroups, ...; all U rows of
+  // a batch are loaded before any is summed
+  constexpr int U = 16;
   const int group = t >> 4;
   const int sub = t & 15;
   const uint16_t* vh = V + (int64_t)bh * ctx_stride * kD + sub * 8;
@@ -609,14 +752,9 @@ __global__ __launch_bounds__(kT2) void decode_finish_kernel(const uint64_t* __re
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int ii = i + kVGroups * u;
-      if (ii < n) {
-        const uint64_t key = sel[ii];
-        v[u] = *reinterpret_cast<const uint4*>(vh + (int64_t)key_idx(key) * kD);
-        w[u] = expf(key_value_f32(key) - mx);
-      } else {
-        v[u] = make_uint4(0, 0, 0, 0);
-        w[u] = 0.0f;
-      }
+      const uint64_t key = ii < n ? sel[ii] : 0;
+      v[u] = key != 0 ? *reinterpret_cast<const uint4*>(vh + (int64_t)key_idx(key) * kD) : make_uint4(0, 0, 0, 0);
+      w[u] = key != 0 ? expf(key_value_f32(key) - mx) : 0.0f;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -679,6 +817,36 @@ DecodePlan plan_decode(int64_t batch, int64_t hq, int64_t hkv, int64_t ctx, int6
   chunk = (chunk + kSub - 1) / kSub * kSub;
   p.chunk = chunk;
   p.nchunks = (int)((ctx + chunk - 1) / chunk);
+  p.nsplit = p.nchunks;
+  p.lgR = -1;
+  p.tpp = 1;
+  // Bucket-range mode: with b a power of two, split the buckets instead of
+  // the context -- workgroup c owns buckets [c*R, c*R + R) over every sweep
+  // of the keys -- so each workgroup's lists are final and the finish merges
+  // nothing.  Needs runs of R >= 16 consecutive keys (whole 16-key groups)
+  // and at most one (head, bucket) pair per thread.
+  // Its lists do not grow with the number of workgroups, so it takes up to
+  // two scoring workgroups per CU (512) for more loads in flight, as long as
+  // the ranges keep 32 buckets (16-key runs measured slower).
+  if (p.fused && p.nchunks >= 2 && b >= 16 && (b & (b - 1)) == 0) {
+    const int64_t want = (512 + heads - 1) / heads;
+    int64_t ns = 1;
+    while (ns < p.nchunks) ns <<= 1;
+    while (ns < want && b / (2 * ns) >= 32) ns <<= 1;
+    while (ns <= b / 16 && g * (b / ns) > threads) ns <<= 1;
+    if (ns <= b / 16 && b / ns <= kSub) {
+      const int64_t R = b / ns;
+      int lg = 0;
+      while ((1LL << lg) < R) ++lg;
+      int tpp = 1;
+      while (g * R * tpp * 2 <= threads && tpp * 2 <= kSub / R && tpp * 2 <= kWave) tpp *= 2;
+      p.lgR = lg;
+      p.tpp = tpp;
+      p.ppt = 1;
+      p.nsplit = (int)ns;
+      p.nchunks = 1;
+    }
+  }
   p.partial_bytes = (size_t)heads * p.nchunks * g * b * kbs * 8;
   return p;
 }
@@ -686,14 +854,14 @@ DecodePlan plan_decode(int64_t batch, int64_t hq, int64_t hkv, int64_t ctx, int6
 hipError_t launch_decode_scores(const uint16_t* q, const uint16_t* K, int64_t batch, int64_t hq, int64_t hkv,
                                 int64_t ctx, int64_t ctx_stride, float scale, float* scores, hipStream_t s) {
   // the scoring kernels with no bucket (b = 0): every score to `scores`
-  const DecodePlan p = plan_decode(batch, hq, hkv, ctx, 1, 1, 1);
+  const DecodePlan p = plan_decode(batch, hq, hkv, ctx, 1, 1, 1);  // context chunks (b = 1)
   dim3 g1((unsigned)p.nchunks, (unsigned)(batch * hkv));
   if (p.mfma)
     ATOPK_LAUNCH((decode_select_mfma_kernel<1, 1>), g1, dim3(kT1M), 0, s, q, K, (int)hq, (int)hkv, (int)ctx,
-                       ctx_stride, scale, 0, p.chunk, p.nchunks, nullptr, scores);
+                       ctx_stride, scale, 0, p.chunk, p.nchunks, -1, 1, nullptr, scores);
   else
     ATOPK_LAUNCH((decode_select_kernel<1, 1>), g1, dim3(kT1), 0, s, q, K, (int)hq, (int)hkv, (int)ctx,
-                       ctx_stride, scale, 0, p.chunk, p.nchunks, nullptr, scores);
+                       ctx_stride, scale, 0, p.chunk, p.nchunks, -1, 1, nullptr, scores);
   return hipGetLastError();
 }
 
@@ -704,15 +872,15 @@ hipError_t launch_decode_fused(const DecodePlan& p, const uint16_t* q, const uin
   if (certify && cert_buf == nullptr) return hipErrorInvalidValue;
   if (certify && certify != (p.mfma ? 1 : 2)) return hipErrorInvalidValue;  // the rescan repeats kernel 1's arithmetic
   const int kbs = kb_pow2(kb);
-  dim3 g1((unsigned)p.nchunks, (unsigned)(batch * hkv));
+  dim3 g1((unsigned)p.nsplit, (unsigned)(batch * hkv));
 #define ATOPK_D1(P, KBV)                                                                                            \
   if (p.ppt == P && kbs == KBV) {                                                                                   \
     if (p.mfma)                                                                                                     \
       ATOPK_LAUNCH((decode_select_mfma_kernel<P, KBV>), g1, dim3(kT1M), 0, s, q, K, (int)hq, (int)hkv,         \
-                         (int)ctx, ctx_stride, scale, (int)b, p.chunk, p.nchunks, partial, scores);                  \
+                         (int)ctx, ctx_stride, scale, (int)b, p.chunk, p.nchunks, p.lgR, p.tpp, partial, scores);    \
     else                                                                                                            \
       ATOPK_LAUNCH((decode_select_kernel<P, KBV>), g1, dim3(kT1), 0, s, q, K, (int)hq, (int)hkv, (int)ctx,     \
-                         ctx_stride, scale, (int)b, p.chunk, p.nchunks, partial, scores);                            \
+                         ctx_stride, scale, (int)b, p.chunk, p.nchunks, p.lgR, p.tpp, partial, scores);              \
   } else
   ATOPK_D1(1, 1) ATOPK_D1(1, 2) ATOPK_D1(1, 4) ATOPK_D1(1, 8) ATOPK_D1(1, 16)
   ATOPK_D1(2, 1) ATOPK_D1(2, 2) ATOPK_D1(2, 4) ATOPK_D1(2, 8) ATOPK_D1(2, 16)

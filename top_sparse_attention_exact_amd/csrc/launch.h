@@ -128,9 +128,12 @@ struct DecodePlan {
   bool fused;            // false: scores, selection and softmax-V as separate passes
   bool mfma;             // query-head groups: scores on the matrix cores
   int ppt;               // (head, bucket) pairs per thread in the scoring kernel
-  int64_t chunk;         // keys per scoring workgroup
-  int nchunks;
-  size_t partial_bytes;  // per-chunk k_b-lists
+  int64_t chunk;         // keys per scoring workgroup (context-chunk mode)
+  int nchunks;           // k_b-lists per (head, bucket) the finish merges
+  int lgR;               // >= 0: bucket-range mode, 2^lgR buckets per scoring workgroup
+  int tpp;               // bucket-range mode: threads folding one (head, bucket) pair
+  int nsplit;            // scoring workgroups per (batch, KV head)
+  size_t partial_bytes;  // k_b-lists in the workspace
 };
 DecodePlan plan_decode(int64_t batch, int64_t hq, int64_t hkv, int64_t ctx, int64_t k_sel, int64_t b, int64_t kb);
 // certify != 0: (b, kb) is a certified plan for the exact Top-K and

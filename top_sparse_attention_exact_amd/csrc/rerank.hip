@@ -69,7 +69,7 @@ __global__ __launch_bounds__(kRT) void rerank_score_kernel(const uint16_t* __res
   constexpr int T = kRT;
   __shared__ uint32_t list[kRerankMaxCand];
   __shared__ uint32_t bits[kRerankMaxCtx / 32];
-  __shared__ uint32_t ctl[1];
+  __shared__ int wsum[T / kWave];
 
   const int t = threadIdx.x;
   const int r_out = blockIdx.x;  // = bi * hq + h
@@ -82,10 +82,11 @@ __global__ __launch_bounds__(kRT) void rerank_score_kernel(const uint16_t* __res
   const int lo = sp * range;
   const int hi = min(ctx, lo + range);
 
-  // 1. the split's candidates, made unique
+  // 1. the split's candidates, made unique: a bitmap over the range, then
+  // its set bits listed in position order (thread t owns a run of words; a
+  // block scan of the runs' counts gives each run its place)
   const int words = (max(hi - lo, 0) + 31) / 32;
   for (int i = t; i < words; i += T) bits[i] = 0;
-  if (t == 0) ctl[0] = 0;
   __syncthreads();
   const int32_t* cr = cand + (int64_t)r_out * cand_stride;
   const int total = ncand + window;
@@ -93,12 +94,31 @@ __global__ __launch_bounds__(kRT) void rerank_score_kernel(const uint16_t* __res
     const int j = i < ncand ? cr[i] : ctx - window + (i - ncand);
     if (j >= lo && j < hi) {
       const int jl = j - lo;
-      const uint32_t bit = 1u << (jl & 31);
-      if ((atomicOr(&bits[jl >> 5], bit) & bit) == 0) list[atomicAdd(&ctl[0], 1u)] = (uint32_t)j;
+      atomicOr(&bits[jl >> 5], 1u << (jl & 31));
     }
   }
   __syncthreads();
-  const int nc = (int)ctl[0];  // <= ncand + window
+  const int per = (words + T - 1) / T;
+  const int w0 = min(words, t * per), w1 = min(words, w0 + per);
+  int mine = 0;
+  for (int w = w0; w < w1; ++w) mine += __popc(bits[w]);
+  const int incl = wave_incl_scan(mine);
+  if (lane_id() == kWave - 1) wsum[t / kWave] = incl;
+  __syncthreads();
+  int pos = incl - mine, nc = 0;
+#pragma unroll
+  for (int w = 0; w < T / kWave; ++w) {
+    pos += w < t / kWave ? wsum[w] : 0;
+    nc += wsum[w];  // <= ncand + window
+  }
+  for (int w = w0; w < w1; ++w) {
+    uint32_t m = bits[w];
+    while (m) {
+      list[pos++] = (uint32_t)(lo + 32 * w + __builtin_ctz(m));
+      m &= m - 1;
+    }
+  }
+  __syncthreads();
 
   // 2. scores
   const int group = t >> 4;
@@ -137,6 +157,7 @@ __global__ __launch_bounds__(kRT) void rerank_score_kernel(const uint16_t* __res
 // exact Top-K of them (all of them when fewer), softmax and the weighted sum
 // of the selected V rows.
 constexpr int kST = 1024;              // select kernel threads
+constexpr int kRerankStableMax = 1024;  // selections up to this size are summed in position order
 constexpr int kSGroups = kST / 16;
 
 __global__ __launch_bounds__(kST) void rerank_select_kernel(const uint64_t* __restrict__ keys_in,
@@ -167,16 +188,38 @@ __global__ __launch_bounds__(kST) void rerank_select_kernel(const uint64_t* __re
   }
   __syncthreads();
 
-  // 3. exact Top-K of the set (the whole set when it is smaller)
+  // 3. exact Top-K of the set (the whole set when it is smaller), kept in
+  // position order: the keys arrive in position order (splits in order, each
+  // split's list ascending) and the compaction keeps it, so the softmax-V
+  // sums below run in one order whether or not the selection is written;
+  // past kRerankStableMax keys the selection is sorted instead
   if (n > k_sel) {
-    const uint64_t thr = block_kth_key<T, kKthSub>(keys, n, k_sel, hist, ctl);
-    n = block_compact_ge<T, kRerankMaxCand / T>(keys, n, thr, ctl);
+    const uint64_t thr = block_kth_key_binned<T>(keys, n, k_sel, hist, ctl);
+    n = block_compact_ge_stable<T, kRerankMaxCand / T>(keys, n, thr, hist);
   }
-  // the selection in descending order: the output, and the order of the
-  // softmax-V sums whether or not the selection is written
-  const uint64_t* sel = block_order_desc<T>(keys, n, kRerankMaxCand);
-  if (sel_idx != nullptr)
-    for (int i = t; i < k_sel; i += T) sel_idx[(int64_t)r_out * k_sel + i] = i < n ? (int32_t)key_idx(sel[i]) : -1;
+  const bool sorted = n > kRerankStableMax;
+  const uint64_t* sel = sorted ? block_order_desc<T>(keys, n, kRerankMaxCand) : keys;
+  if (sel_idx != nullptr) {
+    int32_t* dst = sel_idx + (int64_t)r_out * k_sel;
+    for (int i = n + t; i < k_sel; i += T) dst[i] = -1;
+    if (sorted) {
+      for (int i = t; i < n; i += T) dst[i] = (int32_t)key_idx(sel[i]);
+    } else {
+      for (int c = t; c < n; c += T) {  // a key's place: the number of larger keys
+        const uint64_t key = sel[c];
+        int c0 = 0, c1 = 0, c2 = 0, c3 = 0;
+        int j = 0;
+        for (; j + 4 <= n; j += 4) {
+          c0 += sel[j] > key ? 1 : 0;
+          c1 += sel[j + 1] > key ? 1 : 0;
+          c2 += sel[j + 2] > key ? 1 : 0;
+          c3 += sel[j + 3] > key ? 1 : 0;
+        }
+        for (; j < n; ++j) c0 += sel[j] > key ? 1 : 0;
+        dst[c0 + c1 + c2 + c3] = (int32_t)key_idx(key);
+      }
+    }
+  }
 
   // 4. softmax over the selected scores, weighted sum of their V rows
   float mx = -INFINITY;
