@@ -640,6 +640,286 @@ __global__ __launch_bounds__(kFinT) void wide_final_kernel(const float* __restri
   sort_and_write(cand, cnt, k, xr, n, ov, oi, bins, red);
 }
 
+// ---- one-pass stage 1 (bucketed, b a multiple of 64, k_b <= 16) ----------
+//
+// A workgroup owns 64 buckets of one row -- lane l is bucket 64*g + l -- over
+// the whole row, its 16 waves taking interleaved batches of sweeps, so every
+// element of a bucket passes through the workgroup that owns it.  Per
+// bucket, in LDS:
+//  - a window [lo, lo + span] of order keys: lo is the k_b-th largest of the
+//    bucket's 256 first-batch samples (k_b elements of the bucket reach it,
+//    so its k_b-th largest does too), lo + span their largest;
+//  - a histogram of the window (256 bins, two 16-bit counts per word);
+//  - thr, the highest bin whose count together with the bins above reaches
+//    k_b, refreshed at a few points of the stream.  Counts only grow, so thr
+//    never passes the bin of the bucket's final k_b-th largest key, and the
+//    bins below thr can never matter again: elements below them are dropped
+//    without being counted;
+//  - a log of (key, index) for every element at or above thr when it
+//    arrives.  An element of the bucket's exact top-k_b has a key >= the
+//    final k_b-th, so its bin is >= every thr the stream ever saw: it is
+//    logged.
+// A lane tests each of its elements against one float (the lower edge of
+// its bucket's threshold bin); the few that pass go through a per-wave LDS
+// ring, and the histogram and log updates run on full 64-element chunks of
+// it.  At the end the keys of the log in bins >= the final thr (the k_b-th
+// largest's bin: fewer than k_b keys above it, all of it logged) are ranked
+// and the first k_b kept, sorted.  A bucket whose log overflowed or whose
+// threshold bin holds more keys than a wave ranks at once is redone by its
+// wave with a full scan of the bucket, so the result is exact for any input.
+// Two 512-thread workgroups fit on a CU (LDS), so one's window and end
+// phases overlap the other's streaming; each lane keeps two batches of
+// loads in flight behind the one it works on.
+constexpr int kOpT = 512;
+constexpr int kOpW = kOpT / kWave;    // waves
+constexpr int kOpU = 16;              // sweeps per wave and batch (loads per lane per batch)
+constexpr int kOpNB = 64;             // histogram bins per bucket: lane l of a tick owns bin l
+constexpr int kOpHW = kOpNB / 2 + 1;  // histogram words per bucket (padded row)
+constexpr int kOpCap = 120;           // logged keys per bucket
+constexpr int kOpQ = 128;             // per-wave ring of staged elements
+
+struct OnepassShared {
+  uint32_t hist[kWave][kOpHW];
+  uint64_t logk[kWave][kOpCap];  // the first batch's value lists merge here before any key is logged
+  uint64_t ring[kOpW][kOpQ];     // staged (value bits, sweep, bucket); candidates of the end phase
+  uint32_t logn[kWave];
+  int thr[kWave];
+  uint32_t lo[kWave], span[kWave];
+  int sh[kWave];
+};
+
+// Exact top-16 keys of bucket r of the row (elements r, r + b, ...), sorted,
+// by one wave: per-lane key queues over a strided scan, merged across lanes.
+// Lane j returns entry j.
+__device__ __noinline__ uint64_t wave_bucket_top16(const float* __restrict__ xrow, int n, int b, int r) {
+  const int lane = lane_id();
+  const uint32_t* xb = reinterpret_cast<const uint32_t*>(xrow);
+  uint64_t q[kWideKB];
+#pragma unroll
+  for (int j = 0; j < kWideKB; ++j) q[j] = 0;
+  for (int64_t i = (int64_t)r + (int64_t)lane * b; i < n; i += (int64_t)kWave * b)
+    queue_insert<kWideKB>(q, make_key(ord_f32(xb[i]), (uint32_t)i));
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    uint64_t other[kWideKB];
+#pragma unroll
+    for (int j = 0; j < kWideKB; ++j) other[j] = shfl_xor_u64(q[j], o);
+    queue_merge<kWideKB>(q, other);
+  }
+  uint64_t mine = 0;
+#pragma unroll
+  for (int j = 0; j < kWideKB; ++j)
+    if (j == lane) mine = q[j];
+  return mine;
+}
+
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__global__ __launch_bounds__(kOpT) void wide_onepass_kernel(const float* __restrict__ x, int64_t ldx, int n, int b,
+                                                           int kb, int groups, int final_exact,
+                                                           uint64_t* __restrict__ cand, float* __restrict__ out_vals,
+                                                           int32_t* __restrict__ out_idx) {
+  __shared__ OnepassShared S;
+  const int t = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = t / kWave;
+  const int row = blockIdx.x / groups;
+  const int g = blockIdx.x - row * groups;
+  const int r = g * kWave + lane;  // this lane's bucket
+  const float* xrow = x + (int64_t)row * ldx;
+  const float* xr = xrow + r;
+  const int nsw = (n + b - 1) / b;  // sweeps; the last may be partial
+  const int nbatch = (nsw + kOpW * kOpU - 1) / (kOpW * kOpU);
+
+  for (int i = t; i < kWave * kOpHW; i += kOpT) (&S.hist[0][0])[i] = 0;
+  if (t < kWave) {
+    S.logn[t] = 0;
+    S.thr[t] = 0;
+  }
+
+  // batch bt of wave w holds sweeps w + W*(U*bt + u), u < U
+  auto sweep_of = [&](int bt, int u) { return wave + kOpW * (kOpU * bt + u); };
+  // branch-free: a sweep past the lane's last element is read at that
+  // element instead (every load is unconditional) and masked afterwards
+  const int last = (n - 1 - r) / b;  // the lane's last sweep
+  auto live = [&](int s) { return s <= last; };
+  float wa[kOpU], wb[kOpU], wc[kOpU];
+  auto load = [&](float (&w)[kOpU], int bt) {
+#pragma unroll
+    for (int u = 0; u < kOpU; ++u) w[u] = xr[(int64_t)min(sweep_of(bt, u), last) * b];
+  };
+  load(wa, 0);
+  if (nbatch > 1) load(wb, 1);
+
+  // the window: the k_b-th largest and the largest of each bucket's first
+  // two batches (256 samples), from the waves' value lists merged into wave
+  // 0; its top goes half its width above the largest sample, where the
+  // bucket's k_b-th largest often lies
+  {
+    float q[kWideKB];
+#pragma unroll
+    for (int j = 0; j < kWideKB; ++j) q[j] = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kOpU; ++u) fnet_insert<kWideKB>(q, live(sweep_of(0, u)) ? wa[u] : -INFINITY);
+#pragma unroll
+    for (int u = 0; u < kOpU; ++u)
+      fnet_insert<kWideKB>(q, (nbatch > 1 && live(sweep_of(1, u))) ? wb[u] : -INFINITY);
+    tree_merge<kWideKB>(q, reinterpret_cast<float*>(&S.logk[0][0]), kOpW);
+    if (wave == 0) {
+      float lo_v = q[0];
+#pragma unroll
+      for (int j = 0; j < kWideKB; ++j)
+        if (j == kb - 1) lo_v = q[j];
+      const uint32_t lo = ord_f32(__float_as_uint(lo_v));
+      const uint32_t width = ord_f32(__float_as_uint(q[0])) - lo;
+      const uint32_t span = (uint32_t)min((uint64_t)width + width / 2, (uint64_t)(0xffffffffu - lo));
+      int sh = 0;
+      while ((span >> sh) >= (uint32_t)kOpNB) ++sh;
+      S.lo[lane] = lo;
+      S.span[lane] = span;
+      S.sh[lane] = sh;
+    }
+  }
+  __syncthreads();
+  if (nbatch > 2) load(wc, 2);
+  const uint32_t my_lo = S.lo[lane];
+  const int my_sh = S.sh[lane];
+  float fthr = __uint_as_float(bits_from_ord(my_lo));  // lower edge of the threshold bin
+
+  // staged elements: ring entries head .. tail (wave-uniform counters)
+  int head = 0, tail = 0;
+  uint64_t* ring = S.ring[wave];
+  auto drain = [&](int cnt) {  // the oldest cnt (<= 64) staged elements
+    wave_sync_lds();
+    if (lane < cnt) {
+      const uint64_t e = ring[(head + lane) & (kOpQ - 1)];
+      const uint32_t o = ord_f32((uint32_t)e);
+      const int s = (int)((e >> 32) & 0xffffu);
+      const int bl = (int)(e >> 48);
+      const int bin = (int)(min(o - S.lo[bl], S.span[bl]) >> S.sh[bl]);
+      atomicAdd(&S.hist[bl][bin >> 1], 1u << ((bin & 1) << 4));
+      if (bin >= S.thr[bl]) {
+        const uint32_t slot = atomicAdd(&S.logn[bl], 1u);
+        if (slot < (uint32_t)kOpCap) S.logk[bl][slot] = make_key(o, (uint32_t)(s * b + g * kWave + bl));
+      }
+    }
+    head += cnt;
+    wave_sync_lds();
+  };
+  auto process = [&](const float (&w)[kOpU], int bt) {
+#pragma unroll
+    for (int u = 0; u < kOpU; ++u) {
+      const bool pass = live(sweep_of(bt, u)) & (w[u] >= fthr);
+      const uint64_t m = __ballot(pass);
+      if (m) {
+        if (pass)
+          ring[(tail + (int)lanes_below(m)) & (kOpQ - 1)] =
+              (uint64_t)__float_as_uint(w[u]) | ((uint64_t)(uint32_t)sweep_of(bt, u) << 32) | ((uint64_t)lane << 48);
+        tail += __popcll(m);
+        if (tail - head >= kWave) drain(kWave);
+      }
+    }
+  };
+  // threshold bins from the histograms: wave w refreshes buckets w, w + W, ...
+  auto tick = [&]() {
+    if (tail > head) drain(tail - head);
+    lds_barrier();
+#pragma unroll
+    for (int q = 0; q < kWave / kOpW; ++q) {
+      const int rb = wave + kOpW * q;
+      const int c = (int)((S.hist[rb][lane >> 1] >> ((lane & 1) << 4)) & 0xffffu);  // bin `lane`
+      int suf = c;  // bins >= lane
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int v = __shfl_down(suf, o, kWave);
+        suf += lane + o < kWave ? v : 0;
+      }
+      if (suf - c < kb && kb <= suf) S.thr[rb] = lane;
+    }
+    lds_barrier();
+    fthr = __uint_as_float(bits_from_ord(my_lo + ((uint32_t)S.thr[lane] << my_sh)));
+  };
+  auto ticks_after = [&](int bt) { return (bt & (bt + 1)) == 0 || bt == nbatch - 1; };
+
+  // batch bt sits in buffer bt mod 3; the loads of bt + 1 and bt + 2 are in
+  // flight while it is worked on
+  for (int bt = 0; bt < nbatch; bt += 3) {
+    if (bt > 0 && bt + 2 < nbatch) load(wc, bt + 2);
+    process(wa, bt);
+    if (ticks_after(bt)) tick();
+    if (bt + 1 < nbatch) {
+      if (bt + 3 < nbatch) load(wa, bt + 3);
+      process(wb, bt + 1);
+      if (ticks_after(bt + 1)) tick();
+    }
+    if (bt + 2 < nbatch) {
+      if (bt + 4 < nbatch) load(wb, bt + 4);
+      process(wc, bt + 2);
+      if (ticks_after(bt + 2)) tick();
+    }
+  }
+  // the tick after the last batch left every bucket's final threshold bin
+
+  // each bucket's exact top-k_b, wave w taking buckets w, w + 16, ...
+  for (int q = 0; q < kWave / kOpW; ++q) {
+    const int rb = wave + kOpW * q;
+    const int bucket = g * kWave + rb;
+    const int nl = (int)S.logn[rb];
+    const int B = S.thr[rb];
+    const uint32_t blo = S.lo[rb], bspan = S.span[rb];
+    const int bsh = S.sh[rb];
+    int cnt = 0;
+    if (nl <= kOpCap) {
+      for (int i0 = 0; i0 < nl; i0 += kWave) {
+        const int i = i0 + lane;
+        const uint64_t key = i < nl ? S.logk[rb][i] : 0;
+        const bool keep = i < nl && (int)(min(key_ord(key) - blo, bspan) >> bsh) >= B;
+        const uint64_t m = __ballot(keep);
+        const int slot = cnt + (int)lanes_below(m);
+        if (keep && slot < kWave) ring[slot] = key;
+        cnt += __popcll(m);
+      }
+    }
+    wave_sync_lds();
+    const bool ok = nl <= kOpCap && cnt >= kb && cnt <= kWave;
+    uint64_t mine = 0;
+    int rank = kWave;
+    if (ok) {
+      // rank of each candidate among the candidates (lane = candidate)
+      mine = lane < cnt ? ring[lane] : 0;
+      const uint32_t mlo = (uint32_t)mine, mhi = (uint32_t)(mine >> 32);
+      rank = 0;
+      for (int j = 0; j < cnt; ++j) {
+        const uint64_t o = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)mhi, j) << 32) |
+                           (uint32_t)__builtin_amdgcn_readlane((int)mlo, j);
+        rank += o > mine ? 1 : 0;
+      }
+      if (lane >= cnt) rank = kWave;
+    } else {
+      mine = wave_bucket_top16(xrow, n, b, bucket);
+      rank = lane;
+    }
+    if (rank < kb) {
+      const int64_t slot = ((int64_t)row * b + bucket) * kb + rank;
+      if (final_exact) {
+        cand[slot] = mine;
+      } else {
+        uint32_t idx = key_idx(mine);
+        idx = idx < (uint32_t)n ? idx : 0u;  // only reachable with NaN inputs
+        const uint32_t o = key_ord(mine);
+        out_idx[slot] = (int32_t)idx;
+        reinterpret_cast<uint32_t*>(out_vals)[slot] =
+            o == 0x80000000u ? reinterpret_cast<const uint32_t*>(xrow)[idx] : bits_from_ord(o);
+      }
+    }
+    wave_sync_lds();
+  }
+}
+
 }  // namespace
 
 WidePlan plan_wide(int dtype, int64_t m, int64_t n, int64_t k, int64_t b, int64_t kb, bool exact, bool final_exact) {
@@ -675,6 +955,16 @@ hipError_t launch_wide(const WidePlan& p, const float* x, int64_t m, int64_t n, 
                        bool final_exact, const WideBuffers& w, void* out_vals, int32_t* out_idx, hipStream_t s) {
   const int b = (int)p.b, kb = (int)p.kb;
   const dim3 grid((unsigned)p.blocks), block((unsigned)(kWave * p.nchunks));
+  // bucketed rows whose buckets hold at most 65535 elements (16-bit
+  // histogram counts): one pass over the input
+  if (!exact && (n + b - 1) / b <= 65535) {
+    ATOPK_LAUNCH(wide_onepass_kernel, grid, dim3(kOpT), 0, s, x, ldx, (int)n, b, kb, (int)p.groups,
+                 final_exact ? 1 : 0, w.cand, static_cast<float*>(out_vals), out_idx);
+    if (final_exact)
+      ATOPK_LAUNCH(wide_final_kernel, dim3((unsigned)m), dim3(kFinT), 0, s, x, ldx, (int)n, b, kb, (int)k, 0, w.cand,
+                   w.row_cnt, w.row_keys, static_cast<float*>(out_vals), out_idx);
+    return hipGetLastError();
+  }
   if (p.kbn == 8)
     ATOPK_LAUNCH(wide_values_kernel<8>, grid, block, 0, s, x, ldx, (int)n, b, kb, (int)p.groups,
                        p.sweeps_per_chunk, exact ? 1 : 0, w.thr, w.need, w.vals);
