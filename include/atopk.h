@@ -119,6 +119,22 @@ int atopk_bucketed(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, 
                    int64_t kb, int final_exact, void* out_vals, int32_t* out_idx, void* ws,
                    size_t ws_bytes, void* stream);
 
+/*
+ * atopk_bucketed for callers that cannot allocate device memory (code under
+ * HIP graph capture, serving loops, harnesses that forbid allocation): the
+ * same arguments and results without the workspace, which comes from a
+ * device array inside the library of ATOPK_NOALLOC_SCRATCH_BYTES per GPU,
+ * held from the library's first use on that GPU until the process ends.
+ * Shapes whose workspace (atopk_bucketed_workspace) exceeds that size give
+ * ATOPK_ERR_WORKSPACE before anything runs.  The call allocates nothing and
+ * calls no allocating routine.  All calls on one GPU share the array, so two
+ * such calls that may run at the same time on one GPU (different streams or
+ * unordered threads) race: order them on one stream.
+ */
+#define ATOPK_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int atopk_bucketed_noalloc(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k, int64_t b,
+                           int64_t kb, int final_exact, void* out_vals, int32_t* out_idx, void* stream);
+
 /* bucket assignments for atopk_bucketed_ex */
 typedef enum atopk_assignment {
   ATOPK_INTERLEAVED = 0, /* bucket of i = i mod b (what atopk_bucketed uses)    */

@@ -33,7 +33,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 17
+    assert len(names) == 18
     handle = ctypes.CDLL(lib_mod.LIB_PATH)
     for name in names:
         assert hasattr(handle, name), name
@@ -58,6 +58,19 @@ def test_stage_events_arguments(L):
     sz = ctypes.c_size_t(0)
     assert L.atopk_exact(None, F32, 1, 10, 10, 5, None, None, None, 0, None) == ENULL
     assert L.atopk_stage_count() == 0
+
+
+def test_noalloc_validation(L):
+    """The no-allocation variant refuses, before any HIP call, what
+    atopk_bucketed refuses, and shapes whose workspace exceeds its array."""
+    big = ctypes.c_size_t(0)
+    assert L.atopk_bucketed_workspace(F32, 8, 1 << 24, 1 << 24, 64, 4096, 16, 1, ctypes.byref(big)) == OK
+    assert big.value > 32 << 20
+    assert L.atopk_bucketed_noalloc(FAKE, F32, 8, 1 << 24, 1 << 24, 64, 4096, 16, 1, FAKE, FAKE, None) == EWS
+    assert L.atopk_bucketed_noalloc(FAKE, F32, 2, 100, 99, 5, 4, 2, 1, FAKE, FAKE, None) == ESHAPE  # ldx < n
+    assert L.atopk_bucketed_noalloc(FAKE, F32, 2, 100, 100, 50, 4, 2, 1, FAKE, FAKE, None) == EPARAM  # b*kb < k
+    assert L.atopk_bucketed_noalloc(FAKE, 7, 2, 100, 100, 5, 4, 2, 1, FAKE, FAKE, None) == EUNSUP  # dtype
+    assert L.atopk_bucketed_noalloc(None, F32, 0, 100, 100, 5, 4, 2, 1, None, None, None) == OK  # m == 0
 
 
 def _ws_exact(L, dt, m, n, ldx, k):

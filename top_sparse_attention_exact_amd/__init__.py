@@ -126,6 +126,25 @@ def bucketed(x, k, b, kb, final_exact=True, workspace=None, assignment="interlea
     return vals, idx
 
 
+NOALLOC_SCRATCH_BYTES = 32 << 20  # ATOPK_NOALLOC_SCRATCH_BYTES
+
+
+def bucketed_noalloc(x, k, b, kb, final_exact=True):
+    """bucketed() through atopk_bucketed_noalloc: the library's own device
+    scratch array is the workspace (no workspace allocation).  Outputs are
+    allocated here as usual."""
+    _check_rows(x)
+    m, n = x.shape
+    ldx = x.stride(0) if m > 1 else n
+    width = k if final_exact else b * kb
+    vals = torch.empty((m, width), dtype=x.dtype, device=x.device)
+    idx = torch.empty((m, width), dtype=torch.int32, device=x.device)
+    st = lib().atopk_bucketed_noalloc(_ptr(x), _DTYPES[x.dtype], m, n, ldx, k, b, kb, int(bool(final_exact)),
+                                      _ptr(vals), _ptr(idx), _stream_ptr(x.device))
+    check(st, "atopk_bucketed_noalloc")
+    return vals, idx
+
+
 def sparse_attn_decode(q, K, V, k_sel, b=1, kb=None, scale=None, ctx=None, return_sel=False, return_scores=False,
                        workspace=None):
     """Top-K sparse-attention decode.  q [B, Hq, D], K/V [B, Hkv, Lmax, D]

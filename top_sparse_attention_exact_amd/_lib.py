@@ -23,6 +23,10 @@ _SIGNATURES = {
         _c_int,
         [_c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_vp, ctypes.c_size_t, _c_vp],
     ),
+    "atopk_bucketed_noalloc": (
+        _c_int,
+        [_c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_vp],
+    ),
     "atopk_bucketed_ex_workspace": (
         _c_int, [_c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_int, _c_int, _c_size_p]
     ),
