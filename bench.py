@@ -249,8 +249,10 @@ def roofline_block(stages, call_alg, call_us, traffic_name):
     if dom is not None and "alg_bytes" in dom and dom["us"] >= 0.75 * total:
         kernel, alg, us = dom["kernel"], dom["alg_bytes"], dom["us"]
     else:
+        # the whole call, timed back to back (the stage events add their own
+        # overhead between the kernels)
         kernel = " + ".join(s["kernel"] for s in stages) if stages else "whole call"
-        alg, us = call_alg, (total if stages else call_us)
+        alg, us = call_alg, call_us
     achieved = alg / (us * 1e-6) / 1e9
     rec = recorded_traffic(traffic_name)
     traffic = rec[1] if rec is not None and rec[0] == kernel else None

@@ -630,8 +630,17 @@ __global__ __launch_bounds__(kFinT) void wide_final_kernel(const float* __restri
     sort_and_write(cand, kept, k, xr, n, ov, oi, bins, red);
     return;
   }
-  int cnt = b * kb;
-  for (int i = t; i < cnt; i += T) cand[i] = bucket_cand[(int64_t)row * cnt + i];
+  int cnt = b * kb;  // <= kFinMax = T * kFinP (the plan checks it)
+  {
+    // every load in flight before the first LDS store
+    const uint64_t* src = bucket_cand + (int64_t)row * cnt;
+    uint64_t v[kFinP];
+#pragma unroll
+    for (int p = 0; p < kFinP; ++p) v[p] = t + p * T < cnt ? src[t + p * T] : 0;
+#pragma unroll
+    for (int p = 0; p < kFinP; ++p)
+      if (t + p * T < cnt) cand[t + p * T] = v[p];
+  }
   __syncthreads();
   if (cnt > k) {
     const uint64_t kth = block_kth_key<T>(cand, cnt, k, hist, ctl);
@@ -642,14 +651,15 @@ __global__ __launch_bounds__(kFinT) void wide_final_kernel(const float* __restri
 
 // ---- one-pass stage 1 (bucketed, b a multiple of 64, k_b <= 16) ----------
 //
-// A workgroup owns 64 buckets of one row -- lane l is bucket 64*g + l -- over
-// the whole row, its 16 waves taking interleaved batches of sweeps, so every
-// element of a bucket passes through the workgroup that owns it.  Per
-// bucket, in LDS:
+// A workgroup owns 64 consecutive buckets of one row over the whole row --
+// lane l is bucket 64 * g + l -- and its 8 waves take interleaved batches of
+// sweeps, so every element of a bucket passes through the workgroup that
+// owns it.  Per bucket, in LDS:
 //  - a window [lo, lo + span] of order keys: lo is the k_b-th largest of the
-//    bucket's 256 first-batch samples (k_b elements of the bucket reach it,
-//    so its k_b-th largest does too), lo + span their largest;
-//  - a histogram of the window (256 bins, two 16-bit counts per word);
+//    bucket's 256 first samples (k_b elements of the bucket reach it, so its
+//    k_b-th largest does too), the window's top half its width above their
+//    largest, where the bucket's k_b-th largest often lies;
+//  - a histogram of the window (64 bins, two 16-bit counts per word);
 //  - thr, the highest bin whose count together with the bins above reaches
 //    k_b, refreshed at a few points of the stream.  Counts only grow, so thr
 //    never passes the bin of the bucket's final k_b-th largest key, and the
@@ -665,23 +675,21 @@ __global__ __launch_bounds__(kFinT) void wide_final_kernel(const float* __restri
 // it.  At the end the keys of the log in bins >= the final thr (the k_b-th
 // largest's bin: fewer than k_b keys above it, all of it logged) are ranked
 // and the first k_b kept, sorted.  A bucket whose log overflowed or whose
-// threshold bin holds more keys than a wave ranks at once is redone by its
+// threshold bin holds more keys than a wave ranks at once is redone by one
 // wave with a full scan of the bucket, so the result is exact for any input.
-// Two 512-thread workgroups fit on a CU (LDS), so one's window and end
-// phases overlap the other's streaming; each lane keeps two batches of
-// loads in flight behind the one it works on.
-constexpr int kOpT = 512;
-constexpr int kOpW = kOpT / kWave;    // waves
-constexpr int kOpU = 16;              // sweeps per wave and batch (loads per lane per batch)
-constexpr int kOpNB = 64;             // histogram bins per bucket: lane l of a tick owns bin l
+// Each lane keeps two batches of loads in flight behind the one it works on.
+constexpr int kOpW = 8;    // waves per 64 buckets
+constexpr int kBufferWord3 = 0x00020000;  // buffer resource flags word (raw 32-bit loads)
+constexpr int kOpU = 16;   // sweeps per wave and batch (loads per lane per batch)
+constexpr int kOpNB = 64;  // histogram bins per bucket: lane l of a tick owns bin l
 constexpr int kOpHW = kOpNB / 2 + 1;  // histogram words per bucket (padded row)
 constexpr int kOpCap = 120;           // logged keys per bucket
 constexpr int kOpQ = 128;             // per-wave ring of staged elements
 
 struct OnepassShared {
   uint32_t hist[kWave][kOpHW];
-  uint64_t logk[kWave][kOpCap];  // the first batch's value lists merge here before any key is logged
-  uint64_t ring[kOpW][kOpQ];     // staged (value bits, sweep, bucket); candidates of the end phase
+  uint64_t logk[kWave][kOpCap];  // the first samples' value lists merge here before any key is logged
+  alignas(16) uint64_t ring[kOpW][kOpQ];  // staged (value bits, sweep, bucket); candidates of the end phase
   uint32_t logn[kWave];
   int thr[kWave];
   uint32_t lo[kWave], span[kWave];
@@ -713,63 +721,126 @@ __device__ __noinline__ uint64_t wave_bucket_top16(const float* __restrict__ xro
   return mine;
 }
 
+// Inclusive prefix sum over the 64 lanes with DPP: row shifts build each
+// row's prefix, then row broadcasts carry the totals of the rows below.
+__device__ __forceinline__ int wave_prefix_dpp(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1 and 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+// A workgroup-scope relaxed load of an LDS word other waves may be updating.
+template <typename U>
+__device__ __forceinline__ U lds_load_relaxed(const U* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
 __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__global__ __launch_bounds__(kOpT) void wide_onepass_kernel(const float* __restrict__ x, int64_t ldx, int n, int b,
-                                                           int kb, int groups, int final_exact,
-                                                           uint64_t* __restrict__ cand, float* __restrict__ out_vals,
-                                                           int32_t* __restrict__ out_idx) {
+__global__ __launch_bounds__(kOpW * kWave) void wide_onepass_kernel(const float* __restrict__ x, int64_t ldx, int n,
+                                                                    int b, int kb, int groups, int final_exact,
+                                                                    uint64_t* __restrict__ cand,
+                                                                    float* __restrict__ out_vals,
+                                                                    int32_t* __restrict__ out_idx) {
+  constexpr int NB = kWave;  // buckets per workgroup
+  constexpr int NW = kOpW;   // waves
+  constexpr int T = NW * kWave;
   __shared__ OnepassShared S;
   const int t = threadIdx.x;
   const int lane = lane_id();
-  const int wave = t / kWave;
-  const int row = blockIdx.x / groups;
-  const int g = blockIdx.x - row * groups;
-  const int r = g * kWave + lane;  // this lane's bucket
+  const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
+  const int sw = wave;  // the wave takes sweeps sw + W * (U * bt + u)
+  // consecutive workgroups go to different XCDs: taking the row from the low
+  // part of the index spreads every bucket group over the XCDs, so that no
+  // XCD's L2 channels see only one column slice of the sweeps
+  const int mrows = (int)(gridDim.x / groups);
+  const int row = (int)blockIdx.x % mrows;
+  const int g = (int)blockIdx.x / mrows;
+  const int lb = lane;        // this lane's bucket in the group
+  const int r = g * NB + lb;  // ... in the row
   const float* xrow = x + (int64_t)row * ldx;
   const float* xr = xrow + r;
   const int nsw = (n + b - 1) / b;  // sweeps; the last may be partial
   const int nbatch = (nsw + kOpW * kOpU - 1) / (kOpW * kOpU);
 
-  for (int i = t; i < kWave * kOpHW; i += kOpT) (&S.hist[0][0])[i] = 0;
-  if (t < kWave) {
+  for (int i = t; i < NB * kOpHW; i += T) (&S.hist[0][0])[i] = 0;
+  if (t < NB) {
     S.logn[t] = 0;
     S.thr[t] = 0;
   }
 
-  // batch bt of wave w holds sweeps w + W*(U*bt + u), u < U
-  auto sweep_of = [&](int bt, int u) { return wave + kOpW * (kOpU * bt + u); };
-  // branch-free: a sweep past the lane's last element is read at that
-  // element instead (every load is unconditional) and masked afterwards
+  // batch bt of the stream is batch (bt + rot) mod nbatch of the row:
+  // workgroups start at different offsets, so the ones in flight together
+  // read addresses spread over the rows instead of one offset of every row
+  // (which crowds a few HBM channels); any order sees every element once
+  const int rot = (int)(blockIdx.x % (unsigned)nbatch);
+  auto phys = [&](int bt) { return bt + rot < nbatch ? bt + rot : bt + rot - nbatch; };
+  auto sweep_of = [&](int bt, int u) { return sw + kOpW * (kOpU * phys(bt) + u); };
+  // A batch below the row's first partial sweep is full: every lane has an
+  // element in each of its sweeps, so a load is a buffer load at the lane's
+  // byte offset in a resource over the sweep (scalar address arithmetic
+  // only), and no element needs a liveness test.  In the others a sweep past
+  // the lane's last element is read at that element instead (every load is
+  // unconditional) and masked afterwards.
+  const int full_sweeps = n / b;
+  auto full = [&](int bt) { return kOpW * kOpU * (phys(bt) + 1) <= full_sweeps; };
   const int last = (n - 1 - r) / b;  // the lane's last sweep
   auto live = [&](int s) { return s <= last; };
   float wa[kOpU], wb[kOpU], wc[kOpU];
   auto load = [&](float (&w)[kOpU], int bt) {
+    if (full(bt)) {
 #pragma unroll
-    for (int u = 0; u < kOpU; ++u) w[u] = xr[(int64_t)min(sweep_of(bt, u), last) * b];
+      for (int u = 0; u < kOpU; ++u) {
+        const __amdgpu_buffer_rsrc_t sweep_rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(xrow + (int64_t)sweep_of(bt, u) * b), (short)0, b * 4, kBufferWord3);
+        w[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sweep_rs, r * 4, 0, 0));
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kOpU; ++u) w[u] = xr[(int64_t)min(sweep_of(bt, u), last) * b];
+    }
   };
   load(wa, 0);
   if (nbatch > 1) load(wb, 1);
+  if (nbatch > 2) load(wc, 2);  // in flight while the window is computed
 
   // the window: the k_b-th largest and the largest of each bucket's first
-  // two batches (256 samples), from the waves' value lists merged into wave
-  // 0; its top goes half its width above the largest sample, where the
-  // bucket's k_b-th largest often lies
+  // two batches (256 samples), the value lists of the W waves merged into
+  // the first of them
   {
     float q[kWideKB];
 #pragma unroll
     for (int j = 0; j < kWideKB; ++j) q[j] = -INFINITY;
+    const bool full0 = full(0), full1 = nbatch > 1 && full(1);
 #pragma unroll
-    for (int u = 0; u < kOpU; ++u) fnet_insert<kWideKB>(q, live(sweep_of(0, u)) ? wa[u] : -INFINITY);
+    for (int u = 0; u < kOpU; ++u) fnet_insert<kWideKB>(q, (full0 || live(sweep_of(0, u))) ? wa[u] : -INFINITY);
 #pragma unroll
     for (int u = 0; u < kOpU; ++u)
-      fnet_insert<kWideKB>(q, (nbatch > 1 && live(sweep_of(1, u))) ? wb[u] : -INFINITY);
-    tree_merge<kWideKB>(q, reinterpret_cast<float*>(&S.logk[0][0]), kOpW);
-    if (wave == 0) {
+      fnet_insert<kWideKB>(q, (full1 || (nbatch > 1 && live(sweep_of(1, u)))) ? wb[u] : -INFINITY);
+    float* mbuf = reinterpret_cast<float*>(&S.logk[0][0]);
+    for (int half = kOpW / 2; half >= 1; half /= 2) {
+      if (sw >= half && sw < 2 * half) {
+#pragma unroll
+        for (int j = 0; j < kWideKB; ++j) mbuf[((sw - half) * kWideKB + j) * kWave + lane] = q[j];
+      }
+      __syncthreads();
+      if (sw < half) {
+        float c[kWideKB];
+#pragma unroll
+        for (int j = 0; j < kWideKB; ++j) c[j] = mbuf[(sw * kWideKB + j) * kWave + lane];
+        queue_merge<kWideKB>(q, c);
+      }
+      __syncthreads();
+    }
+    if (sw == 0) {
       float lo_v = q[0];
 #pragma unroll
       for (int j = 0; j < kWideKB; ++j)
@@ -779,15 +850,14 @@ __global__ __launch_bounds__(kOpT) void wide_onepass_kernel(const float* __restr
       const uint32_t span = (uint32_t)min((uint64_t)width + width / 2, (uint64_t)(0xffffffffu - lo));
       int sh = 0;
       while ((span >> sh) >= (uint32_t)kOpNB) ++sh;
-      S.lo[lane] = lo;
-      S.span[lane] = span;
-      S.sh[lane] = sh;
+      S.lo[lb] = lo;
+      S.span[lb] = span;
+      S.sh[lb] = sh;
     }
   }
   __syncthreads();
-  if (nbatch > 2) load(wc, 2);
-  const uint32_t my_lo = S.lo[lane];
-  const int my_sh = S.sh[lane];
+  const uint32_t my_lo = S.lo[lb];
+  const int my_sh = S.sh[lb];
   float fthr = __uint_as_float(bits_from_ord(my_lo));  // lower edge of the threshold bin
 
   // staged elements: ring entries head .. tail (wave-uniform counters)
@@ -802,76 +872,116 @@ __global__ __launch_bounds__(kOpT) void wide_onepass_kernel(const float* __restr
       const int bl = (int)(e >> 48);
       const int bin = (int)(min(o - S.lo[bl], S.span[bl]) >> S.sh[bl]);
       atomicAdd(&S.hist[bl][bin >> 1], 1u << ((bin & 1) << 4));
-      if (bin >= S.thr[bl]) {
+      if (bin >= lds_load_relaxed(&S.thr[bl])) {
         const uint32_t slot = atomicAdd(&S.logn[bl], 1u);
-        if (slot < (uint32_t)kOpCap) S.logk[bl][slot] = make_key(o, (uint32_t)(s * b + g * kWave + bl));
+        if (slot < (uint32_t)kOpCap) S.logk[bl][slot] = make_key(o, (uint32_t)(s * b + g * NB + bl));
       }
     }
     head += cnt;
     wave_sync_lds();
   };
+  // a staged element: value bits, then (sweep | bucket << 16)
+  auto stage = [&](bool pass, float v, uint32_t hi) {
+    const uint64_t m = __builtin_amdgcn_ballot_w64(pass);
+    if (m) {
+      if (pass) {
+        const uint32_t pos =
+            __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, (uint32_t)tail));
+        uint32_t* e = reinterpret_cast<uint32_t*>(ring + (pos & (kOpQ - 1)));
+        e[0] = __float_as_uint(v);
+        e[1] = hi;
+      }
+      tail += __popcll(m);
+      if (tail - head >= kWave) drain(kWave);
+    }
+  };
   auto process = [&](const float (&w)[kOpU], int bt) {
+    const uint32_t hi0 = (uint32_t)sweep_of(bt, 0) | ((uint32_t)lb << 16);
+    if (full(bt)) {
 #pragma unroll
-    for (int u = 0; u < kOpU; ++u) {
-      const bool pass = live(sweep_of(bt, u)) & (w[u] >= fthr);
-      const uint64_t m = __ballot(pass);
-      if (m) {
-        if (pass)
-          ring[(tail + (int)lanes_below(m)) & (kOpQ - 1)] =
-              (uint64_t)__float_as_uint(w[u]) | ((uint64_t)(uint32_t)sweep_of(bt, u) << 32) | ((uint64_t)lane << 48);
-        tail += __popcll(m);
-        if (tail - head >= kWave) drain(kWave);
-      }
+      for (int u = 0; u < kOpU; ++u) stage(w[u] >= fthr, w[u], hi0 + (uint32_t)(kOpW * u));
+    } else {
+#pragma unroll
+      for (int u = 0; u < kOpU; ++u)
+        stage(live(sweep_of(bt, u)) && w[u] >= fthr, w[u], hi0 + (uint32_t)(kOpW * u));
     }
   };
-  // threshold bins from the histograms: wave w refreshes buckets w, w + W, ...
-  auto tick = [&]() {
+  // threshold bins from the histograms: wave w refreshes buckets w, w + NW,
+  // ...  Only the last refresh waits for every wave's counts.  Before it a
+  // wave reads counts other waves are still adding to: they are lower bounds
+  // of the counts so far, so the bin it finds is at or below the one the
+  // full counts give -- still never above the bin of the bucket's final k_b-th
+  // largest key, which is all the filter and the log rely on
+  constexpr int kQ = NB / NW;
+  auto tick = [&](bool last_tick) {
     if (tail > head) drain(tail - head);
-    lds_barrier();
+    if (last_tick) lds_barrier();
+    // lane l holds bin 63 - l, so a prefix sum over the lanes is the count
+    // of keys in the bins from 63 - l up; the first lane reaching k_b names
+    // the threshold bin
+    const int bin = kOpNB - 1 - lane;
 #pragma unroll
-    for (int q = 0; q < kWave / kOpW; ++q) {
-      const int rb = wave + kOpW * q;
-      const int c = (int)((S.hist[rb][lane >> 1] >> ((lane & 1) << 4)) & 0xffffu);  // bin `lane`
-      int suf = c;  // bins >= lane
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const int v = __shfl_down(suf, o, kWave);
-        suf += lane + o < kWave ? v : 0;
-      }
-      if (suf - c < kb && kb <= suf) S.thr[rb] = lane;
+    for (int q = 0; q < kQ; ++q) {
+      const int rb = wave + NW * q;
+      const int c = (int)((lds_load_relaxed(&S.hist[rb][bin >> 1]) >> ((bin & 1) << 4)) & 0xffffu);
+      const uint64_t reach = __builtin_amdgcn_ballot_w64(wave_prefix_dpp(c) >= kb);
+      if (reach != 0 && lane == 0)
+        __hip_atomic_store(&S.thr[rb], kOpNB - 1 - (int)__builtin_ctzll(reach), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_WORKGROUP);
     }
-    lds_barrier();
-    fthr = __uint_as_float(bits_from_ord(my_lo + ((uint32_t)S.thr[lane] << my_sh)));
+    if (last_tick) {
+      lds_barrier();
+    } else {
+      wave_sync_lds();
+    }
+    fthr = __uint_as_float(bits_from_ord(my_lo + ((uint32_t)lds_load_relaxed(&S.thr[lb]) << my_sh)));
   };
-  auto ticks_after = [&](int bt) { return (bt & (bt + 1)) == 0 || bt == nbatch - 1; };
+  // refreshes after 3, 4, 6, 8, 12, 16, 24, ... batches and the last one
+  // (after the first two the counted keys are the samples at or above lo,
+  // exactly k_b of which reach it: the bin could not move yet)
+  auto ticks_after = [&](int bt) {
+    const int c = bt + 1, c3 = c / 3;
+    return bt == nbatch - 1 || (c >= 3 && ((c & (c - 1)) == 0 || (c == 3 * c3 && (c3 & (c3 - 1)) == 0)));
+  };
 
   // batch bt sits in buffer bt mod 3; the loads of bt + 1 and bt + 2 are in
   // flight while it is worked on
   for (int bt = 0; bt < nbatch; bt += 3) {
     if (bt > 0 && bt + 2 < nbatch) load(wc, bt + 2);
     process(wa, bt);
-    if (ticks_after(bt)) tick();
+    if (ticks_after(bt)) tick(bt == nbatch - 1);
     if (bt + 1 < nbatch) {
       if (bt + 3 < nbatch) load(wa, bt + 3);
       process(wb, bt + 1);
-      if (ticks_after(bt + 1)) tick();
+      if (ticks_after(bt + 1)) tick(bt + 1 == nbatch - 1);
     }
     if (bt + 2 < nbatch) {
       if (bt + 4 < nbatch) load(wb, bt + 4);
       process(wc, bt + 2);
-      if (ticks_after(bt + 2)) tick();
+      if (ticks_after(bt + 2)) tick(bt + 2 == nbatch - 1);
     }
   }
   // the tick after the last batch left every bucket's final threshold bin
 
-  // each bucket's exact top-k_b, wave w taking buckets w, w + 16, ...
-  for (int q = 0; q < kWave / kOpW; ++q) {
-    const int rb = wave + kOpW * q;
-    const int bucket = g * kWave + rb;
-    const int nl = (int)S.logn[rb];
-    const int B = S.thr[rb];
-    const uint32_t blo = S.lo[rb], bspan = S.span[rb];
-    const int bsh = S.sh[rb];
+  // each bucket's exact top-k_b, wave w taking buckets w, w + NW, ...  Lane
+  // l holds bucket l's final parameters; the candidates of consecutive
+  // buckets go to alternate halves of the wave's ring (no wait between
+  // buckets), and the results are stored together at the end (a store in
+  // flight would otherwise hold up the next bucket's LDS reads)
+  const int p_nl = (int)S.logn[lane];
+  const int p_thr = S.thr[lane];
+  const int p_span = (int)S.span[lane];
+  uint64_t res[kQ];
+  int rk[kQ];
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) {
+    const int rb = wave + NW * q;
+    const int nl = __builtin_amdgcn_readlane(p_nl, rb);
+    const int B = __builtin_amdgcn_readlane(p_thr, rb);
+    const uint32_t blo = (uint32_t)__builtin_amdgcn_readlane((int)my_lo, rb);
+    const uint32_t bspan = (uint32_t)__builtin_amdgcn_readlane(p_span, rb);
+    const int bsh = __builtin_amdgcn_readlane(my_sh, rb);
+    uint64_t* cb = ring + (q & 1) * kWave;
     int cnt = 0;
     if (nl <= kOpCap) {
       for (int i0 = 0; i0 < nl; i0 += kWave) {
@@ -880,43 +990,49 @@ __global__ __launch_bounds__(kOpT) void wide_onepass_kernel(const float* __restr
         const bool keep = i < nl && (int)(min(key_ord(key) - blo, bspan) >> bsh) >= B;
         const uint64_t m = __ballot(keep);
         const int slot = cnt + (int)lanes_below(m);
-        if (keep && slot < kWave) ring[slot] = key;
+        if (keep && slot < kWave) cb[slot] = key;
         cnt += __popcll(m);
       }
     }
-    wave_sync_lds();
     const bool ok = nl <= kOpCap && cnt >= kb && cnt <= kWave;
+    // zero keys pad the candidates to a multiple of 4 (a zero key is above none)
+    if (ok && lane >= cnt && lane < ((cnt + 3) & ~3)) cb[lane] = 0;
+    wave_sync_lds();
     uint64_t mine = 0;
     int rank = kWave;
     if (ok) {
-      // rank of each candidate among the candidates (lane = candidate)
-      mine = lane < cnt ? ring[lane] : 0;
-      const uint32_t mlo = (uint32_t)mine, mhi = (uint32_t)(mine >> 32);
+      // rank of each candidate among the candidates (lane = candidate), the
+      // others read as LDS broadcasts four at a time
+      mine = lane < cnt ? cb[lane] : 0;
       rank = 0;
-      for (int j = 0; j < cnt; ++j) {
-        const uint64_t o = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)mhi, j) << 32) |
-                           (uint32_t)__builtin_amdgcn_readlane((int)mlo, j);
-        rank += o > mine ? 1 : 0;
+      for (int j = 0; j < cnt; j += 4) {
+        const ulonglong2 p0 = *reinterpret_cast<const ulonglong2*>(cb + j);
+        const ulonglong2 p1 = *reinterpret_cast<const ulonglong2*>(cb + j + 2);
+        rank += (p0.x > mine ? 1 : 0) + (p0.y > mine ? 1 : 0) + (p1.x > mine ? 1 : 0) + (p1.y > mine ? 1 : 0);
       }
       if (lane >= cnt) rank = kWave;
     } else {
-      mine = wave_bucket_top16(xrow, n, b, bucket);
+      mine = wave_bucket_top16(xrow, n, b, g * NB + rb);
       rank = lane;
     }
-    if (rank < kb) {
-      const int64_t slot = ((int64_t)row * b + bucket) * kb + rank;
+    res[q] = mine;
+    rk[q] = rank;
+  }
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) {
+    if (rk[q] < kb) {
+      const int64_t slot = ((int64_t)row * b + g * NB + wave + NW * q) * kb + rk[q];
       if (final_exact) {
-        cand[slot] = mine;
+        cand[slot] = res[q];
       } else {
-        uint32_t idx = key_idx(mine);
+        uint32_t idx = key_idx(res[q]);
         idx = idx < (uint32_t)n ? idx : 0u;  // only reachable with NaN inputs
-        const uint32_t o = key_ord(mine);
+        const uint32_t o = key_ord(res[q]);
         out_idx[slot] = (int32_t)idx;
         reinterpret_cast<uint32_t*>(out_vals)[slot] =
             o == 0x80000000u ? reinterpret_cast<const uint32_t*>(xrow)[idx] : bits_from_ord(o);
       }
     }
-    wave_sync_lds();
   }
 }
 
@@ -958,7 +1074,7 @@ hipError_t launch_wide(const WidePlan& p, const float* x, int64_t m, int64_t n, 
   // bucketed rows whose buckets hold at most 65535 elements (16-bit
   // histogram counts): one pass over the input
   if (!exact && (n + b - 1) / b <= 65535) {
-    ATOPK_LAUNCH(wide_onepass_kernel, grid, dim3(kOpT), 0, s, x, ldx, (int)n, b, kb, (int)p.groups,
+    ATOPK_LAUNCH(wide_onepass_kernel, grid, dim3(kOpW * kWave), 0, s, x, ldx, (int)n, b, kb, (int)p.groups,
                  final_exact ? 1 : 0, w.cand, static_cast<float*>(out_vals), out_idx);
     if (final_exact)
       ATOPK_LAUNCH(wide_final_kernel, dim3((unsigned)m), dim3(kFinT), 0, s, x, ldx, (int)n, b, kb, (int)k, 0, w.cand,
