@@ -169,8 +169,13 @@ __global__ __launch_bounds__(kT1) void decode_select_kernel(const uint16_t* __re
   const int bpr = brange ? t / tpp : 0;
   const int bpart = brange ? t - bpr * tpp : 0;
 
+  // steps in rotated order: workgroups in flight together read different
+  // offsets of their key ranges instead of one offset of every range (which
+  // crowds a few HBM channels); the selection does not depend on the order
+  const int rot = nsteps > 0 ? (int)((blockIdx.x + blockIdx.y) % (unsigned)nsteps) : 0;
   int buf = 0;
-  for (int st = 0; st < nsteps; ++st) {
+  for (int st0 = 0; st0 < nsteps; ++st0) {
+    const int st = st0 + rot < nsteps ? st0 + rot : st0 + rot - nsteps;
     const int s0 = j0 + st * kSub;
     const int s1 = min(j1, s0 + kSub);
     // score the staged slots li = slot + 16 * (u + U * p)
@@ -315,12 +320,18 @@ __global__ __launch_bounds__(kT1M, 2) void decode_select_mfma_kernel(const uint1
   // share the load counter).  Loads of keys that are not live are masked off.
   static_assert(GR == 4, "the group schedule below is written for 4 groups per wave and step");
   uint4 kv0[KS], kv1[KS];
+  // steps in rotated order: workgroups in flight together read different
+  // offsets of their key ranges instead of one offset of every range (which
+  // crowds a few HBM channels); the selection does not depend on the order.
+  // phys(nsteps) = nsteps: the prefetch past the last step loads nothing.
+  const int rot = nsteps > 0 ? (int)((blockIdx.x + blockIdx.y) % (unsigned)nsteps) : 0;
+  auto phys = [&](int st) { return st >= nsteps ? nsteps : (st + rot < nsteps ? st + rot : st + rot - nsteps); };
   auto load_grp = [&](uint4 (&kv)[KS], int st, int gi) {
-    const int jj = key_of(st, (wave * GR + gi) * 16 + col);
+    const int ps = phys(st);
+    const int jj = ps < nsteps ? key_of(ps, (wave * GR + gi) * 16 + col) : ctx;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      kv[ks] = (st < nsteps && jj < ctx) ? *reinterpret_cast<const uint4*>(kh + (int64_t)jj * kD + 32 * ks)
-                                         : make_uint4(0, 0, 0, 0);
+      kv[ks] = jj < ctx ? *reinterpret_cast<const uint4*>(kh + (int64_t)jj * kD + 32 * ks) : make_uint4(0, 0, 0, 0);
   };
   int buf = 0;
   auto mma_grp = [&](const uint4 (&kv)[KS], int gi) {
@@ -349,12 +360,13 @@ __global__ __launch_bounds__(kT1M, 2) void decode_select_mfma_kernel(const uint1
     mma_grp(kv0, 2);
     mma_grp(kv1, 3);
     lds_barrier();
+    const int ps = phys(st);
     if (brange) {
-      if (scores != nullptr) dump_scores_brange<kT1M>(scores, (int64_t)(bi * hq + h * G), ctx, st, lgR, b, r0, G, sc[buf]);
+      if (scores != nullptr) dump_scores_brange<kT1M>(scores, (int64_t)(bi * hq + h * G), ctx, ps, lgR, b, r0, G, sc[buf]);
       load_grp(kv0, st + 1, 0);
-      if (bpr < npairs) fold_brange<KB>(qq[0], sc[buf], bpr >> lgR, bpr & ((1 << lgR) - 1), bpart, tpp, st, lgR, b, r0, ctx);
+      if (bpr < npairs) fold_brange<KB>(qq[0], sc[buf], bpr >> lgR, bpr & ((1 << lgR) - 1), bpart, tpp, ps, lgR, b, r0, ctx);
     } else {
-      const int s0 = j0 + st * kSub;
+      const int s0 = j0 + ps * kSub;
       const int nk = min(j1, s0 + kSub) - s0;
       if (scores != nullptr) dump_scores<kT1M>(scores, (int64_t)(bi * hq + h * G), ctx, s0, G, nk, sc[buf]);
       load_grp(kv0, st + 1, 0);
