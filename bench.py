@@ -280,8 +280,7 @@ def selection_kernels(workload, mode, m, n, k, es, width):
         return [name], [read + write]
     if workload == "wide-1m":
         if mode == "exact":
-            return (["wide_values_kernel<16>", "wide_exact_threshold_kernel", "wide_collect_exact_kernel",
-                     "wide_final_kernel"], [read, 0, 0, write])
+            return (["wide_sample_kernel", "wide_collect_row_kernel", "wide_final_kernel"], [0, read, write])
         return (["wide_onepass_kernel", "wide_final_kernel"], [read, write])
     return [], []
 

@@ -102,6 +102,11 @@ struct WidePlan {
   int sweeps_per_chunk;
   int64_t blocks;        // streaming workgroups: rows * groups
   size_t vals_bytes, bucket_bytes, cand_bytes, row_bytes;
+  // exact mode, one read: a sampled threshold, then a contiguous collect
+  bool sampled;
+  int sample_r;          // rank of the threshold among the row's samples
+  int row_chunks;        // collect workgroups per row
+  int steps_per_chunk;   // collect steps per workgroup
 };
 struct WideBuffers {
   float* vals;         // exact: top values per bucket

@@ -27,6 +27,9 @@
 //     sort on the value, and the output.  If the exact collection overflowed
 //     (rows made of few distinct values) the workgroup runs a full radix
 //     select over its row instead.
+#include <algorithm>
+#include <cmath>
+
 #include "common.h"
 #include "launch.h"
 
@@ -41,6 +44,7 @@ constexpr int kRowCap = 32768;  // exact-mode candidate keys per row
 constexpr int kFinT = 1024;
 constexpr int kFinP = 8;                // keys per thread in the final sort
 constexpr int kFinMax = kFinT * kFinP;  // 8192 candidates in LDS
+constexpr int kExactP = kRowCap / kFinT;  // collected keys per thread in the exact final
 constexpr int kExactB = 1024;           // bucketing that bounds the exact k-th value
 constexpr int kFlush = 256;             // per-wave key buffer of the exact collect
 
@@ -601,27 +605,68 @@ __global__ __launch_bounds__(kFinT) void wide_final_kernel(const float* __restri
   int32_t* oi = out_idx + (int64_t)row * k;
   if (exact_mode) {
     const int cnt = row_cnt[row];
-    if (cnt > kRowCap) {
+    if (cnt > kRowCap || cnt < k) {  // overflow, or a sampled threshold above the k-th
       row_radix_topk(xr, n, k, cand, hist, ctl);
       sort_and_write(cand, k, k, xr, n, ov, oi, bins, red);
       return;
     }
-    // cnt >= k unique keys: the k-th largest, then exactly k survive
+    // k <= cnt <= kRowCap unique keys, all loaded once (kExactP per thread,
+    // key i in thread i mod T): the k-th largest order word v by a radix
+    // select; the k - rem keys above it are in, and of the keys equal to it
+    // the rem with the largest index words (the lowest indices), found by a
+    // second select on those words when more than rem tie
     const uint64_t* keys = row_keys + (int64_t)row * kRowCap;
-    const uint64_t kth = block_kth_key<T>(keys, cnt, k, hist, ctl);
+    uint64_t kk[kExactP];
+#pragma unroll
+    for (int p = 0; p < kExactP; ++p) kk[p] = t + p * T < cnt ? keys[t + p * T] : 0;
+    auto valid = [&](int p) { return t + p * T < cnt; };
+    int rem;
+    const uint32_t v = block_radix_kth32<T>(
+        k, hist, ctl,
+        [&](uint32_t mask, uint32_t prefix, int shift) {
+#pragma unroll
+          for (int p = 0; p < kExactP; ++p) {
+            const uint32_t o = key_ord(kk[p]);
+            hist_add_grouped(hist, (o >> shift) & 255u, valid(p) && (o & mask) == prefix);
+          }
+        },
+        &rem);
+    int ties = 0;
+#pragma unroll
+    for (int p = 0; p < kExactP; ++p) ties += (valid(p) && key_ord(kk[p]) == v) ? 1 : 0;
+    ties = wave_sum(ties);
+    if (lane_id() == 0) red[t / kWave] = (uint32_t)ties;
+    __syncthreads();
+    ties = 0;
+    for (int w2 = 0; w2 < T / kWave; ++w2) ties += (int)red[w2];
+    __syncthreads();
+    uint32_t v2 = 0;  // keys equal to v with an index word >= v2 are in
+    if (ties > rem) {
+      int rem2;
+      v2 = block_radix_kth32<T>(
+          rem, hist, ctl,
+          [&](uint32_t mask, uint32_t prefix, int shift) {
+#pragma unroll
+            for (int p = 0; p < kExactP; ++p) {
+              const uint32_t lo = (uint32_t)kk[p];
+              hist_add(hist, (lo >> shift) & 255u,
+                       valid(p) && key_ord(kk[p]) == v && (lo & mask) == prefix);
+            }
+          },
+          &rem2);
+    }
     if (t == 0) ctl[4] = 0;
     __syncthreads();
-    for (int i0 = 0; i0 < cnt; i0 += T) {
-      const int i = i0 + t;
-      const uint64_t key = i < cnt ? keys[i] : 0;
-      const bool keep = key != 0 && key >= kth;
+#pragma unroll
+    for (int p = 0; p < kExactP; ++p) {
+      const uint32_t o = key_ord(kk[p]);
+      const bool keep = valid(p) && (o > v || (o == v && (uint32_t)kk[p] >= v2));
       const uint64_t m = __ballot(keep);
       if (m) {
         uint32_t pos = 0;
         if (lane_id() == 0) pos = atomicAdd(&ctl[4], (uint32_t)__popcll(m));
         pos = wave_lane0(pos);
-        const uint32_t slot = pos + lanes_below(m);
-        if (keep && slot < (uint32_t)kFinMax) cand[slot] = key;
+        if (keep) cand[pos + lanes_below(m)] = kk[p];
       }
     }
     __syncthreads();
@@ -647,6 +692,190 @@ __global__ __launch_bounds__(kFinT) void wide_final_kernel(const float* __restri
     cnt = block_compact_ge<T, kFinMax / T>(cand, cnt, kth, ctl);
   }
   sort_and_write(cand, cnt, k, xr, n, ov, oi, bins, red);
+}
+
+constexpr int kBufferWord3 = 0x00020000;  // buffer resource flags word (raw 32-bit loads)
+
+// Orders a wave's LDS accesses around cross-lane exchanges (the wave's LDS
+// operations complete in order; this keeps the compiler from moving them).
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ---- exact top-k in one read: sampled threshold, contiguous collect ---------
+//
+// The row's k-th largest key bounds what must be collected; a threshold at
+// or below it, close to it, comes from a sample: stratum t of the row (n /
+// 1024 elements) gives one 16-element chunk at a pseudo-random offset, so
+// every element of the strata has the same chance to be drawn, whatever the
+// row's structure.  The threshold is the r-th largest of the maxima of the
+// 4096 groups of four consecutive samples -- at most the r-th largest
+// sample, since r groups hold a sample at or above it -- with r above the
+// sample's expected count of top-k elements by a wide margin, so that the
+// row almost surely holds k elements at or above it.  The collect
+// then keeps every element at or above it in one contiguous read, and the
+// final takes the exact top-k of the kept keys -- or, when fewer than k were
+// kept (the margin failed) or the list overflowed, a full-row exact select.
+// The sample decides the cost, never the result.
+constexpr int kSampleT = 1024;    // strata (threads) per row
+constexpr int kSampleChunk = 16;  // elements per sample chunk
+constexpr int kCrT = 512;         // collect workgroup
+constexpr int kCrU = 16;          // loads per lane per step
+constexpr int kCrStep = kCrT * kCrU;
+
+__device__ __forceinline__ uint32_t mix32(uint32_t v) {  // an integer hash (xorshift-multiply rounds)
+  v ^= v >> 16;
+  v *= 0x7feb352du;
+  v ^= v >> 15;
+  v *= 0x846ca68bu;
+  v ^= v >> 16;
+  return v;
+}
+
+__global__ __launch_bounds__(kSampleT) void wide_sample_kernel(const float* __restrict__ x, int64_t ldx, int n,
+                                                              int r_sel, float* __restrict__ rowthr,
+                                                              int* __restrict__ row_cnt) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t ctl[4];
+  const int row = blockIdx.x;
+  const int t = threadIdx.x;
+  const int st = n / kSampleT;  // stratum length, >= kSampleChunk
+  const uint32_t slots = (uint32_t)(st / kSampleChunk);
+  const int off = (int)(mix32((uint32_t)row * kSampleT + (uint32_t)t + 0x9e3779b9u) % slots) * kSampleChunk;
+  const uint32_t* xs = reinterpret_cast<const uint32_t*>(x + (int64_t)row * ldx) + (int64_t)t * st + off;
+  constexpr int G = kSampleChunk / 4;
+  uint32_t o[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j)
+    o[j] = max(max(ord_f32(xs[4 * j]), ord_f32(xs[4 * j + 1])), max(ord_f32(xs[4 * j + 2]), ord_f32(xs[4 * j + 3])));
+  int rem;
+  const uint32_t v = block_radix_kth32<kSampleT>(
+      r_sel, hist, ctl,
+      [&](uint32_t mask, uint32_t prefix, int shift) {
+#pragma unroll
+        for (int j = 0; j < G; ++j) hist_add_grouped(hist, (o[j] >> shift) & 255u, (o[j] & mask) == prefix);
+      },
+      &rem);
+  if (t == 0) {
+    rowthr[row] = __uint_as_float(bits_from_ord(v));
+    row_cnt[row] = 0;
+  }
+}
+
+// Collect: workgroup (row, c) -- the chunks of a row on different XCDs --
+// reads steps [c * spc, (c + 1) * spc) of the row (step s: elements s *
+// kCrStep + u * kCrT + t) in order, two steps of loads in flight behind the
+// one it filters; an element
+// at or above the row's threshold goes to the row's key list through the
+// wave's LDS buffer, which holds a whole step's worth above its flush mark,
+// so that it is flushed between steps only (one atomic on the row's counter
+// per flush; the waves' last keys take one atomic between them).
+constexpr int kCrMark = 192;                     // flush above this many keys (two workgroups per CU)
+constexpr int kCrBuf = kCrMark + kCrU * kWave;  // + one step's worth
+__global__ __launch_bounds__(kCrT) void wide_collect_row_kernel(const float* __restrict__ x, int64_t ldx, int n,
+                                                               int chunks, int spc, const float* __restrict__ rowthr,
+                                                               int* __restrict__ row_cnt,
+                                                               uint64_t* __restrict__ row_keys) {
+  constexpr int W = kCrT / kWave;
+  __shared__ uint64_t wbuf[W][kCrBuf];
+  __shared__ uint32_t wg_off[W];
+  __shared__ uint32_t wg_base;
+  const int row = (int)blockIdx.x / chunks;
+  const int c = (int)blockIdx.x % chunks;
+  const int t = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
+  uint64_t* buf = wbuf[wave];
+  const float* xrow = x + (int64_t)row * ldx;
+  const float th = rowthr[row];
+  uint64_t* out = row_keys + (int64_t)row * kRowCap;
+  const int nsteps_row = (n + kCrStep - 1) / kCrStep;
+  const int full_steps = n / kCrStep;
+  const int s_begin = c * spc;
+  const int ns = max(0, min(nsteps_row, s_begin + spc) - s_begin);
+  auto phys = [&](int i) { return s_begin + i; };
+  int fill = 0;  // wave-uniform
+  auto flush = [&]() {
+    wave_sync_lds();
+    int base = 0;
+    if (lane == 0) base = atomicAdd(&row_cnt[row], fill);
+    base = (int)wave_lane0((uint32_t)base);
+    for (int j = lane; j < fill; j += kWave)
+      if (base + j < kRowCap) out[base + j] = buf[j];
+    wave_sync_lds();
+    fill = 0;
+  };
+  auto see = [&](bool keep, float v, uint32_t idx) {
+    const uint64_t m = __builtin_amdgcn_ballot_w64(keep);
+    if (m) {
+      if (keep) buf[fill + (int)lanes_below(m)] = make_key(ord_f32(__float_as_uint(v)), idx);
+      fill += __popcll(m);
+    }
+  };
+  float wa[kCrU], wb[kCrU], wc[kCrU];
+  auto load = [&](float (&w)[kCrU], int i) {
+    const int s = phys(i);
+    if (s < full_steps) {
+      const float* p = xrow + (int64_t)s * kCrStep + t;
+#pragma unroll
+      for (int u = 0; u < kCrU; ++u) w[u] = p[u * kCrT];
+    } else {
+#pragma unroll
+      for (int u = 0; u < kCrU; ++u) {
+        const int64_t e = (int64_t)s * kCrStep + u * kCrT + t;
+        w[u] = e < n ? xrow[e] : 0.0f;
+      }
+    }
+  };
+  auto filt = [&](const float (&w)[kCrU], int i) {
+    if (fill > kCrMark) flush();
+    const int s = phys(i);
+    const uint32_t i0 = (uint32_t)s * kCrStep + (uint32_t)t;
+    if (s < full_steps) {
+#pragma unroll
+      for (int u = 0; u < kCrU; ++u) see(w[u] >= th, w[u], i0 + (uint32_t)(u * kCrT));
+    } else {
+#pragma unroll
+      for (int u = 0; u < kCrU; ++u) {
+        const uint32_t e = i0 + (uint32_t)(u * kCrT);
+        see(e < (uint32_t)n && w[u] >= th, w[u], e);
+      }
+    }
+  };
+  // step i sits in buffer i mod 3; steps i + 1 and i + 2 load while it is
+  // filtered
+  if (ns > 0) load(wa, 0);
+  if (ns > 1) load(wb, 1);
+  for (int i = 0; i < ns; i += 3) {
+    if (i + 2 < ns) load(wc, i + 2);
+    filt(wa, i);
+    if (i + 1 < ns) {
+      if (i + 3 < ns) load(wa, i + 3);
+      filt(wb, i + 1);
+    }
+    if (i + 2 < ns) {
+      if (i + 4 < ns) load(wb, i + 4);
+      filt(wc, i + 2);
+    }
+  }
+  // the waves' last keys: offsets inside the workgroup, one atomic in all
+  if (lane == 0) wg_off[wave] = (uint32_t)fill;
+  __syncthreads();
+  if (t == 0) {
+    uint32_t tot = 0;
+    for (int w2 = 0; w2 < W; ++w2) {
+      const uint32_t cw = wg_off[w2];
+      wg_off[w2] = tot;
+      tot += cw;
+    }
+    wg_base = tot ? (uint32_t)atomicAdd(&row_cnt[row], (int)tot) : 0u;
+  }
+  __syncthreads();
+  const int base = (int)(wg_base + wg_off[wave]);
+  for (int j = lane; j < fill; j += kWave)
+    if (base + j < kRowCap) out[base + j] = buf[j];
 }
 
 // ---- one-pass stage 1 (bucketed, b a multiple of 64, k_b <= 16) ----------
@@ -679,7 +908,6 @@ __global__ __launch_bounds__(kFinT) void wide_final_kernel(const float* __restri
 // wave with a full scan of the bucket, so the result is exact for any input.
 // Each lane keeps two batches of loads in flight behind the one it works on.
 constexpr int kOpW = 8;    // waves per 64 buckets
-constexpr int kBufferWord3 = 0x00020000;  // buffer resource flags word (raw 32-bit loads)
 constexpr int kOpU = 16;   // sweeps per wave and batch (loads per lane per batch)
 constexpr int kOpNB = 64;  // histogram bins per bucket: lane l of a tick owns bin l
 constexpr int kOpHW = kOpNB / 2 + 1;  // histogram words per bucket (padded row)
@@ -739,11 +967,6 @@ __device__ __forceinline__ U lds_load_relaxed(const U* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-__device__ __forceinline__ void wave_sync_lds() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 __global__ __launch_bounds__(kOpW * kWave) void wide_onepass_kernel(const float* __restrict__ x, int64_t ldx, int n,
                                                                     int b, int kb, int groups, int final_exact,
@@ -1060,7 +1283,23 @@ WidePlan plan_wide(int dtype, int64_t m, int64_t n, int64_t k, int64_t b, int64_
   p.nchunks = nc;
   p.sweeps_per_chunk = (int)((nsweeps + nc - 1) / nc);
   p.blocks = m * p.groups;
-  p.vals_bytes = exact ? (size_t)m * kWideKB * b * 4 : 0;
+  if (exact) {
+    // one read when the list the sampled threshold is expected to keep fits
+    // well inside the row's list: r = the sample's expected count of top-k
+    // elements plus six of its standard deviations (the chunks make the
+    // count lumpier than independent draws) plus 16
+    const double S = (double)kSampleT * kSampleChunk;
+    const double rate = (double)k * S / (double)n;
+    const double r = std::min(S / 4, std::ceil(rate + 6.0 * std::sqrt(rate)) + 16.0);
+    p.sample_r = (int)r;
+    p.sampled = n / kSampleT >= kSampleChunk && r * (double)n / S <= 0.75 * kRowCap;
+    const int64_t nsteps_row = (n + kCrStep - 1) / kCrStep;
+    int64_t chunks = std::min<int64_t>(std::max<int64_t>(1, (512 + m - 1) / m), nsteps_row);
+    const int64_t spc = (nsteps_row + chunks - 1) / chunks;
+    p.steps_per_chunk = (int)spc;
+    p.row_chunks = (int)((nsteps_row + spc - 1) / spc);
+  }
+  p.vals_bytes = exact && !p.sampled ? (size_t)m * kWideKB * b * 4 : 0;
   p.bucket_bytes = exact ? (size_t)m * 4 : (size_t)m * b * 4;
   p.cand_bytes = (!exact && final_exact) ? (size_t)m * b * kb * 8 : 0;
   p.row_bytes = exact ? (size_t)m * kRowCap * 8 : 0;
@@ -1079,6 +1318,15 @@ hipError_t launch_wide(const WidePlan& p, const float* x, int64_t m, int64_t n, 
     if (final_exact)
       ATOPK_LAUNCH(wide_final_kernel, dim3((unsigned)m), dim3(kFinT), 0, s, x, ldx, (int)n, b, kb, (int)k, 0, w.cand,
                    w.row_cnt, w.row_keys, static_cast<float*>(out_vals), out_idx);
+    return hipGetLastError();
+  }
+  if (exact && p.sampled) {
+    ATOPK_LAUNCH(wide_sample_kernel, dim3((unsigned)m), dim3(kSampleT), 0, s, x, ldx, (int)n, p.sample_r, w.rowthr,
+                 w.row_cnt);
+    ATOPK_LAUNCH(wide_collect_row_kernel, dim3((unsigned)(m * p.row_chunks)), dim3(kCrT), 0, s, x, ldx, (int)n,
+                 p.row_chunks, p.steps_per_chunk, w.rowthr, w.row_cnt, w.row_keys);
+    ATOPK_LAUNCH(wide_final_kernel, dim3((unsigned)m), dim3(kFinT), 0, s, x, ldx, (int)n, b, kb, (int)k, 1, w.cand,
+                 w.row_cnt, w.row_keys, static_cast<float*>(out_vals), out_idx);
     return hipGetLastError();
   }
   if (p.kbn == 8)
