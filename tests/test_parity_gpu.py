@@ -396,6 +396,42 @@ def test_wide_exact_ties(gpu):
     check_exact(x, 3000)  # -0.0 and +0.0 are one value: lowest indices win
 
 
+def _sampled_positions(row, n):
+    """Element positions the wide exact route samples in `row` (n / 1024
+    strata, one 16-element chunk at a hashed offset in each), written from
+    the kernel's sampling rule so that a test can plant values exactly there."""
+    def mix32(v):
+        v &= 0xFFFFFFFF
+        v ^= v >> 16
+        v = (v * 0x7FEB352D) & 0xFFFFFFFF
+        v ^= v >> 15
+        v = (v * 0x846CA68B) & 0xFFFFFFFF
+        v ^= v >> 16
+        return v
+
+    st = n // 1024
+    slots = st // 16
+    pos = []
+    for t in range(1024):
+        off = (mix32(row * 1024 + t + 0x9E3779B9) % slots) * 16
+        pos.extend(range(t * st + off, t * st + off + 16))
+    return np.array(pos)
+
+
+def test_wide_exact_sample_fallback(gpu):
+    """The largest values of the row sit exactly on the sampled positions, so
+    the sampled threshold lands above the row's k-th largest and fewer than k
+    elements reach it: the final must fall back to the full-row select and
+    still return the exact top-k."""
+    m, n, k = 2, 131072, 4096
+    g = torch.Generator(device="cpu").manual_seed(17)
+    x = torch.rand((m, n), generator=g)
+    for row in range(m):
+        pos = torch.from_numpy(_sampled_positions(row, n))
+        x[row, pos] = 1000.0 + torch.rand(len(pos), generator=g)
+    check_exact(x.to(gpu), k)
+
+
 def test_wide_exact_special_values(gpu):
     x = workloads.rows_ties_bf16(3, 70000, 8, seed=3, device="cpu").float().to(gpu)
     for k in (100, 4000):
