@@ -114,6 +114,15 @@ bool wide_exact(int dtype, int64_t m, int64_t n, int64_t k) {
   return k > 64 && plan_wide(dtype, m, n, k, 0, 0, true, true).ok;
 }
 
+// fp32 rows whose exact top-k the sampled one-read route takes (ahead of the
+// certified route: one read with a cheap filter, where the certified stage 1
+// keeps 64-bit key queues).
+bool wide_sampled_exact(int dtype, int64_t m, int64_t n, int64_t k) {
+  if (k <= 64) return false;
+  const WidePlan p = plan_wide(dtype, m, n, k, 0, 0, true, true);
+  return p.ok && p.sampled;
+}
+
 // fp32 rows with k_b > 4 go to the two-pass path.
 bool wide_bucketed(int dtype, int64_t m, int64_t n, int64_t k, int64_t b, int64_t kb, int final_exact) {
   return kb > 4 && plan_wide(dtype, m, n, k, b, kb, false, final_exact != 0).ok;
@@ -145,6 +154,7 @@ int run_certified(const CertPlan& c, const void* x, int dtype, int64_t m, int64_
                   void* out_vals, int32_t* out_idx, void* ws, hipStream_t s);
 
 size_t exact_ws_bytes(int dtype, int64_t m, int64_t n, int64_t k) {
+  if (wide_sampled_exact(dtype, m, n, k)) return wide_layout(dtype, m, n, k, 0, 0, true, true).total;
   const CertPlan cert = plan_certified(dtype, m, n, k);
   if (cert.ok) return certified_ws_bytes(dtype, m, n, cert);
   if (wide_exact(dtype, m, n, k)) return wide_layout(dtype, m, n, k, 0, 0, true, true).total;
@@ -164,6 +174,9 @@ int run_exact(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, int64
   const int64_t es = dtype == ATOPK_F32 ? 4 : 2;
   if (row_exact_ok(dtype, m, n, k, rows_aligned(x, ldx, es)))
     return hip_status(launch_row_exact(x, dtype, m, n, ldx, k, out_vals, out_idx, s));
+  if (wide_sampled_exact(dtype, m, n, k))
+    return run_wide(wide_layout(dtype, m, n, k, 0, 0, true, true), x, m, n, ldx, k, true, true, out_vals, out_idx, ws,
+                    s);
   const CertPlan cert = plan_certified(dtype, m, n, k);
   if (cert.ok) return run_certified(cert, x, dtype, m, n, ldx, k, out_vals, out_idx, ws, s);
   if (wide_exact(dtype, m, n, k))

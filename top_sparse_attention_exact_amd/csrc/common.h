@@ -712,13 +712,16 @@ __device__ int block_compact_ge(uint64_t* keys, int n, uint64_t thr, uint32_t* c
 // largest v with #{keys >= v} >= k (the k-th largest key, with
 // multiplicity).  `count(mask, prefix, shift)` histograms, into hist[256],
 // the digit at `shift` of every key whose bits under `mask` equal `prefix`.
-// Returns v; *rem_out = how many copies of v the top k take.
+// Returns v; *rem_out = how many copies of v the top k take.  When every key
+// shares its `common` leading bytes, `lead` (those bytes in place, the rest
+// zero) skips their passes.
 template <int T, typename Count>
-__device__ uint32_t block_radix_kth32(int k, uint32_t* hist, uint32_t* ctl, Count&& count, int* rem_out) {
+__device__ uint32_t block_radix_kth32(int k, uint32_t* hist, uint32_t* ctl, Count&& count, int* rem_out,
+                                      int common = 0, uint32_t lead = 0) {
   const int t = threadIdx.x;
-  uint32_t prefix = 0, mask = 0;
+  uint32_t prefix = common > 0 ? lead : 0u, mask = common > 0 ? 0xffffffffu << (32 - 8 * common) : 0u;
   int rem = k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
+  for (int shift = 24 - 8 * common; shift >= 0; shift -= 8) {
     for (int i = t; i < 256; i += T) hist[i] = 0;
     __syncthreads();
     count(mask, prefix, shift);

@@ -615,25 +615,54 @@ __global__ __launch_bounds__(kFinT) void wide_final_kernel(const float* __restri
     // select; the k - rem keys above it are in, and of the keys equal to it
     // the rem with the largest index words (the lowest indices), found by a
     // second select on those words when more than rem tie
+    // (loops over the register slots stop at np = the slots in use; the
+    // leading bytes every kept key shares skip their radix passes)
     const uint64_t* keys = row_keys + (int64_t)row * kRowCap;
+    const int np = (cnt + T - 1) / T;
     uint64_t kk[kExactP];
 #pragma unroll
-    for (int p = 0; p < kExactP; ++p) kk[p] = t + p * T < cnt ? keys[t + p * T] : 0;
+    for (int p = 0; p < kExactP; ++p) kk[p] = p < np && t + p * T < cnt ? keys[t + p * T] : 0;
     auto valid = [&](int p) { return t + p * T < cnt; };
+    uint32_t wa = 0xffffffffu, wo = 0;
+#pragma unroll
+    for (int p = 0; p < kExactP; ++p) {
+      if (p < np && valid(p)) {
+        wa &= key_ord(kk[p]);
+        wo |= key_ord(kk[p]);
+      }
+    }
+    wa = wave_reduce_dpp(wa, [](uint32_t a, uint32_t c) { return a & c; });
+    wo = wave_reduce_dpp(wo, [](uint32_t a, uint32_t c) { return a | c; });
+    if (lane_id() == 0) {
+      red[2 * (t / kWave)] = wa;
+      red[2 * (t / kWave) + 1] = wo;
+    }
+    __syncthreads();
+    wa = 0xffffffffu;
+    wo = 0;
+    for (int w2 = 0; w2 < T / kWave; ++w2) {
+      wa &= red[2 * w2];
+      wo |= red[2 * w2 + 1];
+    }
+    __syncthreads();
+    const int common = (wa ^ wo) == 0 ? 3 : min(3, __builtin_clz(wa ^ wo) / 8);
+    const uint32_t lead = common > 0 ? wa & (0xffffffffu << (32 - 8 * common)) : 0u;
     int rem;
     const uint32_t v = block_radix_kth32<T>(
         k, hist, ctl,
         [&](uint32_t mask, uint32_t prefix, int shift) {
 #pragma unroll
           for (int p = 0; p < kExactP; ++p) {
-            const uint32_t o = key_ord(kk[p]);
-            hist_add_grouped(hist, (o >> shift) & 255u, valid(p) && (o & mask) == prefix);
+            if (p < np) {
+              const uint32_t o = key_ord(kk[p]);
+              hist_add_grouped(hist, (o >> shift) & 255u, valid(p) && (o & mask) == prefix);
+            }
           }
         },
-        &rem);
+        &rem, common, lead);
     int ties = 0;
 #pragma unroll
-    for (int p = 0; p < kExactP; ++p) ties += (valid(p) && key_ord(kk[p]) == v) ? 1 : 0;
+    for (int p = 0; p < kExactP; ++p) ties += (p < np && valid(p) && key_ord(kk[p]) == v) ? 1 : 0;
     ties = wave_sum(ties);
     if (lane_id() == 0) red[t / kWave] = (uint32_t)ties;
     __syncthreads();
@@ -648,9 +677,10 @@ __global__ __launch_bounds__(kFinT) void wide_final_kernel(const float* __restri
           [&](uint32_t mask, uint32_t prefix, int shift) {
 #pragma unroll
             for (int p = 0; p < kExactP; ++p) {
-              const uint32_t lo = (uint32_t)kk[p];
-              hist_add(hist, (lo >> shift) & 255u,
-                       valid(p) && key_ord(kk[p]) == v && (lo & mask) == prefix);
+              if (p < np) {
+                const uint32_t lo = (uint32_t)kk[p];
+                hist_add(hist, (lo >> shift) & 255u, valid(p) && key_ord(kk[p]) == v && (lo & mask) == prefix);
+              }
             }
           },
           &rem2);
@@ -659,6 +689,7 @@ __global__ __launch_bounds__(kFinT) void wide_final_kernel(const float* __restri
     __syncthreads();
 #pragma unroll
     for (int p = 0; p < kExactP; ++p) {
+      if (p >= np) continue;
       const uint32_t o = key_ord(kk[p]);
       const bool keep = valid(p) && (o > v || (o == v && (uint32_t)kk[p] >= v2));
       const uint64_t m = __ballot(keep);
