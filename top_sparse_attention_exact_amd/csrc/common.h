@@ -583,6 +583,30 @@ __device__ void block_sort_desc(uint64_t* keys, int n_pow2) {
   __syncthreads();
 }
 
+// The number of keys[0..n16) above `key`: keys in LDS, 16-byte aligned, n16 a
+// multiple of 16 (the caller pads with zero keys, which are above none).
+// Eight 16-byte broadcast reads are in flight per step, so the count runs at
+// LDS throughput rather than one read latency per comparison.
+__device__ __forceinline__ int count_above16(const uint64_t* keys, int n16, uint64_t key) {
+  int c = 0;
+  for (int j = 0; j < n16; j += 16) {
+    ulonglong2 p[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) p[u] = *reinterpret_cast<const ulonglong2*>(keys + j + 2 * u);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) c += (p[u].x > key ? 1 : 0) + (p[u].y > key ? 1 : 0);
+  }
+  return c;
+}
+
+// Zero keys[n .. n rounded up to 16) and return that length (all threads of
+// the block; the caller synchronises before the keys are read).
+__device__ __forceinline__ int block_pad16(uint64_t* keys, int n) {
+  const int n16 = (n + 15) & ~15;
+  for (int i = n + (int)threadIdx.x; i < n16; i += (int)blockDim.x) keys[i] = 0;
+  return n16;
+}
+
 // The n unique nonzero keys of keys[0..n) (LDS, capacity cap >= 2048, a
 // power of two) in descending order, returned as a pointer into keys: for
 // n <= 1024 each key's rank -- the number of larger keys, counted over the
@@ -594,18 +618,11 @@ template <int T>
 __device__ uint64_t* block_order_desc(uint64_t* keys, int n, int cap) {
   if (n <= 1024) {
     uint64_t* dst = keys + cap / 2;
+    const int n16 = block_pad16(keys, n);
+    __syncthreads();
     for (int c = (int)threadIdx.x; c < n; c += T) {
       const uint64_t key = keys[c];
-      int c0 = 0, c1 = 0, c2 = 0, c3 = 0;
-      int j = 0;
-      for (; j + 4 <= n; j += 4) {
-        c0 += keys[j] > key ? 1 : 0;
-        c1 += keys[j + 1] > key ? 1 : 0;
-        c2 += keys[j + 2] > key ? 1 : 0;
-        c3 += keys[j + 3] > key ? 1 : 0;
-      }
-      for (; j < n; ++j) c0 += keys[j] > key ? 1 : 0;
-      dst[c0 + c1 + c2 + c3] = key;
+      dst[count_above16(keys, n16, key)] = key;
     }
     __syncthreads();
     return dst;

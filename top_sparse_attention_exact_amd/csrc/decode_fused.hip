@@ -596,7 +596,7 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(4))) void d
                                                            const uint16_t* __restrict__ q,
                                                            const uint16_t* __restrict__ K, float scale) {
   constexpr int T = kT2;
-  __shared__ uint64_t cand[kMaxCand];
+  __shared__ alignas(16) uint64_t cand[kMaxCand];
   __shared__ uint32_t hist[256 * kKthSub];
   __shared__ uint32_t ctl[8];
   __shared__ uint32_t flg_r[kFlagMax];
@@ -720,20 +720,11 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(4))) void d
     if (sorted) {
       for (int i = t; i < n; i += T) dst[i] = (int32_t)key_idx(sel[i]);
     } else {
-      // a key's place in descending order: the number of larger keys
-      for (int c = t; c < n; c += T) {
-        const uint64_t key = sel[c];
-        int c0 = 0, c1 = 0, c2 = 0, c3 = 0;
-        int j = 0;
-        for (; j + 4 <= n; j += 4) {
-          c0 += sel[j] > key ? 1 : 0;
-          c1 += sel[j + 1] > key ? 1 : 0;
-          c2 += sel[j + 2] > key ? 1 : 0;
-          c3 += sel[j + 3] > key ? 1 : 0;
-        }
-        for (; j < n; ++j) c0 += sel[j] > key ? 1 : 0;
-        dst[c0 + c1 + c2 + c3] = (int32_t)key_idx(key);
-      }
+      // a key's place in descending order: the number of larger keys (the
+      // padding past n is read by the count only)
+      const int n16 = block_pad16(cand, n);
+      __syncthreads();
+      for (int c = t; c < n; c += T) dst[count_above16(cand, n16, cand[c])] = (int32_t)key_idx(cand[c]);
     }
   }
 

@@ -166,7 +166,7 @@ __global__ __launch_bounds__(kST) void rerank_select_kernel(const uint64_t* __re
                                                            const uint16_t* __restrict__ V, int k_sel,
                                                            uint16_t* __restrict__ out, int32_t* __restrict__ sel_idx) {
   constexpr int T = kST;
-  __shared__ uint64_t keys[kRerankMaxCand];
+  __shared__ alignas(16) uint64_t keys[kRerankMaxCand];
   __shared__ uint32_t hist[256 * kKthSub];
   __shared__ uint32_t ctl[8];
   __shared__ float w_lds[kSGroups];
@@ -205,19 +205,11 @@ __global__ __launch_bounds__(kST) void rerank_select_kernel(const uint64_t* __re
     if (sorted) {
       for (int i = t; i < n; i += T) dst[i] = (int32_t)key_idx(sel[i]);
     } else {
-      for (int c = t; c < n; c += T) {  // a key's place: the number of larger keys
-        const uint64_t key = sel[c];
-        int c0 = 0, c1 = 0, c2 = 0, c3 = 0;
-        int j = 0;
-        for (; j + 4 <= n; j += 4) {
-          c0 += sel[j] > key ? 1 : 0;
-          c1 += sel[j + 1] > key ? 1 : 0;
-          c2 += sel[j + 2] > key ? 1 : 0;
-          c3 += sel[j + 3] > key ? 1 : 0;
-        }
-        for (; j < n; ++j) c0 += sel[j] > key ? 1 : 0;
-        dst[c0 + c1 + c2 + c3] = (int32_t)key_idx(key);
-      }
+      // a key's place: the number of larger keys (the padding past n is read
+      // by the count only)
+      const int n16 = block_pad16(keys, n);
+      __syncthreads();
+      for (int c = t; c < n; c += T) dst[count_above16(keys, n16, keys[c])] = (int32_t)key_idx(keys[c]);
     }
   }
 
