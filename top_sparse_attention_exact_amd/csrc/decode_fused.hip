@@ -657,8 +657,9 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(4))) void d
   int n = b * kb;
   // Order of the selection for the softmax-V sums (and its ranks for
   // sel_idx): the stable compaction's order -- a function of the candidates
-  // alone -- or, after a rescan or a fallback (which append keys in arrival
-  // order) and for selections above kStableMax keys, descending order.
+  // alone, a rescan's keys put in descending order behind them -- or, after a
+  // fallback (which collects keys in arrival order), a rescan of more than T
+  // keys, and for selections above kStableMax keys, descending order.
   bool sorted = false;
   if (certify) {
     const uint64_t thr = block_kth_key_binned<T>(cand, n, k_sel, hist, ctl);
@@ -680,7 +681,6 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(4))) void d
     n = block_compact_ge_stable<T, kMaxCand / T>(cand, n, thr, hist);  // k_sel keys
     const int nflag = (int)ctl[5];
     if (nflag > 0) {
-      sorted = true;
       bool overflow = nflag > kFlagMax;
       const uint16_t* kh = K + (int64_t)bh * ctx_stride * kD;
       const uint16_t* qg = q + (int64_t)(r_out - g) * kD;  // the G query rows of the KV head
@@ -695,11 +695,30 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(4))) void d
         overflow = k_sel + extra > kMaxCand;
         if (!overflow && extra > 0) {
           n = k_sel + extra;
+          // The rescan appended its keys in the order its waves' atomics ran;
+          // put them in descending order so that the list -- the selected
+          // keys in their stable order, then these -- is one function of the
+          // scores and the compaction below keeps a canonical order.  More
+          // than T of them: the selection is sorted instead.
+          if (extra <= T) {
+            uint64_t key = 0;
+            int rank = 0;
+            if (t < extra) {
+              key = cand[k_sel + t];
+              for (int j = 0; j < extra; ++j) rank += cand[k_sel + j] > key ? 1 : 0;
+            }
+            __syncthreads();
+            if (t < extra) cand[k_sel + rank] = key;
+            __syncthreads();
+          } else {
+            sorted = true;
+          }
           const uint64_t thr2 = block_kth_key<T, kKthSub>(cand, n, k_sel, hist, ctl);
           n = block_compact_ge_stable<T, kMaxCand / T>(cand, n, thr2, hist);
         }
       }
       if (overflow) {
+        sorted = true;
         float* row = scores + (int64_t)r_out * ctx;
         if (certify == 1)
           decode_fill_scores_mfma(qg, G, g, kh, scale, ctx, row);
