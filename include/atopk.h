@@ -94,7 +94,7 @@ int atopk_stage_count(void);
  * Exact top-k of every row of x.
  *   x         [m, ldx] row-major, dtype `dtype`; row r is x[r*ldx .. r*ldx+n).
  *   out_vals  [m, k] same dtype as x; out_idx [m, k] int32.  Row r lists the
- *             k largest entries of row r, value descending then index ascending.
+ *             k greatest values of row r, value descending then index ascending.
  * Limits: 1 <= k <= min(n, 8192), n < 2^31.  m == 0 is a no-op.  x and
  * out_vals must be aligned to the element size, out_idx to 4 bytes
  * (ATOPK_ERR_PARAM otherwise); rows need no further alignment.

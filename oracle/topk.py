@@ -47,9 +47,9 @@ def _rank_order(vals, idx):
 def exact_topk(x, k, dtype="f32"):
     """Exact top-k of every row of x (shape [m, n]).
 
-    The k largest entries of each row (the exact problem stated in the
-    Approximate Top-k page, "The reading"), ordered by value descending and
-    then by index ascending.
+    Each row's k greatest values with their positions (the exact problem of
+    the Approximate Top-k page, "The reading"), ordered by value descending
+    and then by index ascending.
 
     Returns (idx [m, k] int64, vals [m, k] in x's own dtype / bit pattern).
     """

@@ -9,24 +9,28 @@
 // carries the argument": the two-stage bucketed selection stands in for the
 // single global Top-K.
 //
-// Kernel 1 (grid: context chunks x (batch, KV head)): 16 lanes read one
-// 256-byte key row with 16-byte loads and form its dot products with the g
-// query heads that share the KV head (packed bf16 dot products, fp32
-// accumulation, DPP row sums).  Scores of 512 keys at a time are staged in
-// LDS (double buffered, one LDS-only barrier per step, so K loads stay in
-// flight); then every thread folds the staged scores of the (head, bucket)
-// pairs it owns into sorted k_b-queues of 64-bit keys (order key of the
-// score, then ~key index).  Scores never go to HBM unless a debug dump is
-// asked for.  Each workgroup writes its per-pair lists to the workspace.
+// Kernel 1 (grid: context chunks or bucket ranges x (batch, KV head)): 16
+// lanes read one 256-byte key row with 16-byte loads and form its dot
+// products with the g query heads that share the KV head (packed bf16 dot
+// products, fp32 accumulation, DPP row sums; query-head groups on the matrix
+// cores).  Scores of 512 keys at a time are staged in LDS (double buffered,
+// one LDS-only barrier per step, so K loads stay in flight); then every
+// thread folds the staged scores of the (head, bucket) pairs it owns into
+// sorted k_b-queues of 64-bit keys (order key of the score, then ~key index).
+// In bucket-range mode a workgroup owns whole buckets over the whole context,
+// so its lists are final.  A workgroup visits its steps in a rotated order,
+// so that the workgroups in flight read different offsets of their ranges.
+// Scores never go to HBM unless a debug dump is asked for.  Each workgroup
+// writes its per-pair lists to the workspace.
 //
 // With b = 0 kernel 1 only writes every score (the exact Top-K route selects
 // on the written scores).
 //
 // Kernel 2 (grid: batch x query heads): merge the chunk lists of every
-// bucket, take the exact Top-K of the b*k_b candidates in LDS (radix select),
-// optionally sort them for the index output, then softmax over the selected
-// scores (maximum subtracted, fp32) and the weighted sum of the gathered V
-// rows, rounded to bf16.
+// bucket (bucket-range lists need none), take the exact Top-K of the b*k_b
+// candidates in LDS (binned select, order-preserving compaction), then the
+// softmax over the selected scores (maximum subtracted, fp32) and the
+// weighted sum of the gathered V rows in rank order, rounded to bf16.
 #include "common.h"
 #include "launch.h"
 
