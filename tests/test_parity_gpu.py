@@ -450,6 +450,16 @@ def test_wide_bucketed(gpu, b, kb):
         check_bucketed(x, b * kb // 3, b, kb, True)
 
 
+@pytest.mark.parametrize("m", [100, 300])
+def test_wide_final_parts(gpu, m):
+    # 100 rows: each row's final sort split over two workgroups; 300 rows:
+    # one workgroup per row
+    x = rand_rows(m, 12000, torch.float32, m, gpu)
+    check_bucketed(x, 8192, 512, 16, True)
+    check_bucketed(x, 1000, 512, 16, True)
+    check_exact(x, 2000)
+
+
 @pytest.mark.parametrize("levels", [2, 64, 1024])
 def test_wide_bucketed_ties(gpu, levels):
     # 2 levels: hundreds of ties per bucket (index-ordered walk); 64 and 1024

@@ -107,6 +107,7 @@ struct WidePlan {
   int sample_r;          // rank of the threshold among the row's samples
   int row_chunks;        // collect workgroups per row
   int steps_per_chunk;   // collect steps per workgroup
+  int final_parts;       // final workgroups per row (they split the sort by value)
 };
 struct WideBuffers {
   float* vals;         // exact: top values per bucket

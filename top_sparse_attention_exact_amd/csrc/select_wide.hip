@@ -22,11 +22,12 @@
 //     collects separately (Figure 12) -- and the waves merge their key
 //     queues, leaving each bucket's exact top-k_b; exact, every element
 //     >= T goes to the row's key list.
-//  3. final, one workgroup per row (skipped by stage-1-only calls): the
-//     exact top-k of the candidates (radix select on the keys), a counting
-//     sort on the value, and the output.  If the exact collection overflowed
-//     (rows made of few distinct values) the workgroup runs a full radix
-//     select over its row instead.
+//  3. final (skipped by stage-1-only calls): the exact top-k of the
+//     candidates (radix select on the keys), a counting sort on the value,
+//     and the output; with few rows up to four workgroups per row split the
+//     sort by value.  If the exact collection overflowed (rows made of few
+//     distinct values) the workgroup runs a full radix select over its row
+//     instead.
 #include <algorithm>
 #include <cmath>
 
@@ -45,6 +46,8 @@ constexpr int kFinT = 1024;
 constexpr int kFinP = 8;                // keys per thread in the final sort
 constexpr int kFinMax = kFinT * kFinP;  // 8192 candidates in LDS
 constexpr int kExactP = kRowCap / kFinT;  // collected keys per thread in the exact final
+constexpr int kFinParts = 4;             // most final workgroups per row
+constexpr int64_t kFinCUs = 256;         // compute units the final fills
 constexpr int kExactB = 1024;           // bucketing that bounds the exact k-th value
 constexpr int kFlush = 256;             // per-wave key buffer of the exact collect
 
@@ -402,27 +405,89 @@ __device__ void block_sort_desc_regs(uint64_t (&key)[P], uint64_t* lds) {
   }
 }
 
-// Sort cand[0..cnt) (LDS, cnt <= kFinMax, unique nonzero keys) descending.
-// Counting sort on the value over equi-depth bins (bin 0 = largest values;
-// see below), a scan and a scatter; then every key's place is its bin's
-// start plus the number of larger keys in its bin.  A bin above kBinRank
-// keys (heavy ties) sends the whole set to the bitonic sort.  `bins` holds
-// kFinMax words, `red` 64 + 2 * kCoarse.
+// Sorted output of part `part` of `parts` of a row's cnt unique nonzero
+// keys (global memory, cnt <= kFinT * PIN): the keys of rank r < k whose
+// rank falls in this part, written as values (bit copies of the row) and
+// indices.  The parts of a row run in separate workgroups that each read
+// every key and split the work by value.
+//
+// Counting sort on the value over equi-depth bins.  Each key's distance
+// below the largest, hi - ord, maps monotonically onto x in [0, kCoarse]
+// (an fp32 conversion and a product, both monotone).  Coarse bin floor(x):
+// a histogram and its scan give every coarse bin its place in the order,
+// and part q takes the coarse bins that start in [q * kk / parts,
+// (q + 1) * kk / parts), kk = min(cnt, k) (bins starting at kk or later
+// hold no rank below k).  Its keys are compacted, every coarse bin is cut
+// into as many fine bins as it holds keys, the fractional part of x (exact:
+// x - floor(x) loses no bits) picks the fine bin, and a scan and a scatter
+// group the keys by fine bin -- about one key per bin, even when a few
+// outliers stretch the range.  A key's rank is its fine bin's start plus
+// the larger keys in its bin.
+//
+// Returns false, having written nothing, when the part holds more than
+// kFinMax keys or a fine bin more than kBinRank (heavy ties); [*r0, *r1)
+// is then the part's rank range, which the caller fills another way.
+// `cand` holds kFinMax keys, `bins` kFinMax words, `red` kFinRed.
 constexpr int kBinRank = 256;
 constexpr int kCoarse = 256;
+constexpr int kCoarseSub = 4;
+constexpr int kFinRed = 64 + (2 + kCoarseSub) * kCoarse;  // words of `red`
 
-__device__ bool block_sort_desc_binned(uint64_t* cand, int cnt, uint32_t* bins, uint32_t* red) {
+// Bitonic sort (out of line: it needs its own registers): cand[0..cnt)
+// descending, kFinMax entries (zeros past cnt).
+__device__ __noinline__ void block_sort_desc_bitonic(uint64_t* cand, int cnt) {
+  const int t = threadIdx.x;
+  uint64_t key[kFinP];
+#pragma unroll
+  for (int p = 0; p < kFinP; ++p) {
+    const int i = t * kFinP + p;
+    key[p] = i < cnt ? cand[i] : 0;
+  }
+  __syncthreads();
+  block_sort_desc_regs<kFinT, kFinP>(key, cand);
+#pragma unroll
+  for (int p = 0; p < kFinP; ++p) cand[t * kFinP + p] = key[p];
+  __syncthreads();
+}
+
+// Output entry r of the sorted row from its key.
+__device__ __forceinline__ void write_ranked(uint64_t key, int r, const float* __restrict__ xr, int n,
+                                             float* __restrict__ out_vals, int32_t* __restrict__ out_idx) {
+  uint32_t idx = key_idx(key);
+  idx = idx < (uint32_t)n ? idx : 0u;  // only reachable with NaN inputs
+  out_idx[r] = (int32_t)idx;
+  // the order key gives the value back, except the sign of a zero
+  const uint32_t o = key_ord(key);
+  reinterpret_cast<uint32_t*>(out_vals)[r] =
+      o == 0x80000000u ? reinterpret_cast<const uint32_t*>(xr)[idx] : bits_from_ord(o);
+}
+
+template <int PIN>
+__device__ __forceinline__ bool sort_part_and_write(const uint64_t* __restrict__ src, int cnt, int k, int part,
+                                                    int parts, const float* __restrict__ xr, int n,
+                                                    float* __restrict__ out_vals, int32_t* __restrict__ out_idx,
+                                                    uint64_t* cand, uint32_t* bins, uint32_t* red, int* r0, int* r1) {
   constexpr int T = kFinT, P = kFinP;
   const int t = threadIdx.x;
   const int lane = lane_id();
   const int wave = t / kWave;
-  uint64_t key[P];
+  // the coarse counts (kCoarseSub copies: lane l counts into copy
+  // l mod kCoarseSub, so that the lanes of a wave whose keys crowd a few
+  // coarse bins hit more addresses), then their sums and exclusive scan
+  uint32_t* coarse = red + 64;
+  uint32_t* coarse_sub = coarse + 2 * kCoarse;
+  // key p of thread t is entry p * T + t: at one p a wave reads 64 entries
+  // in a row, which hold keys of different ranks, so the histogram atomics
+  // of one instruction spread over many bins.  Slots past np stay unused.
+  const int np = (cnt + T - 1) / T;
+  uint64_t key[PIN];
+#pragma unroll
+  for (int p = 0; p < PIN; ++p) key[p] = p < np && p * T + t < cnt ? src[p * T + t] : 0;
+  auto valid = [&](int p) { return p < np && p * T + t < cnt; };
   uint32_t lo = 0xffffffffu, hi = 0;
 #pragma unroll
-  for (int p = 0; p < P; ++p) {
-    const int i = t * P + p;
-    key[p] = i < cnt ? cand[i] : 0;
-    if (i < cnt) {
+  for (int p = 0; p < PIN; ++p) {
+    if (valid(p)) {
       lo = min(lo, key_ord(key[p]));
       hi = max(hi, key_ord(key[p]));
     }
@@ -434,7 +499,11 @@ __device__ bool block_sort_desc_binned(uint64_t* cand, int cnt, uint32_t* bins, 
     red[16 + wave] = hi;
   }
   for (int j = t; j < kFinMax; j += T) bins[j] = 0;
-  if (t == 0) red[32] = 0;  // a bin above kBinRank
+  for (int j = t; j < kCoarse * kCoarseSub; j += T) coarse_sub[j] = 0;
+  if (t == 0) {
+    red[32] = 0;  // a fine bin above kBinRank
+    red[33] = 0;  // the part's keys compacted so far
+  }
   __syncthreads();
   lo = red[0];
   hi = red[16];
@@ -442,53 +511,88 @@ __device__ bool block_sort_desc_binned(uint64_t* cand, int cnt, uint32_t* bins, 
     lo = min(lo, red[w]);
     hi = max(hi, red[16 + w]);
   }
-  const uint64_t span = (uint64_t)(hi - lo) + 1;
-  // Equi-depth bins: a coarse histogram (kCoarse bins evenly over the
-  // order-key range), then each coarse bin is cut into as many fine bins as
-  // it holds keys, evenly over its own range -- about one key per fine bin
-  // even when a few outliers stretch the range.  red[64 ..) holds the coarse
-  // counts, then their exclusive scan.
-  uint32_t* coarse = red + 64;
-  for (int j = t; j < kCoarse; j += T) coarse[j] = 0;
-  __syncthreads();
-  uint32_t cb[P];
+  const float scale = (float)kCoarse / ((float)(hi - lo) + 1.0f);
+  auto pos_of = [&](uint64_t kv) { return (float)(hi - key_ord(kv)) * scale; };
+  auto coarse_of = [&](float xv) { return min((uint32_t)xv, (uint32_t)kCoarse - 1); };
+  uint32_t* my_sub = coarse_sub + (lane % kCoarseSub) * kCoarse;
 #pragma unroll
-  for (int p = 0; p < P; ++p) {
-    cb[p] = (uint32_t)(((uint64_t)(hi - key_ord(key[p])) * kCoarse) / span);
-    hist_add(coarse, cb[p], t * P + p < cnt);
-  }
+  for (int p = 0; p < PIN; ++p)
+    if (p < np) hist_add(my_sub, coarse_of(pos_of(key[p])), valid(p));
   __syncthreads();
+  const int kk = min(cnt, k);
   if (t < kWave) {  // lane l scans coarse bins [4l, 4l + 4)
     uint32_t c4[4], s4 = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      c4[j] = coarse[4 * t + j];
+      c4[j] = 0;
+#pragma unroll
+      for (int u = 0; u < kCoarseSub; ++u) c4[j] += coarse_sub[u * kCoarse + 4 * t + j];
+      coarse[4 * t + j] = c4[j];
       s4 += c4[j];
     }
     uint32_t run = (uint32_t)wave_incl_scan((int)s4) - s4;
+    // this part's coarse bins: those starting in [cut0, cut1)
+    const uint32_t cut0 = (uint32_t)((int64_t)part * kk / parts);
+    const uint32_t cut1 = (uint32_t)((int64_t)(part + 1) * kk / parts);
+    int below0 = 0, below1 = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       coarse[kCoarse + 4 * t + j] = run;  // start of coarse bin j
+      below0 += run < cut0 ? 1 : 0;
+      below1 += run < cut1 ? 1 : 0;
       run += c4[j];
+    }
+    below0 = wave_sum(below0);
+    below1 = wave_sum(below1);
+    if (t == 0) {
+      red[34] = (uint32_t)below0;
+      red[35] = (uint32_t)below1;
     }
   }
   __syncthreads();
+  const uint32_t c0 = red[34], c1 = red[35];
+  const int start0 = c0 < (uint32_t)kCoarse ? (int)coarse[kCoarse + c0] : cnt;  // the part's first rank
+  const int count = (c1 < (uint32_t)kCoarse ? (int)coarse[kCoarse + c1] : cnt) - start0;
+  *r0 = start0;
+  *r1 = start0 + count;
+  if (count > kFinMax) return false;
+  // the part's keys to cand[0..count), one atomic per wave
+  uint32_t mine = 0, wave_keys = 0;
+#pragma unroll
+  for (int p = 0; p < PIN; ++p) {
+    if (p < np) {
+      const uint32_t c = coarse_of(pos_of(key[p]));
+      const bool in = valid(p) && c >= c0 && c < c1;
+      mine |= in ? 1u << p : 0u;
+      wave_keys += (uint32_t)__popcll(__ballot(in));
+    }
+  }
+  uint32_t at = 0;
+  if (lane == 0 && wave_keys > 0) at = atomicAdd(&red[33], wave_keys);
+  at = wave_lane0(at);
+#pragma unroll
+  for (int p = 0; p < PIN; ++p) {
+    if (p < np) {
+      const bool in = (mine >> p) & 1u;
+      const uint64_t m = __ballot(in);
+      if (in) cand[at + lanes_below(m)] = key[p];
+      at += (uint32_t)__popcll(m);
+    }
+  }
+  __syncthreads();
+  // fine bins, numbered from the part's first rank
+  uint64_t own[P];
   uint32_t bin[P];
 #pragma unroll
   for (int p = 0; p < P; ++p) {
-    const uint64_t rel = hi - key_ord(key[p]);
-    const uint32_t c = cb[p];
-    // coarse bin c covers rel in [ceil(c * span / K), ceil((c + 1) * span / K))
-    const uint64_t c_lo = (c * span + kCoarse - 1) / kCoarse;
-    const uint64_t c_hi = ((c + 1) * span + kCoarse - 1) / kCoarse;
-    const uint32_t cn = coarse[c];
-    // a monotone map of rel inside the coarse bin (the rank step below only
-    // needs the bins in value order), in fp32: rel - c_lo and the bin width
-    // stay below 2^24 + 1, so both convert exactly
-    const uint32_t f =
-        (uint32_t)((float)(uint32_t)(rel - c_lo) * (float)cn / (float)(uint32_t)max<uint64_t>(c_hi - c_lo, 1));
-    bin[p] = coarse[kCoarse + c] + min(f, cn > 0 ? cn - 1 : 0u);
-    hist_add(bins, bin[p], t * P + p < cnt);
+    const int j = p * T + t;
+    own[p] = j < count ? cand[j] : 0;
+    const float xv = pos_of(own[p]);
+    const uint32_t c = coarse_of(xv);
+    const uint32_t cn = coarse[c];  // >= 1 for a key of the part: it was counted there
+    const uint32_t f = (uint32_t)((xv - (float)c) * (float)cn);
+    bin[p] = j < count ? coarse[kCoarse + c] - (uint32_t)start0 + min(f, cn - 1) : 0u;
+    hist_add(bins, bin[p], j < count);
   }
   __syncthreads();
   // exclusive scan over the bins; thread t owns bins [t*P, t*P + P)
@@ -506,7 +610,7 @@ __device__ bool block_sort_desc_binned(uint64_t* cand, int cnt, uint32_t* bins, 
   __syncthreads();
   uint32_t before = incl - sum;
   for (int w = 0; w < wave; ++w) before += red[40 + w];
-  if (red[32] != 0) return false;  // cand untouched
+  if (red[32] != 0) return false;
 #pragma unroll
   for (int p = 0; p < P; ++p) {
     bins[t * P + p] = before;  // start of the bin: the scatter cursor
@@ -515,65 +619,33 @@ __device__ bool block_sort_desc_binned(uint64_t* cand, int cnt, uint32_t* bins, 
   __syncthreads();
 #pragma unroll
   for (int p = 0; p < P; ++p)
-    if (t * P + p < cnt) cand[atomicAdd(&bins[bin[p]], 1u)] = key[p];
+    if (p * T + t < count) cand[atomicAdd(&bins[bin[p]], 1u)] = own[p];
   __syncthreads();
   // bins[j] is now the end of bin j
   uint32_t rank[P];
 #pragma unroll
   for (int p = 0; p < P; ++p) {
     rank[p] = 0;
-    if (t * P + p < cnt) {
+    if (p * T + t < count) {
       const int s0 = bin[p] == 0 ? 0 : (int)bins[bin[p] - 1];
       const int e = (int)bins[bin[p]];
       int r = s0;
       int i = s0;
       for (; i + 4 <= e; i += 4) {
         const uint64_t a0 = cand[i], a1 = cand[i + 1], a2 = cand[i + 2], a3 = cand[i + 3];
-        r += (a0 > key[p]) + (a1 > key[p]) + (a2 > key[p]) + (a3 > key[p]);
+        r += (a0 > own[p]) + (a1 > own[p]) + (a2 > own[p]) + (a3 > own[p]);
       }
-      for (; i < e; ++i) r += cand[i] > key[p];
+      for (; i < e; ++i) r += cand[i] > own[p];
       rank[p] = (uint32_t)r;
     }
   }
   __syncthreads();
 #pragma unroll
   for (int p = 0; p < P; ++p)
-    if (t * P + p < cnt) cand[rank[p]] = key[p];
+    if (p * T + t < count) cand[rank[p]] = own[p];
   __syncthreads();
+  for (int i = t; i < count && start0 + i < k; i += T) write_ranked(cand[i], start0 + i, xr, n, out_vals, out_idx);
   return true;
-}
-
-// Bitonic fallback (out of line: it needs its own registers).
-__device__ __noinline__ void block_sort_desc_bitonic(uint64_t* cand, int cnt) {
-  const int t = threadIdx.x;
-  uint64_t key[kFinP];
-#pragma unroll
-  for (int p = 0; p < kFinP; ++p) {
-    const int i = t * kFinP + p;
-    key[p] = i < cnt ? cand[i] : 0;
-  }
-  __syncthreads();
-  block_sort_desc_regs<kFinT, kFinP>(key, cand);
-#pragma unroll
-  for (int p = 0; p < kFinP; ++p) cand[t * kFinP + p] = key[p];
-  __syncthreads();
-}
-
-// Sort cand[0..cnt) and write the first k as values (bit copies of the row)
-// and indices.
-__device__ void sort_and_write(uint64_t* cand, int cnt, int k, const float* __restrict__ xr, int n,
-                               float* __restrict__ out_vals, int32_t* __restrict__ out_idx, uint32_t* bins,
-                               uint32_t* red) {
-  if (!block_sort_desc_binned(cand, cnt, bins, red)) block_sort_desc_bitonic(cand, cnt);
-  for (int i = threadIdx.x; i < k; i += kFinT) {
-    uint32_t idx = key_idx(cand[i]);
-    idx = idx < (uint32_t)n ? idx : 0u;  // only reachable with NaN inputs
-    out_idx[i] = (int32_t)idx;
-    // the order key gives the value back, except the sign of a zero
-    const uint32_t o = key_ord(cand[i]);
-    reinterpret_cast<uint32_t*>(out_vals)[i] =
-        o == 0x80000000u ? reinterpret_cast<const uint32_t*>(xr)[idx] : bits_from_ord(o);
-  }
 }
 
 // Full-row exact top-k of an fp32 row (the fallback for rows whose
@@ -584,32 +656,34 @@ __device__ __noinline__ void row_radix_topk(const float* __restrict__ xr, int n,
   block_row_topk<kFinT>([&](int i) { return ord_f32(xb[i]); }, n, k, cand, hist, ctl);
 }
 
-// 3. final: one workgroup per row.  exact_mode: the collected keys; else
-//    the b * kb bucket candidates.
-__global__ __launch_bounds__(kFinT) void wide_final_kernel(const float* __restrict__ x, int64_t ldx, int n, int b,
-                                                          int kb, int k, int exact_mode,
-                                                          const uint64_t* __restrict__ bucket_cand,
-                                                          const int* __restrict__ row_cnt,
-                                                          const uint64_t* __restrict__ row_keys,
-                                                          float* __restrict__ out_vals, int32_t* __restrict__ out_idx) {
+// The final's other route (out of line: rows of heavy ties, a part above
+// kFinMax keys, an overflowed or failed exact collection): the row's exact
+// top-k keys into cand by a radix select, a bitonic sort, and the ranks in
+// [r0, r1) below k written out.
+__device__ __noinline__ void final_by_select(int exact_mode, const float* __restrict__ xr, int n, int k, int b,
+                                             int kb, const uint64_t* __restrict__ bucket_keys,
+                                             const uint64_t* __restrict__ keys, int cnt, uint64_t* cand,
+                                             uint32_t* bins, uint32_t* red, int r0, int r1,
+                                             float* __restrict__ ov, int32_t* __restrict__ oi) {
   constexpr int T = kFinT;
-  __shared__ uint64_t cand[kFinMax];
-  __shared__ uint32_t bins[kFinMax];
-  __shared__ uint32_t red[64 + 2 * kCoarse];
-  uint32_t* hist = bins;  // the radix selects run before the sort
-  uint32_t* ctl = bins + 256;
   const int t = threadIdx.x;
-  const int row = blockIdx.x;
-  const float* xr = x + (int64_t)row * ldx;
-  float* ov = out_vals + (int64_t)row * k;
-  int32_t* oi = out_idx + (int64_t)row * k;
-  if (exact_mode) {
-    const int cnt = row_cnt[row];
-    if (cnt > kRowCap || cnt < k) {  // overflow, or a sampled threshold above the k-th
-      row_radix_topk(xr, n, k, cand, hist, ctl);
-      sort_and_write(cand, k, k, xr, n, ov, oi, bins, red);
-      return;
+  uint32_t* hist = bins;
+  uint32_t* ctl = bins + 256;
+  __syncthreads();  // the caller's last reads of cand, bins and red are done
+  int have;
+  if (!exact_mode) {
+    cnt = b * kb;  // <= kFinMax (the plan checks it)
+    for (int i = t; i < cnt; i += T) cand[i] = bucket_keys[i];
+    __syncthreads();
+    if (cnt > k) {
+      const uint64_t kth = block_kth_key<T>(cand, cnt, k, hist, ctl);
+      cnt = block_compact_ge<T, kFinMax / T>(cand, cnt, kth, ctl);
     }
+    have = cnt;
+  } else if (cnt > kRowCap || cnt < k) {  // overflow, or a sampled threshold above the k-th
+    row_radix_topk(xr, n, k, cand, hist, ctl);
+    have = k;
+  } else {
     // k <= cnt <= kRowCap unique keys, all loaded once (kExactP per thread,
     // key i in thread i mod T): the k-th largest order word v by a radix
     // select; the k - rem keys above it are in, and of the keys equal to it
@@ -617,7 +691,6 @@ __global__ __launch_bounds__(kFinT) void wide_final_kernel(const float* __restri
     // second select on those words when more than rem tie
     // (loops over the register slots stop at np = the slots in use; the
     // leading bytes every kept key shares skip their radix passes)
-    const uint64_t* keys = row_keys + (int64_t)row * kRowCap;
     const int np = (cnt + T - 1) / T;
     uint64_t kk[kExactP];
 #pragma unroll
@@ -703,26 +776,40 @@ __global__ __launch_bounds__(kFinT) void wide_final_kernel(const float* __restri
     __syncthreads();
     const int kept = min((int)ctl[4], kFinMax);
     __syncthreads();
-    sort_and_write(cand, kept, k, xr, n, ov, oi, bins, red);
-    return;
+    have = kept;
   }
-  int cnt = b * kb;  // <= kFinMax = T * kFinP (the plan checks it)
-  {
-    // every load in flight before the first LDS store
-    const uint64_t* src = bucket_cand + (int64_t)row * cnt;
-    uint64_t v[kFinP];
-#pragma unroll
-    for (int p = 0; p < kFinP; ++p) v[p] = t + p * T < cnt ? src[t + p * T] : 0;
-#pragma unroll
-    for (int p = 0; p < kFinP; ++p)
-      if (t + p * T < cnt) cand[t + p * T] = v[p];
-  }
-  __syncthreads();
-  if (cnt > k) {
-    const uint64_t kth = block_kth_key<T>(cand, cnt, k, hist, ctl);
-    cnt = block_compact_ge<T, kFinMax / T>(cand, cnt, kth, ctl);
-  }
-  sort_and_write(cand, cnt, k, xr, n, ov, oi, bins, red);
+  block_sort_desc_bitonic(cand, have);
+  for (int i = r0 + t; i < r1 && i < k; i += T) write_ranked(cand[i], i, xr, n, ov, oi);
+}
+
+// 3. final: `parts` workgroups per row (workgroup part * rows + row), each
+//    writing the ranks of its share of the values.  exact_mode: the
+//    collected keys; else the b * kb bucket candidates.
+__global__ __launch_bounds__(kFinT) void wide_final_kernel(const float* __restrict__ x, int64_t ldx, int n, int b,
+                                                          int kb, int k, int exact_mode,
+                                                          const uint64_t* __restrict__ bucket_cand,
+                                                          const int* __restrict__ row_cnt,
+                                                          const uint64_t* __restrict__ row_keys,
+                                                          float* __restrict__ out_vals, int32_t* __restrict__ out_idx,
+                                                          int parts) {
+  __shared__ uint64_t cand[kFinMax];
+  __shared__ uint32_t bins[kFinMax];
+  __shared__ uint32_t red[kFinRed];
+  const int m = (int)gridDim.x / parts;
+  const int row = (int)blockIdx.x % m;  // the parts of a row on different XCDs
+  const int part = (int)blockIdx.x / m;
+  const float* xr = x + (int64_t)row * ldx;
+  float* ov = out_vals + (int64_t)row * k;
+  int32_t* oi = out_idx + (int64_t)row * k;
+  const uint64_t* bucket_keys = bucket_cand + (int64_t)row * b * kb;
+  const uint64_t* keys = row_keys + (int64_t)row * kRowCap;
+  const int cnt = exact_mode ? row_cnt[row] : b * kb;
+  int r0 = (int)((int64_t)part * k / parts), r1 = (int)((int64_t)(part + 1) * k / parts);
+  bool done = false;
+  if (!exact_mode || (cnt <= kRowCap && cnt >= k))
+    done = sort_part_and_write<kExactP>(exact_mode ? keys : bucket_keys, cnt, k, part, parts, xr, n, ov, oi, cand,
+                                        bins, red, &r0, &r1);
+  if (!done) final_by_select(exact_mode, xr, n, k, b, kb, bucket_keys, keys, cnt, cand, bins, red, r0, r1, ov, oi);
 }
 
 constexpr int kBufferWord3 = 0x00020000;  // buffer resource flags word (raw 32-bit loads)
@@ -1314,6 +1401,9 @@ WidePlan plan_wide(int dtype, int64_t m, int64_t n, int64_t k, int64_t b, int64_
   p.nchunks = nc;
   p.sweeps_per_chunk = (int)((nsweeps + nc - 1) / nc);
   p.blocks = m * p.groups;
+  // final: one 1024-thread workgroup holds a CU; with fewer rows than CUs a
+  // row's sort is split over up to kFinParts workgroups
+  p.final_parts = (int)std::max<int64_t>(1, std::min<int64_t>(kFinParts, kFinCUs / m));
   if (exact) {
     // one read when the list the sampled threshold is expected to keep fits
     // well inside the row's list: r = the sample's expected count of top-k
@@ -1341,14 +1431,15 @@ hipError_t launch_wide(const WidePlan& p, const float* x, int64_t m, int64_t n, 
                        bool final_exact, const WideBuffers& w, void* out_vals, int32_t* out_idx, hipStream_t s) {
   const int b = (int)p.b, kb = (int)p.kb;
   const dim3 grid((unsigned)p.blocks), block((unsigned)(kWave * p.nchunks));
+  const int fparts = p.final_parts;
   // bucketed rows whose buckets hold at most 65535 elements (16-bit
   // histogram counts): one pass over the input
   if (!exact && (n + b - 1) / b <= 65535) {
     ATOPK_LAUNCH(wide_onepass_kernel, grid, dim3(kOpW * kWave), 0, s, x, ldx, (int)n, b, kb, (int)p.groups,
                  final_exact ? 1 : 0, w.cand, static_cast<float*>(out_vals), out_idx);
     if (final_exact)
-      ATOPK_LAUNCH(wide_final_kernel, dim3((unsigned)m), dim3(kFinT), 0, s, x, ldx, (int)n, b, kb, (int)k, 0, w.cand,
-                   w.row_cnt, w.row_keys, static_cast<float*>(out_vals), out_idx);
+      ATOPK_LAUNCH(wide_final_kernel, dim3((unsigned)(m * fparts)), dim3(kFinT), 0, s, x, ldx, (int)n, b, kb, (int)k,
+                   0, w.cand, w.row_cnt, w.row_keys, static_cast<float*>(out_vals), out_idx, fparts);
     return hipGetLastError();
   }
   if (exact && p.sampled) {
@@ -1356,8 +1447,8 @@ hipError_t launch_wide(const WidePlan& p, const float* x, int64_t m, int64_t n, 
                  w.row_cnt);
     ATOPK_LAUNCH(wide_collect_row_kernel, dim3((unsigned)(m * p.row_chunks)), dim3(kCrT), 0, s, x, ldx, (int)n,
                  p.row_chunks, p.steps_per_chunk, w.rowthr, w.row_cnt, w.row_keys);
-    ATOPK_LAUNCH(wide_final_kernel, dim3((unsigned)m), dim3(kFinT), 0, s, x, ldx, (int)n, b, kb, (int)k, 1, w.cand,
-                 w.row_cnt, w.row_keys, static_cast<float*>(out_vals), out_idx);
+    ATOPK_LAUNCH(wide_final_kernel, dim3((unsigned)(m * fparts)), dim3(kFinT), 0, s, x, ldx, (int)n, b, kb, (int)k, 1,
+                 w.cand, w.row_cnt, w.row_keys, static_cast<float*>(out_vals), out_idx, fparts);
     return hipGetLastError();
   }
   if (p.kbn == 8)
@@ -1381,8 +1472,8 @@ hipError_t launch_wide(const WidePlan& p, const float* x, int64_t m, int64_t n, 
                        static_cast<float*>(out_vals), out_idx);
   }
   if (exact || final_exact)
-    ATOPK_LAUNCH(wide_final_kernel, dim3((unsigned)m), dim3(kFinT), 0, s, x, ldx, (int)n, b, kb, (int)k,
-                       exact ? 1 : 0, w.cand, w.row_cnt, w.row_keys, static_cast<float*>(out_vals), out_idx);
+    ATOPK_LAUNCH(wide_final_kernel, dim3((unsigned)(m * fparts)), dim3(kFinT), 0, s, x, ldx, (int)n, b, kb, (int)k,
+                       exact ? 1 : 0, w.cand, w.row_cnt, w.row_keys, static_cast<float*>(out_vals), out_idx, fparts);
   return hipGetLastError();
 }
 
