@@ -335,7 +335,7 @@ def test_choose(gpu, name, dtype):
 def test_certified_exact_shapes(gpu, dtype, m, n, k):
     """Shapes whose exact top-k runs as a bucketed pass plus the finish's
     certification (k above the one-row kernel's limit, or few long rows);
-    fp32 rows of 2^20 or more elements with k > 64 take the sampled wide
+    fp32 rows of 2^14 or more elements with k > 64 take the sampled wide
     route instead, which these shapes then cover."""
     x = rand_rows(m, n, dtype, m + n + k, gpu)
     rows = sorted({0, m - 1})

@@ -115,13 +115,14 @@ bool wide_exact(int dtype, int64_t m, int64_t n, int64_t k) {
 }
 
 // fp32 rows whose exact top-k the sampled one-read route takes ahead of the
-// certified route: rows of 2^20 elements or more, where its one read with a
-// cheap filter beats the certified stage 1's 64-bit key queues (2.65M-element
-// rows, k = 100: 356 -> 311 us); on shorter rows its fixed costs -- the
-// sample and a final of many short phases -- do not pay (128256-element rows,
-// k = 256: 57 against 52 us).
+// certified route: rows of 2^14 elements or more, where one read with a cheap
+// filter and a final that ranks the collected keys directly (split over up
+// to four workgroups per row) beat the certified stage 1's 64-bit key queues
+// and its rescan (64 x 128256, k = 256: 45 -> 33 us; 256 x 262144, k = 470:
+// 91 -> 70 us; 128 x 2653751, k = 100: 356 -> 281 us).  Below that the row
+// is too short for the sample's strata.
 bool wide_sampled_exact(int dtype, int64_t m, int64_t n, int64_t k) {
-  if (k <= 64 || n < ((int64_t)1 << 20)) return false;
+  if (k <= 64 || n < ((int64_t)1 << 14)) return false;
   const WidePlan p = plan_wide(dtype, m, n, k, 0, 0, true, true);
   return p.ok && p.sampled;
 }
