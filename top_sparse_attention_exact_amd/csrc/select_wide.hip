@@ -429,9 +429,9 @@ __device__ void block_sort_desc_regs(uint64_t (&key)[P], uint64_t* lds) {
 // is then the part's rank range, which the caller fills another way.
 // `cand` holds kFinMax keys, `bins` kFinMax words, `red` kFinRed.
 constexpr int kBinRank = 256;
-constexpr int kCoarse = 256;
+constexpr int kCoarse = 1024;  // one coarse bin per thread of the final
 constexpr int kCoarseSub = 4;
-constexpr int kFinRed = 64 + (2 + kCoarseSub) * kCoarse;  // words of `red`
+constexpr int kFinRed = 128 + (2 + kCoarseSub) * kCoarse;  // words of `red`
 
 // Bitonic sort (out of line: it needs its own registers): cand[0..cnt)
 // descending, kFinMax entries (zeros past cnt).
@@ -474,7 +474,8 @@ __device__ __forceinline__ bool sort_part_and_write(const uint64_t* __restrict__
   // the coarse counts (kCoarseSub copies: lane l counts into copy
   // l mod kCoarseSub, so that the lanes of a wave whose keys crowd a few
   // coarse bins hit more addresses), then their sums and exclusive scan
-  uint32_t* coarse = red + 64;
+  static_assert(kCoarse == T, "one coarse bin per thread");
+  uint32_t* coarse = red + 128;
   uint32_t* coarse_sub = coarse + 2 * kCoarse;
   // key p of thread t is entry p * T + t: at one p a wave reads 64 entries
   // in a row, which hold keys of different ranks, so the histogram atomics
@@ -520,37 +521,33 @@ __device__ __forceinline__ bool sort_part_and_write(const uint64_t* __restrict__
     if (p < np) hist_add(my_sub, coarse_of(pos_of(key[p])), valid(p));
   __syncthreads();
   const int kk = min(cnt, k);
-  if (t < kWave) {  // lane l scans coarse bins [4l, 4l + 4)
-    uint32_t c4[4], s4 = 0;
+  // coarse bin t: its count (the copies summed), then the exclusive scan
+  uint32_t cc = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      c4[j] = 0;
-#pragma unroll
-      for (int u = 0; u < kCoarseSub; ++u) c4[j] += coarse_sub[u * kCoarse + 4 * t + j];
-      coarse[4 * t + j] = c4[j];
-      s4 += c4[j];
-    }
-    uint32_t run = (uint32_t)wave_incl_scan((int)s4) - s4;
+  for (int u = 0; u < kCoarseSub; ++u) cc += coarse_sub[u * kCoarse + t];
+  const uint32_t cincl = (uint32_t)wave_incl_scan((int)cc);
+  if (lane == kWave - 1) red[40 + wave] = cincl;
+  __syncthreads();
+  uint32_t cstart = cincl - cc;
+  for (int w = 0; w < wave; ++w) cstart += red[40 + w];
+  coarse[t] = cc;
+  coarse[kCoarse + t] = cstart;
+  {
     // this part's coarse bins: those starting in [cut0, cut1)
     const uint32_t cut0 = (uint32_t)((int64_t)part * kk / parts);
     const uint32_t cut1 = (uint32_t)((int64_t)(part + 1) * kk / parts);
-    int below0 = 0, below1 = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      coarse[kCoarse + 4 * t + j] = run;  // start of coarse bin j
-      below0 += run < cut0 ? 1 : 0;
-      below1 += run < cut1 ? 1 : 0;
-      run += c4[j];
-    }
-    below0 = wave_sum(below0);
-    below1 = wave_sum(below1);
-    if (t == 0) {
-      red[34] = (uint32_t)below0;
-      red[35] = (uint32_t)below1;
+    const uint64_t m0 = __ballot(cstart < cut0), m1 = __ballot(cstart < cut1);
+    if (lane == 0) {
+      red[64 + wave] = (uint32_t)__popcll(m0);
+      red[80 + wave] = (uint32_t)__popcll(m1);
     }
   }
   __syncthreads();
-  const uint32_t c0 = red[34], c1 = red[35];
+  uint32_t c0 = 0, c1 = 0;
+  for (int w = 0; w < T / kWave; ++w) {
+    c0 += red[64 + w];
+    c1 += red[80 + w];
+  }
   const int start0 = c0 < (uint32_t)kCoarse ? (int)coarse[kCoarse + c0] : cnt;  // the part's first rank
   const int count = (c1 < (uint32_t)kCoarse ? (int)coarse[kCoarse + c1] : cnt) - start0;
   *r0 = start0;
@@ -829,10 +826,11 @@ __device__ __forceinline__ void wave_sync_lds() {
 // 1024 elements) gives one 16-element chunk at a pseudo-random offset, so
 // every element of the strata has the same chance to be drawn, whatever the
 // row's structure.  The threshold is the r-th largest of the maxima of the
-// 4096 groups of four consecutive samples -- at most the r-th largest
-// sample, since r groups hold a sample at or above it -- with r above the
-// sample's expected count of top-k elements by a wide margin, so that the
-// row almost surely holds k elements at or above it.  The collect
+// 4096 groups of four consecutive samples, rounded down to a multiple of 256
+// order steps -- at most the r-th largest sample, since r groups hold a
+// sample at or above it -- with r above the sample's expected count of
+// top-k elements by a wide margin, so that the row almost surely holds k
+// elements at or above it.  The collect
 // then keeps every element at or above it in one contiguous read, and the
 // final takes the exact top-k of the kept keys -- or, when fewer than k were
 // kept (the margin failed) or the list overflowed, a full-row exact select.
@@ -852,11 +850,73 @@ __device__ __forceinline__ uint32_t mix32(uint32_t v) {  // an integer hash (xor
   return v;
 }
 
+// The r-th largest of the T * G order words o[] (G per thread, r <= T * G)
+// with its low 8 bits cleared: a lower bound of it, at most 255 order steps
+// below, from two 12-bit radix passes (bits 31..20, then bits 19..8 of the
+// words that match the first digit) -- half the passes of a full 8-bit
+// select.  hist: 4096 words, ctl: 2 + T / 64 words.
+template <int T, int G>
+__device__ uint32_t block_kth32_floor(const uint32_t (&o)[G], int r, uint32_t* hist, uint32_t* ctl) {
+  constexpr int NB = 4096, Q = NB / T;  // bins per thread
+  const int t = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = t / kWave;
+  uint32_t prefix = 0, mask = 0;
+  int rem = r;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int shift = pass == 0 ? 20 : 8;
+    for (int i = t; i < NB; i += T) hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const uint32_t d = (o[j] >> shift) & 0xfffu;
+      if (pass == 0)
+        hist_add_grouped(hist, d, true);  // the leading digit crowds a few bins
+      else
+        hist_add(hist, d, (o[j] & mask) == prefix);
+    }
+    __syncthreads();
+    // thread t owns the Q bins below NB - Q t, high digits first
+    uint32_t h[Q];
+    int sum = 0;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      h[q] = hist[NB - 1 - Q * t - q];
+      sum += (int)h[q];
+    }
+    const int incl = wave_incl_scan(sum);
+    if (lane == kWave - 1) ctl[2 + wave] = (uint32_t)incl;
+    __syncthreads();
+    int acc = incl - sum;
+    for (int w = 0; w < wave; ++w) acc += (int)ctl[2 + w];
+    if (acc < rem && rem <= acc + sum) {
+      int d = -1;
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        if (d < 0) {
+          if (acc + (int)h[q] >= rem)
+            d = NB - 1 - Q * t - q;
+          else
+            acc += (int)h[q];
+        }
+      }
+      ctl[0] = (uint32_t)d;
+      ctl[1] = (uint32_t)(rem - acc);
+    }
+    __syncthreads();
+    prefix |= ctl[0] << shift;
+    mask |= 0xfffu << shift;
+    rem = (int)ctl[1];
+  }
+  return prefix;
+}
+
 __global__ __launch_bounds__(kSampleT) void wide_sample_kernel(const float* __restrict__ x, int64_t ldx, int n,
                                                               int r_sel, float* __restrict__ rowthr,
                                                               int* __restrict__ row_cnt) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t ctl[4];
+  __shared__ uint32_t hist[4096];
+  __shared__ uint32_t ctl[2 + kSampleT / kWave];
   const int row = blockIdx.x;
   const int t = threadIdx.x;
   const int st = n / kSampleT;  // stratum length, >= kSampleChunk
@@ -868,14 +928,7 @@ __global__ __launch_bounds__(kSampleT) void wide_sample_kernel(const float* __re
 #pragma unroll
   for (int j = 0; j < G; ++j)
     o[j] = max(max(ord_f32(xs[4 * j]), ord_f32(xs[4 * j + 1])), max(ord_f32(xs[4 * j + 2]), ord_f32(xs[4 * j + 3])));
-  int rem;
-  const uint32_t v = block_radix_kth32<kSampleT>(
-      r_sel, hist, ctl,
-      [&](uint32_t mask, uint32_t prefix, int shift) {
-#pragma unroll
-        for (int j = 0; j < G; ++j) hist_add_grouped(hist, (o[j] >> shift) & 255u, (o[j] & mask) == prefix);
-      },
-      &rem);
+  const uint32_t v = block_kth32_floor<kSampleT, G>(o, r_sel, hist, ctl);
   if (t == 0) {
     rowthr[row] = __uint_as_float(bits_from_ord(v));
     row_cnt[row] = 0;
