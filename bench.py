@@ -285,15 +285,20 @@ def selection_kernels(workload, mode, m, n, k, es, width):
     return [], []
 
 
-def decode_kernels(c, mode, group):
+def decode_kernels(c, mode, group, nkernels=2):
     """Scoring + stage 1, then the finish.  Both workloads plan at most one
     (head, bucket) pair per thread (the scoring kernel's first template
-    argument); the exact Top-K runs the certified plan with k_b = 8."""
+    argument); the exact Top-K runs the certified plan with k_b = 8.  One
+    kernel: the scoring workgroups finished their heads in place (b k_b = K,
+    one workgroup per head), so that kernel carries the V gather and the
+    output too."""
     kbytes = c["bsz"] * c["hkv"] * c["ctx"] * c["d"] * 2
     qbytes = c["bsz"] * c["hq"] * c["d"] * 2
     vbytes = c["bsz"] * c["hq"] * c["k_sel"] * c["d"] * 2
     score = "decode_select_mfma_kernel<1, %d>" if group > 1 else "decode_select_kernel<1, %d>"
     kb = c["kb"] if mode == "bucketed" else 8
+    if nkernels == 1:
+        return [score % kb], [kbytes + 2 * qbytes + vbytes]
     return [score % kb, "decode_finish_kernel<%d>" % kb], [kbytes + qbytes, vbytes + qbytes]
 
 
@@ -417,7 +422,7 @@ def run_decode(args, timer, name):
              "scores_per_s": c["bsz"] * c["hq"] * c["ctx"] / t}
         if not args.no_stages:
             st_us, _ = stage_split(fn, steps, timer.spin)
-            names, algs = decode_kernels(c, mode, group)
+            names, algs = decode_kernels(c, mode, group, len(st_us))
             d["stages"] = describe_stages(names, algs, st_us)
         res["modes"][mode] = d
     if cand is not None:

@@ -716,6 +716,35 @@ def test_decode_exact_without_scores_matches(gpu, hq, hkv, planted):
     assert torch.equal(out1, out2)
 
 
+def test_decode_in_place_finish_matches_finish_kernel(gpu):
+    """With one query head per KV head, one context chunk per head and
+    b * k_b = K, the scoring workgroup finishes its head itself (512 heads:
+    one workgroup each).  The first half of the same batch alone has 256
+    heads and is planned in bucket ranges, whose lists go to the separate
+    finish kernel: the same candidates, so sel_idx and the output must agree
+    bit for bit, with and without the selection output."""
+    g = torch.Generator(device=gpu).manual_seed(5)
+    bsz, h, ctx, k_sel, b, kb = 16, 32, 8192, 512, 256, 2
+    q = torch.randn((bsz, h, 128), generator=g, device=gpu).to(torch.bfloat16)
+    K = torch.randn((bsz, h, ctx, 128), generator=g, device=gpu).to(torch.bfloat16)
+    V = torch.randn((bsz, h, ctx, 128), generator=g, device=gpu).to(torch.bfloat16)
+    out, sel = atk.sparse_attn_decode(q, K, V, k_sel, b, kb, return_sel=True)
+    out_only = atk.sparse_attn_decode(q, K, V, k_sel, b, kb)
+    half = bsz // 2
+    ref, rsel = atk.sparse_attn_decode(q[:half].contiguous(), K[:half].contiguous(), V[:half].contiguous(), k_sel, b,
+                                       kb, return_sel=True)
+    assert torch.equal(sel[:half], rsel)
+    assert torch.equal(out[:half], ref)
+    assert torch.equal(out_only, out)
+    # and the selection is the oracle's on the kernel's own scores for a few heads
+    _, _, sc = atk.sparse_attn_decode(q[:1].contiguous(), K[:1].contiguous(), V[:1].contiguous(), k_sel, b, kb,
+                                      return_sel=True, return_scores=True)
+    got = sc.cpu().numpy()
+    for hh in (0, 17, 31):
+        own = oracle.attention.select(got[0, hh][None].astype(np.float64), k_sel, b, kb)[0]
+        assert np.array_equal(sel[0, hh].cpu().numpy(), own)
+
+
 def test_decode_ctx_stride(gpu):
     g = torch.Generator(device="cpu").manual_seed(3)
     q = torch.randn((1, 4, 128), generator=g).to(torch.bfloat16).to(gpu)

@@ -21,7 +21,12 @@
 // so its lists are final.  A workgroup visits its steps in a rotated order,
 // so that the workgroups in flight read different offsets of their ranges.
 // Scores never go to HBM unless a debug dump is asked for.  Each workgroup
-// writes its per-pair lists to the workspace.
+// writes its per-pair lists to the workspace -- except when one workgroup
+// holds every candidate of its query head and the b*k_b candidates are the
+// selection (b*k_b = K, one context chunk, one query head per KV head): then
+// it runs kernel 2's softmax and value sum itself, right after its own
+// scoring, while other workgroups still stream (no second launch; the same
+// order of every floating-point sum, so the same output bits).
 //
 // With b = 0 kernel 1 only writes every score (the exact Top-K route selects
 // on the written scores).
@@ -43,6 +48,9 @@ constexpr int kT1 = 256;
 constexpr int kSub = 512;          // keys staged per step
 constexpr int kSubPad = kSub + 1;  // LDS row pitch (heads on different banks)
 constexpr int kMaxG = 8;
+constexpr int kStableMax = 1024;  // selections up to this size are summed in compaction order
+constexpr int kVGroups = 32;      // 16-lane groups of the finish's softmax-V sums (kernel 2's 512 threads / 16)
+constexpr int kVU = 16;           // V rows in flight per lane group
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -129,19 +137,112 @@ __device__ __forceinline__ void merge_parts(uint64_t (&qq)[KB], int tpp) {
   }
 }
 
+// Kernel 2's work for a head whose candidates one workgroup of T threads holds
+// (queue i of thread t: bucket t + T i) and whose b*k_b candidates are the
+// selection: candidates to LDS in kernel 2's layout (slot r k_b + j), sel_idx
+// by rank counting, the maximum score, then the weighted V sums in kernel 2's
+// 32 lane groups (lane group g of this workgroup takes groups g, g + T/16, ...,
+// each with kernel 2's row order and in-flight batch) and the same final sum
+// over the groups.  `lds` holds at least 2 (kStableMax + 16) + 32 (kD + 1) + 16
+// floats, 16-byte aligned; the caller's last reads of it are done.
+template <int T, int PPT, int KB>
+__device__ __forceinline__ void finish_in_place(const uint64_t (&qq)[PPT][KB], int b, int kb, float* lds,
+                                                const uint16_t* __restrict__ vh, uint16_t* __restrict__ outp,
+                                                int32_t* __restrict__ selp) {
+  uint64_t* cand = reinterpret_cast<uint64_t*>(lds);
+  float (*acc_lds)[kD] = reinterpret_cast<float (*)[kD]>(lds + 2 * (kStableMax + 16));
+  float* w_lds = lds + 2 * (kStableMax + 16) + kVGroups * kD;
+  float* red = w_lds + kVGroups;
+  const int t = threadIdx.x;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < PPT; ++i) {
+    const int r = t + T * i;
+    if (r < b) {
+#pragma unroll
+      for (int j = 0; j < KB; ++j)
+        if (j < kb) cand[r * kb + j] = qq[i][j];
+    }
+  }
+  __syncthreads();
+  const int n = b * kb;
+  if (selp != nullptr) {
+    const int n16 = block_pad16(cand, n);
+    __syncthreads();
+    for (int c = t; c < n; c += T) selp[count_above16(cand, n16, cand[c])] = (int32_t)key_idx(cand[c]);
+  }
+  float mx = -INFINITY;
+  for (int i = t; i < n; i += T) mx = fmaxf(mx, key_value_f32(cand[i]));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+  if (lane_id() == 0) red[t / kWave] = mx;
+  __syncthreads();
+  mx = red[0];
+#pragma unroll
+  for (int w = 1; w < T / kWave; ++w) mx = fmaxf(mx, red[w]);
+  const int sub = t & 15;
+  const uint16_t* vrow = vh + sub * 8;
+  for (int group = t >> 4; group < kVGroups; group += T / 16) {
+    float acc[8];
+#pragma unroll
+    for (int d = 0; d < 8; ++d) acc[d] = 0.0f;
+    float wsum = 0.0f;
+    for (int i = group; i < n; i += kVGroups * kVU) {
+      uint4 v[kVU];
+      float w[kVU];
+#pragma unroll
+      for (int u = 0; u < kVU; ++u) {
+        const int ii = i + kVGroups * u;
+        const uint64_t key = ii < n ? cand[ii] : 0;
+        v[u] = key != 0 ? *reinterpret_cast<const uint4*>(vrow + (int64_t)key_idx(key) * kD) : make_uint4(0, 0, 0, 0);
+        w[u] = key != 0 ? expf(key_value_f32(key) - mx) : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < kVU; ++u) {
+        const uint32_t word[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          acc[2 * d] += w[u] * __uint_as_float(word[d] << 16);
+          acc[2 * d + 1] += w[u] * __uint_as_float(word[d] & 0xffff0000u);
+        }
+        wsum += w[u];
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < 8; ++d) acc_lds[group][sub * 8 + d] = acc[d];
+    if (sub == 0) w_lds[group] = wsum;
+  }
+  __syncthreads();
+  if (t < kD) {
+    float sum = 0.0f, wt = 0.0f;
+#pragma unroll
+    for (int gg = 0; gg < kVGroups; ++gg) {
+      sum += acc_lds[gg][t];
+      wt += w_lds[gg];
+    }
+    outp[t] = f32_to_bf16_rne(sum / wt);
+  }
+}
+
 // PPT (head, bucket) pairs per thread, KB queue slots per pair.  Context
 // chunks (lgR < 0) or bucket ranges (lgR >= 0, tpp threads per pair), as in
-// decode_select_mfma_kernel below.
+// decode_select_mfma_kernel below.  finish != 0: the head's softmax-V in
+// place (finish_in_place; one chunk, G = 1, b*kb = K <= kStableMax).
 template <int PPT, int KB>
 __global__ __launch_bounds__(kT1) void decode_select_kernel(const uint16_t* __restrict__ q,
                                                            const uint16_t* __restrict__ K, int hq, int hkv,
                                                            int ctx, int64_t ctx_stride, float scale, int b,
                                                            int64_t chunk, int nchunks, int lgR, int tpp,
                                                            uint64_t* __restrict__ partial,
-                                                           float* __restrict__ scores) {
+                                                           float* __restrict__ scores, int finish, int kb,
+                                                           const uint16_t* __restrict__ V,
+                                                           uint16_t* __restrict__ out,
+                                                           int32_t* __restrict__ sel_idx, int k_sel) {
   constexpr int U = 8;                 // keys in flight per 16-lane group
   constexpr int PASSES = kSub / (16 * U);
-  __shared__ float sc[2][kMaxG][kSubPad];
+  __shared__ alignas(16) float sc[2][kMaxG][kSubPad];
+  static_assert(sizeof(sc) >= sizeof(float) * (2 * (kStableMax + 16) + kVGroups * (kD + 1) + 16),
+                "the in-place finish fits in the staged-score tile");
 
   const int t = threadIdx.x;
   const int sub = t & 15;   // 16-byte slice of a key row
@@ -239,6 +340,11 @@ __global__ __launch_bounds__(kT1) void decode_select_kernel(const uint16_t* __re
 #pragma unroll
       for (int j = 0; j < KB; ++j) dst[j] = qq[0][j];
     }
+    return;
+  }
+  if (finish) {
+    finish_in_place<kT1, PPT, KB>(qq, b, kb, &sc[0][0][0], V + (int64_t)bh * ctx_stride * kD,
+                                  out + (int64_t)bh * kD, sel_idx != nullptr ? sel_idx + (int64_t)bh * k_sel : nullptr);
     return;
   }
 #pragma unroll
@@ -418,8 +524,7 @@ __global__ __launch_bounds__(kT1M, 2) void decode_select_mfma_kernel(const uint1
 
 constexpr int kT2 = 512;
 constexpr int kMaxCand = 8192;
-constexpr int kStableMax = 1024;  // selections up to this size are summed in compaction order
-constexpr int kVGroups = kT2 / 16;  // 16-lane groups gathering V rows
+static_assert(kVGroups == kT2 / 16, "kernel 2 sums in one group per 16 of its threads");
 
 constexpr int kFlagMax = 256;  // flagged buckets rescanned in LDS; more take the full-row fallback
 
@@ -887,7 +992,8 @@ hipError_t launch_decode_scores(const uint16_t* q, const uint16_t* K, int64_t ba
                        ctx_stride, scale, 0, p.chunk, p.nchunks, -1, 1, nullptr, scores);
   else
     ATOPK_LAUNCH((decode_select_kernel<1, 1>), g1, dim3(kT1), 0, s, q, K, (int)hq, (int)hkv, (int)ctx,
-                       ctx_stride, scale, 0, p.chunk, p.nchunks, -1, 1, nullptr, scores);
+                       ctx_stride, scale, 0, p.chunk, p.nchunks, -1, 1, nullptr, scores, 0, 1, nullptr, nullptr,
+                       nullptr, 0);
   return hipGetLastError();
 }
 
@@ -899,6 +1005,10 @@ hipError_t launch_decode_fused(const DecodePlan& p, const uint16_t* q, const uin
   if (certify && certify != (p.mfma ? 1 : 2)) return hipErrorInvalidValue;  // the rescan repeats kernel 1's arithmetic
   const int kbs = kb_pow2(kb);
   dim3 g1((unsigned)p.nsplit, (unsigned)(batch * hkv));
+  // one workgroup holds every candidate of its head and they are the
+  // selection: the scoring kernel finishes the head itself
+  const int in_place = !p.mfma && p.lgR < 0 && p.nchunks == 1 && hq == hkv && b * kb == k_sel && certify == 0 &&
+                       k_sel <= kStableMax;
 #define ATOPK_D1(P, KBV)                                                                                            \
   if (p.ppt == P && kbs == KBV) {                                                                                   \
     if (p.mfma)                                                                                                     \
@@ -906,7 +1016,8 @@ hipError_t launch_decode_fused(const DecodePlan& p, const uint16_t* q, const uin
                          (int)ctx, ctx_stride, scale, (int)b, p.chunk, p.nchunks, p.lgR, p.tpp, partial, scores);    \
     else                                                                                                            \
       ATOPK_LAUNCH((decode_select_kernel<P, KBV>), g1, dim3(kT1), 0, s, q, K, (int)hq, (int)hkv, (int)ctx,     \
-                         ctx_stride, scale, (int)b, p.chunk, p.nchunks, p.lgR, p.tpp, partial, scores);              \
+                         ctx_stride, scale, (int)b, p.chunk, p.nchunks, p.lgR, p.tpp, partial, scores, in_place,     \
+                         (int)kb, V, out, sel_idx, (int)k_sel);                                                     \
   } else
   ATOPK_D1(1, 1) ATOPK_D1(1, 2) ATOPK_D1(1, 4) ATOPK_D1(1, 8) ATOPK_D1(1, 16)
   ATOPK_D1(2, 1) ATOPK_D1(2, 2) ATOPK_D1(2, 4) ATOPK_D1(2, 8) ATOPK_D1(2, 16)
@@ -915,7 +1026,7 @@ hipError_t launch_decode_fused(const DecodePlan& p, const uint16_t* q, const uin
   { return hipErrorInvalidValue; }
 #undef ATOPK_D1
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || in_place) return e;
   dim3 g2((unsigned)(batch * hq));
 #define ATOPK_D2(KBV)                                                                                              \
   case KBV:                                                                                                        \

@@ -1055,10 +1055,11 @@ __global__ __launch_bounds__(kCrT) void wide_collect_row_kernel(const float* __r
 // lane l is bucket 64 * g + l -- and its 8 waves take interleaved batches of
 // sweeps, so every element of a bucket passes through the workgroup that
 // owns it.  Per bucket, in LDS:
-//  - a window [lo, lo + span] of order keys: lo is the k_b-th largest of the
-//    bucket's 256 first samples (k_b elements of the bucket reach it, so its
-//    k_b-th largest does too), the window's top half its width above their
-//    largest, where the bucket's k_b-th largest often lies;
+//  - a window [lo, lo + span] of order keys: of the bucket's 256 first
+//    samples each wave keeps the four largest of its 32, and lo is the k_b-th
+//    largest of those 32 (k_b elements of the bucket reach it, so its k_b-th
+//    largest does too); the window's top sits half its width above the
+//    largest sample, where the bucket's k_b-th largest often lies;
 //  - a histogram of the window (64 bins, two 16-bit counts per word);
 //  - thr, the highest bin whose count together with the bins above reaches
 //    k_b, refreshed at a few points of the stream.  Counts only grow, so thr
@@ -1206,19 +1207,21 @@ __global__ __launch_bounds__(kOpW * kWave) void wide_onepass_kernel(const float*
   if (nbatch > 1) load(wb, 1);
   if (nbatch > 2) load(wc, 2);  // in flight while the window is computed
 
-  // the window: the k_b-th largest and the largest of each bucket's first
-  // two batches (256 samples), the value lists of the W waves merged into
-  // the first of them
+  // the window, from each bucket's first two batches (256 samples): every
+  // lane keeps the four largest of its 32, the waves' lists merge into the
+  // first wave (top 16), and lo is the k_b-th largest of the merged list --
+  // k_b distinct elements of the bucket reach it
   {
-    float q[kWideKB];
-#pragma unroll
-    for (int j = 0; j < kWideKB; ++j) q[j] = -INFINITY;
+    float q4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     const bool full0 = full(0), full1 = nbatch > 1 && full(1);
 #pragma unroll
-    for (int u = 0; u < kOpU; ++u) fnet_insert<kWideKB>(q, (full0 || live(sweep_of(0, u))) ? wa[u] : -INFINITY);
+    for (int u = 0; u < kOpU; ++u) fnet_insert<4>(q4, (full0 || live(sweep_of(0, u))) ? wa[u] : -INFINITY);
 #pragma unroll
     for (int u = 0; u < kOpU; ++u)
-      fnet_insert<kWideKB>(q, (full1 || (nbatch > 1 && live(sweep_of(1, u)))) ? wb[u] : -INFINITY);
+      fnet_insert<4>(q4, (full1 || (nbatch > 1 && live(sweep_of(1, u)))) ? wb[u] : -INFINITY);
+    float q[kWideKB];
+#pragma unroll
+    for (int j = 0; j < kWideKB; ++j) q[j] = j < 4 ? q4[j] : -INFINITY;
     float* mbuf = reinterpret_cast<float*>(&S.logk[0][0]);
     for (int half = kOpW / 2; half >= 1; half /= 2) {
       if (sw >= half && sw < 2 * half) {
