@@ -938,20 +938,24 @@ __global__ __launch_bounds__(kSampleT) void wide_sample_kernel(const float* __re
 // Collect: workgroup (row, c) -- the chunks of a row on different XCDs --
 // reads steps [c * spc, (c + 1) * spc) of the row (step s: elements s *
 // kCrStep + u * kCrT + t) in order, two steps of loads in flight behind the
-// one it filters; an element
-// at or above the row's threshold goes to the row's key list through the
-// wave's LDS buffer, which holds a whole step's worth above its flush mark,
-// so that it is flushed between steps only (one atomic on the row's counter
-// per flush; the waves' last keys take one atomic between them).
-constexpr int kCrMark = 192;                     // flush above this many keys (two workgroups per CU)
-constexpr int kCrBuf = kCrMark + kCrU * kWave;  // + one step's worth
+// one it filters.  An element at or above the row's threshold goes to the
+// wave's LDS buffer; a buffer past its mark moves to the workgroup's LDS list
+// (one LDS atomic), and at the end the list goes to the row's key list with
+// one atomic on the row's counter per workgroup.  (Atomics on one global
+// counter from many workgroups are slow here -- they serialise across the
+// XCDs -- so none are taken while the loads stream.)  Keys beyond the list's
+// capacity go to the row's list directly, with an atomic of their own.
+constexpr int kCrMark = 192;                 // move a wave's buffer above this many keys
+constexpr int kCrBuf = kCrMark + kWave;      // + one instruction's worth
+constexpr int kCrList = 6144;                // keys per workgroup list (48 KiB)
 __global__ __launch_bounds__(kCrT) void wide_collect_row_kernel(const float* __restrict__ x, int64_t ldx, int n,
                                                                int chunks, int spc, const float* __restrict__ rowthr,
                                                                int* __restrict__ row_cnt,
                                                                uint64_t* __restrict__ row_keys) {
   constexpr int W = kCrT / kWave;
   __shared__ uint64_t wbuf[W][kCrBuf];
-  __shared__ uint32_t wg_off[W];
+  __shared__ uint64_t wg_list[kCrList];
+  __shared__ uint32_t wg_n;
   __shared__ uint32_t wg_base;
   const int row = (int)blockIdx.x / chunks;
   const int c = (int)blockIdx.x % chunks;
@@ -967,14 +971,25 @@ __global__ __launch_bounds__(kCrT) void wide_collect_row_kernel(const float* __r
   const int s_begin = c * spc;
   const int ns = max(0, min(nsteps_row, s_begin + spc) - s_begin);
   auto phys = [&](int i) { return s_begin + i; };
+  if (t == 0) wg_n = 0;
+  __syncthreads();
   int fill = 0;  // wave-uniform
-  auto flush = [&]() {
+  // the wave's buffer to the workgroup list; what does not fit goes to the
+  // row's list
+  auto move = [&]() {
     wave_sync_lds();
-    int base = 0;
-    if (lane == 0) base = atomicAdd(&row_cnt[row], fill);
-    base = (int)wave_lane0((uint32_t)base);
-    for (int j = lane; j < fill; j += kWave)
-      if (base + j < kRowCap) out[base + j] = buf[j];
+    uint32_t base = 0;
+    if (lane == 0) base = atomicAdd(&wg_n, (uint32_t)fill);
+    base = wave_lane0(base);
+    const int fit = (int)min((uint32_t)fill, base < (uint32_t)kCrList ? (uint32_t)kCrList - base : 0u);
+    for (int j = lane; j < fit; j += kWave) wg_list[base + j] = buf[j];
+    if (fit < fill) {
+      int gb = 0;
+      if (lane == 0) gb = atomicAdd(&row_cnt[row], fill - fit);
+      gb = (int)wave_lane0((uint32_t)gb);
+      for (int j = fit + lane; j < fill; j += kWave)
+        if (gb + j - fit < kRowCap) out[gb + j - fit] = buf[j];
+    }
     wave_sync_lds();
     fill = 0;
   };
@@ -983,6 +998,7 @@ __global__ __launch_bounds__(kCrT) void wide_collect_row_kernel(const float* __r
     if (m) {
       if (keep) buf[fill + (int)lanes_below(m)] = make_key(ord_f32(__float_as_uint(v)), idx);
       fill += __popcll(m);
+      if (fill > kCrMark) move();
     }
   };
   float wa[kCrU], wb[kCrU], wc[kCrU];
@@ -1001,7 +1017,6 @@ __global__ __launch_bounds__(kCrT) void wide_collect_row_kernel(const float* __r
     }
   };
   auto filt = [&](const float (&w)[kCrU], int i) {
-    if (fill > kCrMark) flush();
     const int s = phys(i);
     const uint32_t i0 = (uint32_t)s * kCrStep + (uint32_t)t;
     if (s < full_steps) {
@@ -1031,22 +1046,14 @@ __global__ __launch_bounds__(kCrT) void wide_collect_row_kernel(const float* __r
       filt(wc, i + 2);
     }
   }
-  // the waves' last keys: offsets inside the workgroup, one atomic in all
-  if (lane == 0) wg_off[wave] = (uint32_t)fill;
+  if (fill > 0) move();
   __syncthreads();
-  if (t == 0) {
-    uint32_t tot = 0;
-    for (int w2 = 0; w2 < W; ++w2) {
-      const uint32_t cw = wg_off[w2];
-      wg_off[w2] = tot;
-      tot += cw;
-    }
-    wg_base = tot ? (uint32_t)atomicAdd(&row_cnt[row], (int)tot) : 0u;
-  }
+  const int tot = (int)min(wg_n, (uint32_t)kCrList);
+  if (t == 0) wg_base = tot ? (uint32_t)atomicAdd(&row_cnt[row], tot) : 0u;
   __syncthreads();
-  const int base = (int)(wg_base + wg_off[wave]);
-  for (int j = lane; j < fill; j += kWave)
-    if (base + j < kRowCap) out[base + j] = buf[j];
+  const int base = (int)wg_base;
+  for (int j = t; j < tot; j += kCrT)
+    if (base + j < kRowCap) out[base + j] = wg_list[j];
 }
 
 // ---- one-pass stage 1 (bucketed, b a multiple of 64, k_b <= 16) ----------
