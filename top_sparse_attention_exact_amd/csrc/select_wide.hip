@@ -1478,7 +1478,11 @@ WidePlan plan_wide(int dtype, int64_t m, int64_t n, int64_t k, int64_t b, int64_
     p.sample_r = (int)r;
     p.sampled = n / kSampleT >= kSampleChunk && r * (double)n / S <= 0.75 * kRowCap;
     const int64_t nsteps_row = (n + kCrStep - 1) / kCrStep;
-    int64_t chunks = std::min<int64_t>(std::max<int64_t>(1, (512 + m - 1) / m), nsteps_row);
+    // collect workgroups: about 512 in all, and chunks of at most 512 KiB
+    // (longer chunks leave the last co-resident workgroups streaming alone:
+    // 128 rows of 2653751 with 4 chunks each, 289 us; with 21, 268 us)
+    int64_t chunks = std::min<int64_t>(
+        std::max<int64_t>({(int64_t)1, (512 + m - 1) / m, (n * 4 + (512 << 10) - 1) / (512 << 10)}), nsteps_row);
     const int64_t spc = (nsteps_row + chunks - 1) / chunks;
     p.steps_per_chunk = (int)spc;
     p.row_chunks = (int)((nsteps_row + spc - 1) / spc);
