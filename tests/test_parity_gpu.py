@@ -777,6 +777,15 @@ def test_decode_mha32k_all_heads(gpu):
             assert kept == np.minimum(t, c["kb"]).sum()
     del out, sel, sc
     _decode_check(q, K, V, c["k_sel"], 1, c["k_sel"])
+    # The certified route is one function of the inputs: repeated calls, with
+    # and without the selection output, give the same bits.  (Its select once
+    # returned a threshold that the finish then overwrote in LDS before every
+    # thread had read it; that showed in about one call in eight.)
+    out0, sel0 = atk.sparse_attn_decode(q, K, V, c["k_sel"], 1, c["k_sel"], return_sel=True)
+    for _ in range(6):
+        out1, sel1 = atk.sparse_attn_decode(q, K, V, c["k_sel"], 1, c["k_sel"], return_sel=True)
+        assert torch.equal(sel1, sel0) and torch.equal(out1, out0)
+        assert torch.equal(atk.sparse_attn_decode(q, K, V, c["k_sel"], 1, c["k_sel"]), out0)
 
 
 @pytest.mark.timeout(900)

@@ -557,7 +557,9 @@ __device__ __forceinline__ uint64_t block_kth_key_binned(const uint64_t* keys, i
     }
   }
   __syncthreads();
-  return ((uint64_t)ctl[5] << 32) | ctl[4];
+  const uint64_t res = ((uint64_t)ctl[5] << 32) | ctl[4];
+  __syncthreads();  // every thread has read ctl before a caller reuses it
+  return res;
 }
 
 // Sort keys[0..n_pow2) descending in LDS (bitonic network).
