@@ -781,7 +781,10 @@ __device__ __noinline__ void final_by_select(int exact_mode, const float* __rest
 
 // 3. final: `parts` workgroups per row (workgroup part * rows + row), each
 //    writing the ranks of its share of the values.  exact_mode: the
-//    collected keys; else the b * kb bucket candidates.
+//    collected keys (up to PIN = kExactP register slots per thread, fewer
+//    when the row kept fewer keys); else the b * kb <= kFinMax bucket
+//    candidates (PIN = kFinP).
+template <int PIN>
 __global__ __launch_bounds__(kFinT) void wide_final_kernel(const float* __restrict__ x, int64_t ldx, int n, int b,
                                                           int kb, int k, int exact_mode,
                                                           const uint64_t* __restrict__ bucket_cand,
@@ -803,9 +806,23 @@ __global__ __launch_bounds__(kFinT) void wide_final_kernel(const float* __restri
   const int cnt = exact_mode ? row_cnt[row] : b * kb;
   int r0 = (int)((int64_t)part * k / parts), r1 = (int)((int64_t)(part + 1) * k / parts);
   bool done = false;
-  if (!exact_mode || (cnt <= kRowCap && cnt >= k))
-    done = sort_part_and_write<kExactP>(exact_mode ? keys : bucket_keys, cnt, k, part, parts, xr, n, ov, oi, cand,
-                                        bins, red, &r0, &r1);
+  // the fewest register slots that hold the row's keys: the sort's loops
+  // over the slots are unrolled, so unused slots still cost time
+  auto sort = [&](auto pin_c) {
+    constexpr int P = decltype(pin_c)::value;
+    return sort_part_and_write<P>(exact_mode ? keys : bucket_keys, cnt, k, part, parts, xr, n, ov, oi, cand, bins,
+                                  red, &r0, &r1);
+  };
+  if (!exact_mode) {
+    done = sort(std::integral_constant<int, PIN>{});
+  } else if (cnt <= kRowCap && cnt >= k) {
+    if (PIN > kFinP && cnt <= kFinP * kFinT)
+      done = sort(std::integral_constant<int, kFinP>{});
+    else if (PIN > 2 * kFinP && cnt <= 2 * kFinP * kFinT)
+      done = sort(std::integral_constant<int, 2 * kFinP>{});
+    else
+      done = sort(std::integral_constant<int, PIN>{});
+  }
   if (!done) final_by_select(exact_mode, xr, n, k, b, kb, bucket_keys, keys, cnt, cand, bins, red, r0, r1, ov, oi);
 }
 
@@ -1505,8 +1522,8 @@ hipError_t launch_wide(const WidePlan& p, const float* x, int64_t m, int64_t n, 
     ATOPK_LAUNCH(wide_onepass_kernel, grid, dim3(kOpW * kWave), 0, s, x, ldx, (int)n, b, kb, (int)p.groups,
                  final_exact ? 1 : 0, w.cand, static_cast<float*>(out_vals), out_idx);
     if (final_exact)
-      ATOPK_LAUNCH(wide_final_kernel, dim3((unsigned)(m * fparts)), dim3(kFinT), 0, s, x, ldx, (int)n, b, kb, (int)k,
-                   0, w.cand, w.row_cnt, w.row_keys, static_cast<float*>(out_vals), out_idx, fparts);
+      ATOPK_LAUNCH(wide_final_kernel<kFinP>, dim3((unsigned)(m * fparts)), dim3(kFinT), 0, s, x, ldx, (int)n, b, kb,
+                   (int)k, 0, w.cand, w.row_cnt, w.row_keys, static_cast<float*>(out_vals), out_idx, fparts);
     return hipGetLastError();
   }
   if (exact && p.sampled) {
@@ -1514,7 +1531,8 @@ hipError_t launch_wide(const WidePlan& p, const float* x, int64_t m, int64_t n, 
                  w.row_cnt);
     ATOPK_LAUNCH(wide_collect_row_kernel, dim3((unsigned)(m * p.row_chunks)), dim3(kCrT), 0, s, x, ldx, (int)n,
                  p.row_chunks, p.steps_per_chunk, w.rowthr, w.row_cnt, w.row_keys);
-    ATOPK_LAUNCH(wide_final_kernel, dim3((unsigned)(m * fparts)), dim3(kFinT), 0, s, x, ldx, (int)n, b, kb, (int)k, 1,
+    ATOPK_LAUNCH(wide_final_kernel<kExactP>, dim3((unsigned)(m * fparts)), dim3(kFinT), 0, s, x, ldx, (int)n, b, kb,
+                 (int)k, 1,
                  w.cand, w.row_cnt, w.row_keys, static_cast<float*>(out_vals), out_idx, fparts);
     return hipGetLastError();
   }
@@ -1538,9 +1556,12 @@ hipError_t launch_wide(const WidePlan& p, const float* x, int64_t m, int64_t n, 
                        p.sweeps_per_chunk, final_exact ? 1 : 0, w.thr, w.need, w.cand,
                        static_cast<float*>(out_vals), out_idx);
   }
-  if (exact || final_exact)
-    ATOPK_LAUNCH(wide_final_kernel, dim3((unsigned)(m * fparts)), dim3(kFinT), 0, s, x, ldx, (int)n, b, kb, (int)k,
-                       exact ? 1 : 0, w.cand, w.row_cnt, w.row_keys, static_cast<float*>(out_vals), out_idx, fparts);
+  if (exact)
+    ATOPK_LAUNCH(wide_final_kernel<kExactP>, dim3((unsigned)(m * fparts)), dim3(kFinT), 0, s, x, ldx, (int)n, b, kb,
+                 (int)k, 1, w.cand, w.row_cnt, w.row_keys, static_cast<float*>(out_vals), out_idx, fparts);
+  else if (final_exact)
+    ATOPK_LAUNCH(wide_final_kernel<kFinP>, dim3((unsigned)(m * fparts)), dim3(kFinT), 0, s, x, ldx, (int)n, b, kb,
+                 (int)k, 0, w.cand, w.row_cnt, w.row_keys, static_cast<float*>(out_vals), out_idx, fparts);
   return hipGetLastError();
 }
 
