@@ -696,7 +696,9 @@ __device__ __forceinline__ void decode_rescan_mfma(const uint16_t* qg, int G, in
 // with the 16-lane dot products.  Past kFlagMax flagged buckets, or past the
 // LDS candidate array, the workgroup recomputes every score of its head into
 // its row of `scores` ([B*Hq, ctx] workspace) and selects from that row.
-template <int KB>
+// MP: register slots per thread of the bucketed route's compaction (b*kb <=
+// kT2 * MP candidates); the certification keeps kMaxCand / kT2.
+template <int KB, int MP>
 __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(4))) void decode_finish_kernel(const uint64_t* __restrict__ partial, int nchunks, int hq,
                                                            int hkv, int b, int kb, int k_sel,
                                                            const uint16_t* __restrict__ V, int64_t ctx_stride,
@@ -839,7 +841,7 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(4))) void d
     }
   } else if (n > k_sel) {
     const uint64_t thr = block_kth_key_binned<T>(cand, n, k_sel, hist, ctl);
-    n = block_compact_ge_stable<T, kMaxCand / T>(cand, n, thr, hist);
+    n = block_compact_ge_stable<T, MP>(cand, n, thr, hist);
   }
   sorted = sorted || n > kStableMax;
   const uint64_t* sel = sorted ? block_order_desc<T>(cand, n, kMaxCand) : cand;
@@ -1030,9 +1032,14 @@ hipError_t launch_decode_fused(const DecodePlan& p, const uint16_t* q, const uin
   dim3 g2((unsigned)(batch * hq));
 #define ATOPK_D2(KBV)                                                                                              \
   case KBV:                                                                                                        \
-    ATOPK_LAUNCH((decode_finish_kernel<KBV>), g2, dim3(kT2), 0, s, partial, p.nchunks, (int)hq, (int)hkv,     \
-                       (int)b, (int)kb, (int)k_sel, V, ctx_stride, out, sel_idx, certify, cert_buf, (int)ctx, q, K, \
-                       scale);                                                                                      \
+    if (!certify && b * kb <= (int64_t)kT2 * 4)                                                                    \
+      ATOPK_LAUNCH((decode_finish_kernel<KBV, 4>), g2, dim3(kT2), 0, s, partial, p.nchunks, (int)hq, (int)hkv,    \
+                   (int)b, (int)kb, (int)k_sel, V, ctx_stride, out, sel_idx, certify, cert_buf, (int)ctx, q, K,     \
+                   scale);                                                                                         \
+    else                                                                                                           \
+      ATOPK_LAUNCH((decode_finish_kernel<KBV, kMaxCand / kT2>), g2, dim3(kT2), 0, s, partial, p.nchunks, (int)hq,  \
+                   (int)hkv, (int)b, (int)kb, (int)k_sel, V, ctx_stride, out, sel_idx, certify, cert_buf, (int)ctx, \
+                   q, K, scale);                                                                                   \
     break;
   switch (kbs) {
     ATOPK_D2(1) ATOPK_D2(2) ATOPK_D2(4) ATOPK_D2(8) ATOPK_D2(16)
