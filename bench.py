@@ -299,7 +299,8 @@ def decode_kernels(c, mode, group, nkernels=2):
     kb = c["kb"] if mode == "bucketed" else 8
     if nkernels == 1:
         return [score % kb], [kbytes + 2 * qbytes + vbytes]
-    mp = 4 if mode == "bucketed" and c["b"] * kb <= 2048 else 16  # the finish's compaction slots per thread
+    nb = c["b"] if mode == "bucketed" else 256  # the certified plan's b on both decode workloads
+    mp = 4 if nb * kb <= 2048 else 16  # the finish's compaction slots per thread
     return [score % kb, "decode_finish_kernel<%d, %d>" % (kb, mp)], [kbytes + qbytes, vbytes + qbytes]
 
 

@@ -696,8 +696,9 @@ __device__ __forceinline__ void decode_rescan_mfma(const uint16_t* qg, int G, in
 // with the 16-lane dot products.  Past kFlagMax flagged buckets, or past the
 // LDS candidate array, the workgroup recomputes every score of its head into
 // its row of `scores` ([B*Hq, ctx] workspace) and selects from that row.
-// MP: register slots per thread of the bucketed route's compaction (b*kb <=
-// kT2 * MP candidates); the certification keeps kMaxCand / kT2.
+// MP: register slots per thread of the compaction of the b*kb <= kT2 * MP
+// candidates; the certification's second compaction (after a rescan) keeps
+// kMaxCand / kT2.
 template <int KB, int MP>
 __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(4))) void decode_finish_kernel(const uint64_t* __restrict__ partial, int nchunks, int hq,
                                                            int hkv, int b, int kb, int k_sel,
@@ -789,7 +790,7 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(4))) void d
         }
       }
     }
-    n = block_compact_ge_stable<T, kMaxCand / T>(cand, n, thr, hist);  // k_sel keys
+    n = block_compact_ge_stable<T, MP>(cand, n, thr, hist);  // k_sel keys
     const int nflag = (int)ctl[5];
     if (nflag > 0) {
       bool overflow = nflag > kFlagMax;
@@ -1032,7 +1033,7 @@ hipError_t launch_decode_fused(const DecodePlan& p, const uint16_t* q, const uin
   dim3 g2((unsigned)(batch * hq));
 #define ATOPK_D2(KBV)                                                                                              \
   case KBV:                                                                                                        \
-    if (!certify && b * kb <= (int64_t)kT2 * 4)                                                                    \
+    if (b * kb <= (int64_t)kT2 * 4)                                                                                \
       ATOPK_LAUNCH((decode_finish_kernel<KBV, 4>), g2, dim3(kT2), 0, s, partial, p.nchunks, (int)hq, (int)hkv,    \
                    (int)b, (int)kb, (int)k_sel, V, ctx_stride, out, sel_idx, certify, cert_buf, (int)ctx, q, K,     \
                    scale);                                                                                         \

@@ -1496,8 +1496,8 @@ WidePlan plan_wide(int dtype, int64_t m, int64_t n, int64_t k, int64_t b, int64_
     p.sampled = n / kSampleT >= kSampleChunk && r * (double)n / S <= 0.75 * kRowCap;
     const int64_t nsteps_row = (n + kCrStep - 1) / kCrStep;
     // collect workgroups: about 512 in all, and chunks of at most 512 KiB
-    // (longer chunks leave the last co-resident workgroups streaming alone:
-    // 128 rows of 2653751 with 4 chunks each, 289 us; with 21, 268 us)
+    // (128 rows of 2653751 elements: 4 chunks per row took 289 us, 21 took
+    // 268 us; 256 KiB chunks on 64 rows of 2^20 were slower than 512 KiB)
     int64_t chunks = std::min<int64_t>(
         std::max<int64_t>({(int64_t)1, (512 + m - 1) / m, (n * 4 + (512 << 10) - 1) / (512 << 10)}), nsteps_row);
     const int64_t spc = (nsteps_row + chunks - 1) / chunks;
