@@ -106,6 +106,21 @@ def test_exact_shapes(gpu, dtype, n):
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("n", [64, 520, 1024, 1536, 3000, 4096, 8192 - 8])
+def test_exact_short_aligned_rows(gpu, dtype, n):
+    # 16-byte aligned rows with k <= 64 take the one-workgroup row kernel; a
+    # row shorter than one pass of its 16 waves (4096 fp32 / 8192 bf16
+    # elements) leaves the last waves without elements, and the first-tile
+    # bound is pooled over the waves that hold some
+    x = rand_rows(5, n, dtype, 40 + n, gpu)
+    for k in sorted({1, 2, 17, min(n, 63), min(n, 64)}):
+        check_exact(x, k)
+    xt = workloads.rows_ties_bf16(3, n, 4, seed=n, device="cpu").to(dtype).to(gpu)
+    for k in sorted({1, 33, min(n, 64)}):
+        check_exact(xt, k)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_exact_large_k(gpu, dtype):
     x = rand_rows(2, 40000, dtype, 5, gpu)
     for k in (2047, 2049, 5000, 8192):

@@ -14,9 +14,10 @@
 // Exact (same page, "The reading"; Figures 11-14 on radix select and its
 // tie "collect" step): the row is streamed once through a threshold filter.
 // The first tile seeds the threshold with a provable lower bound of the k-th
-// largest value -- in each of the 16 waves the ceil(k/16)-th largest of its
-// 64 lane maxima; 16*ceil(k/16) >= k distinct elements reach the smallest of
-// those -- so from the start only a small fraction of elements is appended
+// largest value -- in each of the a waves that hold elements (16 unless the
+// row is short) the ceil(k/a)-th largest of its 64 lane maxima; a*ceil(k/a)
+// >= k distinct elements reach the smallest of those -- so from the start
+// only a small fraction of elements is appended
 // to the LDS candidate buffer, which is compacted by radix select when full.
 #include <type_traits>
 
@@ -428,7 +429,13 @@ __global__ __launch_bounds__(kRowT) void row_exact_kernel(const uint8_t* __restr
   const int row = blockIdx.x;
   const uint8_t* xr = x + (int64_t)row * ld_bytes;
   uint64_t* mine = buf + wave * kWaveRegion;
-  const int cpw = (k + kRowWaves - 1) / kRowWaves;  // lane maxima each wave vouches for
+  // Waves that hold elements: on a row shorter than one pass of the block
+  // the last waves hold none, and a bound pooled over them would be 0.
+  // Each of the `act` waves vouches for ceil(k / act) <= 64 lane maxima; the
+  // others publish no bound.
+  const int64_t waves_n = ((int64_t)n + kWave * V - 1) / (kWave * V);
+  const int act = waves_n < kRowWaves ? (int)waves_n : kRowWaves;
+  const int cpw = (k + act - 1) / act;  // lane maxima each wave vouches for
 
   uint32_t lmax = 0;  // largest order key this lane has seen
   uint32_t thr = 1;   // filter: order key >= thr (real keys are >= 0x00800000)
@@ -452,11 +459,11 @@ __global__ __launch_bounds__(kRowT) void row_exact_kernel(const uint8_t* __restr
       }
       lmax = max(lmax, vm[u]);
     }
-    // The c-th largest lane maximum of each wave, c = ceil(k / 16): 16 * c
-    // >= k distinct elements reach the smallest of the 16 published values.
-    // The first tile waits once for every wave to publish: the pooled bound
-    // is far tighter than any one wave's.
-    const uint32_t tc = wave_cth_largest(lmax, cpw);
+    // The c-th largest lane maximum of each active wave, c = ceil(k / act):
+    // act * c >= k distinct elements reach the smallest of the published
+    // values.  The first tile waits once for every wave to publish: the
+    // pooled bound is far tighter than any one wave's.
+    const uint32_t tc = wave < act ? wave_cth_largest(lmax, cpw) : 0xffffffffu;
     if (lane == 0) pub_store(wave, tc);
     if (first) {
       lds_barrier();
