@@ -111,13 +111,18 @@ def test_exact_short_aligned_rows(gpu, dtype, n):
     # 16-byte aligned rows with k <= 64 take the one-workgroup row kernel; a
     # row shorter than one pass of its 16 waves (4096 fp32 / 8192 bf16
     # elements) leaves the last waves without elements, and the first-tile
-    # bound is pooled over the waves that hold some
+    # bound is pooled over the waves that hold some.  k > 64 takes the kernel
+    # that ranks a row of at most 8192 elements whole in LDS.
     x = rand_rows(5, n, dtype, 40 + n, gpu)
-    for k in sorted({1, 2, 17, min(n, 63), min(n, 64)}):
+    for k in sorted({1, 2, 17, min(n, 63), min(n, 64), min(n, 65), min(n, 300), min(n, 1025), n}):
         check_exact(x, k)
     xt = workloads.rows_ties_bf16(3, n, 4, seed=n, device="cpu").to(dtype).to(gpu)
-    for k in sorted({1, 33, min(n, 64)}):
+    for k in sorted({1, 33, min(n, 64), min(n, 200), n}):
         check_exact(xt, k)
+    # odd row strides (not 16-byte aligned): every k takes the whole-row kernel
+    xs = rand_rows(4, n + 3, dtype, 7 + n, gpu)[:, 1:n + 1]
+    for k in sorted({1, min(n, 64), min(n, 500)}):
+        check_exact(xs, k)
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
@@ -346,7 +351,7 @@ def test_choose(gpu, name, dtype):
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("m,n,k", [(1, 1 << 20, 100), (2, 300007, 256), (64, 128256, 256), (3, 70001, 16),
-                                   (1, 4_000_003, 64), (5, 5000, 300)])
+                                   (1, 4_000_003, 64), (5, 9000, 300)])
 def test_certified_exact_shapes(gpu, dtype, m, n, k):
     """Shapes whose exact top-k runs as a bucketed pass plus the finish's
     certification (k above the one-row kernel's limit, or few long rows);

@@ -158,6 +158,7 @@ int run_certified(const CertPlan& c, const void* x, int dtype, int64_t m, int64_
                   void* out_vals, int32_t* out_idx, void* ws, hipStream_t s);
 
 size_t exact_ws_bytes(int dtype, int64_t m, int64_t n, int64_t k) {
+  if (row_small_exact_ok(dtype, m, n, k)) return 0;
   if (wide_sampled_exact(dtype, m, n, k)) return wide_layout(dtype, m, n, k, 0, 0, true, true).total;
   const CertPlan cert = plan_certified(dtype, m, n, k);
   if (cert.ok) return certified_ws_bytes(dtype, m, n, cert);
@@ -178,6 +179,8 @@ int run_exact(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, int64
   const int64_t es = dtype == ATOPK_F32 ? 4 : 2;
   if (row_exact_ok(dtype, m, n, k, rows_aligned(x, ldx, es)))
     return hip_status(launch_row_exact(x, dtype, m, n, ldx, k, out_vals, out_idx, s));
+  if (row_small_exact_ok(dtype, m, n, k))
+    return hip_status(launch_row_small_exact(x, dtype, m, n, ldx, k, out_vals, out_idx, s));
   if (wide_sampled_exact(dtype, m, n, k))
     return run_wide(wide_layout(dtype, m, n, k, 0, 0, true, true), x, m, n, ldx, k, true, true, out_vals, out_idx, ws,
                     s);

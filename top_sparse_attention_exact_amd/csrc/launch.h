@@ -79,6 +79,11 @@ hipError_t launch_exact(const ExactPlan& p, const void* x, int in_kind, int64_t 
 
 bool row_bucket_ok(int dtype, int64_t m, int64_t n, int64_t b, int64_t kb, bool aligned);
 bool row_exact_ok(int dtype, int64_t m, int64_t n, int64_t k, bool aligned);
+// Rows of at most 8192 elements, any alignment and any k: the whole row is
+// ranked in LDS by one workgroup.
+bool row_small_exact_ok(int dtype, int64_t m, int64_t n, int64_t k);
+hipError_t launch_row_small_exact(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k,
+                                  void* out_vals, int32_t* out_idx, hipStream_t s);
 hipError_t launch_row_bucket(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k, int64_t b,
                              int64_t kb, int final_exact, void* out_vals, int32_t* out_idx, hipStream_t s);
 hipError_t launch_row_exact(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k, void* out_vals,

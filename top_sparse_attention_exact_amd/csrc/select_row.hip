@@ -710,6 +710,55 @@ __global__ __launch_bounds__(kRowT) void row_contig_kernel(const uint8_t* __rest
   }
 }
 
+// Exact top-k of a row that fits LDS whole (n <= kRowLds / 8 elements, any
+// alignment, any k <= n): every element becomes an (order key, index) key
+// and the block's radix select and exact final rank them: one read of the
+// row and no threshold filter.  Short rows with k above the filtering kernel's limit
+// otherwise pay several launches for a few KiB.
+constexpr int kRowSmallMaxN = kRowLds / 8;
+
+template <int DT>
+__global__ __launch_bounds__(kRowT) void row_small_exact_kernel(const uint8_t* __restrict__ x, int64_t ld_bytes,
+                                                               int n, int k, uint8_t* __restrict__ out_vals,
+                                                               int32_t* __restrict__ out_idx) {
+  __shared__ uint64_t cand[kRowSmallMaxN];
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t ctl[8];
+  const int row = blockIdx.x;
+  const uint8_t* xr = x + (int64_t)row * ld_bytes;
+  for (int i = threadIdx.x; i < n; i += kRowT) {
+    uint32_t o;
+    if constexpr (DT == IN_F32)
+      o = ord_f32(reinterpret_cast<const uint32_t*>(xr)[i]);
+    else
+      o = ord_bf16x2((uint32_t)reinterpret_cast<const uint16_t*>(xr)[i]) << 16;
+    cand[i] = make_key(o, (uint32_t)i);
+  }
+  __syncthreads();
+  // Above 256 keys, select the k-th key and keep the k keys that reach it
+  // first: the final then ranks or sorts k keys instead of the whole row.
+  int cnt = n;
+  if (n > 256 && k < n) {
+    const uint64_t thr = block_kth_key<kRowT>(cand, n, k, hist, ctl);
+    cnt = block_compact_ge<kRowT, kRowSmallMaxN / kRowT>(cand, n, thr, ctl);
+  }
+  block_final(cand, cnt, k, hist, ctl, [&](int i, uint64_t kk) {
+    // the order key gives the value back, except the sign of a zero
+    const uint32_t idx = key_idx(kk);
+    const uint32_t o = key_ord(kk);
+    const int64_t at = (int64_t)row * k + i;
+    out_idx[at] = (int32_t)idx;
+    if constexpr (DT == IN_F32) {
+      reinterpret_cast<uint32_t*>(out_vals)[at] =
+          o == 0x80000000u ? reinterpret_cast<const uint32_t*>(xr)[idx] : bits_from_ord(o);
+    } else {
+      const uint32_t o16 = o >> 16;
+      reinterpret_cast<uint16_t*>(out_vals)[at] =
+          o16 == 0x8000u ? reinterpret_cast<const uint16_t*>(xr)[idx] : bf16_from_ord16(o16);
+    }
+  });
+}
+
 }  // namespace
 
 bool row_bucket_ok(int dtype, int64_t m, int64_t n, int64_t b, int64_t kb, bool aligned) {
@@ -726,6 +775,12 @@ bool row_bucket_ok(int dtype, int64_t m, int64_t n, int64_t b, int64_t kb, bool 
 bool row_exact_ok(int dtype, int64_t m, int64_t n, int64_t k, bool aligned) {
   if (!aligned || k > kRowExactMaxK) return false;
   return m >= 128 || n <= 65536;
+}
+
+bool row_small_exact_ok(int dtype, int64_t m, int64_t n, int64_t k) {
+  (void)m;
+  (void)k;
+  return (dtype == IN_F32 || dtype == IN_BF16) && n <= kRowSmallMaxN;
 }
 
 hipError_t launch_row_bucket(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k, int64_t b,
@@ -797,6 +852,21 @@ hipError_t launch_row_contig(const void* x, int dtype, int64_t m, int64_t n, int
   } else {
     if (final_exact) launch_contig_kb<IN_BF16, true>(kbs, grid, s, xb, ldx * es, n, b, kb, k, vec, pack, ov, out_idx);
     else launch_contig_kb<IN_BF16, false>(kbs, grid, s, xb, ldx * es, n, b, kb, k, vec, pack, ov, out_idx);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_row_small_exact(const void* x, int dtype, int64_t m, int64_t n, int64_t ldx, int64_t k,
+                                  void* out_vals, int32_t* out_idx, hipStream_t s) {
+  if (n > kRowSmallMaxN || k > n) return hipErrorInvalidValue;
+  dim3 grid((unsigned)m);
+  const uint8_t* xb = static_cast<const uint8_t*>(x);
+  uint8_t* ov = static_cast<uint8_t*>(out_vals);
+  if (dtype == IN_F32) {
+    ATOPK_LAUNCH((row_small_exact_kernel<IN_F32>), grid, dim3(kRowT), 0, s, xb, ldx * 4, (int)n, (int)k, ov, out_idx);
+  } else {
+    ATOPK_LAUNCH((row_small_exact_kernel<IN_BF16>), grid, dim3(kRowT), 0, s, xb, ldx * 2, (int)n, (int)k, ov,
+                 out_idx);
   }
   return hipGetLastError();
 }
