@@ -304,6 +304,58 @@ __device__ __noinline__ void finish_row_fallback(const uint8_t* xr, int dt, int 
 
 constexpr int kFlagMax = 256;  // flagged buckets rescanned in LDS; more take the full-row fallback
 
+// Sort keys[0..n_pow2) (LDS) descending, n_pow2 a power of two in [128,
+// kFinishMaxCand]: each wave first sorts runs of 64 in registers, storing the
+// odd runs ascending, so that every pair of runs is a bitonic sequence; then
+// come the bitonic merges of sizes 128 .. n_pow2.  Stages with a stride of 64
+// or more run in LDS, one barrier each; the six stages below pair keys inside
+// one run of 64, which a wave merges in registers by shuffles (the direction
+// is the same for the whole run).  After the merges of one size, the blocks
+// of that size alternate descending / ascending, and the last size leaves the
+// whole array descending.  Strides are powers of two, so the pair index
+// arithmetic is shifts and masks.
+template <int T>
+__device__ void finish_sort_desc(uint64_t* keys, int n_pow2) {
+  constexpr int NW = T / kWave;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid / kWave;
+  __syncthreads();
+  for (int r = wave; r < n_pow2 / kWave; r += NW) {
+    const uint64_t v = wave_sort64_desc(keys[r * kWave + lane]);
+    keys[r * kWave + ((r & 1) ? kWave - 1 - lane : lane)] = v;
+  }
+  for (int size = 2 * kWave; size <= n_pow2; size <<= 1) {
+    for (int ls = __builtin_ctz((unsigned)size) - 1; (1 << ls) >= kWave; --ls) {
+      __syncthreads();
+      const int stride = 1 << ls;
+      for (int i = tid; i < (n_pow2 >> 1); i += T) {
+        const int lo = ((i >> ls) << (ls + 1)) | (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool desc = (lo & size) == 0;
+        const uint64_t a = keys[lo], c = keys[hi];
+        if (desc ? (a < c) : (a > c)) {
+          keys[lo] = c;
+          keys[hi] = a;
+        }
+      }
+    }
+    __syncthreads();
+    for (int r = wave; r < n_pow2 / kWave; r += NW) {
+      uint64_t v = keys[r * kWave + lane];
+      const bool desc = ((r * kWave) & size) == 0;
+#pragma unroll
+      for (int j = kWave / 2; j > 0; j >>= 1) {
+        const uint64_t o = shfl_xor_u64(v, j);
+        const bool keep_max = ((lane & j) == 0) == desc;
+        v = keep_max ? (v > o ? v : o) : (v < o ? v : o);
+      }
+      keys[r * kWave + lane] = v;
+    }
+  }
+  __syncthreads();
+}
+
 // mode 3 (certified exact top-k from the bucket candidates).  With T the
 // k-th largest candidate key: a true top-k element e missing from the
 // candidates was dropped by its bucket, so that bucket kept k_b keys above
@@ -491,7 +543,7 @@ __global__ __launch_bounds__(kFinishThreads) void bucket_finish_kernel(const uin
   int npow = 1;
   while (npow < k) npow <<= 1;
   for (int i = cnt + t; i < npow; i += T) cand[i] = 0;
-  block_sort_desc<T>(cand, npow);
+  finish_sort_desc<T>(cand, npow);  // npow >= 2048 here (k > T)
   for (int j = t; j < k; j += T) write_result(out_vals, out_idx, (int64_t)row * k + j, xr, dt, cand[j]);
 }
 
