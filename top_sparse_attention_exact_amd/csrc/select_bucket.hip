@@ -534,16 +534,10 @@ __global__ __launch_bounds__(kFinishThreads) void bucket_finish_kernel(const uin
     }
     return;
   }
-  if (cnt <= T) {  // waves sort runs of 64 and each key's rank is found by binary search
-    block_sortmerge_final<T>(cand, cand, cnt, k, [&](int j, uint64_t key) {
-      write_result(out_vals, out_idx, (int64_t)row * k + j, xr, dt, key);
-    });
-    return;
-  }
   int npow = 1;
   while (npow < k) npow <<= 1;
   for (int i = cnt + t; i < npow; i += T) cand[i] = 0;
-  finish_sort_desc<T>(cand, npow);  // npow >= 2048 here (k > T)
+  finish_sort_desc<T>(cand, npow);  // npow >= 128 here (k >= cnt > 64)
   for (int j = t; j < k; j += T) write_result(out_vals, out_idx, (int64_t)row * k + j, xr, dt, cand[j]);
 }
 
