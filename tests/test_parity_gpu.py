@@ -222,9 +222,9 @@ def test_bucketed_few_rows_many_splits(gpu, m, n):
 @pytest.mark.parametrize("dtype,m,n", [(torch.float32, 3, 50000), (torch.float32, 1, 16384 + 5),
                                       (torch.bfloat16, 2, 70001)])
 def test_bucketed_final_large_k(gpu, dtype, m, n):
-    """Split-row finish with more than 1024 survivors: runs of 64 sorted in
-    registers, then bitonic merges in LDS (k = b * k_b keeps every candidate,
-    without the select).  k <= 1024 takes the run sort and merge."""
+    """Split-row finish sorting many survivors (64 < k <= 8192): runs of 64
+    sorted in registers, then bitonic merges in LDS and by shuffles (k = b *
+    k_b keeps every candidate, without the select)."""
     x = rand_rows(m, n, dtype, 60 + m + n, gpu)
     for b, kb, k in [(2048, 1, 2000), (4096, 2, 5000), (8192, 1, 8192), (4096, 2, 1024), (1024, 1, 1000),
                      (2048, 4, 1025)]:
